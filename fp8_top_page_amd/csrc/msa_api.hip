@@ -1,0 +1,254 @@
+// C-ABI entry points: host-side validation, workspace sizing and launches.
+// Every check runs before any HIP call, so each error path can be exercised
+// without a GPU.  Unsupported configurations return MSA_ERR_UNSUPPORTED, the
+// analogue of the indexer's admission rule (vLLM PR 60930, Details: the CuTe
+// scorer is admitted only for E4M3, D128, page 128, H in {1,2,4} per rank and
+// sparse_local_block >= 1; otherwise the caller keeps another backend).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+
+#include "msa_internal.h"
+
+using namespace msa;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+msa_status_t fail(msa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+msa_status_t hip_fail(hipError_t e, const char* where) {
+  return fail(MSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define MSA_CHECK(cond, st, ...) \
+  do {                           \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+msa_status_t check_varlen(const msa_varlen_t* vl) {
+  MSA_CHECK(vl != nullptr, MSA_ERR_INVALID_ARGUMENT, "varlen descriptor is NULL");
+  MSA_CHECK(vl->batch >= 1, MSA_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", vl->batch);
+  MSA_CHECK(vl->total_q >= 0 && vl->max_seqlen_q >= 0 && vl->max_seqlen_k >= 0 &&
+                vl->total_rows >= 0 && vl->max_pages >= 0,
+            MSA_ERR_INVALID_ARGUMENT, "negative size in varlen descriptor");
+  MSA_CHECK(vl->max_seqlen_q <= vl->max_seqlen_k, MSA_ERR_INVALID_ARGUMENT,
+            "max_seqlen_q (%d) exceeds max_seqlen_k (%d)", vl->max_seqlen_q, vl->max_seqlen_k);
+  MSA_CHECK(vl->total_q == 0 || vl->max_seqlen_q >= 1, MSA_ERR_INVALID_ARGUMENT,
+            "total_q > 0 needs max_seqlen_q >= 1");
+  MSA_CHECK((int64_t)vl->max_pages * kPage >= vl->max_seqlen_k, MSA_ERR_INVALID_ARGUMENT,
+            "max_pages (%d) cannot hold max_seqlen_k (%d)", vl->max_pages, vl->max_seqlen_k);
+  MSA_CHECK((int64_t)vl->total_q <= (int64_t)vl->batch * vl->max_seqlen_q,
+            MSA_ERR_INVALID_ARGUMENT, "total_q exceeds batch * max_seqlen_q");
+  MSA_CHECK((int64_t)vl->total_rows <= (int64_t)vl->batch * vl->max_pages,
+            MSA_ERR_INVALID_ARGUMENT, "total_rows exceeds batch * max_pages");
+  MSA_CHECK(vl->cu_seqlens_q && vl->cu_seqlens_k && vl->block_table, MSA_ERR_INVALID_ARGUMENT,
+            "cu_seqlens_q, cu_seqlens_k and block_table must be non-NULL");
+  MSA_CHECK(vl->block_table_stride >= vl->max_pages, MSA_ERR_INVALID_ARGUMENT,
+            "block_table_stride (%lld) < max_pages (%d)", (long long)vl->block_table_stride,
+            vl->max_pages);
+  return MSA_OK;
+}
+
+msa_status_t check_device() {
+  static const int n_dev = [] {
+    int n = 0;
+    return hipGetDeviceCount(&n) == hipSuccess ? n : 0;
+  }();
+  if (n_dev == 0) return fail(MSA_ERR_NO_DEVICE, "no HIP device available");
+  return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* msa_status_string(msa_status_t st) {
+  switch (st) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_INVALID_ARGUMENT: return "MSA_ERR_INVALID_ARGUMENT";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED";
+    case MSA_ERR_WORKSPACE_TOO_SMALL: return "MSA_ERR_WORKSPACE_TOO_SMALL";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP";
+    case MSA_ERR_NO_DEVICE: return "MSA_ERR_NO_DEVICE";
+  }
+  return "MSA_ERR_UNKNOWN";
+}
+
+const char* msa_last_error(void) { return g_last_error; }
+
+int32_t msa_abi_version(void) { return MSA_ABI_VERSION; }
+
+// ---------------------------------------------------------------------------
+size_t msa_index_score_workspace_size(const msa_varlen_t* vl, int32_t num_index_heads) {
+  if (!vl || vl->batch < 1 || vl->total_q < 0 || vl->max_pages < 0) return 0;
+  if (num_index_heads != 1 && num_index_heads != 2 && num_index_heads != 4) return 0;
+  return score_plan(vl, num_index_heads).workspace_bytes;
+}
+
+msa_status_t msa_index_score(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
+                             int32_t num_index_heads, const uint8_t* k_cache, int32_t num_pages,
+                             const float* q_scale, const float* k_scale, float* scores,
+                             int64_t ld_scores, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  msa_status_t st = check_varlen(vl);
+  if (st != MSA_OK) return st;
+  const int H = num_index_heads;
+  MSA_CHECK(H == 1 || H == 2 || H == 4, MSA_ERR_UNSUPPORTED,
+            "num_index_heads must be 1, 2 or 4 (got %d)", H);
+  if (vl->total_q == 0) return MSA_OK;   // nothing to score
+  MSA_CHECK(q && k_cache && q_scale && k_scale && scores && workspace, MSA_ERR_INVALID_ARGUMENT,
+            "NULL pointer argument");
+  MSA_CHECK(q_stride >= (int64_t)H * kDim && q_stride % 16 == 0, MSA_ERR_INVALID_ARGUMENT,
+            "q_stride must be >= H*128 and a multiple of 16 (got %lld)", (long long)q_stride);
+  MSA_CHECK(aligned(q, 16) && aligned(k_cache, 16), MSA_ERR_INVALID_ARGUMENT,
+            "q and k_cache must be 16-byte aligned");
+  MSA_CHECK(num_pages >= 1, MSA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
+  MSA_CHECK(ld_scores >= vl->max_pages && ld_scores >= 1, MSA_ERR_INVALID_ARGUMENT,
+            "ld_scores (%lld) < max_pages (%d)", (long long)ld_scores, vl->max_pages);
+  MSA_CHECK(aligned(workspace, 256), MSA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  const ScorePlan plan = score_plan(vl, H);
+  MSA_CHECK(workspace_bytes >= plan.workspace_bytes, MSA_ERR_WORKSPACE_TOO_SMALL,
+            "workspace has %zu bytes, needs %zu", workspace_bytes, plan.workspace_bytes);
+  MSA_CHECK(plan.max_items < (int64_t)INT32_MAX, MSA_ERR_UNSUPPORTED, "batch too large");
+  st = check_device();
+  if (st != MSA_OK) return st;
+  ScoreArgs a{*vl, q, q_stride, H, k_cache, num_pages, q_scale, k_scale,
+              scores, ld_scores, workspace, plan};
+  hipError_t e = launch_index_score(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "msa_index_score");
+  return MSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+msa_status_t msa_topk_select(const msa_varlen_t* vl, const float* scores, int64_t ld_scores,
+                             int32_t topk, int32_t n_local, int32_t* topk_idx,
+                             int64_t topk_stride, void* stream) {
+  msa_status_t st = check_varlen(vl);
+  if (st != MSA_OK) return st;
+  MSA_CHECK(topk == kTopK, MSA_ERR_UNSUPPORTED, "topk must be 16 (got %d)", topk);
+  MSA_CHECK(n_local >= 1 && n_local <= kTopK, MSA_ERR_UNSUPPORTED,
+            "n_local must be in [1, 16] (got %d)", n_local);
+  if (vl->total_q == 0) return MSA_OK;   // nothing to select
+  MSA_CHECK(scores && topk_idx, MSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  MSA_CHECK(ld_scores >= vl->max_pages && ld_scores >= 1, MSA_ERR_INVALID_ARGUMENT,
+            "ld_scores (%lld) < max_pages (%d)", (long long)ld_scores, vl->max_pages);
+  MSA_CHECK(topk_stride >= kTopK, MSA_ERR_INVALID_ARGUMENT, "topk_stride must be >= 16");
+  st = check_device();
+  if (st != MSA_OK) return st;
+  TopkArgs a{*vl, scores, ld_scores, n_local, topk_idx, topk_stride};
+  hipError_t e = launch_topk(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "msa_topk_select");
+  return MSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+size_t msa_k2q_schedule_size(const msa_varlen_t* vl, int32_t n_sel_heads, int32_t topk) {
+  if (!vl || vl->batch < 1 || vl->total_q < 0 || vl->total_rows < 0 || n_sel_heads < 1 ||
+      topk != kTopK)
+    return 0;
+  return sched_layout(vl, n_sel_heads, topk).total;
+}
+
+msa_status_t msa_build_k2q_csr(const msa_varlen_t* vl, const int32_t* topk_idx,
+                               int64_t topk_q_stride, int64_t topk_h_stride, int32_t n_sel_heads,
+                               int32_t topk, int32_t* row_ptr, int32_t* q_indices, void* schedule,
+                               size_t schedule_bytes, void* stream) {
+  msa_status_t st = check_varlen(vl);
+  if (st != MSA_OK) return st;
+  MSA_CHECK(topk == kTopK, MSA_ERR_UNSUPPORTED, "topk must be 16 (got %d)", topk);
+  MSA_CHECK(n_sel_heads >= 1, MSA_ERR_INVALID_ARGUMENT, "n_sel_heads must be >= 1");
+  MSA_CHECK(row_ptr && schedule, MSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  MSA_CHECK(vl->total_q == 0 || (topk_idx && q_indices), MSA_ERR_INVALID_ARGUMENT,
+            "NULL pointer argument");
+  MSA_CHECK(topk_h_stride >= 0 && topk_q_stride >= 0, MSA_ERR_INVALID_ARGUMENT,
+            "negative top-k stride");
+  MSA_CHECK(n_sel_heads == 1 || topk_h_stride >= kTopK, MSA_ERR_INVALID_ARGUMENT,
+            "topk_h_stride must be >= 16 with several selection heads");
+  MSA_CHECK(topk_q_stride >= (int64_t)(n_sel_heads - 1) * topk_h_stride + kTopK,
+            MSA_ERR_INVALID_ARGUMENT, "topk_q_stride too small for the head layout");
+  MSA_CHECK(aligned(schedule, 256), MSA_ERR_INVALID_ARGUMENT, "schedule must be 256-byte aligned");
+  const SchedLayout L = sched_layout(vl, n_sel_heads, topk);
+  MSA_CHECK(schedule_bytes >= L.total, MSA_ERR_WORKSPACE_TOO_SMALL,
+            "schedule has %zu bytes, needs %zu", schedule_bytes, L.total);
+  MSA_CHECK(L.max_items < (int64_t)INT32_MAX && L.n_rows < (int64_t)INT32_MAX / 4,
+            MSA_ERR_UNSUPPORTED, "batch too large");
+  st = check_device();
+  if (st != MSA_OK) return st;
+  CsrArgs a{*vl, topk_idx, topk_q_stride, topk_h_stride, n_sel_heads, row_ptr, q_indices,
+            reinterpret_cast<uint8_t*>(schedule), L};
+  hipError_t e = launch_k2q_csr(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "msa_build_k2q_csr");
+  return MSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+size_t msa_sparse_attn_workspace_size(const msa_varlen_t* vl, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t n_sel_heads, int32_t topk) {
+  if (!vl || vl->batch < 1 || vl->total_q < 0 || num_kv_heads < 1 || num_q_heads < 1 ||
+      num_q_heads % num_kv_heads != 0 || topk != kTopK ||
+      (n_sel_heads != 1 && n_sel_heads != num_kv_heads))
+    return 0;
+  return attn_workspace_bytes(vl, num_q_heads, num_kv_heads, n_sel_heads, topk);
+}
+
+msa_status_t msa_sparse_attn_prefill(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
+                                     int32_t num_q_heads, const uint8_t* kv_cache,
+                                     int32_t num_pages, int32_t num_kv_heads,
+                                     const int32_t* row_ptr, const int32_t* q_indices,
+                                     int32_t n_sel_heads, const void* schedule,
+                                     size_t schedule_bytes, int32_t topk, float softmax_scale,
+                                     const float* q_scale, const float* k_scale,
+                                     const float* v_scale, uint16_t* out, int64_t out_stride,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  msa_status_t st = check_varlen(vl);
+  if (st != MSA_OK) return st;
+  const int Hq = num_q_heads, Hkv = num_kv_heads;
+  MSA_CHECK(Hq >= 1 && Hkv >= 1, MSA_ERR_INVALID_ARGUMENT, "head counts must be >= 1");
+  MSA_CHECK(Hq % Hkv == 0, MSA_ERR_UNSUPPORTED, "num_q_heads (%d) %% num_kv_heads (%d) != 0", Hq,
+            Hkv);
+  MSA_CHECK(topk == kTopK, MSA_ERR_UNSUPPORTED, "topk must be 16 (got %d)", topk);
+  MSA_CHECK(n_sel_heads == 1 || n_sel_heads == Hkv, MSA_ERR_UNSUPPORTED,
+            "n_sel_heads must be 1 or num_kv_heads (got %d)", n_sel_heads);
+  if (vl->total_q == 0) return MSA_OK;   // no query, no output
+  MSA_CHECK(q && kv_cache && row_ptr && q_indices && schedule && out && workspace,
+            MSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  MSA_CHECK(q_stride >= (int64_t)Hq * kDim && q_stride % 16 == 0, MSA_ERR_INVALID_ARGUMENT,
+            "q_stride must be >= Hq*128 and a multiple of 16");
+  MSA_CHECK(out_stride >= (int64_t)Hq * kDim && out_stride % 2 == 0, MSA_ERR_INVALID_ARGUMENT,
+            "out_stride must be >= Hq*128 and even");
+  MSA_CHECK(aligned(q, 16) && aligned(kv_cache, 16) && aligned(out, 4), MSA_ERR_INVALID_ARGUMENT,
+            "q and kv_cache must be 16-byte aligned, out 4-byte aligned");
+  MSA_CHECK(num_pages >= 1, MSA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
+  MSA_CHECK(softmax_scale > 0.f, MSA_ERR_INVALID_ARGUMENT, "softmax_scale must be > 0");
+  MSA_CHECK(aligned(schedule, 256) && aligned(workspace, 256), MSA_ERR_INVALID_ARGUMENT,
+            "schedule and workspace must be 256-byte aligned");
+  const SchedLayout L = sched_layout(vl, n_sel_heads, topk);
+  MSA_CHECK(schedule_bytes >= L.total, MSA_ERR_WORKSPACE_TOO_SMALL,
+            "schedule has %zu bytes, needs %zu", schedule_bytes, L.total);
+  const size_t need = attn_workspace_bytes(vl, Hq, Hkv, n_sel_heads, topk);
+  MSA_CHECK(workspace_bytes >= need, MSA_ERR_WORKSPACE_TOO_SMALL,
+            "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  MSA_CHECK(Hkv <= 65535 && L.max_items < (int64_t)INT32_MAX, MSA_ERR_UNSUPPORTED,
+            "batch or head count too large");
+  st = check_device();
+  if (st != MSA_OK) return st;
+  AttnArgs a{*vl, q, q_stride, Hq, Hkv, n_sel_heads, kv_cache, num_pages, row_ptr, q_indices,
+             reinterpret_cast<const uint8_t*>(schedule), L, softmax_scale, q_scale, k_scale,
+             v_scale, out, out_stride, workspace};
+  hipError_t e = launch_sparse_attn(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_prefill");
+  return MSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Device helpers for the gfx950 kernels: fp8 matrix-core op, wave reductions,
+// orderable float keys, E4M3 packing, bfloat16 rounding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// D = A * B + C on one 16x16x128 E4M3 tile (v_mfma_f32_16x16x128_f8f6f4, no block
+// scales).  Lane l holds row (l % 16) of A and column (l % 16) of B, each with the
+// 32 K-elements of K-group (l / 16); C/D lane l holds column (l % 16), rows
+// 4 * (l / 16) + {0,1,2,3}.  Both operands use the same lane -> K mapping, so a
+// contraction is correct for any fixed assignment of the 128 K indices to
+// (K-group, byte) slots, as long as A and B use the same one.
+__device__ __forceinline__ v4f mfma_e4m3(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (nontemporal: data read once per block).
+__device__ __forceinline__ uint4 load16_nt(const void* p) {
+  v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ v8i load_frag_global(const uint8_t* p) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+  uint4 x = q[0];
+  uint4 y = q[1];
+  v8i r;
+  r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
+  r[4] = y.x; r[5] = y.y; r[6] = y.z; r[7] = y.w;
+  return r;
+}
+
+__device__ __forceinline__ v8i load_frag_lds(const uint8_t* p) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+  uint4 x = q[0];
+  uint4 y = q[1];
+  v8i r;
+  r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
+  r[4] = y.x; r[5] = y.y; r[6] = y.z; r[7] = y.w;
+  return r;
+}
+
+// Reductions across the four 16-lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float max_across_groups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float sum_across_groups(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Monotone map float -> uint32 (larger float, larger key).  NaN maps to 0, below
+// every number (-inf maps to 0x007FFFFF).
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (f != f) return 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Four floats in [0, 448] -> one dword of E4M3 codes (byte k = value k), hardware
+// round-to-nearest-even conversion (gfx950 converts to OCP E4M3).
+__device__ __forceinline__ int pack4_e4m3(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return w;
+}
+
+// float -> bfloat16 bits, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (f != f) return 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// Inclusive scan over a 64-lane wave.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Request owning global query i: largest b with cu_q[b] <= i (cu_q has B+1 entries).
+__device__ __forceinline__ int find_request(const int32_t* cu, int B, int64_t i) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)cu[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace msa

@@ -1,0 +1,108 @@
+// Internal declarations shared by the host API and the HIP kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "msa.h"
+
+namespace msa {
+
+constexpr int kPage = MSA_PAGE_SIZE;   // tokens per page
+constexpr int kDim = MSA_HEAD_DIM;     // head dimension (bytes per E4M3 row)
+constexpr int kTopK = MSA_TOPK;
+
+// ---- index scorer tiling -------------------------------------------------
+// A work item is (request, block of up to kScoreQB(H) queries, chunk of pages).
+// Every wave keeps 128/H queries' fragments in registers; 8 waves per block.
+constexpr int kScoreWaves = 8;
+constexpr int score_qblock(int H) { return kScoreWaves * 128 / H; }
+
+struct ScorePlan {
+  int32_t pages_per_item;   // multiple of 4
+  int64_t max_items;        // host upper bound (grid size before padding)
+  size_t workspace_bytes;
+};
+ScorePlan score_plan(const msa_varlen_t* vl, int H);
+
+struct ScoreArgs {
+  msa_varlen_t vl;
+  const uint8_t* q;
+  int64_t q_stride;
+  int H;
+  const uint8_t* k_cache;
+  int32_t num_pages;
+  const float* q_scale;
+  const float* k_scale;
+  float* scores;
+  int64_t ld;
+  void* workspace;
+  ScorePlan plan;
+};
+hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream);
+
+// ---- top-k ---------------------------------------------------------------
+struct TopkArgs {
+  msa_varlen_t vl;
+  const float* scores;
+  int64_t ld;
+  int n_local;
+  int32_t* out;
+  int64_t out_stride;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
+
+// ---- k2q CSR + attention schedule ----------------------------------------
+// Queries (CSR entries) per attention work item.
+constexpr int kAttnQC = 32;
+
+struct SchedLayout {
+  // byte offsets inside the schedule buffer
+  size_t hdr, row_base, row_items, items, inv, bitmap, total;
+  int64_t n_rows;       // n_sel * total_rows
+  int64_t words_per_row;
+  int64_t max_items;
+  int64_t inv_len;      // total_q * n_sel * topk
+};
+SchedLayout sched_layout(const msa_varlen_t* vl, int n_sel, int topk);
+
+struct CsrArgs {
+  msa_varlen_t vl;
+  const int32_t* topk;
+  int64_t tq_stride, th_stride;
+  int n_sel;
+  int32_t* row_ptr;
+  int32_t* q_indices;
+  uint8_t* sched;
+  SchedLayout L;
+};
+hipError_t launch_k2q_csr(const CsrArgs& a, hipStream_t stream);
+
+// ---- sparse attention -------------------------------------------------------
+struct AttnArgs {
+  msa_varlen_t vl;
+  const uint8_t* q;
+  int64_t q_stride;
+  int Hq, Hkv, n_sel;
+  const uint8_t* kv;
+  int32_t num_pages;
+  const int32_t* row_ptr;
+  const int32_t* q_indices;
+  const uint8_t* sched;
+  SchedLayout L;
+  float softmax_scale;
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+  uint16_t* out;
+  int64_t out_stride;
+  void* workspace;
+};
+size_t attn_workspace_bytes(const msa_varlen_t* vl, int Hq, int Hkv, int n_sel, int topk);
+hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace msa

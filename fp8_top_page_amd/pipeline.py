@@ -1,0 +1,119 @@
+"""Device buffers and the four-call sequence of the MSA prefill path.
+
+Plumbing only: torch allocates device memory; every step runs in libmsa.so.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (PAGE, TOPK, Varlen, msa_build_k2q_csr, msa_index_score,
+               msa_index_score_workspace_size, msa_k2q_schedule_size, msa_sparse_attn_prefill,
+               msa_sparse_attn_workspace_size, msa_topk_select)
+
+
+def _dev(x, device, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(device)
+
+
+class DeviceBatch:
+    """Host arrays of one prefill batch copied to the device, with the host-side sizes."""
+
+    def __init__(self, cu_seqlens_q, cu_seqlens_k, block_table, index_q, index_k_cache,
+                 index_q_scale, index_k_scale, attn_q=None, kv_cache=None, attn_q_scale=1.0,
+                 attn_k_scale=1.0, attn_v_scale=1.0, softmax_scale=None, device="cuda"):
+        cu_q = np.asarray(cu_seqlens_q, np.int64)
+        cu_k = np.asarray(cu_seqlens_k, np.int64)
+        sq, sk = np.diff(cu_q), np.diff(cu_k)
+        pages = (sk + PAGE - 1) // PAGE
+        self.total_q = int(cu_q[-1])
+        self.max_seqlen_q = int(sq.max()) if len(sq) else 0
+        self.max_seqlen_k = int(sk.max()) if len(sk) else 0
+        self.total_rows = int(pages.sum())
+        self.max_pages = max(int(pages.max()) if len(pages) else 0, 1)
+        self.device = device
+        self.cu_q = _dev(cu_q.astype(np.int32), device)
+        self.cu_k = _dev(cu_k.astype(np.int32), device)
+        self.block_table = _dev(np.asarray(block_table, np.int32), device)
+        self.vl = Varlen(self.cu_q, self.cu_k, self.block_table, total_q=self.total_q,
+                         max_seqlen_q=self.max_seqlen_q, max_seqlen_k=self.max_seqlen_k,
+                         total_rows=self.total_rows, max_pages=self.max_pages)
+        self.H = int(index_q.shape[1])
+        self.index_q = _dev(np.asarray(index_q).reshape(index_q.shape[0], -1), device)
+        self.k_cache = _dev(index_k_cache, device)
+        self.num_pages = int(index_k_cache.shape[0])
+        self.iq_scale = torch.tensor([index_q_scale], dtype=torch.float32, device=device)
+        self.ik_scale = torch.tensor([index_k_scale], dtype=torch.float32, device=device)
+        self.attn_q = None
+        if attn_q is not None:
+            self.Hq = int(attn_q.shape[1])
+            self.Hkv = int(kv_cache.shape[1])
+            self.attn_q = _dev(np.asarray(attn_q).reshape(attn_q.shape[0], -1), device)
+            self.kv = _dev(kv_cache, device)
+            self.aq_scale = torch.tensor([attn_q_scale], dtype=torch.float32, device=device)
+            self.ak_scale = torch.tensor([attn_k_scale], dtype=torch.float32, device=device)
+            self.av_scale = torch.tensor([attn_v_scale], dtype=torch.float32, device=device)
+            self.softmax_scale = float(softmax_scale if softmax_scale is not None else 128 ** -0.5)
+
+    @classmethod
+    def from_inputs(cls, inp, device="cuda"):
+        return cls(inp.cu_seqlens_q, inp.cu_seqlens_k, inp.block_table, inp.index_q,
+                   inp.index_k_cache, inp.index_q_scale, inp.index_k_scale, inp.attn_q,
+                   inp.kv_cache, inp.attn_q_scale, inp.attn_k_scale, inp.attn_v_scale,
+                   inp.softmax_scale, device)
+
+
+class MsaPath:
+    """Outputs and workspaces for one batch; run the four calls in order."""
+
+    def __init__(self, db: DeviceBatch, n_local: int = 1, n_sel: int = 1, score_fill=float("nan")):
+        self.db = db
+        self.n_local = n_local
+        self.n_sel = n_sel
+        dev = db.device
+        vl = db.vl
+        self.ld = (db.max_pages + 3) // 4 * 4
+        self.scores = torch.full((db.total_q, self.ld), score_fill, dtype=torch.float32, device=dev)
+        self.ws_score = torch.empty(max(msa_index_score_workspace_size(vl, db.H), 256),
+                                    dtype=torch.uint8, device=dev)
+        self.topk = torch.full((db.total_q, n_sel, TOPK), -7, dtype=torch.int32, device=dev)
+        rows = n_sel * db.total_rows
+        self.row_ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+        self.q_indices = torch.empty(max(n_sel * db.total_q * TOPK, 1), dtype=torch.int32, device=dev)
+        self.schedule = torch.empty(msa_k2q_schedule_size(vl, n_sel, TOPK), dtype=torch.uint8,
+                                    device=dev)
+        if db.attn_q is not None:
+            self.out = torch.empty((db.total_q, db.Hq * 128), dtype=torch.bfloat16, device=dev)
+            self.ws_attn = torch.empty(max(msa_sparse_attn_workspace_size(vl, db.Hq, db.Hkv, n_sel,
+                                                                          TOPK), 256),
+                                       dtype=torch.uint8, device=dev)
+
+    def score(self, stream=None):
+        db = self.db
+        msa_index_score(db.vl, db.index_q, db.H, db.k_cache, db.num_pages, db.iq_scale,
+                        db.ik_scale, self.scores, self.ws_score, stream)
+
+    def select(self, stream=None):
+        assert self.n_sel == 1
+        msa_topk_select(self.db.vl, self.scores, TOPK, self.n_local, self.topk[:, 0, :], stream)
+
+    def csr(self, stream=None, topk=None):
+        t = self.topk if topk is None else topk
+        msa_build_k2q_csr(self.db.vl, t if self.n_sel > 1 else t.reshape(t.shape[0], -1)[:, :TOPK],
+                          self.n_sel, TOPK, self.row_ptr, self.q_indices, self.schedule, stream)
+
+    def attend(self, stream=None):
+        db = self.db
+        msa_sparse_attn_prefill(db.vl, db.attn_q, db.Hq, db.kv, db.num_pages, db.Hkv, self.row_ptr,
+                                self.q_indices, self.n_sel, self.schedule, TOPK, db.softmax_scale,
+                                db.aq_scale, db.ak_scale, db.av_scale, self.out, self.ws_attn,
+                                stream)
+
+    def run(self, stream=None):
+        self.score(stream)
+        self.select(stream)
+        self.csr(stream)
+        self.attend(stream)

@@ -1,0 +1,202 @@
+/*
+ * msa.h -- MI355X (gfx950) library for the MiniMax-M3 MSA sparse-prefill path:
+ * FP8 (E4M3) page indexer, causal top-16 page selection, KV-page -> query CSR,
+ * and block-sparse attention over a paged E4M3 K|V cache.
+ *
+ * Sources, cited by page and section:
+ *   [P1] vLLM PR 60930 (MiniMax M3 FP8 indexer prefill on MSA's persistent
+ *        CuTe scorer): Overview, Details (score-only plan/run_scores API, device
+ *        planning without host sync, admission: E4M3, D128, page 128,
+ *        H in {1,2,4} per rank, sparse_local_block >= 1).
+ *   [P2] vLLM PR 60684 (MSA prefill reads the E4M3 query natively): Overview,
+ *        Validation (benchmark script: case() top-k construction, packed K|V
+ *        pages, q_scale 0.5, unit K/V scales), Details (q_scale folds into the
+ *        softmax scale; probabilities rounded to E4M3 per split).
+ *   [P3] vLLM PR 64631 (NVFP4 index-cache sharding): Details (FP8 index rows of
+ *        128 B per token; exact-tie order is implementation-defined).
+ *   [P4] vLLM API docs, vllm.models.minimax_m3.nvidia.sparse_attention_msa:
+ *        MiniMaxM3SparseMSAImpl.forward (build_k2q_csr and sparse_atten_func
+ *        arguments: cu_seqlens_q/k, block size 128, total_rows =
+ *        total_kv_blocks, page_table = block_table, topK = 16, causal).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked [host].  `stream` is a
+ *     hipStream_t (NULL = the null stream).
+ *   - Every call validates its host-side arguments first and returns an error
+ *     before launching anything.  On success the work is queued on `stream`
+ *     and the call returns without synchronising.  No call allocates memory,
+ *     reads device memory from the host, or synchronises, so the calls can be
+ *     recorded in a HIP graph ([P1] Details: the scorer plans on device with no
+ *     D2H and run_scores does no allocation or sync).
+ *   - The caller owns every buffer.  Inputs are only read.  Outputs are
+ *     written as documented; workspace contents are private between calls.
+ *   - Device data that contradicts the host-side sizes (e.g. a cu_seqlens
+ *     entry larger than total_q, a block_table entry >= num_pages) gives
+ *     unspecified results; kernels clamp such indices so they do not fault.
+ *   - E4M3 means OCP E4M3FN (torch.float8_e4m3fn): bias 7, max 448, no inf.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_PAGE_SIZE 128   /* tokens per KV page ([P1] admission: page 128) */
+#define MSA_HEAD_DIM 128    /* D ([P1] admission: D128) */
+#define MSA_TOPK 16         /* selected pages per query ([P2] script: TOPK = 16) */
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative or inconsistent size */
+  MSA_ERR_UNSUPPORTED = 2,        /* outside the admitted set ([P1] Details: otherwise FMHA is kept) */
+  MSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  MSA_ERR_HIP = 4,                /* a HIP launch failed; msa_last_error() has the HIP text */
+  MSA_ERR_NO_DEVICE = 5
+} msa_status_t;
+
+/* Variable-length prefill batch ([P2] script: cu_seqlens_q/k, block_table,
+ * total_kv_blocks; [P4] forward: build_k2q_csr arguments).  The struct itself
+ * is a host object; the three arrays are device arrays.
+ *   Request b has seqlen_q_b = cu_seqlens_q[b+1]-cu_seqlens_q[b] new tokens,
+ *   which are the LAST seqlen_q_b of its seqlen_k_b tokens: query token
+ *   i (cu_seqlens_q[b] <= i < cu_seqlens_q[b+1]) sits at position
+ *   pos_i = seqlen_k_b - seqlen_q_b + (i - cu_seqlens_q[b]).  Requires
+ *   0 <= seqlen_q_b <= seqlen_k_b. */
+typedef struct {
+  int32_t batch;                 /* [host] B >= 1 */
+  int32_t total_q;               /* [host] cu_seqlens_q[B] */
+  int32_t max_seqlen_q;          /* [host] >= every seqlen_q_b */
+  int32_t max_seqlen_k;          /* [host] >= every seqlen_k_b */
+  int32_t total_rows;            /* [host] sum_b ceil(seqlen_k_b / 128) = total_kv_blocks */
+  int32_t max_pages;             /* [host] >= every ceil(seqlen_k_b / 128); <= block_table_stride */
+  const int32_t* cu_seqlens_q;   /* [B+1] non-decreasing, cu_seqlens_q[0] = 0 */
+  const int32_t* cu_seqlens_k;   /* [B+1] non-decreasing, cu_seqlens_k[0] = 0 */
+  const int32_t* block_table;    /* [B, block_table_stride] logical page -> physical page */
+  int64_t block_table_stride;    /* [host] elements between rows of block_table */
+} msa_varlen_t;
+
+/* ---------------------------------------------------------------------------
+ * 1. Index scores  ([P1] Overview and Details: the FP8 indexer scores every
+ *    128-token KV page for each query; score-only plan(..., score_out=) then
+ *    run_scores(), planned on device without host sync.)
+ *
+ * For query i and every logical page j < v_i = pos_i / 128 + 1 of its request:
+ *   scores[i * ld_scores + j] =
+ *       q_scale * k_scale * max_{t in page j, t <= pos_i}
+ *           sum_{h < H} sum_{d < 128} q[i,h,d] * k[block_table[b,j], t % 128, d]
+ * (the pages do not state the reductions; this is the reading the library
+ * implements: maximum over the causally visible tokens of the page of the sum
+ * over index heads of q_h . k).  Entries j >= v_i are NOT written.
+ * Products are exact; sums are accumulated in fp32 by the matrix cores.
+ *
+ *   q          [total_q, H, 128] E4M3, token stride q_stride bytes (>= H*128, multiple of 16)
+ *   H          num_index_heads in {1, 2, 4}          (else MSA_ERR_UNSUPPORTED)
+ *   k_cache    [num_pages, 128, 128] E4M3: one 128-byte index-K row per token
+ *              ([P3] Details), paged through the same block_table
+ *   q_scale, k_scale  device fp32 scalars (per-tensor dequantisation scales)
+ *   scores     fp32 [total_q, ld_scores], ld_scores >= max_pages, multiple of 4
+ *   workspace  >= msa_index_score_workspace_size(vl, H) bytes, 256-byte aligned
+ * ------------------------------------------------------------------------- */
+size_t msa_index_score_workspace_size(const msa_varlen_t* vl, int32_t num_index_heads);
+msa_status_t msa_index_score(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
+                             int32_t num_index_heads, const uint8_t* k_cache,
+                             int32_t num_pages, const float* q_scale, const float* k_scale,
+                             float* scores, int64_t ld_scores, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * 2. Top-k page selection  ([P1] "Native Top16"; [P2] Validation, benchmark
+ *    script case(): local page = visible - 1 always kept, future pages never
+ *    chosen, k = min(16, visible), -1 padding.)
+ *
+ * For query i with v_i visible pages: slots 0..f-1 hold the forced pages
+ * v_i-1, v_i-2, ..., v_i-f with f = min(n_local, topk, v_i) (slot 0 is the
+ * local page); the next min(topk, v_i) - f slots hold the pages
+ * j < v_i - f with the highest scores, in descending score order, equal
+ * scores ordered by lower page index; remaining slots are -1.  Only
+ * scores[i * ld_scores + j] for j < v_i - f are read.
+ *   topk       must be 16; 1 <= n_local <= 16 ([P1]: sparse_local_block >= 1)
+ *   topk_idx   int32 [total_q, topk_stride], topk_stride >= 16; slots 0..15 written
+ * ------------------------------------------------------------------------- */
+msa_status_t msa_topk_select(const msa_varlen_t* vl, const float* scores, int64_t ld_scores,
+                             int32_t topk, int32_t n_local, int32_t* topk_idx,
+                             int64_t topk_stride, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * 3. KV-page -> query CSR  ([P4] forward: build_k2q_csr(topk, cu_seqlens_q,
+ *    cu_seqlens_k, 128, ..., total_rows=total_kv_blocks, qhead_per_kv, ...,
+ *    return_schedule=True) -> (row_ptr, q_indices, schedule).)
+ *
+ * Rows are logical (request, page) pairs: row(b, j) = sum_{b'<b}
+ * ceil(seqlen_k_b' / 128) + j.  With n_sel_heads selections per query
+ * (1 = one selection shared by every KV head; or one per KV head), selection
+ * head g owns rows g * total_rows + row.  Row r lists, in ascending order, the
+ * global indices of the queries whose selection contains its page:
+ *   row_ptr    int32 [n_sel_heads * total_rows + 1], exclusive prefix sums
+ *   q_indices  int32, capacity n_sel_heads * total_q * topk
+ *   topk_idx   int32, entry (i, g, s) at topk_idx[i * topk_q_stride + g * topk_h_stride + s]
+ *              (logical pages; negative = empty slot; pages >= the request's page
+ *              count are ignored)
+ *   schedule   >= msa_k2q_schedule_size(vl, n_sel_heads, topk) bytes, 256-byte
+ *              aligned: the attention's work list, written here and read by
+ *              msa_sparse_attn_prefill.  Opaque.
+ * ------------------------------------------------------------------------- */
+size_t msa_k2q_schedule_size(const msa_varlen_t* vl, int32_t n_sel_heads, int32_t topk);
+msa_status_t msa_build_k2q_csr(const msa_varlen_t* vl, const int32_t* topk_idx,
+                               int64_t topk_q_stride, int64_t topk_h_stride,
+                               int32_t n_sel_heads, int32_t topk, int32_t* row_ptr,
+                               int32_t* q_indices, void* schedule, size_t schedule_bytes,
+                               void* stream);
+
+/* ---------------------------------------------------------------------------
+ * 4. Block-sparse prefill attention  ([P4] forward: sparse_atten_func(q, k, v,
+ *    row_ptr, q_indices, topK=16, blk_kv=128, causal=True, softmax_scale, ...,
+ *    page_table=block_table, schedule, out); [P2] Overview and Details: E4M3
+ *    query over E4M3 K/V with FP8 QK and PV products, probabilities rounded to
+ *    E4M3, q_scale folded into the softmax scale, K scale on the scores, V scale
+ *    on the output; packed page split k = [..., :128], v = [..., 128:].)
+ *
+ * For query i, q-head hq, KV head g = hq / (Hq / Hkv), over the tokens t of the
+ * pages listed for i in selection head (n_sel_heads == 1 ? 0 : g) with t <= pos_i:
+ *   z_t = softmax_scale * q_scale * k_scale * q[i,hq,:] . K[t,g,:]
+ *   out[i,hq,:] = v_scale * sum_t softmax(z)_t V[t,g,:]       (bf16, round to nearest even)
+ * Each (query, page) pair is computed as one split (online-softmax partial with
+ * E4M3 probabilities); the splits are merged by a log-sum-exp combine.
+ * Queries with no attended token get 0.
+ *   q          [total_q, Hq, 128] E4M3, token stride q_stride bytes (>= Hq*128, multiple of 16)
+ *   kv_cache   [num_pages, Hkv, 128, 256] E4M3 (K|V packed per token)
+ *   Hq % Hkv == 0, Hkv >= 1; n_sel_heads in {1, Hkv}; topk == 16
+ *   row_ptr, q_indices, schedule: exactly as written by msa_build_k2q_csr for
+ *              the same vl, n_sel_heads and topk
+ *   q_scale, k_scale, v_scale  device fp32 scalars, or NULL for 1.0
+ *   out        bf16 [total_q, Hq, 128], token stride out_stride elements (>= Hq*128)
+ *   workspace  >= msa_sparse_attn_workspace_size(vl, Hq, Hkv, n_sel_heads, topk) bytes
+ * ------------------------------------------------------------------------- */
+size_t msa_sparse_attn_workspace_size(const msa_varlen_t* vl, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t n_sel_heads, int32_t topk);
+msa_status_t msa_sparse_attn_prefill(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
+                                     int32_t num_q_heads, const uint8_t* kv_cache,
+                                     int32_t num_pages, int32_t num_kv_heads,
+                                     const int32_t* row_ptr, const int32_t* q_indices,
+                                     int32_t n_sel_heads, const void* schedule,
+                                     size_t schedule_bytes, int32_t topk, float softmax_scale,
+                                     const float* q_scale, const float* k_scale,
+                                     const float* v_scale, uint16_t* out, int64_t out_stride,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Diagnostics.
+ * ------------------------------------------------------------------------- */
+const char* msa_status_string(msa_status_t status);  /* static string */
+const char* msa_last_error(void);   /* thread-local detail of this thread's last failed call */
+int32_t msa_abi_version(void);      /* MSA_ABI_VERSION */
+#define MSA_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSA_H_ */

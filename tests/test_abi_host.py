@@ -1,0 +1,159 @@
+"""C-ABI library: loads, exports every declared symbol, validates on the host.
+
+These tests make no compute call on a GPU: every call here either fails host
+validation (before any HIP call) or, where validation passes, runs only in a
+container without a GPU (where it must report MSA_ERR_NO_DEVICE).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import fp8_top_page_amd as msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL, HIP, NO_DEV = 0, 1, 2, 3, 4, 5
+FAKE = 0x10000           # aligned, never dereferenced on the host
+NO_GPU = not torch.cuda.is_available()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?(msa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = msa.lib()
+    names = declared_functions()
+    assert names == sorted([
+        "msa_index_score_workspace_size", "msa_index_score", "msa_topk_select",
+        "msa_k2q_schedule_size", "msa_build_k2q_csr", "msa_sparse_attn_workspace_size",
+        "msa_sparse_attn_prefill", "msa_status_string", "msa_last_error", "msa_abi_version"]), names
+    for n in names:
+        assert hasattr(L, n), n
+    assert msa.msa_abi_version() == 1
+
+
+def test_status_strings():
+    for st, name in [(OK, "MSA_OK"), (INVALID, "MSA_ERR_INVALID_ARGUMENT"),
+                     (UNSUPPORTED, "MSA_ERR_UNSUPPORTED"), (WS_SMALL, "MSA_ERR_WORKSPACE_TOO_SMALL"),
+                     (HIP, "MSA_ERR_HIP"), (NO_DEV, "MSA_ERR_NO_DEVICE")]:
+        assert msa.msa_status_string(st) == name
+
+
+def vl(batch=1, total_q=256, max_q=256, max_k=1024, rows=8, max_pages=8, stride=8):
+    c = msa._VarlenC(batch=batch, total_q=total_q, max_seqlen_q=max_q, max_seqlen_k=max_k,
+                     total_rows=rows, max_pages=max_pages, cu_seqlens_q=FAKE, cu_seqlens_k=FAKE,
+                     block_table=FAKE, block_table_stride=stride)
+    return c
+
+
+def score(v, H=1, q_stride=128, ws=None, ld=8, q=FAKE, num_pages=8):
+    L = msa.lib()
+    if ws is None:
+        ws = L.msa_index_score_workspace_size(ctypes.byref(v), H) or 1 << 20
+    return L.msa_index_score(ctypes.byref(v), q, q_stride, H, FAKE, num_pages, FAKE, FAKE, FAKE, ld,
+                             0x100000, ws, None)
+
+
+def test_index_score_validation():
+    L = msa.lib()
+    assert L.msa_index_score(None, FAKE, 128, 1, FAKE, 8, FAKE, FAKE, FAKE, 8, FAKE, 1 << 20, None) == INVALID
+    assert score(vl(), H=3) == UNSUPPORTED
+    assert score(vl(), H=8) == UNSUPPORTED
+    assert score(vl(), q_stride=64) == INVALID          # < H*128
+    assert score(vl(), H=2, q_stride=128) == INVALID
+    assert score(vl(), q_stride=136) == INVALID         # not a multiple of 16
+    assert score(vl(), q=FAKE + 8) == INVALID           # misaligned
+    assert score(vl(), ld=7) == INVALID                 # ld < max_pages
+    assert score(vl(), num_pages=0) == INVALID
+    assert score(vl(), ws=16) == WS_SMALL
+    assert score(vl(batch=0)) == INVALID
+    assert score(vl(max_pages=4, stride=4)) == INVALID  # 4 pages cannot hold 1024 tokens
+    assert score(vl(stride=4)) == INVALID               # block table stride < max_pages
+    assert score(vl(max_q=2048)) == INVALID             # max_seqlen_q > max_seqlen_k
+    assert "ld_scores" in msa.msa_last_error() or msa.msa_last_error()
+    # empty batch: valid, nothing to do
+    assert score(vl(total_q=0)) == OK
+
+
+@pytest.mark.skipif(not NO_GPU, reason="checks the no-device path")
+def test_valid_calls_report_no_device_without_gpu():
+    assert score(vl()) == NO_DEV
+    L = msa.lib()
+    v = vl()
+    assert L.msa_topk_select(ctypes.byref(v), FAKE, 8, 16, 1, FAKE, 16, None) == NO_DEV
+    sz = L.msa_k2q_schedule_size(ctypes.byref(v), 1, 16)
+    assert L.msa_build_k2q_csr(ctypes.byref(v), FAKE, 16, 0, 1, 16, FAKE, FAKE, 0x100000, sz, None) == NO_DEV
+
+
+def test_topk_validation():
+    L = msa.lib()
+    v = vl()
+    assert L.msa_topk_select(ctypes.byref(v), FAKE, 8, 8, 1, FAKE, 16, None) == UNSUPPORTED
+    assert L.msa_topk_select(ctypes.byref(v), FAKE, 8, 16, 0, FAKE, 16, None) == UNSUPPORTED
+    assert L.msa_topk_select(ctypes.byref(v), FAKE, 8, 16, 17, FAKE, 16, None) == UNSUPPORTED
+    assert L.msa_topk_select(ctypes.byref(v), FAKE, 8, 16, 1, FAKE, 15, None) == INVALID
+    assert L.msa_topk_select(ctypes.byref(v), None, 8, 16, 1, FAKE, 16, None) == INVALID
+    assert L.msa_topk_select(ctypes.byref(v), FAKE, 4, 16, 1, FAKE, 16, None) == INVALID
+
+
+def test_csr_validation():
+    L = msa.lib()
+    v = vl()
+    sz = L.msa_k2q_schedule_size(ctypes.byref(v), 1, 16)
+    assert sz > 0
+    assert L.msa_k2q_schedule_size(ctypes.byref(v), 2, 16) > sz
+    assert L.msa_k2q_schedule_size(ctypes.byref(v), 1, 8) == 0
+    assert L.msa_build_k2q_csr(ctypes.byref(v), FAKE, 16, 0, 1, 8, FAKE, FAKE, 0x100000, sz, None) == UNSUPPORTED
+    assert L.msa_build_k2q_csr(ctypes.byref(v), FAKE, 16, 0, 0, 16, FAKE, FAKE, 0x100000, sz, None) == INVALID
+    assert L.msa_build_k2q_csr(ctypes.byref(v), FAKE, 16, 0, 1, 16, FAKE, FAKE, 0x100000, sz - 1, None) == WS_SMALL
+    assert L.msa_build_k2q_csr(ctypes.byref(v), FAKE, 16, 0, 1, 16, FAKE, FAKE, 0x100010, sz, None) == INVALID
+    assert L.msa_build_k2q_csr(ctypes.byref(v), FAKE, 32, 8, 2, 16, FAKE, FAKE, 0x100000, 1 << 30, None) == INVALID
+    assert L.msa_build_k2q_csr(ctypes.byref(v), None, 16, 0, 1, 16, FAKE, FAKE, 0x100000, sz, None) == INVALID
+
+
+def attn(v, Hq=8, Hkv=1, n_sel=1, topk=16, q_stride=1024, out_stride=1024, ws=None, sched=None,
+         sm=0.088):
+    L = msa.lib()
+    if sched is None:
+        sched = L.msa_k2q_schedule_size(ctypes.byref(v), n_sel, 16) or 1 << 20
+    if ws is None:
+        ws = L.msa_sparse_attn_workspace_size(ctypes.byref(v), Hq, Hkv, n_sel, 16) or 1 << 20
+    return L.msa_sparse_attn_prefill(ctypes.byref(v), FAKE, q_stride, Hq, FAKE, 8, Hkv, FAKE, FAKE,
+                                     n_sel, 0x100000, sched, topk, sm, None, None, None, FAKE,
+                                     out_stride, 0x200000, ws, None)
+
+
+def test_attention_validation():
+    v = vl()
+    assert attn(v, Hq=8, Hkv=3) == UNSUPPORTED
+    assert attn(v, topk=8) == UNSUPPORTED
+    assert attn(v, n_sel=2) == UNSUPPORTED
+    assert attn(v, q_stride=512) == INVALID
+    assert attn(v, out_stride=1023) == INVALID
+    assert attn(v, sm=0.0) == INVALID
+    assert attn(v, ws=100) == WS_SMALL
+    assert attn(v, sched=100) == WS_SMALL
+    assert attn(vl(total_q=0)) == OK
+
+
+def test_workspace_sizes_grow_with_the_batch():
+    L = msa.lib()
+    small, big = vl(), vl(total_q=2048, max_q=2048, max_k=1 << 20, rows=8192, max_pages=8192,
+                          stride=8192)
+    for H in (1, 2, 4):
+        a = L.msa_index_score_workspace_size(ctypes.byref(small), H)
+        b = L.msa_index_score_workspace_size(ctypes.byref(big), H)
+        assert 0 < a <= b
+    assert L.msa_index_score_workspace_size(ctypes.byref(small), 3) == 0
+    a = L.msa_sparse_attn_workspace_size(ctypes.byref(small), 8, 1, 1, 16)
+    b = L.msa_sparse_attn_workspace_size(ctypes.byref(big), 8, 1, 1, 16)
+    assert 0 < a < b
+    # partial rows: 16 slots x 8 heads x (128 bf16 + lse) per query
+    assert b >= 2048 * 16 * 8 * (256 + 4)

@@ -201,8 +201,8 @@ def make_inputs(wl: Workload, attention: bool = True) -> Inputs:
             iq[idx] += shift
         meta["shift_tokens"] = n_shift
         meta["shift_norm"] = float(wl.shift_sigmas)
-    q_scale = float(iq.abs().max()) / E4M3_MAX
-    k_scale = float(ik.abs().max()) / E4M3_MAX
+    q_scale = (float(iq.abs().max()) if iq.numel() else E4M3_MAX) / E4M3_MAX
+    k_scale = (float(ik.abs().max()) if ik.numel() else E4M3_MAX) / E4M3_MAX
     q_scale = float(np.float32(q_scale))
     k_scale = float(np.float32(k_scale))
     iq_codes = to_e4m3_bytes(iq / q_scale)
