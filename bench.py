@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--cold", action="store_true",
                     help="overwrite a 1 GiB buffer before every step (outside the events)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=12, help="queries in the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU time budget of the oracle sample")
     return ap.parse_args()
 
 
@@ -80,16 +81,20 @@ def algorithmic_work(inp, sel):
                 distinct_pages=int(distinct))
 
 
-def cpu_baseline(inp, n_sample):
-    """The oracle's index scoring timed on a bounded sample of queries, scaled
+def cpu_baseline(inp, budget_s):
+    """The oracle's index scoring timed on a bounded sample of queries (chunks of
+    64 evenly spread queries until about budget_s seconds of CPU work), scaled
     linearly to the whole layer."""
     import numpy as np
     import oracle
-    rng = np.random.default_rng(0)
-    q = np.sort(rng.choice(inp.total_q, size=min(n_sample, inp.total_q), replace=False))
+    order = np.random.default_rng(0).permutation(inp.total_q)
+    done = 0
     t0 = time.perf_counter()
-    oracle.index_scores(inp.cu_seqlens_q, inp.cu_seqlens_k, inp.block_table, inp.index_q,
-                        inp.index_k_cache, inp.index_q_scale, inp.index_k_scale, queries=q)
+    while done < inp.total_q and time.perf_counter() - t0 < budget_s:
+        q = np.sort(order[done:done + 64])
+        oracle.index_scores(inp.cu_seqlens_q, inp.cu_seqlens_k, inp.block_table, inp.index_q,
+                            inp.index_k_cache, inp.index_q_scale, inp.index_k_scale, queries=q)
+        done += len(q)
     dt = time.perf_counter() - t0
     threads = None
     try:
@@ -98,10 +103,10 @@ def cpu_baseline(inp, n_sample):
         threads = max((d.get("num_threads") or 1) for d in info) if info else 1
     except Exception:
         threads = os.cpu_count()
-    return {"value": dt / len(q) * inp.total_q * 1e6, "unit": "us/layer (index scoring)",
+    return {"value": round(dt / done * inp.total_q * 1e6, 1), "unit": "us/layer (index scoring)",
             "cores": int(threads or 1), "kind": "oracle",
-            "sample": f"{len(q)} of {inp.total_q} queries of {inp.wl.name}, float64 numpy "
-                      f"oracle index scoring, {dt:.1f} s, scaled linearly by query count"}
+            "sample": f"{done} of {inp.total_q} queries of {inp.wl.name} (random, chunks of 64), "
+                      f"float64 numpy oracle index scoring, {dt:.1f} s, scaled linearly by query count"}
 
 
 def main():
@@ -215,7 +220,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample)
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

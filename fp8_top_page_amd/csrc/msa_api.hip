@@ -116,7 +116,7 @@ msa_status_t msa_index_score(const msa_varlen_t* vl, const uint8_t* q, int64_t q
   MSA_CHECK(num_pages >= 1, MSA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
   MSA_CHECK(ld_scores >= vl->max_pages && ld_scores >= 1, MSA_ERR_INVALID_ARGUMENT,
             "ld_scores (%lld) < max_pages (%d)", (long long)ld_scores, vl->max_pages);
-  MSA_CHECK(aligned(workspace, 256), MSA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  MSA_CHECK(aligned(workspace, 16), MSA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   const ScorePlan plan = score_plan(vl, H);
   MSA_CHECK(workspace_bytes >= plan.workspace_bytes, MSA_ERR_WORKSPACE_TOO_SMALL,
             "workspace has %zu bytes, needs %zu", workspace_bytes, plan.workspace_bytes);
@@ -177,7 +177,7 @@ msa_status_t msa_build_k2q_csr(const msa_varlen_t* vl, const int32_t* topk_idx,
             "topk_h_stride must be >= 16 with several selection heads");
   MSA_CHECK(topk_q_stride >= (int64_t)(n_sel_heads - 1) * topk_h_stride + kTopK,
             MSA_ERR_INVALID_ARGUMENT, "topk_q_stride too small for the head layout");
-  MSA_CHECK(aligned(schedule, 256), MSA_ERR_INVALID_ARGUMENT, "schedule must be 256-byte aligned");
+  MSA_CHECK(aligned(schedule, 16), MSA_ERR_INVALID_ARGUMENT, "schedule must be 16-byte aligned");
   const SchedLayout L = sched_layout(vl, n_sel_heads, topk);
   MSA_CHECK(schedule_bytes >= L.total, MSA_ERR_WORKSPACE_TOO_SMALL,
             "schedule has %zu bytes, needs %zu", schedule_bytes, L.total);
@@ -231,8 +231,8 @@ msa_status_t msa_sparse_attn_prefill(const msa_varlen_t* vl, const uint8_t* q, i
             "q and kv_cache must be 16-byte aligned, out 4-byte aligned");
   MSA_CHECK(num_pages >= 1, MSA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
   MSA_CHECK(softmax_scale > 0.f, MSA_ERR_INVALID_ARGUMENT, "softmax_scale must be > 0");
-  MSA_CHECK(aligned(schedule, 256) && aligned(workspace, 256), MSA_ERR_INVALID_ARGUMENT,
-            "schedule and workspace must be 256-byte aligned");
+  MSA_CHECK(aligned(schedule, 16) && aligned(workspace, 16), MSA_ERR_INVALID_ARGUMENT,
+            "schedule and workspace must be 16-byte aligned");
   const SchedLayout L = sched_layout(vl, n_sel_heads, topk);
   MSA_CHECK(schedule_bytes >= L.total, MSA_ERR_WORKSPACE_TOO_SMALL,
             "schedule has %zu bytes, needs %zu", schedule_bytes, L.total);

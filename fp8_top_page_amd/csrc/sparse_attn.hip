@@ -95,12 +95,18 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnK a) {
     dst[0] = x0; dst[1] = x1; dst[2] = x2; dst[3] = x3;
   }
   {
-    // token group m = tokens 4m..4m+3 -> permuted positions 32*(m&3) + 4*(m>>2) + {0..3}
+    // token group m = tokens 4m..4m+3 -> permuted positions 32*(m&3) + 4*(m>>2) + {0..3}.
+    // Tokens past the end of the sequence hold no data (the page tail may be
+    // anything, even NaN); their probability is exactly 0, so V is zeroed there
+    // to keep 0 * V finite.
+    const int n_valid = (a.cu_k[b + 1] - a.cu_k[b]) - j * kPage;
     const int m = tid >> 3, dc = tid & 7;
     uint4 r[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
       r[i] = *reinterpret_cast<const uint4*>(page + (4 * m + i) * (2 * kDim) + kDim + 16 * dc);
+      if (4 * m + i >= n_valid) r[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
     const int kpos = 32 * (m & 3) + 4 * (m >> 2);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {

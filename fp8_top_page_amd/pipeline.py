@@ -42,7 +42,7 @@ class DeviceBatch:
                          max_seqlen_q=self.max_seqlen_q, max_seqlen_k=self.max_seqlen_k,
                          total_rows=self.total_rows, max_pages=self.max_pages)
         self.H = int(index_q.shape[1])
-        self.index_q = _dev(np.asarray(index_q).reshape(index_q.shape[0], -1), device)
+        self.index_q = _dev(np.asarray(index_q).reshape(index_q.shape[0], self.H * 128), device)
         self.k_cache = _dev(index_k_cache, device)
         self.num_pages = int(index_k_cache.shape[0])
         self.iq_scale = torch.tensor([index_q_scale], dtype=torch.float32, device=device)
@@ -51,7 +51,7 @@ class DeviceBatch:
         if attn_q is not None:
             self.Hq = int(attn_q.shape[1])
             self.Hkv = int(kv_cache.shape[1])
-            self.attn_q = _dev(np.asarray(attn_q).reshape(attn_q.shape[0], -1), device)
+            self.attn_q = _dev(np.asarray(attn_q).reshape(attn_q.shape[0], self.Hq * 128), device)
             self.kv = _dev(kv_cache, device)
             self.aq_scale = torch.tensor([attn_q_scale], dtype=torch.float32, device=device)
             self.ak_scale = torch.tensor([attn_k_scale], dtype=torch.float32, device=device)
@@ -102,8 +102,10 @@ class MsaPath:
 
     def csr(self, stream=None, topk=None):
         t = self.topk if topk is None else topk
-        msa_build_k2q_csr(self.db.vl, t if self.n_sel > 1 else t.reshape(t.shape[0], -1)[:, :TOPK],
-                          self.n_sel, TOPK, self.row_ptr, self.q_indices, self.schedule, stream)
+        if self.n_sel == 1 and t.dim() == 3:
+            t = t[:, 0, :]
+        msa_build_k2q_csr(self.db.vl, t, self.n_sel, TOPK, self.row_ptr, self.q_indices,
+                          self.schedule, stream)
 
     def attend(self, stream=None):
         db = self.db

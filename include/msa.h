@@ -98,8 +98,8 @@ typedef struct {
  *   k_cache    [num_pages, 128, 128] E4M3: one 128-byte index-K row per token
  *              ([P3] Details), paged through the same block_table
  *   q_scale, k_scale  device fp32 scalars (per-tensor dequantisation scales)
- *   scores     fp32 [total_q, ld_scores], ld_scores >= max_pages, multiple of 4
- *   workspace  >= msa_index_score_workspace_size(vl, H) bytes, 256-byte aligned
+ *   scores     fp32 [total_q, ld_scores], ld_scores >= max_pages
+ *   workspace  >= msa_index_score_workspace_size(vl, H) bytes, 16-byte aligned
  * ------------------------------------------------------------------------- */
 size_t msa_index_score_workspace_size(const msa_varlen_t* vl, int32_t num_index_heads);
 msa_status_t msa_index_score(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
@@ -141,7 +141,7 @@ msa_status_t msa_topk_select(const msa_varlen_t* vl, const float* scores, int64_
  *   topk_idx   int32, entry (i, g, s) at topk_idx[i * topk_q_stride + g * topk_h_stride + s]
  *              (logical pages; negative = empty slot; pages >= the request's page
  *              count are ignored)
- *   schedule   >= msa_k2q_schedule_size(vl, n_sel_heads, topk) bytes, 256-byte
+ *   schedule   >= msa_k2q_schedule_size(vl, n_sel_heads, topk) bytes, 16-byte
  *              aligned: the attention's work list, written here and read by
  *              msa_sparse_attn_prefill.  Opaque.
  * ------------------------------------------------------------------------- */

@@ -113,7 +113,7 @@ def test_csr_validation():
     assert L.msa_build_k2q_csr(ctypes.byref(v), FAKE, 16, 0, 1, 8, FAKE, FAKE, 0x100000, sz, None) == UNSUPPORTED
     assert L.msa_build_k2q_csr(ctypes.byref(v), FAKE, 16, 0, 0, 16, FAKE, FAKE, 0x100000, sz, None) == INVALID
     assert L.msa_build_k2q_csr(ctypes.byref(v), FAKE, 16, 0, 1, 16, FAKE, FAKE, 0x100000, sz - 1, None) == WS_SMALL
-    assert L.msa_build_k2q_csr(ctypes.byref(v), FAKE, 16, 0, 1, 16, FAKE, FAKE, 0x100010, sz, None) == INVALID
+    assert L.msa_build_k2q_csr(ctypes.byref(v), FAKE, 16, 0, 1, 16, FAKE, FAKE, 0x100008, sz, None) == INVALID
     assert L.msa_build_k2q_csr(ctypes.byref(v), FAKE, 32, 8, 2, 16, FAKE, FAKE, 0x100000, 1 << 30, None) == INVALID
     assert L.msa_build_k2q_csr(ctypes.byref(v), None, 16, 0, 1, 16, FAKE, FAKE, 0x100000, sz, None) == INVALID
 
@@ -157,3 +157,19 @@ def test_workspace_sizes_grow_with_the_batch():
     assert 0 < a < b
     # partial rows: 16 slots x 8 heads x (128 bf16 + lse) per query
     assert b >= 2048 * 16 * 8 * (256 + 4)
+
+
+@pytest.mark.skipif(not NO_GPU, reason="host-pointer marshalling check, CPU container only")
+def test_pipeline_marshalling_on_host_buffers():
+    """The binding's argument marshalling (empty and non-empty batches) up to the
+    library's device check; nothing is launched without a GPU."""
+    import workloads
+    from fp8_top_page_amd.pipeline import DeviceBatch, MsaPath
+    for sq, sk in [((0, 0), (300, 128)), ((5, 3), (300, 3))]:
+        inp = workloads.make_inputs(workloads.custom("m", 1, sq, sk, 2, 16, 2))
+        path = MsaPath(DeviceBatch.from_inputs(inp, device="cpu"))
+        for step in (path.score, path.select, path.csr, path.attend):
+            try:
+                step()
+            except msa.MsaError as e:
+                assert e.status == NO_DEV, e
