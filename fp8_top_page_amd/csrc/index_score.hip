@@ -29,6 +29,9 @@ namespace {
 constexpr int kLdsRow = 144;                 // 128 B + 16 B pad against bank conflicts
 constexpr int kLdsPage = kPage * kLdsRow;    // 18 KiB
 constexpr int kThreads = kScoreWaves * 64;
+constexpr int kFlush = 16;                   // pages per score-tile flush (divides the item size)
+constexpr int kSRow = kFlush + 1;            // score-tile row stride in floats
+constexpr int kMaxItemPages = 256;           // pages per work item, at most
 
 struct ItemHdr {
   int32_t n_items;
@@ -58,6 +61,8 @@ struct ScoreK {
 // ---------------------------------------------------------------------------
 // Plan: one block.  Items are emitted request by request, q-block by q-block,
 // page chunk by page chunk.  item = {b, first global query, query count, first page}.
+// For each batch of up to 256 q-blocks: one thread per q-block counts its page
+// chunks, a block scan places them, then all threads emit the batch's items.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void score_plan_kernel(const int32_t* __restrict__ cu_q,
                                                          const int32_t* __restrict__ cu_k, int B,
@@ -65,6 +70,8 @@ __global__ __launch_bounds__(256) void score_plan_kernel(const int32_t* __restri
                                                          int32_t* __restrict__ n_items,
                                                          int4* __restrict__ items) {
   __shared__ int wave_tot[4];
+  __shared__ int s_off[257];
+  __shared__ int s_qf[256], s_qn[256];
   __shared__ int64_t running;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) running = 0;
@@ -83,18 +90,31 @@ __global__ __launch_bounds__(256) void score_plan_kernel(const int32_t* __restri
         const int v = (ctx + qf + qn - 1) / kPage + 1;
         nch = (v + pc - 1) / pc;
       }
-      int incl = wave_inclusive_scan(nch);
+      const int incl = wave_inclusive_scan(nch);
       if (lane == 63) wave_tot[wave] = incl;
       __syncthreads();
-      int wave_off = 0;
-      for (int w = 0; w < wave; ++w) wave_off += wave_tot[w];
-      const int64_t off = running + wave_off + incl - nch;
-      for (int c = 0; c < nch; ++c) {
-        const int64_t k = off + c;
-        if (k < max_items) items[k] = make_int4(b, q0 + qf, qn, c * pc);
+      int wave_off = 0, total = 0;
+      for (int w = 0; w < 4; ++w) {
+        if (w < wave) wave_off += wave_tot[w];
+        total += wave_tot[w];
+      }
+      s_off[tid] = wave_off + incl - nch;
+      s_qf[tid] = qf;
+      s_qn[tid] = qn;
+      if (tid == 0) s_off[256] = total;
+      __syncthreads();
+      const int64_t run = running;
+      for (int k = tid; k < total; k += 256) {
+        int lo = 0, hi = 255;             // last q-block of the batch with s_off <= k
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_off[mid] <= k) lo = mid; else hi = mid - 1;
+        }
+        const int64_t dst = run + k;
+        if (dst < max_items) items[dst] = make_int4(b, q0 + s_qf[lo], s_qn[lo], (k - s_off[lo]) * pc);
       }
       __syncthreads();
-      if (tid == 255) running = off + nch;
+      if (tid == 0) running = run + total;
       __syncthreads();
     }
   }
@@ -104,10 +124,73 @@ __global__ __launch_bounds__(256) void score_plan_kernel(const int32_t* __restri
 // ---------------------------------------------------------------------------
 // Scorer.
 // ---------------------------------------------------------------------------
+
+// Max over one page's 128 tokens for every resident query tile.  A fragments
+// (16 tokens x 128 bytes) are read from LDS one tile ahead of their products.
+template <int H, int NQT>
+__device__ __forceinline__ void page_max(const uint8_t* __restrict__ pg, const v8i (&qf)[NQT][H],
+                                         int col, int grp, v4f (&rmax)[NQT]) {
+#pragma unroll
+  for (int n = 0; n < NQT; ++n) rmax[n] = v4f{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  v8i a_cur = load_frag_lds(pg + col * kLdsRow + grp * 32);
+#pragma unroll
+  for (int T = 0; T < 8; ++T) {
+    v8i a_nxt;
+    if (T < 7) a_nxt = load_frag_lds(pg + ((T + 1) * 16 + col) * kLdsRow + grp * 32);
+#pragma unroll
+    for (int n = 0; n < NQT; ++n) {
+      v4f acc = mfma_e4m3(a_cur, qf[n][0], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int h = 1; h < H; ++h) acc = mfma_e4m3(a_cur, qf[n][h], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rmax[n][i] = fmaxf(rmax[n][i], acc[i]);
+    }
+    if (T < 7) a_cur = a_nxt;
+  }
+}
+
+// Same with the causal cut: token (16T + 4*grp + i) of the page counts for the
+// query in lane column n only if it is <= lim0 + 16n (lim0 = last visible token
+// of the wave's first query tile, consecutive queries are consecutive positions).
+// Used only on the few pages that cross a query's position; not unrolled over T.
+template <int H, int NQT>
+__device__ __forceinline__ void page_max_causal(const uint8_t* __restrict__ pg,
+                                                const v8i (&qf)[NQT][H], int lim0, int col,
+                                                int grp, v4f (&rmax)[NQT]) {
+#pragma unroll
+  for (int n = 0; n < NQT; ++n) rmax[n] = v4f{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll 1
+  for (int T = 0; T < 8; ++T) {
+    const v8i a_cur = load_frag_lds(pg + (T * 16 + col) * kLdsRow + grp * 32);
+#pragma unroll
+    for (int n = 0; n < NQT; ++n) {
+      v4f acc = mfma_e4m3(a_cur, qf[n][0], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int h = 1; h < H; ++h) acc = mfma_e4m3(a_cur, qf[n][h], acc);
+      const int lim = lim0 + 16 * n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = (T * 16 + grp * 4 + i > lim) ? -INFINITY : acc[i];
+        rmax[n][i] = fmaxf(rmax[n][i], v);
+      }
+    }
+  }
+}
+
+// LDS per block: a ring of four index-K pages (two being scored, two being
+// filled), one private score tile per wave ([queries of the wave][kFlush pages],
+// rows padded to kSRow floats), and the item's physical page ids.
+template <int H>
+constexpr size_t score_lds_bytes() {
+  return 4 * kLdsPage + (size_t)kScoreWaves * score_qtiles(H) * 16 * kSRow * sizeof(float) +
+         kMaxItemPages * sizeof(int);
+}
+
 template <int H>
 __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
-  constexpr int NQT = 8 / H;   // 16-query tiles per wave
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kLdsPage];
+  constexpr int NQT = score_qtiles(H);   // 16-query tiles per wave
+  static_assert(NQT >= 1, "at least one query tile per wave");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int item = blockIdx.x;
   if (item >= *a.n_items) return;
@@ -116,6 +199,8 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
+  float* sbuf = reinterpret_cast<float*>(lds + 4 * kLdsPage) + wave * (NQT * 16 * kSRow);
+  int* s_phys = reinterpret_cast<int*>(lds + 4 * kLdsPage + kScoreWaves * NQT * 16 * kSRow * 4);
 
   const int cq0 = a.cu_q[b];
   const int sq = a.cu_q[b + 1] - cq0;
@@ -126,21 +211,75 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
   const int v_block = pos_last / kPage + 1;
   const int p_end = min(min(p0 + a.pages_per_item, v_block), a.max_pages);
   if (p0 >= p_end) return;
-  const float scale = (*a.q_scale) * (*a.k_scale);
   const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
 
+  // Physical page ids of the item, read once into LDS so that address
+  // computation in the page loop never waits on a vector-memory load.
+  for (int k = tid; k < p_end - p0; k += kThreads) {
+    const int phys = bt[p0 + k];
+    s_phys[k] = (phys < 0 || phys >= a.num_pages) ? 0 : phys;
+  }
+  __syncthreads();
+
+  // Index-K pages (16 KiB) go global -> registers -> LDS; thread t copies bytes
+  // [kCopy*t, kCopy*(t+1)).  Pages are handled in pairs: while one pair is
+  // scored from LDS, the next pair is written to the other half of the ring and
+  // two more pairs are in flight in registers.  Loads are issued for every
+  // slot (page index clamped to the item) so the number of loads in flight is
+  // the same on every path.
+  constexpr int kCopy = kPage * kDim / kThreads;   // bytes per thread per page
+  constexpr int kV = kCopy / 16;
+  static_assert(kV >= 1 && kCopy % 16 == 0, "page copy must be whole 16-byte pieces");
+  const int st_row = tid / (kDim / kCopy), st_col = (tid % (kDim / kCopy)) * kCopy;
+  auto page_ptr = [&](int p) -> const uint8_t* {
+    const int phys = s_phys[min(p, p_end - 1) - p0];
+    return a.k_cache + (int64_t)phys * (kPage * kDim) + st_row * kDim + st_col;
+  };
+  // page p lives in ring slot p & 3
+  auto lds_slot = [&](int p) -> uint4* {
+    return reinterpret_cast<uint4*>(lds + (p & 3) * kLdsPage + st_row * kLdsRow + st_col);
+  };
+  uint4 stA[2][kV], stB[2][kV];
+  {
+    uint4 x0[kV], x1[kV];
+    const uint8_t* s0 = page_ptr(p0);
+    const uint8_t* s1 = page_ptr(p0 + 1);
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+      x0[v] = load16_nt(s0 + 16 * v);
+      x1[v] = load16_nt(s1 + 16 * v);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint8_t* sa = page_ptr(p0 + 2 + j);
+      const uint8_t* sb = page_ptr(p0 + 4 + j);
+#pragma unroll
+      for (int v = 0; v < kV; ++v) {
+        stA[j][v] = load16_nt(sa + 16 * v);
+        stB[j][v] = load16_nt(sb + 16 * v);
+      }
+    }
+    uint4* d0 = lds_slot(p0);
+    uint4* d1 = lds_slot(p0 + 1);
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+      d0[v] = x0[v];
+      d1[v] = x1[v];
+    }
+  }
+
   // Query fragments (B operand): column = query, K-group = 32-byte slice of D.
+  // Loaded after the first index-K pages are requested so the latencies overlap.
   v8i qf[NQT][H];
-  int qpos[NQT];
-  int qrow[NQT];
+  const int q_end = q_first + q_count;
   const int wave_q0 = q_first + wave * NQT * 16;
-  const bool wave_active = wave_q0 < q_first + q_count;
+  const bool wave_active = wave_q0 < q_end;
+  const int my_q0 = wave_q0 + col;              // query of this lane in tile n: my_q0 + 16n
+  const int my_pos0 = ctx + (my_q0 - cq0);      // its position: my_pos0 + 16n
 #pragma unroll
   for (int n = 0; n < NQT; ++n) {
-    const int qi = wave_q0 + n * 16 + col;
-    const bool ok = qi < q_first + q_count;
-    qrow[n] = ok ? qi : -1;
-    qpos[n] = ok ? ctx + (qi - cq0) : -1;
+    const int qi = my_q0 + n * 16;
+    const bool ok = qi < q_end;
 #pragma unroll
     for (int h = 0; h < H; ++h) {
       if (ok) {
@@ -150,88 +289,95 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
       }
     }
   }
-
-  // Stage one page of index-K (16 KiB) into LDS: thread t copies bytes [32t, 32t+32).
-  const int st_row = tid >> 2, st_col = (tid & 3) * 32;
-  auto page_ptr = [&](int p) -> const uint8_t* {
-    int phys = bt[p];
-    phys = (phys < 0 || phys >= a.num_pages) ? 0 : phys;
-    return a.k_cache + (int64_t)phys * (kPage * kDim) + st_row * kDim + st_col;
-  };
-  uint4 stage0, stage1;
-  {
-    const uint8_t* src = page_ptr(p0);
-    stage0 = load16_nt(src);
-    stage1 = load16_nt(src + 16);
-    uint4* dst = reinterpret_cast<uint4*>(lds + st_row * kLdsRow + st_col);
-    dst[0] = stage0;
-    dst[1] = stage1;
-  }
+  const float scale = (*a.q_scale) * (*a.k_scale);
   __syncthreads();
 
-  float stash[NQT];
+  // Flush the wave's score tile for pages [pg0, pg_hi): lane handles a
+  // (query, 4-page) piece; full pieces go out as one 16-byte store.
+  auto flush = [&](int pg0, int pg_hi) {
 #pragma unroll
-  for (int n = 0; n < NQT; ++n) stash[n] = 0.f;
+    for (int r = 0; r < NQT; ++r) {
+      const int ql = r * 16 + (lane >> 2);
+      const int c = (lane & 3) * 4;
+      const int qi = wave_q0 + ql;
+      const int pos = ctx + (qi - cq0);
+      const int pp = pg0 + c;
+      const float* src = sbuf + ql * kSRow + c;
+      const float v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
+      if (qi < q_end) {
+        float* dst = a.scores + (int64_t)qi * a.ld + pp;
+        const int vis_end = min(pg_hi, pos / kPage + 1);   // pages < vis_end are written
+        if (pp + 3 < vis_end) {
+          *reinterpret_cast<v4f*>(dst) = v4f{v0, v1, v2, v3};
+        } else {
+          if (pp + 0 < vis_end) dst[0] = v0;
+          if (pp + 1 < vis_end) dst[1] = v1;
+          if (pp + 2 < vis_end) dst[2] = v2;
+        }
+      }
+    }
+  };
 
-  int buf = 0;
-  for (int p = p0; p < p_end; ++p) {
-    const bool has_next = p + 1 < p_end;
-    if (has_next) {
-      const uint8_t* src = page_ptr(p + 1);
-      stage0 = load16_nt(src);
-      stage1 = load16_nt(src + 16);
+  auto score_page = [&](int p) {
+    const uint8_t* pg = lds + (p & 3) * kLdsPage;
+    v4f rmax[NQT];
+    if ((p + 1) * kPage - 1 > pos_first)
+      page_max_causal<H, NQT>(pg, qf, my_pos0 - p * kPage, col, grp, rmax);
+    else
+      page_max<H, NQT>(pg, qf, col, grp, rmax);
+    const int pc = p & (kFlush - 1);
+#pragma unroll
+    for (int n = 0; n < NQT; ++n) {
+      float m = fmaxf(fmaxf(rmax[n][0], rmax[n][1]), fmaxf(rmax[n][2], rmax[n][3]));
+      m = max_across_groups(m);
+      if ((n & 3) == grp) sbuf[(n * 16 + col) * kSRow + pc] = m * scale;
     }
+    if (pc == kFlush - 1 || p == p_end - 1) flush(p & ~(kFlush - 1), p + 1);
+  };
+
+  // One step: score pages p, p + 1; write the staged pair p + 2, p + 3 into the
+  // other half of the ring; barrier; start loading pair p + 6, p + 7.
+  auto step = [&](int p, uint4 (&st)[2][kV]) {
     if (wave_active) {
-      const uint8_t* pg = lds + buf * kLdsPage;
-      const bool need_mask = (p + 1) * kPage - 1 > pos_first;
-      v4f rmax[NQT];
-#pragma unroll
-      for (int n = 0; n < NQT; ++n) rmax[n] = v4f{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll 2
-      for (int T = 0; T < 8; ++T) {
-        const v8i ka = load_frag_lds(pg + (T * 16 + col) * kLdsRow + grp * 32);
-#pragma unroll
-        for (int n = 0; n < NQT; ++n) {
-          v4f acc = mfma_e4m3(ka, qf[n][0], v4f{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-          for (int h = 1; h < H; ++h) acc = mfma_e4m3(ka, qf[n][h], acc);
-          if (need_mask) {
-            const int lim = qpos[n] - p * kPage;   // last visible token index in this page
-            const int t0 = T * 16 + grp * 4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (t0 + i > lim) acc[i] = -INFINITY;
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) rmax[n][i] = fmaxf(rmax[n][i], acc[i]);
-        }
-      }
-#pragma unroll
-      for (int n = 0; n < NQT; ++n) {
-        float m = fmaxf(fmaxf(rmax[n][0], rmax[n][1]), fmaxf(rmax[n][2], rmax[n][3]));
-        m = max_across_groups(m);
-        if (grp == (p & 3)) stash[n] = m * scale;
-      }
-      if ((p & 3) == 3 || p == p_end - 1) {
-        const int pp = (p & ~3) + grp;
-#pragma unroll
-        for (int n = 0; n < NQT; ++n) {
-          if (qrow[n] >= 0 && pp >= p0 && pp <= p && pp * kPage <= qpos[n])
-            a.scores[(int64_t)qrow[n] * a.ld + pp] = stash[n];
-        }
-      }
+      if (p < p_end) score_page(p);
+      if (p + 1 < p_end) score_page(p + 1);
     }
-    if (has_next) {
-      uint4* dst = reinterpret_cast<uint4*>(lds + (buf ^ 1) * kLdsPage + st_row * kLdsRow + st_col);
-      dst[0] = stage0;
-      dst[1] = stage1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (p + 2 + j < p_end) {
+        uint4* dst = lds_slot(p + 2 + j);   // last read while scoring pair p - 2
+#pragma unroll
+        for (int v = 0; v < kV; ++v) dst[v] = st[j][v];
+      }
     }
     __syncthreads();
-    buf ^= 1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint8_t* src = page_ptr(p + 6 + j);
+#pragma unroll
+      for (int v = 0; v < kV; ++v) st[j][v] = load16_nt(src + 16 * v);
+    }
+  };
+  // Every iteration runs both steps (a step past the end only keeps the
+  // barrier and load counts uniform).
+  for (int pb = p0; pb < p_end; pb += 4) {
+    step(pb, stA);
+    step(pb + 2, stB);
   }
 }
 
 }  // namespace
+
+template <int H>
+hipError_t launch_scorer(dim3 grid, hipStream_t stream, const ScoreK& k) {
+  constexpr size_t bytes = score_lds_bytes<H>();
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&index_score_kernel<H>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(index_score_kernel<H>, grid, dim3(kThreads), bytes, stream, k);
+  return hipGetLastError();
+}
 
 ScorePlan score_plan(const msa_varlen_t* vl, int H) {
   ScorePlan p;
@@ -241,7 +387,7 @@ ScorePlan score_plan(const msa_varlen_t* vl, int H) {
   const int64_t max_pages = std::max<int32_t>(1, vl->max_pages);
   // about two items per compute unit in total, 4..256 pages per item
   int64_t pc = ceil_div(max_pages * est_qb, 512);
-  pc = std::min<int64_t>(256, std::max<int64_t>(4, ceil_div(pc, 4) * 4));
+  pc = std::min<int64_t>(kMaxItemPages, std::max<int64_t>(kFlush, ceil_div(pc, kFlush) * kFlush));
   p.pages_per_item = (int32_t)pc;
   p.max_items = qb_bound * ceil_div(max_pages, pc);
   p.workspace_bytes = sizeof(ItemHdr) + align_up((size_t)p.max_items * sizeof(int4), 256);
@@ -277,12 +423,11 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
   k.pages_per_item = a.plan.pages_per_item;
   dim3 grid((unsigned)a.plan.max_items);
   switch (a.H) {
-    case 1: hipLaunchKernelGGL(index_score_kernel<1>, grid, dim3(kThreads), 0, stream, k); break;
-    case 2: hipLaunchKernelGGL(index_score_kernel<2>, grid, dim3(kThreads), 0, stream, k); break;
-    case 4: hipLaunchKernelGGL(index_score_kernel<4>, grid, dim3(kThreads), 0, stream, k); break;
+    case 1: return launch_scorer<1>(grid, stream, k);
+    case 2: return launch_scorer<2>(grid, stream, k);
+    case 4: return launch_scorer<4>(grid, stream, k);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace msa

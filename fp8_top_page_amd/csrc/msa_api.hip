@@ -116,6 +116,8 @@ msa_status_t msa_index_score(const msa_varlen_t* vl, const uint8_t* q, int64_t q
   MSA_CHECK(num_pages >= 1, MSA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
   MSA_CHECK(ld_scores >= vl->max_pages && ld_scores >= 1, MSA_ERR_INVALID_ARGUMENT,
             "ld_scores (%lld) < max_pages (%d)", (long long)ld_scores, vl->max_pages);
+  MSA_CHECK(ld_scores % 4 == 0 && aligned(scores, 16), MSA_ERR_INVALID_ARGUMENT,
+            "ld_scores must be a multiple of 4 and scores 16-byte aligned");
   MSA_CHECK(aligned(workspace, 16), MSA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   const ScorePlan plan = score_plan(vl, H);
   MSA_CHECK(workspace_bytes >= plan.workspace_bytes, MSA_ERR_WORKSPACE_TOO_SMALL,

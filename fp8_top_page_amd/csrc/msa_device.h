@@ -48,16 +48,23 @@ __device__ __forceinline__ v8i load_frag_lds(const uint8_t* p) {
   return r;
 }
 
-// Reductions across the four 16-lane groups (lanes l, l^16, l^32, l^48).
+// Reductions across the four 16-lane groups (lanes l, l^16, l^32, l^48), on the
+// VALU with the gfx950 lane-swap instructions: permlane32_swap exchanges the two
+// 32-lane halves between its two operands and permlane16_swap the odd/even
+// 16-lane rows, so with both operands equal to x the pair it returns holds x and
+// x's partner (in some order) and a symmetric max/sum of the two completes one
+// butterfly step.
 __device__ __forceinline__ float max_across_groups(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_across_groups(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Monotone map float -> uint32 (larger float, larger key).  NaN maps to 0, below

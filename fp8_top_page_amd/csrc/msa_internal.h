@@ -14,10 +14,19 @@ constexpr int kDim = MSA_HEAD_DIM;     // head dimension (bytes per E4M3 row)
 constexpr int kTopK = MSA_TOPK;
 
 // ---- index scorer tiling -------------------------------------------------
-// A work item is (request, block of up to kScoreQB(H) queries, chunk of pages).
-// Every wave keeps 128/H queries' fragments in registers; 8 waves per block.
-constexpr int kScoreWaves = 8;
-constexpr int score_qblock(int H) { return kScoreWaves * 128 / H; }
+// A work item is (request, block of score_qblock(H) queries, chunk of pages).
+// Every wave keeps the fragments of kScoreQueriesPerWave / H queries (all H
+// heads) in registers; kScoreWaves waves share one index-K page in LDS.
+#ifndef MSA_SCORE_WAVES
+#define MSA_SCORE_WAVES 16
+#endif
+#ifndef MSA_SCORE_QPW
+#define MSA_SCORE_QPW 64
+#endif
+constexpr int kScoreWaves = MSA_SCORE_WAVES;
+constexpr int kScoreQueriesPerWave = MSA_SCORE_QPW;
+constexpr int score_qtiles(int H) { return kScoreQueriesPerWave / 16 / H; }
+constexpr int score_qblock(int H) { return kScoreWaves * 16 * score_qtiles(H); }
 
 struct ScorePlan {
   int32_t pages_per_item;   // multiple of 4

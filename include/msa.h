@@ -98,7 +98,8 @@ typedef struct {
  *   k_cache    [num_pages, 128, 128] E4M3: one 128-byte index-K row per token
  *              ([P3] Details), paged through the same block_table
  *   q_scale, k_scale  device fp32 scalars (per-tensor dequantisation scales)
- *   scores     fp32 [total_q, ld_scores], ld_scores >= max_pages
+ *   scores     fp32 [total_q, ld_scores], ld_scores >= max_pages and a multiple of 4,
+ *              16-byte aligned
  *   workspace  >= msa_index_score_workspace_size(vl, H) bytes, 16-byte aligned
  * ------------------------------------------------------------------------- */
 size_t msa_index_score_workspace_size(const msa_varlen_t* vl, int32_t num_index_heads);

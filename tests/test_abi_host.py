@@ -71,6 +71,7 @@ def test_index_score_validation():
     assert score(vl(), q_stride=136) == INVALID         # not a multiple of 16
     assert score(vl(), q=FAKE + 8) == INVALID           # misaligned
     assert score(vl(), ld=7) == INVALID                 # ld < max_pages
+    assert score(vl(), ld=10) == INVALID                # ld not a multiple of 4
     assert score(vl(), num_pages=0) == INVALID
     assert score(vl(), ws=16) == WS_SMALL
     assert score(vl(batch=0)) == INVALID
