@@ -32,6 +32,7 @@ constexpr int kThreads = kScoreWaves * 64;
 constexpr int kFlush = 16;                   // pages per score-tile flush (divides the item size)
 constexpr int kSRow = kFlush + 1;            // score-tile row stride in floats
 constexpr int kMaxItemPages = 256;           // pages per work item, at most
+constexpr int kPlanCUs = 256;                // compute units the item sizing aims to fill
 
 struct ItemHdr {
   int32_t n_items;
@@ -385,8 +386,14 @@ ScorePlan score_plan(const msa_varlen_t* vl, int H) {
   const int64_t est_qb = std::max<int64_t>(1, ceil_div(vl->total_q, qb));
   const int64_t qb_bound = ceil_div(vl->total_q, qb) + vl->batch;
   const int64_t max_pages = std::max<int32_t>(1, vl->max_pages);
-  // about two items per compute unit in total, 4..256 pages per item
-  int64_t pc = ceil_div(max_pages * est_qb, 512);
+  // Size items from the estimated page work (q-blocks x visible pages).  When
+  // the queries are a short tail of long contexts every q-block sees about the
+  // same pages, so one item per compute unit balances; when they cover much of
+  // the context (causal prefill) item sizes vary, so aim for two per unit.
+  const int64_t avg_visible =
+      std::max<int64_t>(1, max_pages - ceil_div(std::max(vl->max_seqlen_q, 1), kPage) / 2);
+  const bool uniform = (int64_t)vl->max_seqlen_q * 4 <= vl->max_seqlen_k;
+  int64_t pc = ceil_div(est_qb * avg_visible, kPlanCUs * (uniform ? 1 : 2));
   pc = std::min<int64_t>(kMaxItemPages, std::max<int64_t>(kFlush, ceil_div(pc, kFlush) * kFlush));
   p.pages_per_item = (int32_t)pc;
   p.max_items = qb_bound * ceil_div(max_pages, pc);

@@ -227,10 +227,11 @@ msa_status_t msa_sparse_attn_prefill(const msa_varlen_t* vl, const uint8_t* q, i
             MSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
   MSA_CHECK(q_stride >= (int64_t)Hq * kDim && q_stride % 16 == 0, MSA_ERR_INVALID_ARGUMENT,
             "q_stride must be >= Hq*128 and a multiple of 16");
-  MSA_CHECK(out_stride >= (int64_t)Hq * kDim && out_stride % 2 == 0, MSA_ERR_INVALID_ARGUMENT,
-            "out_stride must be >= Hq*128 and even");
-  MSA_CHECK(aligned(q, 16) && aligned(kv_cache, 16) && aligned(out, 4), MSA_ERR_INVALID_ARGUMENT,
-            "q and kv_cache must be 16-byte aligned, out 4-byte aligned");
+  MSA_CHECK(out_stride >= (int64_t)Hq * kDim && out_stride % 8 == 0, MSA_ERR_INVALID_ARGUMENT,
+            "out_stride must be >= Hq*128 and a multiple of 8");
+  MSA_CHECK(aligned(q, 16) && aligned(kv_cache, 16) && aligned(out, 16), MSA_ERR_INVALID_ARGUMENT,
+            "q, kv_cache and out must be 16-byte aligned");
+  MSA_CHECK(Hq <= 64, MSA_ERR_UNSUPPORTED, "num_q_heads must be <= 64 (got %d)", Hq);
   MSA_CHECK(num_pages >= 1, MSA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
   MSA_CHECK(softmax_scale > 0.f, MSA_ERR_INVALID_ARGUMENT, "softmax_scale must be > 0");
   MSA_CHECK(aligned(schedule, 16) && aligned(workspace, 16), MSA_ERR_INVALID_ARGUMENT,

@@ -63,7 +63,7 @@ struct AttnK {
 
 __device__ __forceinline__ uint32_t byte_of(uint32_t w, int k) { return (w >> (8 * k)) & 0xFFu; }
 
-__global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnK a) {
+__global__ __launch_bounds__(kThreads, 4) void attn_partial_kernel(AttnK a) {
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[kPage * kRowB];
   __shared__ __attribute__((aligned(16))) uint8_t vt_lds[kDim * kRowB];
 
@@ -131,6 +131,12 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnK a) {
   const int n_tiles = (n_rows + 15) >> 4;
 
   for (int tile = wave; tile < n_tiles; tile += kThreads / 64) {
+    // Re-read the page fragments from LDS for every tile instead of keeping all
+    // 16 of them (128 registers) live across tiles: the launder stops the
+    // compiler from hoisting the loads out of the loop.
+    const uint8_t* k_base = k_lds;
+    const uint8_t* v_base = vt_lds;
+    asm volatile("" : "+v"(k_base), "+v"(v_base));
     const int rid = tile * 16 + col;
     const bool valid = rid < n_rows;
     const int ql = valid ? rid / a.G : 0;
@@ -145,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnK a) {
     v4f s[8];
 #pragma unroll
     for (int T = 0; T < 8; ++T) {
-      const v8i ka = load_frag_lds(k_lds + (T * 16 + col) * kRowB + grp * 32);
+      const v8i ka = load_frag_lds(k_base + (T * 16 + col) * kRowB + grp * 32);
       s[T] = mfma_e4m3(ka, qb, v4f{0.f, 0.f, 0.f, 0.f});
     }
     float mx = -INFINITY;
@@ -174,24 +180,33 @@ __global__ __launch_bounds__(kThreads) void attn_partial_kernel(AttnK a) {
     }
     l = sum_across_groups(l);
 
-    v4f o[8];
+    // O^T = V^T P^T in two halves of 64 output dims, each stored as soon as it
+    // is done (keeps the live accumulators to 16 registers).
+    const int64_t pidx = (int64_t)(start + ql) * a.HP + (a.n_sel == 1 ? hq : h);
+    const float inv_l = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* dst = a.part_o + pidx * kDim + grp * 4;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const v8i va = load_frag_lds(vt_lds + (dt * 16 + col) * kRowB + grp * 32);
-      o[dt] = mfma_e4m3(va, pb, v4f{0.f, 0.f, 0.f, 0.f});
+    for (int half = 0; half < 2; ++half) {
+      v4f o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int dt = half * 4 + k;
+        const v8i va = load_frag_lds(v_base + (dt * 16 + col) * kRowB + grp * 32);
+        o[k] = mfma_e4m3(va, pb, v4f{0.f, 0.f, 0.f, 0.f});
+      }
+      if (valid) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int dt = half * 4 + k;
+          const uint32_t lo = (uint32_t)f32_to_bf16(o[k][0] * inv_l) |
+                              ((uint32_t)f32_to_bf16(o[k][1] * inv_l) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16(o[k][2] * inv_l) |
+                              ((uint32_t)f32_to_bf16(o[k][3] * inv_l) << 16);
+          *reinterpret_cast<uint2*>(dst + dt * 16) = make_uint2(lo, hi);
+        }
+      }
     }
     if (valid) {
-      const int64_t pidx = (int64_t)(start + ql) * a.HP + (a.n_sel == 1 ? hq : h);
-      const float inv_l = l > 0.f ? 1.f / l : 0.f;
-      uint16_t* dst = a.part_o + pidx * kDim + grp * 4;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const uint32_t lo = (uint32_t)f32_to_bf16(o[dt][0] * inv_l) |
-                            ((uint32_t)f32_to_bf16(o[dt][1] * inv_l) << 16);
-        const uint32_t hi = (uint32_t)f32_to_bf16(o[dt][2] * inv_l) |
-                            ((uint32_t)f32_to_bf16(o[dt][3] * inv_l) << 16);
-        *reinterpret_cast<uint2*>(dst + dt * 16) = make_uint2(lo, hi);
-      }
       if (grp == 0) a.part_lse[pidx] = (l > 0.f) ? mx + __log2f(l) : -INFINITY;
     }
   }
@@ -208,13 +223,13 @@ struct CombineK {
   int64_t out_stride;
 };
 
-// One wave per (query, q-head); lane l owns output dims 2l, 2l+1.
-__global__ __launch_bounds__(256) void attn_combine_kernel(CombineK a) {
-  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (pair >= a.total_q * a.Hq) return;
-  const int64_t i = pair / a.Hq;
-  const int hq = (int)(pair - i * a.Hq);
+// One block per query, Hq * 16 threads: thread t owns q-head t / 16 and output
+// dims 8 * (t % 16) .. + 7, so each split row (all heads of one (query, page)
+// pair, contiguous) is read with 16-byte loads.
+__global__ __launch_bounds__(1024) void attn_combine_kernel(CombineK a) {
+  const int64_t i = blockIdx.x;
+  const int t = threadIdx.x;
+  const int hq = t >> 4, d0 = (t & 15) * 8;
   const int sel = a.n_sel == 1 ? 0 : hq / a.G;
   const int hp = a.n_sel == 1 ? hq : hq % a.G;
   const int32_t* pos = a.inv + (i * a.n_sel + sel) * kTopK;
@@ -227,25 +242,33 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineK a) {
     ls[s] = pi[s] >= 0 ? a.part_lse[(int64_t)pi[s] * a.HP + hp] : -INFINITY;
     M = fmaxf(M, ls[s]);
   }
-  float o0 = 0.f, o1 = 0.f;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (M != -INFINITY) {
     float W = 0.f;
 #pragma unroll
     for (int s = 0; s < kTopK; ++s) {
       if (ls[s] == -INFINITY) continue;
       const float w = __builtin_amdgcn_exp2f(ls[s] - M);
-      const uint32_t two = *reinterpret_cast<const uint32_t*>(
-          a.part_o + ((int64_t)pi[s] * a.HP + hp) * kDim + 2 * lane);
-      o0 += w * bf16_to_f32((uint16_t)(two & 0xFFFFu));
-      o1 += w * bf16_to_f32((uint16_t)(two >> 16));
+      const uint4 v = *reinterpret_cast<const uint4*>(
+          a.part_o + ((int64_t)pi[s] * a.HP + hp) * kDim + d0);
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        o[2 * k] += w * bf16_to_f32((uint16_t)(wv[k] & 0xFFFFu));
+        o[2 * k + 1] += w * bf16_to_f32((uint16_t)(wv[k] >> 16));
+      }
       W += w;
     }
-    const float vs = a.v_scale ? *a.v_scale : 1.f;
-    o0 = o0 / W * vs;
-    o1 = o1 / W * vs;
+    const float f = (a.v_scale ? *a.v_scale : 1.f) / W;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[k] *= f;
   }
-  const uint32_t packed = (uint32_t)f32_to_bf16(o0) | ((uint32_t)f32_to_bf16(o1) << 16);
-  *reinterpret_cast<uint32_t*>(a.out + i * a.out_stride + hq * kDim + 2 * lane) = packed;
+  uint4 packed;
+  packed.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+  packed.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+  packed.z = (uint32_t)f32_to_bf16(o[4]) | ((uint32_t)f32_to_bf16(o[5]) << 16);
+  packed.w = (uint32_t)f32_to_bf16(o[6]) | ((uint32_t)f32_to_bf16(o[7]) << 16);
+  *reinterpret_cast<uint4*>(a.out + i * a.out_stride + hq * kDim + d0) = packed;
 }
 
 }  // namespace
@@ -309,8 +332,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   c.v_scale = a.v_scale;
   c.out = a.out;
   c.out_stride = a.out_stride;
-  const int64_t pairs = (int64_t)a.vl.total_q * a.Hq;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)ceil_div(pairs, 4)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)a.vl.total_q), dim3(a.Hq * 16), 0, stream,
                      c);
   return hipGetLastError();
 }

@@ -170,11 +170,12 @@ msa_status_t msa_build_k2q_csr(const msa_varlen_t* vl, const int32_t* topk_idx,
  * Queries with no attended token get 0.
  *   q          [total_q, Hq, 128] E4M3, token stride q_stride bytes (>= Hq*128, multiple of 16)
  *   kv_cache   [num_pages, Hkv, 128, 256] E4M3 (K|V packed per token)
- *   Hq % Hkv == 0, Hkv >= 1; n_sel_heads in {1, Hkv}; topk == 16
+ *   Hq % Hkv == 0, Hkv >= 1, Hq <= 64; n_sel_heads in {1, Hkv}; topk == 16
  *   row_ptr, q_indices, schedule: exactly as written by msa_build_k2q_csr for
  *              the same vl, n_sel_heads and topk
  *   q_scale, k_scale, v_scale  device fp32 scalars, or NULL for 1.0
- *   out        bf16 [total_q, Hq, 128], token stride out_stride elements (>= Hq*128)
+ *   out        bf16 [total_q, Hq, 128], token stride out_stride elements (>= Hq*128,
+ *              multiple of 8), 16-byte aligned
  *   workspace  >= msa_sparse_attn_workspace_size(vl, Hq, Hkv, n_sel_heads, topk) bytes
  * ------------------------------------------------------------------------- */
 size_t msa_sparse_attn_workspace_size(const msa_varlen_t* vl, int32_t num_q_heads,

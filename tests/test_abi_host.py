@@ -138,6 +138,8 @@ def test_attention_validation():
     assert attn(v, n_sel=2) == UNSUPPORTED
     assert attn(v, q_stride=512) == INVALID
     assert attn(v, out_stride=1023) == INVALID
+    assert attn(v, out_stride=1028) == INVALID
+    assert attn(v, Hq=128, Hkv=1, q_stride=16384, out_stride=16384) == UNSUPPORTED
     assert attn(v, sm=0.0) == INVALID
     assert attn(v, ws=100) == WS_SMALL
     assert attn(v, sched=100) == WS_SMALL
