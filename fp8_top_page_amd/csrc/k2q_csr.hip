@@ -7,25 +7,31 @@
 // return_schedule=True) returns row_ptr, q_indices and a schedule).
 //
 // Deterministic without sorting: every row owns a bitmap over its request's
-// query slots.  Marking sets bits with atomic OR; a row's popcount is its
-// length; the fill walks the bitmap in order, so each row comes out ascending.
-// The fill also records, for every (query, selection head, slot), the CSR
-// position of that entry (the combine uses it to find a query's partials in
-// slot order) and emits the attention work items: (row, first entry) for
-// chunks of kAttnQC entries.
+// query slots.  Marks are atomic ORs; the bitmap is walked in order, so each row
+// comes out ascending.  A row's bitmap is cut into units of 64 words (2048
+// query slots); units are the grain of the count, scan and fill passes, so long
+// rows (a page chosen by thousands of queries) are spread over many waves.
 //
-// Kernels (all on the caller's stream, no host sync):
-//   prep   -- row_base[b] = sum of page counts of earlier requests; zero header
-//   zero   -- clear the bitmap
-//   mark   -- one thread per (query, head, slot)
-//   count  -- one wave per row: popcount
-//   scan   -- one block: row_ptr and per-row item offsets (exclusive scans)
-//   fill   -- one wave per row: q_indices, positions, work items
+// Four launches on the caller's stream, no host sync:
+//   clear  -- zero the bitmap, set the position table to -1; block 0 also
+//             computes row_base[b] (page rows of earlier requests)
+//   mark   -- one thread per (query, selection head, slot)
+//   count  -- one wave per unit: entries and attention items of the unit, and
+//             per-block totals
+//   fill   -- per block: base offsets from the totals of earlier blocks, scan of
+//             its units, then one wave per unit writes q_indices (ascending),
+//             the (query, slot) -> position table, row_ptr and the work items
+//             (row, first entry, count) of at most kAttnQC entries each
 #include "msa_device.h"
 #include "msa_internal.h"
 
 namespace msa {
 namespace {
+
+constexpr int kUnitWords = 64;                 // bitmap words per unit (one per lane)
+constexpr int kUnitsPerBlock = 4;              // units per count/fill block (one per wave)
+constexpr int kUnitsPerWave = kUnitsPerBlock / (256 / 64);
+constexpr int kThreads = 256;
 
 struct Hdr {
   int32_t n_items;
@@ -33,34 +39,44 @@ struct Hdr {
   int32_t pad[62];
 };
 
-__global__ __launch_bounds__(256) void csr_prep_kernel(const int32_t* __restrict__ cu_k, int B,
-                                                       int32_t* __restrict__ row_base,
-                                                       Hdr* __restrict__ hdr) {
-  // single block: exclusive scan of ceil(seqlen_k / 128) over requests
-  __shared__ int wave_tot[4];
-  __shared__ int running;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) { running = 0; hdr->n_items = 0; hdr->nnz = 0; }
-  __syncthreads();
-  for (int base = 0; base <= B; base += 256) {
-    const int b = base + tid;
-    int pages = 0;
-    if (b < B) pages = (cu_k[b + 1] - cu_k[b] + kPage - 1) / kPage;
-    const int incl = wave_inclusive_scan(pages);
-    if (lane == 63) wave_tot[wave] = incl;
-    __syncthreads();
-    int off = running;
-    for (int w = 0; w < wave; ++w) off += wave_tot[w];
-    if (b <= B) row_base[b] = off + incl - pages;
-    __syncthreads();
-    if (tid == 255) running = off + incl;
-    __syncthreads();
-  }
-}
+struct ClearK {
+  const int32_t* cu_k;
+  int32_t batch;
+  int32_t* row_base;
+  Hdr* hdr;
+  uint32_t* bitmap;
+  int64_t n_words;
+  int32_t* inv;
+  int64_t inv_len;
+};
 
-__global__ void fill_words_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t value) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += stride) p[k] = value;
+__global__ __launch_bounds__(kThreads) void csr_clear_kernel(ClearK a) {
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0) {
+    // exclusive scan of ceil(seqlen_k / 128) over requests
+    __shared__ int wave_tot[kThreads / 64];
+    __shared__ int running;
+    const int lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) { running = 0; a.hdr->n_items = 0; a.hdr->nnz = 0; }
+    __syncthreads();
+    for (int base = 0; base <= a.batch; base += kThreads) {
+      const int b = base + tid;
+      int pages = 0;
+      if (b < a.batch) pages = (a.cu_k[b + 1] - a.cu_k[b] + kPage - 1) / kPage;
+      const int incl = wave_inclusive_scan(pages);
+      if (lane == 63) wave_tot[wave] = incl;
+      __syncthreads();
+      int off = running;
+      for (int w = 0; w < wave; ++w) off += wave_tot[w];
+      if (b <= a.batch) a.row_base[b] = off + incl - pages;
+      __syncthreads();
+      if (tid == kThreads - 1) running = off + incl;
+      __syncthreads();
+    }
+  }
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t k = (int64_t)blockIdx.x * kThreads + tid; k < a.n_words; k += stride) a.bitmap[k] = 0u;
+  for (int64_t k = (int64_t)blockIdx.x * kThreads + tid; k < a.inv_len; k += stride) a.inv[k] = -1;
 }
 
 struct MarkK {
@@ -77,7 +93,7 @@ struct MarkK {
   int64_t words;
 };
 
-__global__ __launch_bounds__(256) void csr_mark_kernel(MarkK a) {
+__global__ __launch_bounds__(kThreads) void csr_mark_kernel(MarkK a) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (query, head, slot)
   const int64_t per_q = (int64_t)a.n_sel * kTopK;
   if (e >= a.total_q * per_q) return;
@@ -97,58 +113,57 @@ __global__ __launch_bounds__(256) void csr_mark_kernel(MarkK a) {
   atomicOr(&a.bitmap[row * a.words + (local >> 5)], 1u << (local & 31));
 }
 
-__global__ __launch_bounds__(256) void csr_count_kernel(const uint32_t* __restrict__ bitmap,
-                                                        int64_t words, int64_t n_rows,
-                                                        int32_t* __restrict__ counts) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= n_rows) return;
-  const uint32_t* w = bitmap + row * words;
-  int c = 0;
-  for (int64_t k = lane; k < words; k += 64) c += __popc(w[k]);
-  c = wave_sum(c);
-  if (lane == 0) counts[row] = c;
+struct CountK {
+  const uint32_t* bitmap;
+  int64_t words;          // per row
+  int32_t units_per_row;
+  int64_t n_units;
+  int32_t* unit_cnt;
+  int32_t* blk_tot;       // [n_blocks]: entries
+  int32_t* blk_items;     // [n_blocks]: attention items
+};
+
+__device__ __forceinline__ int unit_popcount(const uint32_t* bitmap, int64_t words, int upr,
+                                             int64_t u, int lane, uint32_t* bits_out) {
+  const int64_t row = u / upr;
+  const int64_t w = (u % upr) * kUnitWords + lane;
+  const uint32_t bits = w < words ? bitmap[row * words + w] : 0u;
+  *bits_out = bits;
+  return __popc(bits);
 }
 
-// Single block of 1024: row_ptr = exclusive scan of counts (counts live in
-// row_ptr[1..n]); row_items = exclusive scan of ceil(count / kAttnQC).
-__global__ __launch_bounds__(1024) void csr_scan_kernel(int32_t* __restrict__ row_ptr,
-                                                        int32_t* __restrict__ row_items,
-                                                        int64_t n_rows, Hdr* __restrict__ hdr) {
-  __shared__ int wt_a[16], wt_b[16];
-  __shared__ int run_a, run_b;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) { run_a = 0; run_b = 0; }
-  __syncthreads();
-  for (int64_t base = 0; base < n_rows; base += 1024) {
-    const int64_t r = base + tid;
-    const int c = r < n_rows ? row_ptr[r + 1] : 0;
-    const int it = (c + kAttnQC - 1) / kAttnQC;
-    const int ia = wave_inclusive_scan(c);
-    const int ib = wave_inclusive_scan(it);
-    if (lane == 63) { wt_a[wave] = ia; wt_b[wave] = ib; }
-    __syncthreads();
-    int oa = run_a, ob = run_b;
-    for (int w = 0; w < wave; ++w) { oa += wt_a[w]; ob += wt_b[w]; }
-    __syncthreads();   // all reads of row_ptr[r+1] in this chunk precede the writes below
-    if (r < n_rows) {
-      row_ptr[r] = oa + ia - c;
-      row_items[r] = ob + ib - it;
-    }
-    if (tid == 1023) { run_a = oa + ia; run_b = ob + ib; }
-    __syncthreads();
+__global__ __launch_bounds__(kThreads) void csr_count_kernel(CountK a) {
+  __shared__ int s_tot[kThreads / 64], s_it[kThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t u0 = (int64_t)blockIdx.x * kUnitsPerBlock + wave * kUnitsPerWave;
+  uint32_t bits[kUnitsPerWave];
+#pragma unroll
+  for (int k = 0; k < kUnitsPerWave; ++k) {   // all loads in flight together
+    const int64_t u = u0 + k;
+    bits[k] = 0u;
+    if (u < a.n_units) unit_popcount(a.bitmap, a.words, a.units_per_row, u, lane, &bits[k]);
   }
-  if (tid == 0) {
-    row_ptr[n_rows] = run_a;
-    row_items[n_rows] = run_b;
-    hdr->nnz = run_a;
-    hdr->n_items = run_b;
+  int tot = 0, its = 0;
+#pragma unroll
+  for (int k = 0; k < kUnitsPerWave; ++k) {
+    const int64_t u = u0 + k;
+    const int c = wave_sum(__popc(bits[k]));
+    if (u < a.n_units && lane == 0) a.unit_cnt[u] = c;
+    tot += c;
+    its += (c + kAttnQC - 1) / kAttnQC;
+  }
+  if (lane == 0) { s_tot[wave] = tot; s_it[wave] = its; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int t = 0, i = 0;
+    for (int w = 0; w < kThreads / 64; ++w) { t += s_tot[w]; i += s_it[w]; }
+    a.blk_tot[blockIdx.x] = t;
+    a.blk_items[blockIdx.x] = i;
   }
 }
 
 struct FillK {
   const int32_t* cu_q;
-  const int32_t* cu_k;
   int32_t batch;
   const int32_t* topk;
   int64_t tq, th;
@@ -157,56 +172,126 @@ struct FillK {
   const int32_t* row_base;
   const uint32_t* bitmap;
   int64_t words;
+  int32_t units_per_row;
+  int64_t n_units;
   int64_t n_rows;
-  const int32_t* row_ptr;
-  const int32_t* row_items;
+  int32_t n_blocks;
+  const int32_t* unit_cnt;
+  const int32_t* blk_tot;
+  const int32_t* blk_items;
+  int32_t* row_ptr;
   int32_t* q_indices;
-  int32_t* inv;       // [total_q, n_sel, 16]
-  int2* items;
+  int32_t* inv;        // [total_q, n_sel, 16]
+  int4* items;
   int64_t max_items;
+  Hdr* hdr;
 };
 
-__global__ __launch_bounds__(256) void csr_fill_kernel(FillK a) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= a.n_rows) return;
-  const int g = (int)(row / a.total_rows);
-  const int64_t rr = row % a.total_rows;
-  const int b = find_request(a.row_base, a.batch, rr);
-  const int j = (int)(rr - a.row_base[b]);
-  const int cq0 = a.cu_q[b];
-  const int32_t start = a.row_ptr[row];
-  const uint32_t* w = a.bitmap + row * a.words;
-  int base = 0;
-  for (int64_t k0 = 0; k0 < a.words; k0 += 64) {
-    const int64_t k = k0 + lane;
-    uint32_t bits = k < a.words ? w[k] : 0u;
+__global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
+  __shared__ int s_red[2][kThreads / 64];
+  __shared__ int s_pos[kUnitsPerBlock];     // first CSR position of each unit
+  __shared__ int s_item[kUnitsPerBlock];    // first item index of each unit
+  __shared__ uint32_t s_words[kThreads / 64][64];
+  __shared__ int s_excl[kThreads / 64][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int blk = blockIdx.x;
+  const int64_t u0 = (int64_t)blk * kUnitsPerBlock;
+
+  // entries and items of all earlier blocks
+  int base_e = 0, base_i = 0;
+  for (int j = tid; j < blk; j += kThreads) {
+    base_e += a.blk_tot[j];
+    base_i += a.blk_items[j];
+  }
+  base_e = wave_sum(base_e);
+  base_i = wave_sum(base_i);
+  if (lane == 0) { s_red[0][wave] = base_e; s_red[1][wave] = base_i; }
+  __syncthreads();
+  base_e = 0;
+  base_i = 0;
+  for (int w = 0; w < kThreads / 64; ++w) { base_e += s_red[0][w]; base_i += s_red[1][w]; }
+
+  // scan of this block's units (one lane per unit)
+  static_assert(kUnitsPerBlock <= 64, "one lane per unit in the block scan");
+  if (wave == 0) {
+    const int64_t u = u0 + lane;
+    const bool mine = lane < kUnitsPerBlock && u < a.n_units;
+    const int c = mine ? a.unit_cnt[u] : 0;
+    const int it = (c + kAttnQC - 1) / kAttnQC;
+    const int ie = wave_inclusive_scan(c);
+    const int ii = wave_inclusive_scan(it);
+    if (lane < kUnitsPerBlock) {
+      s_pos[lane] = base_e + ie - c;
+      s_item[lane] = base_i + ii - it;
+    }
+    if (mine && u % a.units_per_row == 0) a.row_ptr[u / a.units_per_row] = base_e + ie - c;
+    if (blk == a.n_blocks - 1 && lane == 63) {
+      a.row_ptr[a.n_rows] = base_e + ie;
+      a.hdr->nnz = base_e + ie;
+      a.hdr->n_items = (int)min<int64_t>(base_i + ii, a.max_items);
+    }
+  }
+  __syncthreads();
+
+  uint32_t ubits[kUnitsPerWave];
+#pragma unroll
+  for (int k = 0; k < kUnitsPerWave; ++k) {   // all loads in flight together
+    const int64_t u = u0 + wave * kUnitsPerWave + k;
+    ubits[k] = 0u;
+    if (u < a.n_units) unit_popcount(a.bitmap, a.words, a.units_per_row, u, lane, &ubits[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < kUnitsPerWave; ++k) {
+    const int ku = wave * kUnitsPerWave + k;
+    const int64_t u = u0 + ku;
+    if (u >= a.n_units) break;
+    const int64_t row = u / a.units_per_row;
+    const int g = (int)(row / a.total_rows);
+    const int64_t rr = row % a.total_rows;
+    const int b = find_request(a.row_base, a.batch, rr);
+    const int j = (int)(rr - a.row_base[b]);
+    const int64_t q_base = a.cu_q[b] + (u % a.units_per_row) * (kUnitWords * 32);
+    // The unit's words and their exclusive bit counts go to the wave's LDS
+    // slice; then entry e of the unit (e = round * 64 + lane) is located by a
+    // binary search over the counts, so every lane handles one entry per round
+    // even when a few words hold all the bits.
+    const uint32_t bits = ubits[k];
     const int c = __popc(bits);
     const int incl = wave_inclusive_scan(c);
-    int p = start + base + incl - c;
-    while (bits) {
-      const int bit = __builtin_ctz(bits);
-      bits &= bits - 1;
-      const int64_t qi = cq0 + k * 32 + bit;
-      a.q_indices[p] = (int32_t)qi;
-      const int32_t* sel = a.topk + qi * a.tq + (int64_t)g * a.th;
-      for (int s = 0; s < kTopK; ++s) {
-        if (sel[s] == j) {
-          a.inv[(qi * a.n_sel + g) * kTopK + s] = p;
-          break;
-        }
+    s_words[wave][lane] = bits;
+    s_excl[wave][lane] = incl - c;
+    const int n = __shfl(incl, 63);
+    __builtin_amdgcn_wave_barrier();
+    for (int e = lane; e < n; e += 64) {
+      int lo = 0, hi = 63;              // last word with excl <= e
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_excl[wave][mid] <= e) lo = mid; else hi = mid - 1;
       }
-      ++p;
+      uint32_t x = s_words[wave][lo];
+      for (int r = e - s_excl[wave][lo]; r > 0; --r) x &= x - 1;
+      const int bit = __builtin_ctz(x);
+      const int64_t qi = q_base + lo * 32 + bit;
+      const int p = s_pos[ku] + e;
+      a.q_indices[p] = (int32_t)qi;
+      // slot of page j in the query's selection: read all 16 slots at once
+      const int32_t* sel = a.topk + qi * a.tq + (int64_t)g * a.th;
+      int sv[kTopK];
+#pragma unroll
+      for (int t = 0; t < kTopK; ++t) sv[t] = sel[t];
+      int slot = -1;
+#pragma unroll
+      for (int t = kTopK - 1; t >= 0; --t) slot = (sv[t] == j) ? t : slot;
+      if (slot >= 0) a.inv[(qi * a.n_sel + g) * kTopK + slot] = p;
     }
-    base += __shfl(incl, 63);
-  }
-  // work items of this row
-  const int32_t len = a.row_ptr[row + 1] - start;
-  const int32_t i0 = a.row_items[row];
-  const int n_it = (len + kAttnQC - 1) / kAttnQC;
-  for (int t = lane; t < n_it; t += 64) {
-    const int64_t idx = (int64_t)i0 + t;
-    if (idx < a.max_items) a.items[idx] = make_int2((int)row, start + t * kAttnQC);
+    __builtin_amdgcn_wave_barrier();
+    // work items of the unit: (row, first entry, count)
+    const int n_it = (n + kAttnQC - 1) / kAttnQC;
+    for (int t = lane; t < n_it; t += 64) {
+      const int64_t idx = (int64_t)s_item[ku] + t;
+      if (idx < a.max_items)
+        a.items[idx] = make_int4((int)row, s_pos[ku] + t * kAttnQC, min(kAttnQC, n - t * kAttnQC), 0);
+    }
   }
 }
 
@@ -216,13 +301,18 @@ SchedLayout sched_layout(const msa_varlen_t* vl, int n_sel, int topk) {
   SchedLayout L;
   L.n_rows = (int64_t)n_sel * vl->total_rows;
   L.words_per_row = std::max<int64_t>(1, ceil_div(std::max(vl->max_seqlen_q, 1), 32));
+  L.units_per_row = ceil_div(L.words_per_row, kUnitWords);
+  L.n_units = L.n_rows * L.units_per_row;
+  L.n_blocks = std::max<int64_t>(1, ceil_div(L.n_units, kUnitsPerBlock));
   L.inv_len = (int64_t)vl->total_q * n_sel * topk;
-  L.max_items = ceil_div((int64_t)n_sel * vl->total_q * topk, kAttnQC) + L.n_rows;
+  // every unit holding c entries yields ceil(c / kAttnQC) items
+  L.max_items = ceil_div((int64_t)n_sel * vl->total_q * topk, kAttnQC) + L.n_units;
   size_t off = 0;
   L.hdr = off;        off += sizeof(Hdr);
   L.row_base = off;   off += align_up(sizeof(int32_t) * (vl->batch + 1), 256);
-  L.row_items = off;  off += align_up(sizeof(int32_t) * (L.n_rows + 1), 256);
-  L.items = off;      off += align_up(sizeof(int2) * L.max_items, 256);
+  L.unit_cnt = off;   off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.n_units), 256);
+  L.blk_tot = off;    off += align_up(sizeof(int32_t) * 2 * L.n_blocks, 256);
+  L.items = off;      off += align_up(sizeof(int4) * std::max<int64_t>(1, L.max_items), 256);
   L.inv = off;        off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.inv_len), 256);
   L.bitmap = off;     off += align_up(sizeof(uint32_t) * L.n_rows * L.words_per_row, 256);
   L.total = off;
@@ -233,67 +323,35 @@ hipError_t launch_k2q_csr(const CsrArgs& a, hipStream_t stream) {
   const SchedLayout& L = a.L;
   Hdr* hdr = reinterpret_cast<Hdr*>(a.sched + L.hdr);
   int32_t* row_base = reinterpret_cast<int32_t*>(a.sched + L.row_base);
-  int32_t* row_items = reinterpret_cast<int32_t*>(a.sched + L.row_items);
-  int2* items = reinterpret_cast<int2*>(a.sched + L.items);
+  int32_t* unit_cnt = reinterpret_cast<int32_t*>(a.sched + L.unit_cnt);
+  int32_t* blk_tot = reinterpret_cast<int32_t*>(a.sched + L.blk_tot);
+  int32_t* blk_items = blk_tot + L.n_blocks;
+  int4* items = reinterpret_cast<int4*>(a.sched + L.items);
   int32_t* inv = reinterpret_cast<int32_t*>(a.sched + L.inv);
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(a.sched + L.bitmap);
   const int64_t n_words = L.n_rows * L.words_per_row;
 
-  hipLaunchKernelGGL(csr_prep_kernel, dim3(1), dim3(256), 0, stream, a.vl.cu_seqlens_k,
-                     a.vl.batch, row_base, hdr);
-  auto fill = [&](void* p, int64_t n, uint32_t value) {
-    if (n <= 0) return;
-    const int64_t blocks = std::min<int64_t>(8192, ceil_div(n, 256));
-    hipLaunchKernelGGL(fill_words_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       reinterpret_cast<uint32_t*>(p), n, value);
-  };
-  fill(bitmap, n_words, 0u);
-  fill(inv, L.inv_len, 0xFFFFFFFFu);   // -1: no entry
+  ClearK ck{a.vl.cu_seqlens_k, a.vl.batch, row_base, hdr, bitmap, n_words, inv, L.inv_len};
+  const int64_t clear_blocks =
+      std::min<int64_t>(2048, std::max<int64_t>(1, ceil_div(std::max(n_words, L.inv_len), kThreads)));
+  hipLaunchKernelGGL(csr_clear_kernel, dim3((unsigned)clear_blocks), dim3(kThreads), 0, stream, ck);
 
-  MarkK mk;
-  mk.cu_q = a.vl.cu_seqlens_q;
-  mk.cu_k = a.vl.cu_seqlens_k;
-  mk.batch = a.vl.batch;
-  mk.total_q = a.vl.total_q;
-  mk.topk = a.topk;
-  mk.tq = a.tq_stride;
-  mk.th = a.th_stride;
-  mk.n_sel = a.n_sel;
-  mk.total_rows = a.vl.total_rows;
-  mk.row_base = row_base;
-  mk.bitmap = bitmap;
-  mk.words = L.words_per_row;
+  MarkK mk{a.vl.cu_seqlens_q, a.vl.cu_seqlens_k, a.vl.batch, a.vl.total_q, a.topk, a.tq_stride,
+           a.th_stride, a.n_sel, a.vl.total_rows, row_base, bitmap, L.words_per_row};
   const int64_t n_mark = (int64_t)a.vl.total_q * a.n_sel * kTopK;
   if (n_mark > 0)
-    hipLaunchKernelGGL(csr_mark_kernel, dim3((unsigned)ceil_div(n_mark, 256)), dim3(256), 0,
-                       stream, mk);
-  if (L.n_rows > 0)
-    hipLaunchKernelGGL(csr_count_kernel, dim3((unsigned)ceil_div(L.n_rows, 4)), dim3(256), 0,
-                       stream, bitmap, L.words_per_row, L.n_rows, a.row_ptr + 1);
-  hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, stream, a.row_ptr, row_items,
-                     L.n_rows, hdr);
-  FillK fk;
-  fk.cu_q = a.vl.cu_seqlens_q;
-  fk.cu_k = a.vl.cu_seqlens_k;
-  fk.batch = a.vl.batch;
-  fk.topk = a.topk;
-  fk.tq = a.tq_stride;
-  fk.th = a.th_stride;
-  fk.n_sel = a.n_sel;
-  fk.total_rows = a.vl.total_rows;
-  fk.row_base = row_base;
-  fk.bitmap = bitmap;
-  fk.words = L.words_per_row;
-  fk.n_rows = L.n_rows;
-  fk.row_ptr = a.row_ptr;
-  fk.row_items = row_items;
-  fk.q_indices = a.q_indices;
-  fk.inv = inv;
-  fk.items = items;
-  fk.max_items = L.max_items;
-  if (L.n_rows > 0)
-    hipLaunchKernelGGL(csr_fill_kernel, dim3((unsigned)ceil_div(L.n_rows, 4)), dim3(256), 0,
-                       stream, fk);
+    hipLaunchKernelGGL(csr_mark_kernel, dim3((unsigned)ceil_div(n_mark, kThreads)), dim3(kThreads),
+                       0, stream, mk);
+
+  CountK cnt{bitmap, L.words_per_row, (int32_t)L.units_per_row, L.n_units, unit_cnt, blk_tot,
+             blk_items};
+  hipLaunchKernelGGL(csr_count_kernel, dim3((unsigned)L.n_blocks), dim3(kThreads), 0, stream, cnt);
+
+  FillK fk{a.vl.cu_seqlens_q, a.vl.batch, a.topk, a.tq_stride, a.th_stride, a.n_sel,
+           a.vl.total_rows, row_base, bitmap, L.words_per_row, (int32_t)L.units_per_row,
+           L.n_units, L.n_rows, (int32_t)L.n_blocks, unit_cnt, blk_tot, blk_items, a.row_ptr,
+           a.q_indices, inv, items, L.max_items, hdr};
+  hipLaunchKernelGGL(csr_fill_kernel, dim3((unsigned)L.n_blocks), dim3(kThreads), 0, stream, fk);
   return hipGetLastError();
 }
 

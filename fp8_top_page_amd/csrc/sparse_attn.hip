@@ -52,7 +52,7 @@ struct AttnK {
   const int32_t* row_base;
   const int32_t* row_ptr;
   const int32_t* q_indices;
-  const int2* items;
+  const int4* items;
   const int32_t* n_items;
   float logit_scale_log2;          // softmax_scale * log2(e)
   const float* q_scale;
@@ -69,10 +69,8 @@ __global__ __launch_bounds__(kThreads, 4) void attn_partial_kernel(AttnK a) {
 
   const int item = blockIdx.x;
   if (item >= *a.n_items) return;
-  const int2 it = a.items[item];
-  const int row = it.x, start = it.y;
-  const int end = min(a.row_ptr[row + 1], start + kAttnQC);
-  const int count = end - start;
+  const int4 it = a.items[item];
+  const int row = it.x, start = it.y, count = it.z;
   if (count <= 0) return;
   const int g_sel = row / a.total_rows;
   const int rr = row - g_sel * a.total_rows;
@@ -305,7 +303,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   k.row_base = reinterpret_cast<const int32_t*>(a.sched + L.row_base);
   k.row_ptr = a.row_ptr;
   k.q_indices = a.q_indices;
-  k.items = reinterpret_cast<const int2*>(a.sched + L.items);
+  k.items = reinterpret_cast<const int4*>(a.sched + L.items);
   k.n_items = reinterpret_cast<const int32_t*>(a.sched + L.hdr);
   k.logit_scale_log2 = a.softmax_scale * kLog2e;
   k.q_scale = a.q_scale;

@@ -51,13 +51,58 @@ __device__ __forceinline__ int block_sum(int x, int* red) {
   return s;
 }
 
+// Keys of (score, page) packed so that a larger value is a better candidate:
+// higher score first, then lower page.
+__device__ __forceinline__ uint64_t pack_key(uint32_t key, int page) {
+  return ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)page);
+}
+
+// Load KPT keys of this thread for the chunk starting at c0.  Thread t owns
+// pages c0 + kBlock*4*k + 4t + {0..3} (k < KPT/4) when KPT >= 4, so each load is
+// 16 contiguous bytes; otherwise pages c0 + kBlock*k + t.
+template <int KPT>
+__device__ __forceinline__ int key_page(int c0, int k, int tid) {
+  if constexpr (KPT >= 4) return c0 + (k >> 2) * (kBlock * 4) + tid * 4 + (k & 3);
+  else return c0 + k * kBlock + tid;
+}
+template <int KPT>
+__device__ __forceinline__ void load_keys(const float* row, int c0, int ncand, int tid,
+                                          uint32_t (&key)[KPT]) {
+  if constexpr (KPT >= 4) {
+#pragma unroll
+    for (int k4 = 0; k4 < KPT / 4; ++k4) {
+      const int j = c0 + k4 * (kBlock * 4) + tid * 4;
+      if (j + 3 < ncand) {
+        const float4 v = *reinterpret_cast<const float4*>(row + j);
+        key[4 * k4 + 0] = float_key(v.x);
+        key[4 * k4 + 1] = float_key(v.y);
+        key[4 * k4 + 2] = float_key(v.z);
+        key[4 * k4 + 3] = float_key(v.w);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[4 * k4 + e] = (j + e < ncand) ? float_key(row[j + e]) : 0u;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      const int j = c0 + k * kBlock + tid;
+      key[k] = j < ncand ? float_key(row[j]) : 0u;
+    }
+  }
+}
+
+// KPT keys per thread are held in registers: rows of up to kBlock * KPT
+// candidates are read once; longer rows are processed in chunks of that size and
+// re-read (from cache) by the second pass.
+template <int KPT>
 __global__ __launch_bounds__(kBlock) void topk_kernel(TopkK a) {
-  __shared__ uint32_t c_key[kCap];
-  __shared__ int32_t c_page[kCap];
+  __shared__ uint64_t c_pk[kCap];
   __shared__ uint32_t wave_tau[kBlock / 64];
   __shared__ int red[kBlock / 64];
   __shared__ int n_cand;
   __shared__ int n_eq_taken;
+  constexpr int kChunk = kBlock * KPT;
 
   const int64_t i = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -73,6 +118,7 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkK a) {
   const int ncand = v - f;
   int32_t* out = a.out + i * a.out_stride;
   const float* row = a.scores + i * a.ld;
+  const bool vec_ok = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
 
   if (tid < kTopK) {
     if (tid < f) out[tid] = v - 1 - tid;
@@ -80,33 +126,67 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkK a) {
   }
   if (ksel == 0) return;
 
-  // 1. lane maximum
+  // 1. lane maximum (all loads of a chunk are issued together)
+  uint32_t key[KPT];
   uint32_t m = 0;
-  for (int j = tid; j < ncand; j += kBlock) m = max(m, float_key(row[j]));
-  // 2. wave bound: key of the lane with rank ksel-1 by (key desc, lane asc)
-  int rank = 0;
-  for (int l = 0; l < 64; ++l) {
-    const uint32_t o = __builtin_amdgcn_readlane(m, l);
-    rank += (o > m || (o == m && l < lane)) ? 1 : 0;
+  for (int c0 = 0; c0 < ncand; c0 += kChunk) {
+    if (vec_ok) {
+      load_keys<KPT>(row, c0, ncand, tid, key);
+    } else {
+#pragma unroll
+      for (int k = 0; k < KPT; ++k) {
+        const int j = key_page<KPT>(c0, k, tid);
+        key[k] = j < ncand ? float_key(row[j]) : 0u;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) m = max(m, key[k]);
   }
-  const unsigned long long sel = __ballot(rank == ksel - 1);
-  const uint32_t tau_w = __builtin_amdgcn_readlane(m, __builtin_ctzll(sel));
-  if (lane == 0) wave_tau[wave] = tau_w;
+  const bool one_chunk = ncand <= kChunk;   // then key[] still holds every key
+
+  // 2. wave bound: the ksel-th largest lane maximum of the wave (bit-by-bit
+  //    search with ballots); ksel elements of the row reach it
+  uint32_t tw = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t t = tw | (1u << bit);
+    if (__popcll(__ballot(m >= t)) >= ksel) tw = t;
+  }
+  if (lane == 0) wave_tau[wave] = tw;
   if (tid == 0) n_cand = 0;
   __syncthreads();
   uint32_t tau = 0;
 #pragma unroll
   for (int w = 0; w < kBlock / 64; ++w) tau = max(tau, wave_tau[w]);
 
-  // 3. collect keys >= tau
-  for (int j = tid; j < ncand; j += kBlock) {
-    const uint32_t key = float_key(row[j]);
-    if (key >= tau) {
-      const int slot = atomicAdd(&n_cand, 1);
-      if (slot < kCap) {
-        c_key[slot] = key;
-        c_page[slot] = j;
+  // 3. collect keys >= tau: one atomic per wave, lanes write at their offsets
+  auto collect = [&](int c0, const uint32_t (&kk)[KPT]) {
+    int mine = 0;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) mine += (key_page<KPT>(c0, k, tid) < ncand && kk[k] >= tau) ? 1 : 0;
+    const int incl = wave_inclusive_scan(mine);
+    int base = 0;
+    if (lane == 63 && incl > 0) base = atomicAdd(&n_cand, incl);
+    base = __shfl(base, 63);
+    int slot = base + incl - mine;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      const int j = key_page<KPT>(c0, k, tid);
+      if (j < ncand && kk[k] >= tau) {
+        if (slot < kCap) c_pk[slot] = pack_key(kk[k], j);
+        ++slot;
       }
+    }
+  };
+  if (one_chunk) {
+    collect(0, key);
+  } else {
+    for (int c0 = 0; c0 < ncand; c0 += kChunk) {
+#pragma unroll
+      for (int k = 0; k < KPT; ++k) {
+        const int j = key_page<KPT>(c0, k, tid);
+        key[k] = j < ncand ? float_key(row[j]) : 0u;
+      }
+      collect(c0, key);
     }
   }
   __syncthreads();
@@ -126,12 +206,8 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkK a) {
     if (tid == 0) { n_cand = 0; n_eq_taken = 0; }
     __syncthreads();
     for (int j = tid; j < ncand; j += kBlock) {
-      const uint32_t key = float_key(row[j]);
-      if (key > T) {
-        const int slot = atomicAdd(&n_cand, 1);
-        c_key[slot] = key;
-        c_page[slot] = j;
-      }
+      const uint32_t kj = float_key(row[j]);
+      if (kj > T) c_pk[atomicAdd(&n_cand, 1)] = pack_key(kj, j);
     }
     __syncthreads();
     const int need = ksel - n_cand;
@@ -146,11 +222,7 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkK a) {
       int off = n_eq_taken;
       for (int w = 0; w < wave; ++w) off += red[w];
       const int r = off + incl - is_eq;
-      if (is_eq && r < need) {
-        const int slot = atomicAdd(&n_cand, 1);
-        c_key[slot] = T;
-        c_page[slot] = j;
-      }
+      if (is_eq && r < need) c_pk[atomicAdd(&n_cand, 1)] = pack_key(T, j);
       __syncthreads();
       if (tid == kBlock - 1) n_eq_taken = off + incl;
       __syncthreads();
@@ -160,16 +232,17 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkK a) {
     c = n_cand;
   }
 
-  // 4. exact rank among candidates
+  // 4. exact rank among candidates (packed keys are unique)
   for (int e = tid; e < c; e += kBlock) {
-    const uint32_t key = c_key[e];
-    const int page = c_page[e];
+    const uint64_t me = c_pk[e];
     int r = 0;
-    for (int o = 0; o < c; ++o) {
-      const uint32_t ko = c_key[o];
-      r += (ko > key || (ko == key && c_page[o] < page)) ? 1 : 0;
+    int o = 0;
+    for (; o + 8 <= c; o += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r += c_pk[o + u] > me ? 1 : 0;
     }
-    if (r < ksel) out[f + r] = page;
+    for (; o < c; ++o) r += c_pk[o] > me ? 1 : 0;
+    if (r < ksel) out[f + r] = (int)~(uint32_t)me;
   }
 }
 
@@ -188,7 +261,14 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   k.n_local = a.n_local;
   k.out = a.out;
   k.out_stride = a.out_stride;
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)a.vl.total_q), dim3(kBlock), 0, stream, k);
+  const dim3 grid((unsigned)a.vl.total_q);
+  const int need = std::max(1, a.vl.max_pages);   // candidates per query, at most
+  if (need <= kBlock * 1) hipLaunchKernelGGL(topk_kernel<1>, grid, dim3(kBlock), 0, stream, k);
+  else if (need <= kBlock * 2) hipLaunchKernelGGL(topk_kernel<2>, grid, dim3(kBlock), 0, stream, k);
+  else if (need <= kBlock * 4) hipLaunchKernelGGL(topk_kernel<4>, grid, dim3(kBlock), 0, stream, k);
+  else if (need <= kBlock * 8) hipLaunchKernelGGL(topk_kernel<8>, grid, dim3(kBlock), 0, stream, k);
+  else if (need <= kBlock * 16) hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(kBlock), 0, stream, k);
+  else hipLaunchKernelGGL(topk_kernel<32>, grid, dim3(kBlock), 0, stream, k);
   return hipGetLastError();
 }
 
