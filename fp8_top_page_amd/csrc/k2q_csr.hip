@@ -21,7 +21,8 @@
 //   fill   -- per block: base offsets from the totals of earlier blocks, scan of
 //             its units, then one wave per unit writes q_indices (ascending),
 //             the (query, slot) -> position table, row_ptr and the work items
-//             (row, first entry, count) of at most kAttnQC entries each
+//             of at most kAttnQC entries each: {row, first entry, count,
+//             request} {page j, cu_seqlens_q[b], context length, seqlen_k}
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -164,6 +165,7 @@ __global__ __launch_bounds__(kThreads) void csr_count_kernel(CountK a) {
 
 struct FillK {
   const int32_t* cu_q;
+  const int32_t* cu_k;
   int32_t batch;
   const int32_t* topk;
   int64_t tq, th;
@@ -251,6 +253,8 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
     const int b = find_request(a.row_base, a.batch, rr);
     const int j = (int)(rr - a.row_base[b]);
     const int64_t q_base = a.cu_q[b] + (u % a.units_per_row) * (kUnitWords * 32);
+    const int sk = a.cu_k[b + 1] - a.cu_k[b];
+    const int ctx = sk - (a.cu_q[b + 1] - a.cu_q[b]);
     // The unit's words and their exclusive bit counts go to the wave's LDS
     // slice; then entry e of the unit (e = round * 64 + lane) is located by a
     // binary search over the counts, so every lane handles one entry per round
@@ -289,8 +293,10 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
     const int n_it = (n + kAttnQC - 1) / kAttnQC;
     for (int t = lane; t < n_it; t += 64) {
       const int64_t idx = (int64_t)s_item[ku] + t;
-      if (idx < a.max_items)
-        a.items[idx] = make_int4((int)row, s_pos[ku] + t * kAttnQC, min(kAttnQC, n - t * kAttnQC), 0);
+      if (idx < a.max_items) {
+        a.items[2 * idx] = make_int4((int)row, s_pos[ku] + t * kAttnQC, min(kAttnQC, n - t * kAttnQC), b);
+        a.items[2 * idx + 1] = make_int4(j, a.cu_q[b], ctx, sk);
+      }
     }
   }
 }
@@ -312,7 +318,7 @@ SchedLayout sched_layout(const msa_varlen_t* vl, int n_sel, int topk) {
   L.row_base = off;   off += align_up(sizeof(int32_t) * (vl->batch + 1), 256);
   L.unit_cnt = off;   off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.n_units), 256);
   L.blk_tot = off;    off += align_up(sizeof(int32_t) * 2 * L.n_blocks, 256);
-  L.items = off;      off += align_up(sizeof(int4) * std::max<int64_t>(1, L.max_items), 256);
+  L.items = off;      off += align_up(2 * sizeof(int4) * std::max<int64_t>(1, L.max_items), 256);
   L.inv = off;        off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.inv_len), 256);
   L.bitmap = off;     off += align_up(sizeof(uint32_t) * L.n_rows * L.words_per_row, 256);
   L.total = off;
@@ -347,7 +353,7 @@ hipError_t launch_k2q_csr(const CsrArgs& a, hipStream_t stream) {
              blk_items};
   hipLaunchKernelGGL(csr_count_kernel, dim3((unsigned)L.n_blocks), dim3(kThreads), 0, stream, cnt);
 
-  FillK fk{a.vl.cu_seqlens_q, a.vl.batch, a.topk, a.tq_stride, a.th_stride, a.n_sel,
+  FillK fk{a.vl.cu_seqlens_q, a.vl.cu_seqlens_k, a.vl.batch, a.topk, a.tq_stride, a.th_stride, a.n_sel,
            a.vl.total_rows, row_base, bitmap, L.words_per_row, (int32_t)L.units_per_row,
            L.n_units, L.n_rows, (int32_t)L.n_blocks, unit_cnt, blk_tot, blk_items, a.row_ptr,
            a.q_indices, inv, items, L.max_items, hdr};

@@ -69,20 +69,44 @@ __global__ __launch_bounds__(kThreads, 4) void attn_partial_kernel(AttnK a) {
 
   const int item = blockIdx.x;
   if (item >= *a.n_items) return;
-  const int4 it = a.items[item];
-  const int row = it.x, start = it.y, count = it.z;
+  // work item: {row, first entry, count, request} {page, cu_seqlens_q[b], context, seqlen_k}
+  const int4 it = a.items[2 * item];
+  const int4 it2 = a.items[2 * item + 1];
+  const int row = it.x, start = it.y, count = it.z, b = it.w;
+  const int j = it2.x, cq0 = it2.y, ctx = it2.z, sk = it2.w;
   if (count <= 0) return;
-  const int g_sel = row / a.total_rows;
-  const int rr = row - g_sel * a.total_rows;
-  const int g = (a.n_sel == 1) ? (int)blockIdx.y : g_sel;
-  const int b = find_request(a.row_base, a.batch, rr);
-  const int j = rr - a.row_base[b];
+  const int g = (a.n_sel == 1) ? (int)blockIdx.y : row / a.total_rows;
   int phys = a.block_table[(int64_t)b * a.bt_stride + j];
   phys = (phys < 0 || phys >= a.num_pages) ? 0 : phys;
   const uint8_t* page = a.kv + ((int64_t)phys * a.Hkv + g) * (kPage * 2 * kDim);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
+  const int n_rows = count * a.G;
+  const int n_tiles = (n_rows + 15) >> 4;
+
+  // Row rid = (query ql of the item, head h): its query index, its last visible
+  // token in this page, and its Q fragment (B operand).  The first tile's rows
+  // are fetched before the page is staged so the two latencies overlap.
+  struct TileRow {
+    bool valid;
+    int ql, hq, h, lim;
+    v8i qb;
+  };
+  auto tile_row = [&](int tile) {
+    TileRow r;
+    const int rid = tile * 16 + col;
+    r.valid = tile < n_tiles && rid < n_rows;
+    r.ql = r.valid ? rid / a.G : 0;
+    r.h = r.valid ? rid - r.ql * a.G : 0;
+    r.hq = g * a.G + r.h;
+    const int qi = r.valid ? a.q_indices[start + r.ql] : 0;
+    r.lim = r.valid ? ctx + (qi - cq0) - j * kPage : -1;
+    if (r.valid) r.qb = load_frag_global(a.q + (int64_t)qi * a.q_stride + r.hq * kDim + grp * 32);
+    else r.qb = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    return r;
+  };
+  TileRow cur = tile_row(wave);
 
   // ---- stage K (token-major) and V^T (d-major, token axis permuted) in LDS
   {
@@ -97,7 +121,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_partial_kernel(AttnK a) {
     // Tokens past the end of the sequence hold no data (the page tail may be
     // anything, even NaN); their probability is exactly 0, so V is zeroed there
     // to keep 0 * V finite.
-    const int n_valid = (a.cu_k[b + 1] - a.cu_k[b]) - j * kPage;
+    const int n_valid = sk - j * kPage;
     const int m = tid >> 3, dc = tid & 7;
     uint4 r[4];
 #pragma unroll
@@ -123,11 +147,6 @@ __global__ __launch_bounds__(kThreads, 4) void attn_partial_kernel(AttnK a) {
   const float qs = a.q_scale ? *a.q_scale : 1.f;
   const float ks = a.k_scale ? *a.k_scale : 1.f;
   const float zscale = a.logit_scale_log2 * qs * ks;
-  const int cq0 = a.cu_q[b];
-  const int ctx = (a.cu_k[b + 1] - a.cu_k[b]) - (a.cu_q[b + 1] - cq0);
-  const int n_rows = count * a.G;
-  const int n_tiles = (n_rows + 15) >> 4;
-
   for (int tile = wave; tile < n_tiles; tile += kThreads / 64) {
     // Re-read the page fragments from LDS for every tile instead of keeping all
     // 16 of them (128 registers) live across tiles: the launder stops the
@@ -135,16 +154,10 @@ __global__ __launch_bounds__(kThreads, 4) void attn_partial_kernel(AttnK a) {
     const uint8_t* k_base = k_lds;
     const uint8_t* v_base = vt_lds;
     asm volatile("" : "+v"(k_base), "+v"(v_base));
-    const int rid = tile * 16 + col;
-    const bool valid = rid < n_rows;
-    const int ql = valid ? rid / a.G : 0;
-    const int h = valid ? rid - ql * a.G : 0;
-    const int hq = g * a.G + h;
-    const int qi = valid ? a.q_indices[start + ql] : 0;
-    const int lim = valid ? ctx + (qi - cq0) - j * kPage : -1;   // last visible token in page
-    v8i qb;
-    if (valid) qb = load_frag_global(a.q + (int64_t)qi * a.q_stride + hq * kDim + grp * 32);
-    else qb = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    const bool valid = cur.valid;
+    const int ql = cur.ql, h = cur.h, hq = cur.hq, lim = cur.lim;
+    const v8i qb = cur.qb;
+    cur = tile_row(tile + kThreads / 64);   // next tile's rows, in flight meanwhile
 
     v4f s[8];
 #pragma unroll
@@ -240,16 +253,19 @@ __global__ __launch_bounds__(1024) void attn_combine_kernel(CombineK a) {
     ls[s] = pi[s] >= 0 ? a.part_lse[(int64_t)pi[s] * a.HP + hp] : -INFINITY;
     M = fmaxf(M, ls[s]);
   }
+  // all 16 split rows are loaded together (a missing split reads row 0 with
+  // weight 0) so their latencies overlap
+  uint4 v[kTopK];
+#pragma unroll
+  for (int s = 0; s < kTopK; ++s)
+    v[s] = *reinterpret_cast<const uint4*>(a.part_o + ((int64_t)max(pi[s], 0) * a.HP + hp) * kDim + d0);
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (M != -INFINITY) {
     float W = 0.f;
 #pragma unroll
     for (int s = 0; s < kTopK; ++s) {
-      if (ls[s] == -INFINITY) continue;
-      const float w = __builtin_amdgcn_exp2f(ls[s] - M);
-      const uint4 v = *reinterpret_cast<const uint4*>(
-          a.part_o + ((int64_t)pi[s] * a.HP + hp) * kDim + d0);
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+      const float w = (ls[s] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ls[s] - M);
+      const uint32_t wv[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         o[2 * k] += w * bf16_to_f32((uint16_t)(wv[k] & 0xFFFFu));
