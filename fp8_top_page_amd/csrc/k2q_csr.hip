@@ -21,8 +21,11 @@
 //   fill   -- per block: base offsets from the totals of earlier blocks, scan of
 //             its units, then one wave per unit writes q_indices (ascending),
 //             the (query, slot) -> position table, row_ptr and the work items
-//             of at most kAttnQC entries each: {row, first entry, count,
-//             request} {page j, cu_seqlens_q[b], context length, seqlen_k}
+//             of at most kAttnQC entries each:
+//               {first entry, count, physical page, selection head}
+//               {context - cu_seqlens_q[b] - 128 j, valid tokens of the page, row, request}
+//             (a query i of the item sees the page's tokens up to i + the first
+//             value; the physical page comes from the block table)
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -167,6 +170,8 @@ struct FillK {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int32_t batch;
+  const int32_t* block_table;
+  int64_t bt_stride;
   const int32_t* topk;
   int64_t tq, th;
   int32_t n_sel;
@@ -291,11 +296,12 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
     __builtin_amdgcn_wave_barrier();
     // work items of the unit: (row, first entry, count)
     const int n_it = (n + kAttnQC - 1) / kAttnQC;
+    const int phys = n_it > 0 ? a.block_table[(int64_t)b * a.bt_stride + j] : 0;
     for (int t = lane; t < n_it; t += 64) {
       const int64_t idx = (int64_t)s_item[ku] + t;
       if (idx < a.max_items) {
-        a.items[2 * idx] = make_int4((int)row, s_pos[ku] + t * kAttnQC, min(kAttnQC, n - t * kAttnQC), b);
-        a.items[2 * idx + 1] = make_int4(j, a.cu_q[b], ctx, sk);
+        a.items[2 * idx] = make_int4(s_pos[ku] + t * kAttnQC, min(kAttnQC, n - t * kAttnQC), phys, g);
+        a.items[2 * idx + 1] = make_int4(ctx - a.cu_q[b] - j * kPage, sk - j * kPage, (int)row, b);
       }
     }
   }
@@ -353,7 +359,8 @@ hipError_t launch_k2q_csr(const CsrArgs& a, hipStream_t stream) {
              blk_items};
   hipLaunchKernelGGL(csr_count_kernel, dim3((unsigned)L.n_blocks), dim3(kThreads), 0, stream, cnt);
 
-  FillK fk{a.vl.cu_seqlens_q, a.vl.cu_seqlens_k, a.vl.batch, a.topk, a.tq_stride, a.th_stride, a.n_sel,
+  FillK fk{a.vl.cu_seqlens_q, a.vl.cu_seqlens_k, a.vl.batch, a.vl.block_table,
+           a.vl.block_table_stride, a.topk, a.tq_stride, a.th_stride, a.n_sel,
            a.vl.total_rows, row_base, bitmap, L.words_per_row, (int32_t)L.units_per_row,
            L.n_units, L.n_rows, (int32_t)L.n_blocks, unit_cnt, blk_tot, blk_items, a.row_ptr,
            a.q_indices, inv, items, L.max_items, hdr};

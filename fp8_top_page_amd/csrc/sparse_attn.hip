@@ -14,12 +14,19 @@
 // block stages the page's K (token-major) and V (transposed, d-major) in LDS
 // once and every wave runs 16-row tiles of (query, q-head) rows against it:
 //   S^T = K Q^T           8 MFMA 16x16x128 (tokens on M, rows on N)
-//   softmax over the page's 128 tokens (causal mask on tokens > pos)
+//   softmax over the page's 128 tokens (causal mask only on a query's own page)
 //   O^T = V^T P^T         8 MFMA, P^T packed to E4M3 straight from S^T's lanes
+//   l   = 1^T P^T         1 MFMA against a constant all-ones operand
 // Because S^T leaves each lane with tokens {16T + 4g + i} of one row, V^T is
 // stored with its token axis permuted to the same order, so no shuffles are
-// needed between the two products.  Each (query, q-head, page) split writes a
-// normalised bf16 output row and its log2-sum-exp; the combine merges a
+// needed between the two products.  When an item has enough rows, a wave runs
+// two tiles per fragment read so each K/V fragment fetched from LDS feeds two
+// MFMAs.  Blocks are persistent: while one item is computed, the next item's
+// page and query list are already being fetched into registers.
+//
+// Each (query, q-head, page) split writes its unnormalised output row in bf16
+// (d permuted so that every lane stores 64 contiguous bytes) and the pair
+// (running max m in the log2 domain, probability sum l); the combine merges a
 // query's (at most 16) splits in slot order.
 #include "msa_device.h"
 #include "msa_internal.h"
@@ -28,111 +35,101 @@ namespace msa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 constexpr int kRowB = 144;          // LDS row stride (bytes)
+constexpr int kBlocksPerCU = 2;
 constexpr float kLog2e = 1.4426950408889634f;
-
-struct SchedHdr {
-  int32_t n_items;
-  int32_t nnz;
-  int32_t pad[62];
-};
+constexpr int kOnesE4M3 = 0x38383838;   // four E4M3 1.0 codes
 
 struct AttnK {
-  const int32_t* cu_q;
-  const int32_t* cu_k;
-  const int32_t* block_table;
-  int64_t bt_stride;
-  int32_t batch;
-  int32_t num_pages;
-  int32_t total_rows;
   const uint8_t* q;
   int64_t q_stride;
-  int32_t Hq, Hkv, G, n_sel, HP;
+  int32_t G, n_sel, HP, GY;        // GY: KV heads per schedule item (Hkv if shared selection)
   const uint8_t* kv;
-  const int32_t* row_base;
-  const int32_t* row_ptr;
+  int32_t num_pages, Hkv;
   const int32_t* q_indices;
   const int4* items;
   const int32_t* n_items;
   float logit_scale_log2;          // softmax_scale * log2(e)
   const float* q_scale;
   const float* k_scale;
-  uint16_t* part_o;                // [nnz, HP, 128] bf16, normalised
-  float* part_lse;                 // [nnz, HP] log2-sum-exp
+  uint16_t* part_o;                // [nnz, HP, 128] bf16, unnormalised, d permuted
+  float2* part_ml;                 // [nnz, HP] (max in log2 units, probability sum)
+  int64_t trash;                   // partial row written by rows past an item's end
 };
 
 __device__ __forceinline__ uint32_t byte_of(uint32_t w, int k) { return (w >> (8 * k)) & 0xFFu; }
 
-__global__ __launch_bounds__(kThreads, 4) void attn_partial_kernel(AttnK a) {
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kPage * kRowB];
-  __shared__ __attribute__((aligned(16))) uint8_t vt_lds[kDim * kRowB];
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// two floats -> two bf16 (round to nearest even, gfx950 v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
 
-  const int item = blockIdx.x;
-  if (item >= *a.n_items) return;
-  // work item: {row, first entry, count, request} {page, cu_seqlens_q[b], context, seqlen_k}
-  const int4 it = a.items[2 * item];
-  const int4 it2 = a.items[2 * item + 1];
-  const int row = it.x, start = it.y, count = it.z, b = it.w;
-  const int j = it2.x, cq0 = it2.y, ctx = it2.z, sk = it2.w;
-  if (count <= 0) return;
-  const int g = (a.n_sel == 1) ? (int)blockIdx.y : row / a.total_rows;
-  int phys = a.block_table[(int64_t)b * a.bt_stride + j];
+// One work item as the kernel uses it (wave-uniform values).
+struct Work {
+  int start, count, g, lim_base, n_valid;
+  const uint8_t* page;             // K|V rows of (physical page, KV head g)
+};
+
+__device__ __forceinline__ Work decode_work(const AttnK& a, int64_t w, int4 x, int4 y) {
+  Work r;
+  const int64_t item = w / a.GY;
+  r.start = __builtin_amdgcn_readfirstlane(x.x);
+  r.count = __builtin_amdgcn_readfirstlane(x.y);
+  int phys = __builtin_amdgcn_readfirstlane(x.z);
+  r.g = a.n_sel == 1 ? (int)(w - item * a.GY) : __builtin_amdgcn_readfirstlane(x.w);
   phys = (phys < 0 || phys >= a.num_pages) ? 0 : phys;
-  const uint8_t* page = a.kv + ((int64_t)phys * a.Hkv + g) * (kPage * 2 * kDim);
+  r.page = a.kv + ((int64_t)phys * a.Hkv + r.g) * (kPage * 2 * kDim);
+  r.lim_base = __builtin_amdgcn_readfirstlane(y.x);
+  r.n_valid = min(__builtin_amdgcn_readfirstlane(y.y), kPage);
+  return r;
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, grp = lane >> 4;
-  const int n_rows = count * a.G;
-  const int n_tiles = (n_rows + 15) >> 4;
+// A page in flight: thread t holds 64 bytes of K (token t/2, half t%2) and the
+// V bytes 16*(t%8).. of tokens 4*(t/8)..+3.
+struct PageRegs {
+  v4u k[4];
+  v4u v[4];
+  int qi;                          // q_indices[start + t] for t < count
+};
 
-  // Row rid = (query ql of the item, head h): its query index, its last visible
-  // token in this page, and its Q fragment (B operand).  The first tile's rows
-  // are fetched before the page is staged so the two latencies overlap.
-  struct TileRow {
-    bool valid;
-    int ql, hq, h, lim;
-    v8i qb;
-  };
-  auto tile_row = [&](int tile) {
-    TileRow r;
-    const int rid = tile * 16 + col;
-    r.valid = tile < n_tiles && rid < n_rows;
-    r.ql = r.valid ? rid / a.G : 0;
-    r.h = r.valid ? rid - r.ql * a.G : 0;
-    r.hq = g * a.G + r.h;
-    const int qi = r.valid ? a.q_indices[start + r.ql] : 0;
-    r.lim = r.valid ? ctx + (qi - cq0) - j * kPage : -1;
-    if (r.valid) r.qb = load_frag_global(a.q + (int64_t)qi * a.q_stride + r.hq * kDim + grp * 32);
-    else r.qb = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    return r;
-  };
-  TileRow cur = tile_row(wave);
+__device__ __forceinline__ void fetch_page(PageRegs& r, const AttnK& a, const Work& w, int tid) {
+  const int t = tid >> 1, h = tid & 1;
+  const v4u* ks = reinterpret_cast<const v4u*>(w.page + t * (2 * kDim) + h * 64);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.k[i] = ks[i];
+  const int m = tid >> 3, dc = tid & 7;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r.v[i] = *reinterpret_cast<const v4u*>(w.page + (4 * m + i) * (2 * kDim) + kDim + 16 * dc);
+  r.qi = a.q_indices[w.start + min(tid, w.count - 1)];
+}
 
-  // ---- stage K (token-major) and V^T (d-major, token axis permuted) in LDS
+__device__ __forceinline__ void stage_page(const PageRegs& r, const Work& w, uint8_t* k_lds,
+                                           uint8_t* vt_lds, int* s_qi, int tid) {
   {
     const int t = tid >> 1, h = tid & 1;
-    const uint4* src = reinterpret_cast<const uint4*>(page + t * (2 * kDim) + h * 64);
-    uint4 x0 = src[0], x1 = src[1], x2 = src[2], x3 = src[3];
-    uint4* dst = reinterpret_cast<uint4*>(k_lds + t * kRowB + h * 64);
-    dst[0] = x0; dst[1] = x1; dst[2] = x2; dst[3] = x3;
+    v4u* dst = reinterpret_cast<v4u*>(k_lds + t * kRowB + h * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = r.k[i];
   }
   {
     // token group m = tokens 4m..4m+3 -> permuted positions 32*(m&3) + 4*(m>>2) + {0..3}.
     // Tokens past the end of the sequence hold no data (the page tail may be
     // anything, even NaN); their probability is exactly 0, so V is zeroed there
     // to keep 0 * V finite.
-    const int n_valid = sk - j * kPage;
     const int m = tid >> 3, dc = tid & 7;
-    uint4 r[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      r[i] = *reinterpret_cast<const uint4*>(page + (4 * m + i) * (2 * kDim) + kDim + 16 * dc);
-      if (4 * m + i >= n_valid) r[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
+    const v4u zero = v4u{0u, 0u, 0u, 0u};
+    const v4u v0 = (4 * m + 0 < w.n_valid) ? r.v[0] : zero;
+    const v4u v1 = (4 * m + 1 < w.n_valid) ? r.v[1] : zero;
+    const v4u v2 = (4 * m + 2 < w.n_valid) ? r.v[2] : zero;
+    const v4u v3 = (4 * m + 3 < w.n_valid) ? r.v[3] : zero;
     const int kpos = 32 * (m & 3) + 4 * (m >> 2);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t w0 = (&r[0].x)[e], w1 = (&r[1].x)[e], w2 = (&r[2].x)[e], w3 = (&r[3].x)[e];
+      const uint32_t w0 = v0[e], w1 = v1[e], w2 = v2[e], w3 = v3[e];
 #pragma unroll
       for (int dd = 0; dd < 4; ++dd) {
         const uint32_t c = byte_of(w0, dd) | (byte_of(w1, dd) << 8) | (byte_of(w2, dd) << 16) |
@@ -142,84 +139,215 @@ __global__ __launch_bounds__(kThreads, 4) void attn_partial_kernel(AttnK a) {
       }
     }
   }
-  __syncthreads();
+  if (tid < kAttnQC) s_qi[tid] = r.qi;
+}
 
-  const float qs = a.q_scale ? *a.q_scale : 1.f;
-  const float ks = a.k_scale ? *a.k_scale : 1.f;
-  const float zscale = a.logit_scale_log2 * qs * ks;
-  for (int tile = wave; tile < n_tiles; tile += kThreads / 64) {
-    // Re-read the page fragments from LDS for every tile instead of keeping all
-    // 16 of them (128 registers) live across tiles: the launder stops the
-    // compiler from hoisting the loads out of the loop.
-    const uint8_t* k_base = k_lds;
-    const uint8_t* v_base = vt_lds;
-    asm volatile("" : "+v"(k_base), "+v"(v_base));
-    const bool valid = cur.valid;
-    const int ql = cur.ql, h = cur.h, hq = cur.hq, lim = cur.lim;
-    const v8i qb = cur.qb;
-    cur = tile_row(tile + kThreads / 64);   // next tile's rows, in flight meanwhile
+// The rows of NT consecutive 16-row tiles on one wave: lane (col, grp) of tile
+// u holds row (tile0 + u) * 16 + col.  Rows past the item's end alias its first
+// row for loading (their results go to the trash row), so every load and store
+// below is unconditional and the compiler can count outstanding memory
+// operations exactly instead of draining them.
+template <int NT>
+struct RowSet {
+  v8i qb[NT];
+  int lim[NT];
+  int64_t pidx[NT];
+};
 
-    v4f s[8];
+template <int NT>
+__device__ __forceinline__ RowSet<NT> load_rows(const AttnK& a, const Work& w, int tile0,
+                                                int n_rows, const int* s_qi, int lane) {
+  const int col = lane & 15, grp = lane >> 4;
+  RowSet<NT> r;
 #pragma unroll
-    for (int T = 0; T < 8; ++T) {
-      const v8i ka = load_frag_lds(k_base + (T * 16 + col) * kRowB + grp * 32);
-      s[T] = mfma_e4m3(ka, qb, v4f{0.f, 0.f, 0.f, 0.f});
+  for (int u = 0; u < NT; ++u) {
+    const int rid = (tile0 + u) * 16 + col;
+    const bool valid = rid < n_rows;
+    const int q0 = rid / a.G;                 // branch-free: rows past the end are
+    const int ql = valid ? q0 : 0;            // clamped after the division
+    const int h = valid ? rid - q0 * a.G : 0;
+    const int hq = w.g * a.G + h;
+    const int qi = s_qi[ql];
+    r.lim[u] = valid ? qi + w.lim_base : kPage;
+    const int64_t p = (int64_t)(w.start + ql) * a.HP + (a.n_sel == 1 ? hq : h);
+    r.pidx[u] = valid ? p : a.trash;
+    r.qb[u] = load_frag_global(a.q + (int64_t)qi * a.q_stride + hq * kDim + grp * 32);
+  }
+  return r;
+}
+
+// S^T, softmax and O^T of one row set, written to its partial rows.
+template <int NT>
+__device__ __forceinline__ void compute_set(const AttnK& a, const RowSet<NT>& r,
+                                            const uint8_t* k_lds, const uint8_t* vt_lds,
+                                            float zscale, int lane) {
+  const int col = lane & 15, grp = lane >> 4;
+  // The page fragments are re-read from LDS for every set rather than kept
+  // live across sets (128 registers); the laundered zero offset stops the
+  // compiler from hoisting the reads out of the caller's loop (laundering the
+  // pointers themselves would turn them into generic pointers).
+  int zero = 0;
+  asm volatile("" : "+v"(zero));
+  k_lds += zero;
+  vt_lds += zero;
+
+  // S^T: every K fragment read from LDS feeds NT products
+  v4f s[NT][8];
+#pragma unroll
+  for (int T = 0; T < 8; ++T) {
+    const v8i ka = load_frag_lds(k_lds + (T * 16 + col) * kRowB + grp * 32);
+#pragma unroll
+    for (int u = 0; u < NT; ++u) s[u][T] = mfma_e4m3(ka, r.qb[u], v4f{0.f, 0.f, 0.f, 0.f});
+  }
+
+  // Only the rows of queries whose own page this is see a causal boundary.
+  bool need_mask = false;
+#pragma unroll
+  for (int u = 0; u < NT; ++u) need_mask |= r.lim[u] < kPage - 1;
+  const bool masked = __builtin_amdgcn_ballot_w64(need_mask) != 0;
+
+  v8i pb[NT];
+  float mz[NT];
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    if (masked) {
+#pragma unroll
+      for (int T = 0; T < 8; ++T)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = T * 16 + grp * 4 + i;
+          s[u][T][i] = (t > r.lim[u]) ? -INFINITY : s[u][T][i];
+        }
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int T = 0; T < 8; ++T)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = T * 16 + grp * 4 + i;
-        float z = s[T][i] * zscale;
-        z = (t > lim) ? -INFINITY : z;
-        s[T][i] = z;
-        mx = fmaxf(mx, z);
-      }
+      mx = fmaxf(fmaxf(mx, fmaxf(s[u][T][0], s[u][T][1])), fmaxf(s[u][T][2], s[u][T][3]));
     mx = max_across_groups(mx);
-    const float mref = (mx == -INFINITY) ? 0.f : mx;
-    float l = 0.f;
-    v8i pb;
+    // scales are positive, so the max of the raw products gives the max logit
+    mz[u] = (mx == -INFINITY) ? 0.f : mx * zscale;
 #pragma unroll
     for (int T = 0; T < 8; ++T) {
-      float p0 = __builtin_amdgcn_exp2f(s[T][0] - mref);
-      float p1 = __builtin_amdgcn_exp2f(s[T][1] - mref);
-      float p2 = __builtin_amdgcn_exp2f(s[T][2] - mref);
-      float p3 = __builtin_amdgcn_exp2f(s[T][3] - mref);
-      l += (p0 + p1) + (p2 + p3);
-      pb[T] = pack4_e4m3(p0, p1, p2, p3);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][T][0], zscale, -mz[u]));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][T][1], zscale, -mz[u]));
+      const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][T][2], zscale, -mz[u]));
+      const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][T][3], zscale, -mz[u]));
+      pb[u][T] = pack4_e4m3(p0, p1, p2, p3);
     }
-    l = sum_across_groups(l);
+  }
 
-    // O^T = V^T P^T in two halves of 64 output dims, each stored as soon as it
-    // is done (keeps the live accumulators to 16 registers).
-    const int64_t pidx = (int64_t)(start + ql) * a.HP + (a.n_sel == 1 ? hq : h);
-    const float inv_l = l > 0.f ? 1.f / l : 0.f;
-    uint16_t* dst = a.part_o + pidx * kDim + grp * 4;
+  // l = sum of the E4M3 probabilities (the same values the PV product uses)
+  const v8i ones = v8i{kOnesE4M3, kOnesE4M3, kOnesE4M3, kOnesE4M3,
+                       kOnesE4M3, kOnesE4M3, kOnesE4M3, kOnesE4M3};
+  float l[NT];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      v4f o[4];
+  for (int u = 0; u < NT; ++u) l[u] = mfma_e4m3(ones, pb[u], v4f{0.f, 0.f, 0.f, 0.f})[0];
+
+  // O^T = V^T P^T in two halves of 64 output dims, each stored as soon as it is
+  // done.  Lane (row, group g) holds d = 16 dt + 4 g + i; in the partial row
+  // those 32 values sit at 32 g + 4 dt + i, so a half is 32 contiguous bytes.
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int dt = half * 4 + k;
-        const v8i va = load_frag_lds(v_base + (dt * 16 + col) * kRowB + grp * 32);
-        o[k] = mfma_e4m3(va, pb, v4f{0.f, 0.f, 0.f, 0.f});
-      }
-      if (valid) {
+  for (int half = 0; half < 2; ++half) {
+    v4f o[NT][4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int dt = half * 4 + k;
-          const uint32_t lo = (uint32_t)f32_to_bf16(o[k][0] * inv_l) |
-                              ((uint32_t)f32_to_bf16(o[k][1] * inv_l) << 16);
-          const uint32_t hi = (uint32_t)f32_to_bf16(o[k][2] * inv_l) |
-                              ((uint32_t)f32_to_bf16(o[k][3] * inv_l) << 16);
-          *reinterpret_cast<uint2*>(dst + dt * 16) = make_uint2(lo, hi);
-        }
-      }
+    for (int k = 0; k < 4; ++k) {
+      const v8i va = load_frag_lds(vt_lds + ((half * 4 + k) * 16 + col) * kRowB + grp * 32);
+#pragma unroll
+      for (int u = 0; u < NT; ++u) o[u][k] = mfma_e4m3(va, pb[u], v4f{0.f, 0.f, 0.f, 0.f});
     }
-    if (valid) {
-      if (grp == 0) a.part_lse[pidx] = (l > 0.f) ? mx + __log2f(l) : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      uint4* dst = reinterpret_cast<uint4*>(a.part_o + r.pidx[u] * kDim + grp * 32 + half * 16);
+      dst[0] = make_uint4(pack2_bf16(o[u][0][0], o[u][0][1]), pack2_bf16(o[u][0][2], o[u][0][3]),
+                          pack2_bf16(o[u][1][0], o[u][1][1]), pack2_bf16(o[u][1][2], o[u][1][3]));
+      dst[1] = make_uint4(pack2_bf16(o[u][2][0], o[u][2][1]), pack2_bf16(o[u][2][2], o[u][2][3]),
+                          pack2_bf16(o[u][3][0], o[u][3][1]), pack2_bf16(o[u][3][2], o[u][3][3]));
     }
+  }
+  // every lane of a row holds the same (m, l)
+#pragma unroll
+  for (int u = 0; u < NT; ++u) a.part_ml[r.pidx[u]] = make_float2(mz[u], l[u]);
+}
+
+// All sets of one item on this wave.  Query rows are requested two sets ahead,
+// and the first two sets' rows before `prefetch` issues the next item's loads:
+// memory operations complete in issue order, so a wait for a row requested
+// after the prefetch would also wait for the next page.
+template <int NT, class Prefetch>
+__device__ __forceinline__ void run_item(const AttnK& a, const Work& w, const uint8_t* k_lds,
+                                         const uint8_t* vt_lds, const int* s_qi, float zscale,
+                                         int wave, int lane, Prefetch&& prefetch) {
+  constexpr int kStep = NT * kWaves;
+  const int n_rows = w.count * a.G;
+  const int n_tiles = (n_rows + 15) >> 4;
+  int t = NT * wave;
+  // two row sets alternate roles (unrolled by two), so no loop-carried copy of
+  // a loaded set forces an early wait for its loads
+  RowSet<NT> ra = load_rows<NT>(a, w, t, n_rows, s_qi, lane);
+  RowSet<NT> rb = load_rows<NT>(a, w, t + kStep, n_rows, s_qi, lane);
+  __builtin_amdgcn_sched_barrier(0);        // keep the row loads ahead of the prefetch
+  prefetch();
+  __builtin_amdgcn_sched_barrier(0);
+  for (;;) {
+    if (t >= n_tiles) break;
+    compute_set<NT>(a, ra, k_lds, vt_lds, zscale, lane);
+    ra = load_rows<NT>(a, w, t + 2 * kStep, n_rows, s_qi, lane);
+    t += kStep;
+    if (t >= n_tiles) break;
+    compute_set<NT>(a, rb, k_lds, vt_lds, zscale, lane);
+    rb = load_rows<NT>(a, w, t + 2 * kStep, n_rows, s_qi, lane);
+    t += kStep;
+  }
+}
+
+__global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_partial_kernel(AttnK a) {
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kPage * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t vt_lds[kDim * kRowB];
+  __shared__ int s_qi[kAttnQC];
+
+  const int n_items = *a.n_items;
+  const int64_t n_work = (int64_t)n_items * a.GY;
+  int64_t w = blockIdx.x;
+  if (w >= n_work) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: loops below do not diverge
+  const float zscale = a.logit_scale_log2 * (a.q_scale ? *a.q_scale : 1.f) *
+                       (a.k_scale ? *a.k_scale : 1.f);
+  // metadata of work index x (clamped to the last item, so the load is always valid)
+  auto item_of = [&](int64_t x) -> int64_t {
+    const int64_t it = x / a.GY;
+    return it < n_items - 1 ? it : (int64_t)(n_items - 1);
+  };
+
+  // prologue: the first item's page in registers, the second item's metadata in flight
+  Work cur = decode_work(a, w, a.items[2 * item_of(w)], a.items[2 * item_of(w) + 1]);
+  PageRegs pr;
+  fetch_page(pr, a, cur, tid);
+  int4 mx = a.items[2 * item_of(w + gridDim.x)];
+  int4 my = a.items[2 * item_of(w + gridDim.x) + 1];
+
+  for (;;) {
+    __syncthreads();                         // the previous item is done with LDS
+    stage_page(pr, cur, k_lds, vt_lds, s_qi, tid);
+    __syncthreads();
+    const int64_t wn = w + gridDim.x;
+    const bool has_next = wn < n_work;
+    // past the last item the "next" item is the current one again: its loads
+    // are issued all the same and their data is never used
+    const Work nxt = has_next ? decode_work(a, wn, mx, my) : cur;
+    auto prefetch = [&]() {
+      fetch_page(pr, a, nxt, tid);
+      mx = a.items[2 * item_of(wn + gridDim.x)];
+      my = a.items[2 * item_of(wn + gridDim.x) + 1];
+    };
+    const int n_tiles = (cur.count * a.G + 15) >> 4;
+    if (n_tiles >= 2 * kWaves)
+      run_item<2>(a, cur, k_lds, vt_lds, s_qi, zscale, wave, lane, prefetch);
+    else
+      run_item<1>(a, cur, k_lds, vt_lds, s_qi, zscale, wave, lane, prefetch);
+    if (!has_next) break;
+    cur = nxt;
+    w = wn;
   }
 }
 
@@ -228,96 +356,102 @@ struct CombineK {
   int32_t Hq, G, n_sel, HP;
   const int32_t* inv;             // [total_q, n_sel, 16] CSR position or -1
   const uint16_t* part_o;
-  const float* part_lse;
+  const float2* part_ml;
   const float* v_scale;
   uint16_t* out;
   int64_t out_stride;
 };
 
-// One block per query, Hq * 16 threads: thread t owns q-head t / 16 and output
-// dims 8 * (t % 16) .. + 7, so each split row (all heads of one (query, page)
-// pair, contiguous) is read with 16-byte loads.
+// One block per query, Hq * 16 threads: thread t owns q-head t / 16 and the 16
+// bytes at 8 * (t % 16) of each split row (all heads of one (query, page) pair
+// are contiguous), which hold d = 32 (c % 4) + 4 (c / 4) + {0..3} and those + 16
+// for c = t % 16.
 __global__ __launch_bounds__(1024) void attn_combine_kernel(CombineK a) {
   const int64_t i = blockIdx.x;
   const int t = threadIdx.x;
-  const int hq = t >> 4, d0 = (t & 15) * 8;
+  const int hq = t >> 4, c = t & 15;
   const int sel = a.n_sel == 1 ? 0 : hq / a.G;
   const int hp = a.n_sel == 1 ? hq : hq % a.G;
   const int32_t* pos = a.inv + (i * a.n_sel + sel) * kTopK;
   int32_t pi[kTopK];
-  float ls[kTopK];
-  float M = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < kTopK; ++s) {
-    pi[s] = pos[s];
-    ls[s] = pi[s] >= 0 ? a.part_lse[(int64_t)pi[s] * a.HP + hp] : -INFINITY;
-    M = fmaxf(M, ls[s]);
-  }
-  // all 16 split rows are loaded together (a missing split reads row 0 with
-  // weight 0) so their latencies overlap
+  for (int s = 0; s < kTopK; ++s) pi[s] = pos[s];
+  // all split rows are loaded together (a missing split reads row 0 with weight 0)
+  float2 ml[kTopK];
   uint4 v[kTopK];
 #pragma unroll
-  for (int s = 0; s < kTopK; ++s)
-    v[s] = *reinterpret_cast<const uint4*>(a.part_o + ((int64_t)max(pi[s], 0) * a.HP + hp) * kDim + d0);
+  for (int s = 0; s < kTopK; ++s) {
+    const int64_t r = (int64_t)max(pi[s], 0) * a.HP + hp;
+    ml[s] = a.part_ml[r];
+    v[s] = *reinterpret_cast<const uint4*>(a.part_o + r * kDim + 8 * c);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kTopK; ++s) M = pi[s] >= 0 ? fmaxf(M, ml[s].x) : M;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (M != -INFINITY) {
-    float W = 0.f;
+    float L = 0.f;
 #pragma unroll
     for (int s = 0; s < kTopK; ++s) {
-      const float w = (ls[s] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ls[s] - M);
+      const float wgt = pi[s] >= 0 ? __builtin_amdgcn_exp2f(ml[s].x - M) : 0.f;
       const uint32_t wv[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        o[2 * k] += w * bf16_to_f32((uint16_t)(wv[k] & 0xFFFFu));
-        o[2 * k + 1] += w * bf16_to_f32((uint16_t)(wv[k] >> 16));
+        o[2 * k] += wgt * bf16_to_f32((uint16_t)(wv[k] & 0xFFFFu));
+        o[2 * k + 1] += wgt * bf16_to_f32((uint16_t)(wv[k] >> 16));
       }
-      W += w;
+      L += wgt * ml[s].y;
     }
-    const float f = (a.v_scale ? *a.v_scale : 1.f) / W;
+    const float f = L > 0.f ? (a.v_scale ? *a.v_scale : 1.f) / L : 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) o[k] *= f;
   }
-  uint4 packed;
-  packed.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
-  packed.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
-  packed.z = (uint32_t)f32_to_bf16(o[4]) | ((uint32_t)f32_to_bf16(o[5]) << 16);
-  packed.w = (uint32_t)f32_to_bf16(o[6]) | ((uint32_t)f32_to_bf16(o[7]) << 16);
-  *reinterpret_cast<uint4*>(a.out + i * a.out_stride + hq * kDim + d0) = packed;
+  uint16_t* dst = a.out + i * a.out_stride + hq * kDim + 32 * (c & 3) + 4 * (c >> 2);
+  *reinterpret_cast<uint2*>(dst) = make_uint2(pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3]));
+  *reinterpret_cast<uint2*>(dst + 16) = make_uint2(pack2_bf16(o[4], o[5]), pack2_bf16(o[6], o[7]));
+}
+
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev] = n;
+  return n;
 }
 
 }  // namespace
 
+// Partial rows: one per (CSR entry, head of its selection), plus one trash row.
+static int64_t partial_rows(const msa_varlen_t* vl, int Hq, int n_sel, int topk) {
+  return (int64_t)n_sel * vl->total_q * topk * (Hq / n_sel) + 1;
+}
+
 size_t attn_workspace_bytes(const msa_varlen_t* vl, int Hq, int Hkv, int n_sel, int topk) {
   (void)Hkv;
-  const int64_t nnz_max = (int64_t)n_sel * vl->total_q * topk;
-  const int64_t hp = Hq / n_sel;
-  return align_up((size_t)(nnz_max * hp * kDim * sizeof(uint16_t)), 256) +
-         align_up((size_t)(nnz_max * hp * sizeof(float)), 256);
+  const int64_t rows = partial_rows(vl, Hq, n_sel, topk);
+  return align_up((size_t)(rows * kDim * sizeof(uint16_t)), 256) +
+         align_up((size_t)(rows * sizeof(float2)), 256);
 }
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.vl.total_q == 0) return hipSuccess;
   const SchedLayout& L = a.L;
-  const int64_t nnz_max = (int64_t)a.n_sel * a.vl.total_q * kTopK;
+  const int64_t rows = partial_rows(&a.vl, a.Hq, a.n_sel, kTopK);
   const int HP = a.Hq / a.n_sel;
   AttnK k;
-  k.cu_q = a.vl.cu_seqlens_q;
-  k.cu_k = a.vl.cu_seqlens_k;
-  k.block_table = a.vl.block_table;
-  k.bt_stride = a.vl.block_table_stride;
-  k.batch = a.vl.batch;
-  k.num_pages = a.num_pages;
-  k.total_rows = a.vl.total_rows;
   k.q = a.q;
   k.q_stride = a.q_stride;
-  k.Hq = a.Hq;
-  k.Hkv = a.Hkv;
   k.G = a.Hq / a.Hkv;
   k.n_sel = a.n_sel;
   k.HP = HP;
+  k.GY = a.n_sel == 1 ? a.Hkv : 1;
   k.kv = a.kv;
-  k.row_base = reinterpret_cast<const int32_t*>(a.sched + L.row_base);
-  k.row_ptr = a.row_ptr;
+  k.num_pages = a.num_pages;
+  k.Hkv = a.Hkv;
   k.q_indices = a.q_indices;
   k.items = reinterpret_cast<const int4*>(a.sched + L.items);
   k.n_items = reinterpret_cast<const int32_t*>(a.sched + L.hdr);
@@ -325,12 +459,13 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   k.q_scale = a.q_scale;
   k.k_scale = a.k_scale;
   k.part_o = reinterpret_cast<uint16_t*>(a.workspace);
-  k.part_lse = reinterpret_cast<float*>(
-      reinterpret_cast<uint8_t*>(a.workspace) +
-      align_up((size_t)(nnz_max * HP * kDim * sizeof(uint16_t)), 256));
-  if (L.max_items > 0) {
-    dim3 grid((unsigned)L.max_items, a.n_sel == 1 ? a.Hkv : 1);
-    hipLaunchKernelGGL(attn_partial_kernel, grid, dim3(kThreads), 0, stream, k);
+  k.part_ml = reinterpret_cast<float2*>(reinterpret_cast<uint8_t*>(a.workspace) +
+                                        align_up((size_t)(rows * kDim * sizeof(uint16_t)), 256));
+  k.trash = rows - 1;
+  const int64_t max_work = L.max_items * k.GY;
+  if (max_work > 0) {
+    const int64_t grid = std::min<int64_t>(max_work, (int64_t)device_cu_count() * kBlocksPerCU);
+    hipLaunchKernelGGL(attn_partial_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, k);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -342,7 +477,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   c.HP = HP;
   c.inv = reinterpret_cast<const int32_t*>(a.sched + L.inv);
   c.part_o = k.part_o;
-  c.part_lse = k.part_lse;
+  c.part_ml = k.part_ml;
   c.v_scale = a.v_scale;
   c.out = a.out;
   c.out_stride = a.out_stride;
