@@ -8,11 +8,15 @@ combine).  The workload is 2048 new tokens at the end of a 1,048,576-token KV
 (8192 pages of 128), one index head, 8 query heads over one KV head, D = 128
 (the shape of the pages' headline scorer number, "Q2048 / KV1M").
 
-Prints ONE JSON line.  `value` is the index-scoring time per layer in
-microseconds (the headline quantity), measured with HIP events on the stream
-the kernels run on, averaged over the timed steps; `ms_per_step` is the whole
-path.  Roofline, rocprof-comparable per-call times and the CPU oracle's time on
-a bounded sample are reported beside it.
+Prints ONE JSON line.  The GPU is first kept busy for --prewarm-ms so its
+clocks reach their sustained level, then W warmup steps run, then exactly K
+steps are timed (synchronised on both sides; `ms_per_step`).  `value` is the
+index-scoring time per layer in microseconds: the msa_index_score call (device
+plan + scorer) issued K times back to back on the stream the kernels run on,
+between two HIP events (so no event marker sits between the calls).  Each of
+the other calls is timed the same way for the breakdown.  Roofline,
+per-call times and the CPU oracle's time on a bounded sample are reported
+beside it.
 """
 from __future__ import annotations
 
@@ -37,6 +41,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--prewarm-ms", type=float, default=1000.0,
+                    help="run the path for this long before the warmup steps (clock ramp)")
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--cold", action="store_true",
                     help="overwrite a 1 GiB buffer before every step (outside the events)")
@@ -134,47 +140,60 @@ def main():
     stream = torch.cuda.current_stream()
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.cold else None
 
-    n_ev = 5
     names = ["index_score", "topk_select", "k2q_csr", "sparse_attn"]
+    calls = [path.score, path.select, path.csr, path.attend]
 
-    def step(evs=None):
-        if evs is not None:
-            evs[0].record(stream)
-        path.score()
-        if evs is not None:
-            evs[1].record(stream)
-        path.select()
-        if evs is not None:
-            evs[2].record(stream)
-        path.csr()
-        if evs is not None:
-            evs[3].record(stream)
-        path.attend()
-        if evs is not None:
-            evs[4].record(stream)
-
-    for _ in range(args.warmup):
+    def step():
         if flush_buf is not None:
             flush_buf.fill_(1)
+        for c in calls:
+            c()
+
+    # clock ramp, then the warmup steps
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < args.prewarm_ms:
+        step()
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    print(f"[bench] prewarm {args.prewarm_ms:.0f} ms + warmup {args.warmup} steps done",
+          file=sys.stderr, flush=True)
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    # the K timed steps (whole path)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for k in range(args.steps):
-        if flush_buf is not None:
-            flush_buf.fill_(k & 0xFF)
-        step(events[k])
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    per = np.array([[events[k][j].elapsed_time(events[k][j + 1]) * 1e3 for j in range(n_ev - 1)]
-                    for k in range(args.steps)])               # us
-    mean_us = per.mean(axis=0)
-    med_us = np.median(per, axis=0)
-    step_us = per.sum(axis=1)
-    print(f"[bench] timed {args.steps} steps: " +
+
+    # per call: K back-to-back calls between two events on the kernels' stream
+    # (with --cold: every call after a cache flush, one event pair per call)
+    per_call = []
+    for c in calls:
+        if flush_buf is None:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(args.steps):
+                c()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per_call.append(e0.elapsed_time(e1) * 1e3 / args.steps)      # us
+        else:
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            for k in range(args.steps):
+                flush_buf.fill_(k & 0xFF)
+                evs[k][0].record(stream)
+                c()
+                evs[k][1].record(stream)
+            torch.cuda.synchronize()
+            per_call.append(float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3)
+    mean_us = np.array(per_call)
+    print(f"[bench] timed {args.steps} steps: {wall / args.steps * 1e6:.1f} us/step; per call " +
           ", ".join(f"{n} {m:.1f} us" for n, m in zip(names, mean_us)), file=sys.stderr, flush=True)
 
     sel = path.topk[:, 0, :].cpu().numpy()
@@ -191,6 +210,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "timing": "per call: K calls back to back between two HIP events; step: wall clock",
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -206,8 +226,7 @@ def main():
                      "traffic": None, "kernel": "index_score (plan + scorer)",
                      "flops_per_launch": work["score_flops"]},
         "breakdown_us": {n: round(float(m), 2) for n, m in zip(names, mean_us)},
-        "breakdown_median_us": {n: round(float(m), 2) for n, m in zip(names, med_us)},
-        "path_us_per_step": round(float(step_us.mean()), 2),
+        "path_us_per_call_sum": round(float(mean_us.sum()), 2),
         "sparse_prefill_tflops": round(attn_tflops, 2),
         "sparse_prefill_frac_fp8_peak": round(attn_tflops / PEAK_FP8_TFLOPS, 5),
         "sparse_prefill_gbs": round(work["attn_bytes"] / (attn_us * 1e-6) / 1e9, 1),

@@ -37,7 +37,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRowB = 144;          // LDS row stride (bytes)
-constexpr int kBlocksPerCU = 2;
+// Blocks per CU: the wide kernel (items of many rows, two-tile sets) needs about
+// 240 registers per lane; the narrow one (one-tile sets) fits three blocks.
+constexpr int kBlocksWide = 2;
+constexpr int kBlocksNarrow = 3;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kOnesE4M3 = 0x38383838;   // four E4M3 1.0 codes
 
@@ -300,7 +303,31 @@ __device__ __forceinline__ void run_item(const AttnK& a, const Work& w, const ui
   }
 }
 
-__global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_partial_kernel(AttnK a) {
+// Items of a few rows: one-tile sets, rows requested one set ahead only (a wave
+// rarely has a second set), which keeps the register count at three blocks per CU.
+template <class Prefetch>
+__device__ __forceinline__ void run_item_narrow(const AttnK& a, const Work& w,
+                                                const uint8_t* k_lds, const uint8_t* vt_lds,
+                                                const int* s_qi, float zscale, int wave, int lane,
+                                                Prefetch&& prefetch) {
+  const int n_rows = w.count * a.G;
+  const int n_tiles = (n_rows + 15) >> 4;
+  int t = wave;
+  RowSet<1> r = load_rows<1>(a, w, t, n_rows, s_qi, lane);
+  __builtin_amdgcn_sched_barrier(0);        // keep the row loads ahead of the prefetch
+  prefetch();
+  __builtin_amdgcn_sched_barrier(0);
+  while (t < n_tiles) {
+    compute_set<1>(a, r, k_lds, vt_lds, zscale, lane);
+    t += kWaves;
+    if (t >= n_tiles) break;
+    r = load_rows<1>(a, w, t, n_rows, s_qi, lane);
+  }
+}
+
+template <bool kWide>
+__global__ __launch_bounds__(kThreads, kWide ? kBlocksWide : kBlocksNarrow) void attn_partial_kernel(
+    AttnK a) {
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[kPage * kRowB];
   __shared__ __attribute__((aligned(16))) uint8_t vt_lds[kDim * kRowB];
   __shared__ int s_qi[kAttnQC];
@@ -341,7 +368,9 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void attn_partial_kernel(At
       my = a.items[2 * item_of(wn + gridDim.x) + 1];
     };
     const int n_tiles = (cur.count * a.G + 15) >> 4;
-    if (n_tiles >= 2 * kWaves)
+    if (!kWide)
+      run_item_narrow(a, cur, k_lds, vt_lds, s_qi, zscale, wave, lane, prefetch);
+    else if (n_tiles >= 2 * kWaves)
       run_item<2>(a, cur, k_lds, vt_lds, s_qi, zscale, wave, lane, prefetch);
     else
       run_item<1>(a, cur, k_lds, vt_lds, s_qi, zscale, wave, lane, prefetch);
@@ -464,8 +493,16 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   k.trash = rows - 1;
   const int64_t max_work = L.max_items * k.GY;
   if (max_work > 0) {
-    const int64_t grid = std::min<int64_t>(max_work, (int64_t)device_cu_count() * kBlocksPerCU);
-    hipLaunchKernelGGL(attn_partial_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, k);
+    // Rows per item from the host bound on entries per CSR row (total_q * topk
+    // entries over total_rows rows, at most kAttnQC queries per item).
+    const int64_t per_row = ceil_div((int64_t)a.vl.total_q * kTopK, std::max(a.vl.total_rows, 1));
+    const bool wide = std::min<int64_t>(per_row, kAttnQC) * k.G >= 2 * kWaves * 16;
+    const int per_cu = wide ? kBlocksWide : kBlocksNarrow;
+    const int64_t grid = std::min<int64_t>(max_work, (int64_t)device_cu_count() * per_cu);
+    if (wide)
+      hipLaunchKernelGGL(attn_partial_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, k);
+    else
+      hipLaunchKernelGGL(attn_partial_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, k);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
