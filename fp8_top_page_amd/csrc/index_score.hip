@@ -7,10 +7,13 @@
 // and the scoring call neither allocates nor synchronises).
 //
 // Design (MI355X):
-//  * Planning: one small kernel turns cu_seqlens_q/k into a list of uniform work
-//    items (request, block of queries, chunk of pages), causal-trimmed, in the
-//    workspace.  The scorer grid is sized from host-side upper bounds, and
-//    blocks past the device-side item count exit.
+//  * Planning: one small kernel turns cu_seqlens_q/k into a list of work items
+//    (request, block of queries, chunk of pages), causal-trimmed, in the
+//    workspace.  It first sums the visible pages of every query block and sizes
+//    the page chunks so the items about fill the GPU (one per compute unit when
+//    all query blocks see the same pages, three when they differ).  The scorer
+//    grid is sized from host-side upper bounds, and blocks past the device-side
+//    item count exit.
 //  * Scoring: tokens are the MFMA M axis, queries the N axis.  Each wave keeps
 //    the E4M3 fragments of 128/H queries (all H heads) in registers for the
 //    whole item; the index-K page (16 KiB) is staged once per block in LDS
@@ -29,14 +32,18 @@ namespace {
 constexpr int kLdsRow = 144;                 // 128 B + 16 B pad against bank conflicts
 constexpr int kLdsPage = kPage * kLdsRow;    // 18 KiB
 constexpr int kThreads = kScoreWaves * 64;
-constexpr int kFlush = 16;                   // pages per score-tile flush (divides the item size)
+constexpr int kFlush = 16;                   // pages per score-tile flush
 constexpr int kSRow = kFlush + 1;            // score-tile row stride in floats
 constexpr int kMaxItemPages = 256;           // pages per work item, at most
+constexpr int kMinItemPages = 4;             // ... and at least (keeps score stores 16-byte aligned)
 constexpr int kPlanCUs = 256;                // compute units the item sizing aims to fill
+constexpr int kItemsUniform = kPlanCUs;      // item count aimed at when all q-blocks are alike
+constexpr int kItemsRagged = 3 * kPlanCUs;   // ... and otherwise
 
 struct ItemHdr {
   int32_t n_items;
-  int32_t pad[63];
+  int32_t pages_per_item;                    // chosen by the plan, multiple of 4
+  int32_t pad[62];
 };
 
 struct ScoreK {
@@ -54,29 +61,72 @@ struct ScoreK {
   const float* k_scale;
   float* scores;
   int64_t ld;
-  const int32_t* n_items;
+  const ItemHdr* hdr;
   const int4* items;
-  int32_t pages_per_item;
 };
 
 // ---------------------------------------------------------------------------
-// Plan: one block.  Items are emitted request by request, q-block by q-block,
-// page chunk by page chunk.  item = {b, first global query, query count, first page}.
-// For each batch of up to 256 q-blocks: one thread per q-block counts its page
-// chunks, a block scan places them, then all threads emit the batch's items.
+// Plan: one block.  Pass 1 sums v (visible pages) over every q-block and
+// chooses the pages per item; pass 2 emits the items request by request, q-block
+// by q-block, page chunk by page chunk: item = {b, first global query, query
+// count, first page}.  For each batch of up to 256 q-blocks one thread per
+// q-block counts its page chunks, a block scan places them, then all threads
+// emit the batch's items.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ int qblock_visible(int ctx, int qf, int qn) {
+  return (ctx + qf + qn - 1) / kPage + 1;
+}
+
 __global__ __launch_bounds__(256) void score_plan_kernel(const int32_t* __restrict__ cu_q,
                                                          const int32_t* __restrict__ cu_k, int B,
-                                                         int qblock, int pc, int64_t max_items,
-                                                         int32_t* __restrict__ n_items,
+                                                         int qblock, int64_t max_items,
+                                                         ItemHdr* __restrict__ hdr,
                                                          int4* __restrict__ items) {
   __shared__ int wave_tot[4];
   __shared__ int s_off[257];
   __shared__ int s_qf[256], s_qn[256];
   __shared__ int64_t running;
+  __shared__ int64_t s_w[4];
+  __shared__ int s_vmin[4], s_vmax[4];
+  __shared__ int s_pc;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) running = 0;
+
+  // pass 1: total and spread of the visible pages over all q-blocks
+  int64_t w = 0;
+  int vmin = INT32_MAX, vmax = 0;
+  for (int b = 0; b < B; ++b) {
+    const int sq = cu_q[b + 1] - cu_q[b];
+    const int ctx = (cu_k[b + 1] - cu_k[b]) - sq;
+    const int nqb = (sq + qblock - 1) / qblock;
+    for (int qb = tid; qb < nqb; qb += 256) {
+      const int qf = qb * qblock;
+      const int v = qblock_visible(ctx, qf, min(sq - qf, qblock));
+      w += v;
+      vmin = min(vmin, v);
+      vmax = max(vmax, v);
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    w += __shfl_xor(w, o);
+    vmin = min(vmin, __shfl_xor(vmin, o));
+    vmax = max(vmax, __shfl_xor(vmax, o));
+  }
+  if (lane == 0) { s_w[wave] = w; s_vmin[wave] = vmin; s_vmax[wave] = vmax; }
   __syncthreads();
+  if (tid == 0) {
+    int64_t tw = 0;
+    int lo = INT32_MAX, hi = 0;
+    for (int k = 0; k < 4; ++k) { tw += s_w[k]; lo = min(lo, s_vmin[k]); hi = max(hi, s_vmax[k]); }
+    const int64_t target = (hi - lo) * 8 <= hi ? kItemsUniform : kItemsRagged;
+    int64_t pc = (tw + target - 1) / target;
+    pc = (pc + 3) / 4 * 4;
+    s_pc = (int)min<int64_t>(kMaxItemPages, max<int64_t>(kMinItemPages, pc));
+    running = 0;
+  }
+  __syncthreads();
+  const int pc = s_pc;
+
+  // pass 2: emit
   for (int b = 0; b < B; ++b) {
     const int q0 = cu_q[b], sq = cu_q[b + 1] - q0;
     const int sk = cu_k[b + 1] - cu_k[b];
@@ -88,16 +138,15 @@ __global__ __launch_bounds__(256) void score_plan_kernel(const int32_t* __restri
       if (qb < nqb) {
         qf = qb * qblock;
         qn = min(sq - qf, qblock);
-        const int v = (ctx + qf + qn - 1) / kPage + 1;
-        nch = (v + pc - 1) / pc;
+        nch = (qblock_visible(ctx, qf, qn) + pc - 1) / pc;
       }
       const int incl = wave_inclusive_scan(nch);
       if (lane == 63) wave_tot[wave] = incl;
       __syncthreads();
       int wave_off = 0, total = 0;
-      for (int w = 0; w < 4; ++w) {
-        if (w < wave) wave_off += wave_tot[w];
-        total += wave_tot[w];
+      for (int k = 0; k < 4; ++k) {
+        if (k < wave) wave_off += wave_tot[k];
+        total += wave_tot[k];
       }
       s_off[tid] = wave_off + incl - nch;
       s_qf[tid] = qf;
@@ -119,7 +168,10 @@ __global__ __launch_bounds__(256) void score_plan_kernel(const int32_t* __restri
       __syncthreads();
     }
   }
-  if (tid == 0) *n_items = (int32_t)min<int64_t>(running, max_items);
+  if (tid == 0) {
+    hdr->n_items = (int32_t)min<int64_t>(running, max_items);
+    hdr->pages_per_item = pc;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -194,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int item = blockIdx.x;
-  if (item >= *a.n_items) return;
+  if (item >= a.hdr->n_items) return;
   const int4 it = a.items[item];
   const int b = it.x, q_first = it.y, q_count = it.z, p0 = it.w;
 
@@ -210,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
   const int pos_first = ctx + (q_first - cq0);
   const int pos_last = pos_first + q_count - 1;
   const int v_block = pos_last / kPage + 1;
-  const int p_end = min(min(p0 + a.pages_per_item, v_block), a.max_pages);
+  const int p_end = min(min(p0 + a.hdr->pages_per_item, v_block), a.max_pages);
   if (p0 >= p_end) return;
   const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
 
@@ -294,7 +346,8 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
   __syncthreads();
 
   // Flush the wave's score tile for pages [pg0, pg_hi): lane handles a
-  // (query, 4-page) piece; full pieces go out as one 16-byte store.
+  // (query, 4-page) piece; full pieces go out as one 16-byte store (pg0 is a
+  // multiple of 4: items start at multiples of the pages per item).
   auto flush = [&](int pg0, int pg_hi) {
 #pragma unroll
     for (int r = 0; r < NQT; ++r) {
@@ -326,14 +379,14 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
       page_max_causal<H, NQT>(pg, qf, my_pos0 - p * kPage, col, grp, rmax);
     else
       page_max<H, NQT>(pg, qf, col, grp, rmax);
-    const int pc = p & (kFlush - 1);
+    const int pc = (p - p0) & (kFlush - 1);    // tiles start at the item's first page
 #pragma unroll
     for (int n = 0; n < NQT; ++n) {
       float m = fmaxf(fmaxf(rmax[n][0], rmax[n][1]), fmaxf(rmax[n][2], rmax[n][3]));
       m = max_across_groups(m);
       if ((n & 3) == grp) sbuf[(n * 16 + col) * kSRow + pc] = m * scale;
     }
-    if (pc == kFlush - 1 || p == p_end - 1) flush(p & ~(kFlush - 1), p + 1);
+    if (pc == kFlush - 1 || p == p_end - 1) flush(p - pc, p + 1);
   };
 
   // One step: score pages p, p + 1; write the staged pair p + 2, p + 3 into the
@@ -383,20 +436,14 @@ hipError_t launch_scorer(dim3 grid, hipStream_t stream, const ScoreK& k) {
 ScorePlan score_plan(const msa_varlen_t* vl, int H) {
   ScorePlan p;
   const int qb = score_qblock(H);
-  const int64_t est_qb = std::max<int64_t>(1, ceil_div(vl->total_q, qb));
-  const int64_t qb_bound = ceil_div(vl->total_q, qb) + vl->batch;
+  const int64_t qb_bound = ceil_div(vl->total_q, qb) + vl->batch;   // q-blocks, at most
   const int64_t max_pages = std::max<int32_t>(1, vl->max_pages);
-  // Size items from the estimated page work (q-blocks x visible pages).  When
-  // the queries are a short tail of long contexts every q-block sees about the
-  // same pages, so one item per compute unit balances; when they cover much of
-  // the context (causal prefill) item sizes vary, so aim for two per unit.
-  const int64_t avg_visible =
-      std::max<int64_t>(1, max_pages - ceil_div(std::max(vl->max_seqlen_q, 1), kPage) / 2);
-  const bool uniform = (int64_t)vl->max_seqlen_q * 4 <= vl->max_seqlen_k;
-  int64_t pc = ceil_div(est_qb * avg_visible, kPlanCUs * (uniform ? 1 : 2));
-  pc = std::min<int64_t>(kMaxItemPages, std::max<int64_t>(kFlush, ceil_div(pc, kFlush) * kFlush));
-  p.pages_per_item = (int32_t)pc;
-  p.max_items = qb_bound * ceil_div(max_pages, pc);
+  // The device plan picks pages per item pc >= (sum of visible pages) / target,
+  // so sum over q-blocks of ceil(v / pc) <= target + q-blocks, unless pc hits
+  // kMaxItemPages, where it is at most q-blocks * (max_pages / kMaxItemPages + 1).
+  p.pages_per_item = 0;   // chosen on the device
+  p.max_items = std::max<int64_t>(kItemsRagged, qb_bound * ceil_div(max_pages, kMaxItemPages)) +
+                qb_bound;
   p.workspace_bytes = sizeof(ItemHdr) + align_up((size_t)p.max_items * sizeof(int4), 256);
   return p;
 }
@@ -406,8 +453,8 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
   ItemHdr* hdr = reinterpret_cast<ItemHdr*>(a.workspace);
   int4* items = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(a.workspace) + sizeof(ItemHdr));
   hipLaunchKernelGGL(score_plan_kernel, dim3(1), dim3(256), 0, stream, a.vl.cu_seqlens_q,
-                     a.vl.cu_seqlens_k, a.vl.batch, score_qblock(a.H), a.plan.pages_per_item,
-                     a.plan.max_items, &hdr->n_items, items);
+                     a.vl.cu_seqlens_k, a.vl.batch, score_qblock(a.H), a.plan.max_items, hdr,
+                     items);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   ScoreK k;
@@ -425,9 +472,8 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
   k.k_scale = a.k_scale;
   k.scores = a.scores;
   k.ld = a.ld;
-  k.n_items = &hdr->n_items;
+  k.hdr = hdr;
   k.items = items;
-  k.pages_per_item = a.plan.pages_per_item;
   dim3 grid((unsigned)a.plan.max_items);
   switch (a.H) {
     case 1: return launch_scorer<1>(grid, stream, k);

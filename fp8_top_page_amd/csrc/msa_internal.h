@@ -29,7 +29,7 @@ constexpr int score_qtiles(int H) { return kScoreQueriesPerWave / 16 / H; }
 constexpr int score_qblock(int H) { return kScoreWaves * 16 * score_qtiles(H); }
 
 struct ScorePlan {
-  int32_t pages_per_item;   // multiple of 4
+  int32_t pages_per_item;   // 0: chosen by the device plan
   int64_t max_items;        // host upper bound (grid size before padding)
   size_t workspace_bytes;
 };
