@@ -49,7 +49,24 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB three times (the "
+                         "reference kernel that scales HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def copy_probe(mib):
+    """A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE
+    counters give the factor between counted and actual HBM bytes."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "repeats": 3}), flush=True)
 
 
 def algorithmic_work(inp, sel):
@@ -87,6 +104,24 @@ def algorithmic_work(inp, sel):
                 distinct_pages=int(distinct))
 
 
+def scorer_hbm_traffic(workload):
+    """HBM bytes per scorer launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a 1 GiB
+    copy), or None when there is none for this workload or the scorer's sources
+    have changed since the counters were taken."""
+    import hashlib
+    f = os.path.join(ROOT, "profiles", f"index_score_{workload}_hbm.json")
+    if not os.path.exists(f):
+        return None
+    rec = json.load(open(f))
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    return int(round(rec["hbm_bytes_per_launch"]))
+
+
 def cpu_baseline(inp, budget_s):
     """The oracle's index scoring timed on a bounded sample of queries (chunks of
     64 evenly spread queries until about budget_s seconds of CPU work), scaled
@@ -117,6 +152,9 @@ def cpu_baseline(inp, budget_s):
 
 def main():
     args = parse()
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(the path is per tensor-parallel rank: see DESIGN.md on sharding)", file=sys.stderr)
@@ -223,8 +261,10 @@ def main():
                    else "warm (steps back to back)"},
         "roofline": {"bound": "mfma", "achieved": round(score_tflops, 1), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(score_tflops / PEAK_FP8_TFLOPS, 4),
-                     "traffic": None, "kernel": "index_score (plan + scorer)",
-                     "flops_per_launch": work["score_flops"]},
+                     "traffic": scorer_hbm_traffic(wl.name), "kernel": "index_score (plan + scorer)",
+                     "flops_per_launch": work["score_flops"],
+                     "algorithmic_bytes_per_launch": work["score_bytes"],
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"},
         "breakdown_us": {n: round(float(m), 2) for n, m in zip(names, mean_us)},
         "path_us_per_call_sum": round(float(mean_us.sum()), 2),
         "sparse_prefill_tflops": round(attn_tflops, 2),
