@@ -29,8 +29,7 @@
 namespace msa {
 namespace {
 
-constexpr int kLdsRow = 144;                 // 128 B + 16 B pad against bank conflicts
-constexpr int kLdsPage = kPage * kLdsRow;    // 18 KiB
+constexpr int kLdsPage = kPage * kDim;       // 16 KiB: 128 rows of 128 B, 16-byte pieces swizzled
 constexpr int kThreads = kScoreWaves * 64;
 constexpr int kFlush = 16;                   // pages per score-tile flush
 constexpr int kSRow = kFlush + 1;            // score-tile row stride in floats
@@ -178,18 +177,38 @@ __global__ __launch_bounds__(256) void score_plan_kernel(const int32_t* __restri
 // Scorer.
 // ---------------------------------------------------------------------------
 
+// Index-K page layout in LDS: row t (token) holds its eight 16-byte pieces with
+// piece c stored at position c ^ ((t >> 1) & 7).  The direct-to-LDS copy below
+// fills whole 1 KiB spans lane by lane, so rows cannot be padded; the swizzle
+// makes the fragment reads (16 rows x 32 bytes) free of bank conflicts instead.
+struct Swz {
+  int off0, off1;   // byte offsets in a row of this lane's two pieces (2 grp, 2 grp + 1)
+};
+__device__ __forceinline__ Swz lane_swizzle(int col, int grp) {
+  const int s = (col >> 1) & 7;                 // rows 16T + col share (row >> 1) & 7
+  return Swz{16 * ((2 * grp) ^ s), 16 * ((2 * grp + 1) ^ s)};
+}
+__device__ __forceinline__ v8i load_frag_swz(const uint8_t* row, const Swz& z) {
+  const uint4 x = *reinterpret_cast<const uint4*>(row + z.off0);
+  const uint4 y = *reinterpret_cast<const uint4*>(row + z.off1);
+  v8i r;
+  r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
+  r[4] = y.x; r[5] = y.y; r[6] = y.z; r[7] = y.w;
+  return r;
+}
+
 // Max over one page's 128 tokens for every resident query tile.  A fragments
 // (16 tokens x 128 bytes) are read from LDS one tile ahead of their products.
 template <int H, int NQT>
 __device__ __forceinline__ void page_max(const uint8_t* __restrict__ pg, const v8i (&qf)[NQT][H],
-                                         int col, int grp, v4f (&rmax)[NQT]) {
+                                         int col, const Swz& z, v4f (&rmax)[NQT]) {
 #pragma unroll
   for (int n = 0; n < NQT; ++n) rmax[n] = v4f{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  v8i a_cur = load_frag_lds(pg + col * kLdsRow + grp * 32);
+  v8i a_cur = load_frag_swz(pg + col * kDim, z);
 #pragma unroll
   for (int T = 0; T < 8; ++T) {
     v8i a_nxt;
-    if (T < 7) a_nxt = load_frag_lds(pg + ((T + 1) * 16 + col) * kLdsRow + grp * 32);
+    if (T < 7) a_nxt = load_frag_swz(pg + ((T + 1) * 16 + col) * kDim, z);
 #pragma unroll
     for (int n = 0; n < NQT; ++n) {
       v4f acc = mfma_e4m3(a_cur, qf[n][0], v4f{0.f, 0.f, 0.f, 0.f});
@@ -209,12 +228,12 @@ __device__ __forceinline__ void page_max(const uint8_t* __restrict__ pg, const v
 template <int H, int NQT>
 __device__ __forceinline__ void page_max_causal(const uint8_t* __restrict__ pg,
                                                 const v8i (&qf)[NQT][H], int lim0, int col,
-                                                int grp, v4f (&rmax)[NQT]) {
+                                                int grp, const Swz& z, v4f (&rmax)[NQT]) {
 #pragma unroll
   for (int n = 0; n < NQT; ++n) rmax[n] = v4f{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll 1
   for (int T = 0; T < 8; ++T) {
-    const v8i a_cur = load_frag_lds(pg + (T * 16 + col) * kLdsRow + grp * 32);
+    const v8i a_cur = load_frag_swz(pg + (T * 16 + col) * kDim, z);
 #pragma unroll
     for (int n = 0; n < NQT; ++n) {
       v4f acc = mfma_e4m3(a_cur, qf[n][0], v4f{0.f, 0.f, 0.f, 0.f});
@@ -274,52 +293,27 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
   }
   __syncthreads();
 
-  // Index-K pages (16 KiB) go global -> registers -> LDS; thread t copies bytes
-  // [kCopy*t, kCopy*(t+1)).  Pages are handled in pairs: while one pair is
-  // scored from LDS, the next pair is written to the other half of the ring and
-  // two more pairs are in flight in registers.  Loads are issued for every
-  // slot (page index clamped to the item) so the number of loads in flight is
-  // the same on every path.
-  constexpr int kCopy = kPage * kDim / kThreads;   // bytes per thread per page
-  constexpr int kV = kCopy / 16;
-  static_assert(kV >= 1 && kCopy % 16 == 0, "page copy must be whole 16-byte pieces");
-  const int st_row = tid / (kDim / kCopy), st_col = (tid % (kDim / kCopy)) * kCopy;
-  auto page_ptr = [&](int p) -> const uint8_t* {
+  // Index-K pages (16 KiB) are copied global -> LDS directly (global_load_lds,
+  // 16 bytes per lane, one instruction per wave and page: wave w fills rows
+  // 8w..8w+7), into a ring of four slots: page p lives in slot p & 3.  While a
+  // pair is scored, the next pair is in flight; after the barrier that ends a
+  // pair, the pair after next is requested into the slots just freed.  Every
+  // slot is requested even past the item's end (page index clamped) so the
+  // count of loads in flight is the same on every path.
+  static_assert(kThreads == kPage * kDim / 16, "one 16-byte piece per thread and page");
+  const int ld_row = wave * 8 + (lane >> 3);
+  const int ld_piece = (lane & 7) ^ ((ld_row >> 1) & 7);
+  auto issue_page = [&](int p) {
     const int phys = s_phys[min(p, p_end - 1) - p0];
-    return a.k_cache + (int64_t)phys * (kPage * kDim) + st_row * kDim + st_col;
+    const uint8_t* src = a.k_cache + (int64_t)phys * (kPage * kDim) + ld_row * kDim + ld_piece * 16;
+    __builtin_amdgcn_global_load_lds(
+        src, (__attribute__((address_space(3))) void*)(lds + (p & 3) * kLdsPage + wave * 1024), 16,
+        0, 0);
   };
-  // page p lives in ring slot p & 3
-  auto lds_slot = [&](int p) -> uint4* {
-    return reinterpret_cast<uint4*>(lds + (p & 3) * kLdsPage + st_row * kLdsRow + st_col);
-  };
-  uint4 stA[2][kV], stB[2][kV];
-  {
-    uint4 x0[kV], x1[kV];
-    const uint8_t* s0 = page_ptr(p0);
-    const uint8_t* s1 = page_ptr(p0 + 1);
-#pragma unroll
-    for (int v = 0; v < kV; ++v) {
-      x0[v] = load16_nt(s0 + 16 * v);
-      x1[v] = load16_nt(s1 + 16 * v);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint8_t* sa = page_ptr(p0 + 2 + j);
-      const uint8_t* sb = page_ptr(p0 + 4 + j);
-#pragma unroll
-      for (int v = 0; v < kV; ++v) {
-        stA[j][v] = load16_nt(sa + 16 * v);
-        stB[j][v] = load16_nt(sb + 16 * v);
-      }
-    }
-    uint4* d0 = lds_slot(p0);
-    uint4* d1 = lds_slot(p0 + 1);
-#pragma unroll
-    for (int v = 0; v < kV; ++v) {
-      d0[v] = x0[v];
-      d1[v] = x1[v];
-    }
-  }
+  issue_page(p0);
+  issue_page(p0 + 1);
+  issue_page(p0 + 2);
+  issue_page(p0 + 3);
 
   // Query fragments (B operand): column = query, K-group = 32-byte slice of D.
   // Loaded after the first index-K pages are requested so the latencies overlap.
@@ -343,6 +337,8 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
     }
   }
   const float scale = (*a.q_scale) * (*a.k_scale);
+  const Swz swz = lane_swizzle(col, grp);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's page pieces have landed
   __syncthreads();
 
   // Flush the wave's score tile for pages [pg0, pg_hi): lane handles a
@@ -376,9 +372,9 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
     const uint8_t* pg = lds + (p & 3) * kLdsPage;
     v4f rmax[NQT];
     if ((p + 1) * kPage - 1 > pos_first)
-      page_max_causal<H, NQT>(pg, qf, my_pos0 - p * kPage, col, grp, rmax);
+      page_max_causal<H, NQT>(pg, qf, my_pos0 - p * kPage, col, grp, swz, rmax);
     else
-      page_max<H, NQT>(pg, qf, col, grp, rmax);
+      page_max<H, NQT>(pg, qf, col, swz, rmax);
     const int pc = (p - p0) & (kFlush - 1);    // tiles start at the item's first page
 #pragma unroll
     for (int n = 0; n < NQT; ++n) {
@@ -389,34 +385,20 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
     if (pc == kFlush - 1 || p == p_end - 1) flush(p - pc, p + 1);
   };
 
-  // One step: score pages p, p + 1; write the staged pair p + 2, p + 3 into the
-  // other half of the ring; barrier; start loading pair p + 6, p + 7.
-  auto step = [&](int p, uint4 (&st)[2][kV]) {
+  // One step: score pages p, p + 1; wait for this wave's pieces of p + 2, p + 3;
+  // barrier (pages p + 2, p + 3 complete, slots of p, p + 1 free); request
+  // p + 4, p + 5 into those slots.
+  for (int p = p0; p < p_end; p += 2) {
     if (wave_active) {
-      if (p < p_end) score_page(p);
+      score_page(p);
       if (p + 1 < p_end) score_page(p + 1);
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (p + 2 + j < p_end) {
-        uint4* dst = lds_slot(p + 2 + j);   // last read while scoring pair p - 2
-#pragma unroll
-        for (int v = 0; v < kV; ++v) dst[v] = st[j][v];
-      }
-    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint8_t* src = page_ptr(p + 6 + j);
-#pragma unroll
-      for (int v = 0; v < kV; ++v) st[j][v] = load16_nt(src + 16 * v);
+    if (p + 2 < p_end) {
+      issue_page(p + 4);
+      issue_page(p + 5);
     }
-  };
-  // Every iteration runs both steps (a step past the end only keeps the
-  // barrier and load counts uniform).
-  for (int pb = p0; pb < p_end; pb += 4) {
-    step(pb, stA);
-    step(pb + 2, stB);
   }
 }
 
