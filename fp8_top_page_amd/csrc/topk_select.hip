@@ -7,7 +7,9 @@
 // pages (vLLM PR 64631, Details); here equal scores go to the lower page index,
 // which makes the result deterministic.
 //
-// One 256-thread block per query:
+// Rows of up to 512 visible pages: one wave per query (keys in registers, every
+// key >= the wave bound fits the wave's LDS list, so no fallback is needed).
+// Longer rows: one 256-thread block per query:
 //  1. each lane takes the max orderable key over its strided share of the row;
 //  2. within each wave, the ksel-th largest lane maximum is a lower bound tau_w
 //     on the ksel-th largest key of the row (ksel distinct elements reach it);
@@ -246,6 +248,93 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkK a) {
   }
 }
 
+// One wave per query for rows of at most 64 * KPT candidates.  Lane l owns pages
+// 256k + 4l + {0..3} (16-byte loads); the wave bound is taken as in the block
+// kernel and every key >= it (at most 64 * KPT) is ranked from the wave's LDS list.
+template <int KPT>
+__global__ __launch_bounds__(kBlock) void topk_wave_kernel(TopkK a) {
+  static_assert(KPT % 4 == 0, "four keys per 16-byte load");
+  constexpr int kWaves = kBlock / 64;
+  constexpr int kList = 64 * KPT;
+  __shared__ uint64_t c_pk[kWaves][kList];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t i = (int64_t)blockIdx.x * kWaves + wave;
+  if (i >= a.total_q) return;
+  const int b = find_request(a.cu_q, a.batch, i);
+  const int cq0 = a.cu_q[b];
+  const int sq = a.cu_q[b + 1] - cq0;
+  const int sk = a.cu_k[b + 1] - a.cu_k[b];
+  const int pos = sk - sq + (int)(i - cq0);
+  const int v = min(pos / kPage + 1, a.max_pages);
+  const int k_all = min(kTopK, v);
+  const int f = min(a.n_local, k_all);
+  const int ksel = k_all - f;
+  const int ncand = v - f;
+  int32_t* out = a.out + i * a.out_stride;
+  const float* row = a.scores + i * a.ld;
+  const bool vec_ok = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+
+  if (lane < kTopK) {
+    if (lane < f) out[lane] = v - 1 - lane;
+    else if (lane >= k_all) out[lane] = -1;
+  }
+  if (ksel == 0) return;
+
+  uint32_t key[KPT];
+#pragma unroll
+  for (int k4 = 0; k4 < KPT / 4; ++k4) {
+    const int j = k4 * 256 + lane * 4;
+    if (vec_ok && j + 3 < ncand) {
+      const float4 x = *reinterpret_cast<const float4*>(row + j);
+      key[4 * k4 + 0] = float_key(x.x);
+      key[4 * k4 + 1] = float_key(x.y);
+      key[4 * k4 + 2] = float_key(x.z);
+      key[4 * k4 + 3] = float_key(x.w);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[4 * k4 + e] = (j + e < ncand) ? float_key(row[j + e]) : 0u;
+    }
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) m = max(m, key[k]);
+
+  // the ksel-th largest lane maximum: ksel keys of the row reach it
+  uint32_t tau = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t t = tau | (1u << bit);
+    if (__popcll(__ballot(m >= t)) >= ksel) tau = t;
+  }
+
+  // every candidate key >= tau goes to the list (at most 64 * KPT of them);
+  // slots past ncand are skipped by their page index
+  int mine = 0;
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int j = (k >> 2) * 256 + lane * 4 + (k & 3);
+    mine += (j < ncand && key[k] >= tau) ? 1 : 0;
+  }
+  const int incl = wave_inclusive_scan(mine);
+  const int c = __shfl(incl, 63);
+  int slot = incl - mine;
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int j = (k >> 2) * 256 + lane * 4 + (k & 3);
+    if (j < ncand && key[k] >= tau) c_pk[wave][slot++] = pack_key(key[k], j);
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+
+  // exact rank among the candidates (packed keys are unique)
+  for (int e = lane; e < c; e += 64) {
+    const uint64_t me = c_pk[wave][e];
+    int r = 0;
+    for (int o = 0; o < c; ++o) r += c_pk[wave][o] > me ? 1 : 0;
+    if (r < ksel) out[f + r] = (int)~(uint32_t)me;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
@@ -261,8 +350,14 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   k.n_local = a.n_local;
   k.out = a.out;
   k.out_stride = a.out_stride;
-  const dim3 grid((unsigned)a.vl.total_q);
   const int need = std::max(1, a.vl.max_pages);   // candidates per query, at most
+  if (need <= 512) {
+    const dim3 wgrid((unsigned)ceil_div(a.vl.total_q, kBlock / 64));
+    if (need <= 256) hipLaunchKernelGGL(topk_wave_kernel<4>, wgrid, dim3(kBlock), 0, stream, k);
+    else hipLaunchKernelGGL(topk_wave_kernel<8>, wgrid, dim3(kBlock), 0, stream, k);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)a.vl.total_q);
   if (need <= kBlock * 1) hipLaunchKernelGGL(topk_kernel<1>, grid, dim3(kBlock), 0, stream, k);
   else if (need <= kBlock * 2) hipLaunchKernelGGL(topk_kernel<2>, grid, dim3(kBlock), 0, stream, k);
   else if (need <= kBlock * 4) hipLaunchKernelGGL(topk_kernel<4>, grid, dim3(kBlock), 0, stream, k);
