@@ -7,15 +7,17 @@
 // return_schedule=True) returns row_ptr, q_indices and a schedule).
 //
 // Deterministic without sorting: every row owns a bitmap over its request's
-// query slots.  Marks are atomic ORs; the bitmap is walked in order, so each row
-// comes out ascending.  A row's bitmap is cut into units of 64 words (2048
-// query slots); units are the grain of the count, scan and fill passes, so long
-// rows (a page chosen by thousands of queries) are spread over many waves.
+// query slots, walked in order, so each row comes out ascending.  A row's bitmap
+// is cut into units of 64 words (2048 query slots); units are the grain of the
+// count, scan and fill passes, so long rows (a page chosen by thousands of
+// queries) are spread over many waves.
 //
-// Four launches on the caller's stream, no host sync:
-//   clear  -- zero the bitmap, set the position table to -1; block 0 also
-//             computes row_base[b] (page rows of earlier requests)
-//   mark   -- one thread per (query, selection head, slot)
+// Three launches on the caller's stream, no host sync:
+//   words  -- one block per (request, 32 query slots): sets the bits of those
+//             slots for every row of the request in LDS and writes the word
+//             column out (so the bitmap needs no clearing and no global
+//             atomics); also row_base[b] (page rows of earlier requests) and
+//             the (query, slot) -> position table reset to -1
 //   count  -- one wave per unit: entries and attention items of the unit, and
 //             per-block totals
 //   fill   -- per block: base offsets from the totals of earlier blocks, scan of
@@ -43,78 +45,89 @@ struct Hdr {
   int32_t pad[62];
 };
 
-struct ClearK {
-  const int32_t* cu_k;
-  int32_t batch;
-  int32_t* row_base;
-  Hdr* hdr;
-  uint32_t* bitmap;
-  int64_t n_words;
-  int32_t* inv;
-  int64_t inv_len;
-};
+constexpr int kWordRows = 1024;               // rows per words-kernel block
 
-__global__ __launch_bounds__(kThreads) void csr_clear_kernel(ClearK a) {
-  const int tid = threadIdx.x;
-  if (blockIdx.x == 0) {
-    // exclusive scan of ceil(seqlen_k / 128) over requests
-    __shared__ int wave_tot[kThreads / 64];
-    __shared__ int running;
-    const int lane = tid & 63, wave = tid >> 6;
-    if (tid == 0) { running = 0; a.hdr->n_items = 0; a.hdr->nnz = 0; }
-    __syncthreads();
-    for (int base = 0; base <= a.batch; base += kThreads) {
-      const int b = base + tid;
-      int pages = 0;
-      if (b < a.batch) pages = (a.cu_k[b + 1] - a.cu_k[b] + kPage - 1) / kPage;
-      const int incl = wave_inclusive_scan(pages);
-      if (lane == 63) wave_tot[wave] = incl;
-      __syncthreads();
-      int off = running;
-      for (int w = 0; w < wave; ++w) off += wave_tot[w];
-      if (b <= a.batch) a.row_base[b] = off + incl - pages;
-      __syncthreads();
-      if (tid == kThreads - 1) running = off + incl;
-      __syncthreads();
-    }
-  }
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t k = (int64_t)blockIdx.x * kThreads + tid; k < a.n_words; k += stride) a.bitmap[k] = 0u;
-  for (int64_t k = (int64_t)blockIdx.x * kThreads + tid; k < a.inv_len; k += stride) a.inv[k] = -1;
-}
-
-struct MarkK {
+struct WordsK {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int32_t batch;
-  int64_t total_q;
   const int32_t* topk;
   int64_t tq, th;
   int32_t n_sel;
   int32_t total_rows;
-  const int32_t* row_base;
+  int32_t* row_base;
   uint32_t* bitmap;
-  int64_t words;
+  int64_t words;          // per row
+  int32_t* inv;           // [total_q, n_sel, 16]
+  int32_t n_chunks;       // blocks per (request, word): ceil(n_sel * max_pages / kWordRows)
 };
 
-__global__ __launch_bounds__(kThreads) void csr_mark_kernel(MarkK a) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (query, head, slot)
-  const int64_t per_q = (int64_t)a.n_sel * kTopK;
-  if (e >= a.total_q * per_q) return;
-  const int64_t i = e / per_q;
-  const int g = (int)((e % per_q) / kTopK);
-  const int s = (int)(e % kTopK);
-  const int j = a.topk[i * a.tq + g * a.th + s];
-  if (j < 0) return;
-  const int b = find_request(a.cu_q, a.batch, i);
-  const int pages = (a.cu_k[b + 1] - a.cu_k[b] + kPage - 1) / kPage;
-  if (j >= pages) return;
-  const int64_t rr = a.row_base[b] + j;
-  if (rr >= a.total_rows) return;
-  const int64_t row = (int64_t)g * a.total_rows + rr;
-  const int64_t local = i - a.cu_q[b];
-  if (local >= a.words * 32) return;
-  atomicOr(&a.bitmap[row * a.words + (local >> 5)], 1u << (local & 31));
+__device__ __forceinline__ int request_pages(const int32_t* cu_k, int b) {
+  return (cu_k[b + 1] - cu_k[b] + kPage - 1) / kPage;
+}
+
+// Block ((b * words) + w) * n_chunks + c: query slots 32w .. 32w+31 of request b,
+// rows c * kWordRows .. of the request (g-major: r = g * pages + j).
+__global__ __launch_bounds__(kThreads) void csr_words_kernel(WordsK a) {
+  __shared__ uint32_t s_bits[kWordRows];
+  __shared__ int s_red[kThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t bw = blockIdx.x / a.n_chunks;
+  const int c = (int)(blockIdx.x % a.n_chunks);
+  const int b = (int)(bw / a.words), w = (int)(bw % a.words);
+  const int pages = request_pages(a.cu_k, b);
+  const int rows = a.n_sel * pages;
+  const int r0 = c * kWordRows;
+  if (r0 >= rows && c > 0) return;
+
+  // rows of earlier requests
+  int part = 0;
+  for (int k = tid; k < b; k += kThreads) part += request_pages(a.cu_k, k);
+  part = wave_sum(part);
+  if (lane == 0) s_red[wave] = part;
+  __syncthreads();
+  int base = 0;
+  for (int k = 0; k < kThreads / 64; ++k) base += s_red[k];
+
+  const int q0 = a.cu_q[b], sq = a.cu_q[b + 1] - q0;
+  const int per_q = a.n_sel * kTopK;
+  const int n_e = 32 * per_q;                       // (query, selection head, slot) entries
+  if (c == 0) {
+    if (w == 0 && tid == 0) {
+      a.row_base[b] = base;
+      if (b == a.batch - 1) a.row_base[a.batch] = base + pages;
+    }
+    // reset the position table of this block's queries
+    for (int e = tid; e < n_e; e += kThreads) {
+      const int local = 32 * w + e / per_q;
+      if (local < sq) a.inv[(int64_t)(q0 + local) * per_q + e % per_q] = -1;
+    }
+    // the last request's blocks also clear any rows past the requests' pages
+    if (b == a.batch - 1) {
+      const int end = base + pages;
+      for (int g = 0; g < a.n_sel; ++g)
+        for (int rr = end + tid; rr < a.total_rows; rr += kThreads)
+          a.bitmap[((int64_t)g * a.total_rows + rr) * a.words + w] = 0u;
+    }
+  }
+  const int n_r = min(kWordRows, rows - r0);
+  if (n_r <= 0) return;
+  for (int k = tid; k < n_r; k += kThreads) s_bits[k] = 0u;
+  __syncthreads();
+  for (int e = tid; e < n_e; e += kThreads) {
+    const int ql = e / per_q, g = (e % per_q) / kTopK, sl = e % kTopK;
+    const int local = 32 * w + ql;
+    if (local >= sq) continue;
+    const int j = a.topk[(int64_t)(q0 + local) * a.tq + (int64_t)g * a.th + sl];
+    if (j < 0 || j >= pages) continue;
+    const int r = g * pages + j - r0;
+    if (r >= 0 && r < n_r) atomicOr(&s_bits[r], 1u << ql);
+  }
+  __syncthreads();
+  for (int k = tid; k < n_r; k += kThreads) {
+    const int r = r0 + k, g = r / pages, j = r - g * pages;
+    a.bitmap[((int64_t)g * a.total_rows + base + j) * a.words + w] = s_bits[k];
+  }
 }
 
 struct CountK {
@@ -317,6 +330,8 @@ SchedLayout sched_layout(const msa_varlen_t* vl, int n_sel, int topk) {
   L.n_units = L.n_rows * L.units_per_row;
   L.n_blocks = std::max<int64_t>(1, ceil_div(L.n_units, kUnitsPerBlock));
   L.inv_len = (int64_t)vl->total_q * n_sel * topk;
+  L.word_chunks = std::max<int64_t>(1, ceil_div((int64_t)n_sel * std::max(vl->max_pages, 1), kWordRows));
+  L.word_blocks = L.words_per_row * std::max(vl->batch, 0) * L.word_chunks;
   // every unit holding c entries yields ceil(c / kAttnQC) items
   L.max_items = ceil_div((int64_t)n_sel * vl->total_q * topk, kAttnQC) + L.n_units;
   size_t off = 0;
@@ -341,19 +356,14 @@ hipError_t launch_k2q_csr(const CsrArgs& a, hipStream_t stream) {
   int4* items = reinterpret_cast<int4*>(a.sched + L.items);
   int32_t* inv = reinterpret_cast<int32_t*>(a.sched + L.inv);
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(a.sched + L.bitmap);
-  const int64_t n_words = L.n_rows * L.words_per_row;
 
-  ClearK ck{a.vl.cu_seqlens_k, a.vl.batch, row_base, hdr, bitmap, n_words, inv, L.inv_len};
-  const int64_t clear_blocks =
-      std::min<int64_t>(2048, std::max<int64_t>(1, ceil_div(std::max(n_words, L.inv_len), kThreads)));
-  hipLaunchKernelGGL(csr_clear_kernel, dim3((unsigned)clear_blocks), dim3(kThreads), 0, stream, ck);
-
-  MarkK mk{a.vl.cu_seqlens_q, a.vl.cu_seqlens_k, a.vl.batch, a.vl.total_q, a.topk, a.tq_stride,
-           a.th_stride, a.n_sel, a.vl.total_rows, row_base, bitmap, L.words_per_row};
-  const int64_t n_mark = (int64_t)a.vl.total_q * a.n_sel * kTopK;
-  if (n_mark > 0)
-    hipLaunchKernelGGL(csr_mark_kernel, dim3((unsigned)ceil_div(n_mark, kThreads)), dim3(kThreads),
-                       0, stream, mk);
+  if (a.vl.batch > 0 && L.words_per_row > 0) {
+    WordsK wk{a.vl.cu_seqlens_q, a.vl.cu_seqlens_k, a.vl.batch, a.topk, a.tq_stride, a.th_stride,
+              a.n_sel, a.vl.total_rows, row_base, bitmap, L.words_per_row, inv,
+              (int32_t)L.word_chunks};
+    hipLaunchKernelGGL(csr_words_kernel, dim3((unsigned)L.word_blocks), dim3(kThreads), 0, stream,
+                       wk);
+  }
 
   CountK cnt{bitmap, L.words_per_row, (int32_t)L.units_per_row, L.n_units, unit_cnt, blk_tot,
              blk_items};

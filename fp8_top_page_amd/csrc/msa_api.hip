@@ -183,7 +183,8 @@ msa_status_t msa_build_k2q_csr(const msa_varlen_t* vl, const int32_t* topk_idx,
   const SchedLayout L = sched_layout(vl, n_sel_heads, topk);
   MSA_CHECK(schedule_bytes >= L.total, MSA_ERR_WORKSPACE_TOO_SMALL,
             "schedule has %zu bytes, needs %zu", schedule_bytes, L.total);
-  MSA_CHECK(L.max_items < (int64_t)INT32_MAX && L.n_rows < (int64_t)INT32_MAX / 4,
+  MSA_CHECK(L.max_items < (int64_t)INT32_MAX && L.n_rows < (int64_t)INT32_MAX / 4 &&
+                L.word_blocks < (int64_t)INT32_MAX,
             MSA_ERR_UNSUPPORTED, "batch too large");
   st = check_device();
   if (st != MSA_OK) return st;

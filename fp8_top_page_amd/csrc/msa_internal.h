@@ -76,6 +76,8 @@ struct SchedLayout {
   int64_t n_blocks;       // count/fill blocks
   int64_t max_items;
   int64_t inv_len;        // total_q * n_sel * topk
+  int64_t word_chunks;    // row chunks per (request, bitmap word) in the words pass
+  int64_t word_blocks;    // blocks of the words pass
 };
 SchedLayout sched_layout(const msa_varlen_t* vl, int n_sel, int topk);
 
