@@ -173,6 +173,122 @@ __global__ __launch_bounds__(256) void score_plan_kernel(const int32_t* __restri
   }
 }
 
+// Same plan for batches of at most kPlanMaxB requests and kPlanMaxG q-blocks,
+// with the request table and the q-block offsets in LDS: every pass is spread
+// over all q-blocks (or all items) instead of walking the requests in turn.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanMaxB = 1024;
+constexpr int kPlanMaxG = 4096;
+
+__global__ __launch_bounds__(kPlanThreads) void score_plan_table_kernel(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int B, int qblock,
+    int64_t max_items, ItemHdr* __restrict__ hdr, int4* __restrict__ items) {
+  constexpr int kW = kPlanThreads / 64;
+  __shared__ int s_q0[kPlanMaxB], s_sq[kPlanMaxB], s_ctx[kPlanMaxB], s_qbase[kPlanMaxB + 1];
+  __shared__ int s_first[kPlanMaxG + 1];
+  __shared__ int s_cnt[kW];
+  __shared__ int64_t s_w[kW];
+  __shared__ int s_lo[kW], s_hi[kW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  auto block_scan = [&](int x, int* total) {   // exclusive; adds the block total to *total
+    const int incl = wave_inclusive_scan(x);
+    if (lane == 63) s_cnt[wave] = incl;
+    __syncthreads();
+    int off = 0, tot = 0;
+    for (int k = 0; k < kW; ++k) {
+      if (k < wave) off += s_cnt[k];
+      tot += s_cnt[k];
+    }
+    __syncthreads();
+    *total += tot;
+    return off + incl - x;
+  };
+  auto last_le = [&](const int* arr, int n, int key) {   // last index i < n with arr[i] <= key
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (arr[mid] <= key) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+
+  // pass 0: request table, q-blocks per request and their offsets
+  int nqb = 0;
+  if (tid < B) {
+    const int q0 = cu_q[tid], sq = cu_q[tid + 1] - q0;
+    s_q0[tid] = q0;
+    s_sq[tid] = sq;
+    s_ctx[tid] = (cu_k[tid + 1] - cu_k[tid]) - sq;
+    nqb = (sq + qblock - 1) / qblock;
+  }
+  int G = 0;
+  const int qoff = block_scan(nqb, &G);
+  if (tid < B) s_qbase[tid] = qoff;
+  __syncthreads();
+  G = min(G, kPlanMaxG);
+  auto visible = [&](int g, int* b_out, int* qf_out, int* qn_out) {
+    const int b = last_le(s_qbase, B, g);
+    const int qf = (g - s_qbase[b]) * qblock;
+    *b_out = b;
+    *qf_out = qf;
+    *qn_out = min(s_sq[b] - qf, qblock);
+    return (s_ctx[b] + qf + *qn_out - 1) / kPage + 1;
+  };
+
+  // pass 1: total and spread of v over all q-blocks -> pages per item
+  int64_t w = 0;
+  int vmin = INT32_MAX, vmax = 0;
+  for (int g = tid; g < G; g += kPlanThreads) {
+    int b, qf, qn;
+    const int v = visible(g, &b, &qf, &qn);
+    w += v;
+    vmin = min(vmin, v);
+    vmax = max(vmax, v);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    w += __shfl_xor(w, o);
+    vmin = min(vmin, __shfl_xor(vmin, o));
+    vmax = max(vmax, __shfl_xor(vmax, o));
+  }
+  if (lane == 0) { s_w[wave] = w; s_lo[wave] = vmin; s_hi[wave] = vmax; }
+  __syncthreads();
+  int64_t tw = 0;
+  int lo = INT32_MAX, hi = 0;
+  for (int k = 0; k < kW; ++k) { tw += s_w[k]; lo = min(lo, s_lo[k]); hi = max(hi, s_hi[k]); }
+  const int64_t target = (hi - lo) * 8 <= hi ? kItemsUniform : kItemsRagged;
+  int64_t pc64 = (tw + target - 1) / target;
+  pc64 = (pc64 + 3) / 4 * 4;
+  const int pc = (int)min<int64_t>(kMaxItemPages, max<int64_t>(kMinItemPages, pc64));
+
+  // pass 2: page chunks per q-block, offsets
+  int n_items = 0;
+  for (int base = 0; base < G; base += kPlanThreads) {
+    const int g = base + tid;
+    int c = 0;
+    if (g < G) {
+      int b, qf, qn;
+      c = (visible(g, &b, &qf, &qn) + pc - 1) / pc;
+    }
+    const int first = n_items + block_scan(c, &n_items);
+    if (g < G) s_first[g] = first;
+  }
+  __syncthreads();
+
+  // emit: item k belongs to the last q-block whose first item is <= k
+  const int64_t n_out = min<int64_t>(n_items, max_items);
+  for (int k = tid; k < n_out; k += kPlanThreads) {
+    const int g = last_le(s_first, G, k);
+    int b, qf, qn;
+    visible(g, &b, &qf, &qn);
+    items[k] = make_int4(b, s_q0[b] + qf, qn, (k - s_first[g]) * pc);
+  }
+  if (tid == 0) {
+    hdr->n_items = (int32_t)n_out;
+    hdr->pages_per_item = pc;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Scorer.
 // ---------------------------------------------------------------------------
@@ -434,9 +550,16 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
   if (a.vl.total_q == 0) return hipSuccess;
   ItemHdr* hdr = reinterpret_cast<ItemHdr*>(a.workspace);
   int4* items = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(a.workspace) + sizeof(ItemHdr));
-  hipLaunchKernelGGL(score_plan_kernel, dim3(1), dim3(256), 0, stream, a.vl.cu_seqlens_q,
-                     a.vl.cu_seqlens_k, a.vl.batch, score_qblock(a.H), a.plan.max_items, hdr,
-                     items);
+  const int qb = score_qblock(a.H);
+  // one request: the 256-thread kernel has less to set up; batches: the table kernel
+  if (a.vl.batch > 1 && a.vl.batch <= kPlanMaxB &&
+      ceil_div(a.vl.total_q, qb) + a.vl.batch <= kPlanMaxG)
+    hipLaunchKernelGGL(score_plan_table_kernel, dim3(1), dim3(kPlanThreads), 0, stream,
+                       a.vl.cu_seqlens_q, a.vl.cu_seqlens_k, a.vl.batch, qb, a.plan.max_items, hdr,
+                       items);
+  else
+    hipLaunchKernelGGL(score_plan_kernel, dim3(1), dim3(256), 0, stream, a.vl.cu_seqlens_q,
+                       a.vl.cu_seqlens_k, a.vl.batch, qb, a.plan.max_items, hdr, items);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   ScoreK k;
