@@ -17,17 +17,20 @@
 //             slots for every row of the request in LDS and writes the word
 //             column out (so the bitmap needs no clearing and no global
 //             atomics); also row_base[b] (page rows of earlier requests) and
-//             the (query, slot) -> position table reset to -1
+//             the (query, slot) -> CSR row table (-1 for empty slots)
 //   count  -- one wave per unit: entries and attention items of the unit, and
 //             per-block totals
 //   fill   -- per block: base offsets from the totals of earlier blocks, scan of
-//             its units, then one wave per unit writes q_indices (ascending),
-//             the (query, slot) -> position table, row_ptr and the work items
-//             of at most kAttnQC entries each:
+//             its units, then one wave per unit (one lane per bitmap word)
+//             writes q_indices (ascending), each word's first CSR position,
+//             row_ptr and the work items of at most kAttnQC entries each:
 //               {first entry, count, physical page, selection head}
 //               {context - cu_seqlens_q[b] - 128 j, valid tokens of the page, row, request}
 //             (a query i of the item sees the page's tokens up to i + the first
 //             value; the physical page comes from the block table)
+// The CSR position of (query i, slot s) is then the first position of i's word
+// in its row plus the set bits below i in that word; the attention's combine
+// computes it from the row table, the word positions and the bitmap.
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -58,7 +61,7 @@ struct WordsK {
   int32_t* row_base;
   uint32_t* bitmap;
   int64_t words;          // per row
-  int32_t* inv;           // [total_q, n_sel, 16]
+  int32_t* rowsel;        // [total_q, n_sel, 16]: CSR row of each selected page, or -1
   int32_t n_chunks;       // blocks per (request, word): ceil(n_sel * max_pages / kWordRows)
 };
 
@@ -97,10 +100,14 @@ __global__ __launch_bounds__(kThreads) void csr_words_kernel(WordsK a) {
       a.row_base[b] = base;
       if (b == a.batch - 1) a.row_base[a.batch] = base + pages;
     }
-    // reset the position table of this block's queries
+    // the CSR row of every selection slot of this block's queries
     for (int e = tid; e < n_e; e += kThreads) {
       const int local = 32 * w + e / per_q;
-      if (local < sq) a.inv[(int64_t)(q0 + local) * per_q + e % per_q] = -1;
+      if (local >= sq) continue;
+      const int g = (e % per_q) / kTopK, sl = e % kTopK;
+      const int j = a.topk[(int64_t)(q0 + local) * a.tq + (int64_t)g * a.th + sl];
+      a.rowsel[(int64_t)(q0 + local) * per_q + e % per_q] =
+          (j < 0 || j >= pages) ? -1 : g * a.total_rows + base + j;
     }
     // the last request's blocks also clear any rows past the requests' pages
     if (b == a.batch - 1) {
@@ -201,7 +208,7 @@ struct FillK {
   const int32_t* blk_items;
   int32_t* row_ptr;
   int32_t* q_indices;
-  int32_t* inv;        // [total_q, n_sel, 16]
+  int32_t* wbase;      // [n_rows, words]: CSR position of each word's first entry
   int4* items;
   int64_t max_items;
   Hdr* hdr;
@@ -211,8 +218,6 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
   __shared__ int s_red[2][kThreads / 64];
   __shared__ int s_pos[kUnitsPerBlock];     // first CSR position of each unit
   __shared__ int s_item[kUnitsPerBlock];    // first item index of each unit
-  __shared__ uint32_t s_words[kThreads / 64][64];
-  __shared__ int s_excl[kThreads / 64][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int blk = blockIdx.x;
   const int64_t u0 = (int64_t)blk * kUnitsPerBlock;
@@ -273,40 +278,24 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
     const int64_t q_base = a.cu_q[b] + (u % a.units_per_row) * (kUnitWords * 32);
     const int sk = a.cu_k[b + 1] - a.cu_k[b];
     const int ctx = sk - (a.cu_q[b + 1] - a.cu_q[b]);
-    // The unit's words and their exclusive bit counts go to the wave's LDS
-    // slice; then entry e of the unit (e = round * 64 + lane) is located by a
-    // binary search over the counts, so every lane handles one entry per round
-    // even when a few words hold all the bits.
+    // One lane per bitmap word: the word's first CSR position is the unit's
+    // plus the bits of earlier words; the lane then writes the word's entries
+    // in bit order (a wave-uniform loop as long as any lane has bits left).
     const uint32_t bits = ubits[k];
     const int c = __popc(bits);
     const int incl = wave_inclusive_scan(c);
-    s_words[wave][lane] = bits;
-    s_excl[wave][lane] = incl - c;
     const int n = __shfl(incl, 63);
-    __builtin_amdgcn_wave_barrier();
-    for (int e = lane; e < n; e += 64) {
-      int lo = 0, hi = 63;              // last word with excl <= e
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_excl[wave][mid] <= e) lo = mid; else hi = mid - 1;
+    int pos = s_pos[ku] + incl - c;
+    const int64_t wi = row * a.words + (u % a.units_per_row) * kUnitWords + lane;
+    if ((u % a.units_per_row) * kUnitWords + lane < a.words) a.wbase[wi] = pos;
+    uint32_t x = bits;
+    const int64_t q_word = q_base + lane * 32;
+    while (__builtin_amdgcn_ballot_w64(x != 0u) != 0) {
+      if (x != 0u) {
+        a.q_indices[pos++] = (int32_t)(q_word + __builtin_ctz(x));
+        x &= x - 1u;
       }
-      uint32_t x = s_words[wave][lo];
-      for (int r = e - s_excl[wave][lo]; r > 0; --r) x &= x - 1;
-      const int bit = __builtin_ctz(x);
-      const int64_t qi = q_base + lo * 32 + bit;
-      const int p = s_pos[ku] + e;
-      a.q_indices[p] = (int32_t)qi;
-      // slot of page j in the query's selection: read all 16 slots at once
-      const int32_t* sel = a.topk + qi * a.tq + (int64_t)g * a.th;
-      int sv[kTopK];
-#pragma unroll
-      for (int t = 0; t < kTopK; ++t) sv[t] = sel[t];
-      int slot = -1;
-#pragma unroll
-      for (int t = kTopK - 1; t >= 0; --t) slot = (sv[t] == j) ? t : slot;
-      if (slot >= 0) a.inv[(qi * a.n_sel + g) * kTopK + slot] = p;
     }
-    __builtin_amdgcn_wave_barrier();
     // work items of the unit: (row, first entry, count)
     const int n_it = (n + kAttnQC - 1) / kAttnQC;
     const int phys = n_it > 0 ? a.block_table[(int64_t)b * a.bt_stride + j] : 0;
@@ -340,7 +329,8 @@ SchedLayout sched_layout(const msa_varlen_t* vl, int n_sel, int topk) {
   L.unit_cnt = off;   off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.n_units), 256);
   L.blk_tot = off;    off += align_up(sizeof(int32_t) * 2 * L.n_blocks, 256);
   L.items = off;      off += align_up(2 * sizeof(int4) * std::max<int64_t>(1, L.max_items), 256);
-  L.inv = off;        off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.inv_len), 256);
+  L.rowsel = off;     off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.inv_len), 256);
+  L.wbase = off;      off += align_up(sizeof(int32_t) * L.n_rows * L.words_per_row, 256);
   L.bitmap = off;     off += align_up(sizeof(uint32_t) * L.n_rows * L.words_per_row, 256);
   L.total = off;
   return L;
@@ -354,12 +344,13 @@ hipError_t launch_k2q_csr(const CsrArgs& a, hipStream_t stream) {
   int32_t* blk_tot = reinterpret_cast<int32_t*>(a.sched + L.blk_tot);
   int32_t* blk_items = blk_tot + L.n_blocks;
   int4* items = reinterpret_cast<int4*>(a.sched + L.items);
-  int32_t* inv = reinterpret_cast<int32_t*>(a.sched + L.inv);
+  int32_t* rowsel = reinterpret_cast<int32_t*>(a.sched + L.rowsel);
+  int32_t* wbase = reinterpret_cast<int32_t*>(a.sched + L.wbase);
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(a.sched + L.bitmap);
 
   if (a.vl.batch > 0 && L.words_per_row > 0) {
     WordsK wk{a.vl.cu_seqlens_q, a.vl.cu_seqlens_k, a.vl.batch, a.topk, a.tq_stride, a.th_stride,
-              a.n_sel, a.vl.total_rows, row_base, bitmap, L.words_per_row, inv,
+              a.n_sel, a.vl.total_rows, row_base, bitmap, L.words_per_row, rowsel,
               (int32_t)L.word_chunks};
     hipLaunchKernelGGL(csr_words_kernel, dim3((unsigned)L.word_blocks), dim3(kThreads), 0, stream,
                        wk);
@@ -373,7 +364,7 @@ hipError_t launch_k2q_csr(const CsrArgs& a, hipStream_t stream) {
            a.vl.block_table_stride, a.topk, a.tq_stride, a.th_stride, a.n_sel,
            a.vl.total_rows, row_base, bitmap, L.words_per_row, (int32_t)L.units_per_row,
            L.n_units, L.n_rows, (int32_t)L.n_blocks, unit_cnt, blk_tot, blk_items, a.row_ptr,
-           a.q_indices, inv, items, L.max_items, hdr};
+           a.q_indices, wbase, items, L.max_items, hdr};
   hipLaunchKernelGGL(csr_fill_kernel, dim3((unsigned)L.n_blocks), dim3(kThreads), 0, stream, fk);
   return hipGetLastError();
 }

@@ -43,6 +43,7 @@ constexpr int kBlocksWide = 2;
 constexpr int kBlocksNarrow = 3;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kOnesE4M3 = 0x38383838;   // four E4M3 1.0 codes
+constexpr int kMaxKvHeads = 64;         // selection heads per query, at most (Hq <= 64)
 
 struct AttnK {
   const uint8_t* q;
@@ -383,7 +384,12 @@ __global__ __launch_bounds__(kThreads, kWide ? kBlocksWide : kBlocksNarrow) void
 struct CombineK {
   int64_t total_q;
   int32_t Hq, G, n_sel, HP;
-  const int32_t* inv;             // [total_q, n_sel, 16] CSR position or -1
+  const int32_t* cu_q;
+  int32_t batch;
+  const int32_t* rowsel;          // [total_q, n_sel, 16] CSR row of each selected page, or -1
+  const int32_t* wbase;           // [rows, words] CSR position of each bitmap word's first entry
+  const uint32_t* bitmap;         // [rows, words] the rows' query-slot bitmaps
+  int64_t words;
   const uint16_t* part_o;
   const float2* part_ml;
   const float* v_scale;
@@ -396,15 +402,29 @@ struct CombineK {
 // are contiguous), which hold d = 32 (c % 4) + 4 (c / 4) + {0..3} and those + 16
 // for c = t % 16.
 __global__ __launch_bounds__(1024) void attn_combine_kernel(CombineK a) {
+  __shared__ int32_t s_pos[kMaxKvHeads * kTopK];
   const int64_t i = blockIdx.x;
   const int t = threadIdx.x;
   const int hq = t >> 4, c = t & 15;
   const int sel = a.n_sel == 1 ? 0 : hq / a.G;
   const int hp = a.n_sel == 1 ? hq : hq % a.G;
-  const int32_t* pos = a.inv + (i * a.n_sel + sel) * kTopK;
+  // CSR position of each (selection head, slot): the first position of the
+  // query's bitmap word in the row plus the row's set bits below the query
+  if (t < a.n_sel * kTopK) {
+    const int b = find_request(a.cu_q, a.batch, i);
+    const int local = (int)(i - a.cu_q[b]);
+    const int r = a.rowsel[i * a.n_sel * kTopK + t];
+    int p = -1;
+    if (r >= 0) {
+      const int64_t wi = (int64_t)r * a.words + (local >> 5);
+      p = a.wbase[wi] + __popc(a.bitmap[wi] & ((1u << (local & 31)) - 1u));
+    }
+    s_pos[t] = p;
+  }
+  __syncthreads();
   int32_t pi[kTopK];
 #pragma unroll
-  for (int s = 0; s < kTopK; ++s) pi[s] = pos[s];
+  for (int s = 0; s < kTopK; ++s) pi[s] = s_pos[sel * kTopK + s];
   // all split rows are loaded together (a missing split reads row 0 with weight 0)
   float2 ml[kTopK];
   uint4 v[kTopK];
@@ -512,7 +532,12 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   c.G = a.Hq / a.Hkv;
   c.n_sel = a.n_sel;
   c.HP = HP;
-  c.inv = reinterpret_cast<const int32_t*>(a.sched + L.inv);
+  c.cu_q = a.vl.cu_seqlens_q;
+  c.batch = a.vl.batch;
+  c.rowsel = reinterpret_cast<const int32_t*>(a.sched + L.rowsel);
+  c.wbase = reinterpret_cast<const int32_t*>(a.sched + L.wbase);
+  c.bitmap = reinterpret_cast<const uint32_t*>(a.sched + L.bitmap);
+  c.words = L.words_per_row;
   c.part_o = k.part_o;
   c.part_ml = k.part_ml;
   c.v_scale = a.v_scale;
