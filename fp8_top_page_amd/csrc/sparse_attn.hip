@@ -71,6 +71,42 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
+// Compact partials ("f12"): a float rounded to fp16 (round to nearest even), then
+// to 12 bits by rounding off the 4 low mantissa bits (nearest, ties to even):
+// sign, 5 exponent and 6 mantissa bits, relative error <= 2^-7.  Unnormalised
+// split outputs stay below 128 * 448 = 57344, inside fp16's range.  Eight
+// values pack into three dwords.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2_f12(float a, float b) {   // two 12-bit fields, one per half
+  uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+  h += 0x00070007u + ((h >> 4) & 0x00010001u);   // finite halves: no carry between them
+  return (h >> 4) & 0x0FFF0FFFu;
+}
+__device__ __forceinline__ uint3 pack8_f12(float v0, float v1, float v2, float v3, float v4,
+                                           float v5, float v6, float v7) {
+  const uint32_t h0 = pack2_f12(v0, v1), h1 = pack2_f12(v2, v3);
+  const uint32_t h2 = pack2_f12(v4, v5), h3 = pack2_f12(v6, v7);
+  const uint32_t p0 = (h0 & 0xFFFu) | ((h0 >> 16) << 12);   // 24 bits each
+  const uint32_t p1 = (h1 & 0xFFFu) | ((h1 >> 16) << 12);
+  const uint32_t p2 = (h2 & 0xFFFu) | ((h2 >> 16) << 12);
+  const uint32_t p3 = (h3 & 0xFFFu) | ((h3 >> 16) << 12);
+  return make_uint3(p0 | (p1 << 24), (p1 >> 8) | (p2 << 16), (p2 >> 16) | (p3 << 8));
+}
+__device__ __forceinline__ float f12_to_f32(uint32_t x) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(x << 4));
+}
+__device__ __forceinline__ void unpack8_f12(uint3 w, float (&v)[8]) {
+  const uint32_t p0 = w.x & 0xFFFFFFu;
+  const uint32_t p1 = (w.x >> 24) | ((w.y & 0xFFFFu) << 8);
+  const uint32_t p2 = (w.y >> 16) | ((w.z & 0xFFu) << 16);
+  const uint32_t p3 = w.z >> 8;
+  v[0] = f12_to_f32(p0 & 0xFFFu); v[1] = f12_to_f32(p0 >> 12);
+  v[2] = f12_to_f32(p1 & 0xFFFu); v[3] = f12_to_f32(p1 >> 12);
+  v[4] = f12_to_f32(p2 & 0xFFFu); v[5] = f12_to_f32(p2 >> 12);
+  v[6] = f12_to_f32(p3 & 0xFFFu); v[7] = f12_to_f32(p3 >> 12);
+}
+constexpr int kRowBytesF12 = kDim * 3 / 2;   // 192 bytes per partial row
+
 // One work item as the kernel uses it (wave-uniform values).
 struct Work {
   int start, count, g, lim_base, n_valid;
@@ -181,7 +217,7 @@ __device__ __forceinline__ RowSet<NT> load_rows(const AttnK& a, const Work& w, i
 }
 
 // S^T, softmax and O^T of one row set, written to its partial rows.
-template <int NT>
+template <int NT, bool F12>
 __device__ __forceinline__ void compute_set(const AttnK& a, const RowSet<NT>& r,
                                             const uint8_t* k_lds, const uint8_t* vt_lds,
                                             float zscale, int lane) {
@@ -261,11 +297,21 @@ __device__ __forceinline__ void compute_set(const AttnK& a, const RowSet<NT>& r,
     }
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-      uint4* dst = reinterpret_cast<uint4*>(a.part_o + r.pidx[u] * kDim + grp * 32 + half * 16);
-      dst[0] = make_uint4(pack2_bf16(o[u][0][0], o[u][0][1]), pack2_bf16(o[u][0][2], o[u][0][3]),
-                          pack2_bf16(o[u][1][0], o[u][1][1]), pack2_bf16(o[u][1][2], o[u][1][3]));
-      dst[1] = make_uint4(pack2_bf16(o[u][2][0], o[u][2][1]), pack2_bf16(o[u][2][2], o[u][2][3]),
-                          pack2_bf16(o[u][3][0], o[u][3][1]), pack2_bf16(o[u][3][2], o[u][3][3]));
+      if constexpr (F12) {
+        // same value order; 12 bytes per 8 values
+        uint3* dst = reinterpret_cast<uint3*>(reinterpret_cast<uint8_t*>(a.part_o) +
+                                              r.pidx[u] * kRowBytesF12 + grp * 48 + half * 24);
+        dst[0] = pack8_f12(o[u][0][0], o[u][0][1], o[u][0][2], o[u][0][3], o[u][1][0],
+                           o[u][1][1], o[u][1][2], o[u][1][3]);
+        dst[1] = pack8_f12(o[u][2][0], o[u][2][1], o[u][2][2], o[u][2][3], o[u][3][0],
+                           o[u][3][1], o[u][3][2], o[u][3][3]);
+      } else {
+        uint4* dst = reinterpret_cast<uint4*>(a.part_o + r.pidx[u] * kDim + grp * 32 + half * 16);
+        dst[0] = make_uint4(pack2_bf16(o[u][0][0], o[u][0][1]), pack2_bf16(o[u][0][2], o[u][0][3]),
+                            pack2_bf16(o[u][1][0], o[u][1][1]), pack2_bf16(o[u][1][2], o[u][1][3]));
+        dst[1] = make_uint4(pack2_bf16(o[u][2][0], o[u][2][1]), pack2_bf16(o[u][2][2], o[u][2][3]),
+                            pack2_bf16(o[u][3][0], o[u][3][1]), pack2_bf16(o[u][3][2], o[u][3][3]));
+      }
     }
   }
   // every lane of a row holds the same (m, l)
@@ -294,11 +340,11 @@ __device__ __forceinline__ void run_item(const AttnK& a, const Work& w, const ui
   __builtin_amdgcn_sched_barrier(0);
   for (;;) {
     if (t >= n_tiles) break;
-    compute_set<NT>(a, ra, k_lds, vt_lds, zscale, lane);
+    compute_set<NT, false>(a, ra, k_lds, vt_lds, zscale, lane);
     ra = load_rows<NT>(a, w, t + 2 * kStep, n_rows, s_qi, lane);
     t += kStep;
     if (t >= n_tiles) break;
-    compute_set<NT>(a, rb, k_lds, vt_lds, zscale, lane);
+    compute_set<NT, false>(a, rb, k_lds, vt_lds, zscale, lane);
     rb = load_rows<NT>(a, w, t + 2 * kStep, n_rows, s_qi, lane);
     t += kStep;
   }
@@ -319,7 +365,7 @@ __device__ __forceinline__ void run_item_narrow(const AttnK& a, const Work& w,
   prefetch();
   __builtin_amdgcn_sched_barrier(0);
   while (t < n_tiles) {
-    compute_set<1>(a, r, k_lds, vt_lds, zscale, lane);
+    compute_set<1, true>(a, r, k_lds, vt_lds, zscale, lane);
     t += kWaves;
     if (t >= n_tiles) break;
     r = load_rows<1>(a, w, t, n_rows, s_qi, lane);
@@ -401,6 +447,7 @@ struct CombineK {
 // bytes at 8 * (t % 16) of each split row (all heads of one (query, page) pair
 // are contiguous), which hold d = 32 (c % 4) + 4 (c / 4) + {0..3} and those + 16
 // for c = t % 16.
+template <bool F12>
 __global__ __launch_bounds__(1024) void attn_combine_kernel(CombineK a) {
   __shared__ int32_t s_pos[kMaxKvHeads * kTopK];
   const int64_t i = blockIdx.x;
@@ -432,7 +479,13 @@ __global__ __launch_bounds__(1024) void attn_combine_kernel(CombineK a) {
   for (int s = 0; s < kTopK; ++s) {
     const int64_t r = (int64_t)max(pi[s], 0) * a.HP + hp;
     ml[s] = a.part_ml[r];
-    v[s] = *reinterpret_cast<const uint4*>(a.part_o + r * kDim + 8 * c);
+    if constexpr (F12) {
+      const uint3 x = *reinterpret_cast<const uint3*>(reinterpret_cast<const uint8_t*>(a.part_o) +
+                                                      r * kRowBytesF12 + 12 * c);
+      v[s] = make_uint4(x.x, x.y, x.z, 0u);
+    } else {
+      v[s] = *reinterpret_cast<const uint4*>(a.part_o + r * kDim + 8 * c);
+    }
   }
   float M = -INFINITY;
 #pragma unroll
@@ -443,12 +496,19 @@ __global__ __launch_bounds__(1024) void attn_combine_kernel(CombineK a) {
 #pragma unroll
     for (int s = 0; s < kTopK; ++s) {
       const float wgt = pi[s] >= 0 ? __builtin_amdgcn_exp2f(ml[s].x - M) : 0.f;
-      const uint32_t wv[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
+      float x[8];
+      if constexpr (F12) {
+        unpack8_f12(make_uint3(v[s].x, v[s].y, v[s].z), x);
+      } else {
+        const uint32_t wv[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        o[2 * k] += wgt * bf16_to_f32((uint16_t)(wv[k] & 0xFFFFu));
-        o[2 * k + 1] += wgt * bf16_to_f32((uint16_t)(wv[k] >> 16));
+        for (int k = 0; k < 4; ++k) {
+          x[2 * k] = bf16_to_f32((uint16_t)(wv[k] & 0xFFFFu));
+          x[2 * k + 1] = bf16_to_f32((uint16_t)(wv[k] >> 16));
+        }
       }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] += wgt * x[k];
       L += wgt * ml[s].y;
     }
     const float f = L > 0.f ? (a.v_scale ? *a.v_scale : 1.f) / L : 0.f;
@@ -512,12 +572,14 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
                                         align_up((size_t)(rows * kDim * sizeof(uint16_t)), 256));
   k.trash = rows - 1;
   const int64_t max_work = L.max_items * k.GY;
+  bool f12 = false;   // the narrow kernel writes 12-bit partials
   if (max_work > 0) {
     // Rows per item from the host bound on entries per CSR row (total_q * topk
     // entries over total_rows rows, at most kAttnQC queries per item).
     const int64_t per_row = ceil_div((int64_t)a.vl.total_q * kTopK, std::max(a.vl.total_rows, 1));
     const bool wide = std::min<int64_t>(per_row, kAttnQC) * k.G >= 2 * kWaves * 16;
     const int per_cu = wide ? kBlocksWide : kBlocksNarrow;
+    f12 = !wide;
     const int64_t grid = std::min<int64_t>(max_work, (int64_t)device_cu_count() * per_cu);
     if (wide)
       hipLaunchKernelGGL(attn_partial_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, k);
@@ -543,8 +605,12 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   c.v_scale = a.v_scale;
   c.out = a.out;
   c.out_stride = a.out_stride;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)a.vl.total_q), dim3(a.Hq * 16), 0, stream,
-                     c);
+  if (f12)
+    hipLaunchKernelGGL(attn_combine_kernel<true>, dim3((unsigned)a.vl.total_q), dim3(a.Hq * 16), 0,
+                       stream, c);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<false>, dim3((unsigned)a.vl.total_q), dim3(a.Hq * 16), 0,
+                       stream, c);
   return hipGetLastError();
 }
 
