@@ -24,8 +24,8 @@
 // MFMAs.  Blocks are persistent: while one item is computed, the next item's
 // page and query list are already being fetched into registers.
 //
-// Each (query, q-head, page) split writes its unnormalised output row in bf16
-// (d permuted so that every lane stores 64 contiguous bytes) and the pair
+// Each (query, q-head, page) split writes its unnormalised output row as
+// 12-bit floats (d permuted so that every lane stores 48 contiguous bytes) and the pair
 // (running max m in the log2 domain, probability sum l); the combine merges a
 // query's (at most 16) splits in slot order.
 #include "msa_device.h"
@@ -57,7 +57,7 @@ struct AttnK {
   float logit_scale_log2;          // softmax_scale * log2(e)
   const float* q_scale;
   const float* k_scale;
-  uint16_t* part_o;                // [nnz, HP, 128] bf16, unnormalised, d permuted
+  uint8_t* part_o;                 // [nnz * HP + 1, 192 B]: 12-bit floats, unnormalised, d permuted
   float2* part_ml;                 // [nnz, HP] (max in log2 units, probability sum)
   int64_t trash;                   // partial row written by rows past an item's end
 };
@@ -105,7 +105,7 @@ __device__ __forceinline__ void unpack8_f12(uint3 w, float (&v)[8]) {
   v[4] = f12_to_f32(p2 & 0xFFFu); v[5] = f12_to_f32(p2 >> 12);
   v[6] = f12_to_f32(p3 & 0xFFFu); v[7] = f12_to_f32(p3 >> 12);
 }
-constexpr int kRowBytesF12 = kDim * 3 / 2;   // 192 bytes per partial row
+constexpr int kRowBytes = kDim * 3 / 2;   // 192 bytes per partial row
 
 // One work item as the kernel uses it (wave-uniform values).
 struct Work {
@@ -217,7 +217,7 @@ __device__ __forceinline__ RowSet<NT> load_rows(const AttnK& a, const Work& w, i
 }
 
 // S^T, softmax and O^T of one row set, written to its partial rows.
-template <int NT, bool F12>
+template <int NT>
 __device__ __forceinline__ void compute_set(const AttnK& a, const RowSet<NT>& r,
                                             const uint8_t* k_lds, const uint8_t* vt_lds,
                                             float zscale, int lane) {
@@ -297,21 +297,11 @@ __device__ __forceinline__ void compute_set(const AttnK& a, const RowSet<NT>& r,
     }
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-      if constexpr (F12) {
-        // same value order; 12 bytes per 8 values
-        uint3* dst = reinterpret_cast<uint3*>(reinterpret_cast<uint8_t*>(a.part_o) +
-                                              r.pidx[u] * kRowBytesF12 + grp * 48 + half * 24);
-        dst[0] = pack8_f12(o[u][0][0], o[u][0][1], o[u][0][2], o[u][0][3], o[u][1][0],
-                           o[u][1][1], o[u][1][2], o[u][1][3]);
-        dst[1] = pack8_f12(o[u][2][0], o[u][2][1], o[u][2][2], o[u][2][3], o[u][3][0],
-                           o[u][3][1], o[u][3][2], o[u][3][3]);
-      } else {
-        uint4* dst = reinterpret_cast<uint4*>(a.part_o + r.pidx[u] * kDim + grp * 32 + half * 16);
-        dst[0] = make_uint4(pack2_bf16(o[u][0][0], o[u][0][1]), pack2_bf16(o[u][0][2], o[u][0][3]),
-                            pack2_bf16(o[u][1][0], o[u][1][1]), pack2_bf16(o[u][1][2], o[u][1][3]));
-        dst[1] = make_uint4(pack2_bf16(o[u][2][0], o[u][2][1]), pack2_bf16(o[u][2][2], o[u][2][3]),
-                            pack2_bf16(o[u][3][0], o[u][3][1]), pack2_bf16(o[u][3][2], o[u][3][3]));
-      }
+      uint3* dst = reinterpret_cast<uint3*>(a.part_o + r.pidx[u] * kRowBytes + grp * 48 + half * 24);
+      dst[0] = pack8_f12(o[u][0][0], o[u][0][1], o[u][0][2], o[u][0][3], o[u][1][0], o[u][1][1],
+                         o[u][1][2], o[u][1][3]);
+      dst[1] = pack8_f12(o[u][2][0], o[u][2][1], o[u][2][2], o[u][2][3], o[u][3][0], o[u][3][1],
+                         o[u][3][2], o[u][3][3]);
     }
   }
   // every lane of a row holds the same (m, l)
@@ -340,11 +330,11 @@ __device__ __forceinline__ void run_item(const AttnK& a, const Work& w, const ui
   __builtin_amdgcn_sched_barrier(0);
   for (;;) {
     if (t >= n_tiles) break;
-    compute_set<NT, false>(a, ra, k_lds, vt_lds, zscale, lane);
+    compute_set<NT>(a, ra, k_lds, vt_lds, zscale, lane);
     ra = load_rows<NT>(a, w, t + 2 * kStep, n_rows, s_qi, lane);
     t += kStep;
     if (t >= n_tiles) break;
-    compute_set<NT, false>(a, rb, k_lds, vt_lds, zscale, lane);
+    compute_set<NT>(a, rb, k_lds, vt_lds, zscale, lane);
     rb = load_rows<NT>(a, w, t + 2 * kStep, n_rows, s_qi, lane);
     t += kStep;
   }
@@ -365,7 +355,7 @@ __device__ __forceinline__ void run_item_narrow(const AttnK& a, const Work& w,
   prefetch();
   __builtin_amdgcn_sched_barrier(0);
   while (t < n_tiles) {
-    compute_set<1, true>(a, r, k_lds, vt_lds, zscale, lane);
+    compute_set<1>(a, r, k_lds, vt_lds, zscale, lane);
     t += kWaves;
     if (t >= n_tiles) break;
     r = load_rows<1>(a, w, t, n_rows, s_qi, lane);
@@ -436,7 +426,7 @@ struct CombineK {
   const int32_t* wbase;           // [rows, words] CSR position of each bitmap word's first entry
   const uint32_t* bitmap;         // [rows, words] the rows' query-slot bitmaps
   int64_t words;
-  const uint16_t* part_o;
+  const uint8_t* part_o;
   const float2* part_ml;
   const float* v_scale;
   uint16_t* out;
@@ -447,7 +437,6 @@ struct CombineK {
 // bytes at 8 * (t % 16) of each split row (all heads of one (query, page) pair
 // are contiguous), which hold d = 32 (c % 4) + 4 (c / 4) + {0..3} and those + 16
 // for c = t % 16.
-template <bool F12>
 __global__ __launch_bounds__(1024) void attn_combine_kernel(CombineK a) {
   __shared__ int32_t s_pos[kMaxKvHeads * kTopK];
   const int64_t i = blockIdx.x;
@@ -474,18 +463,12 @@ __global__ __launch_bounds__(1024) void attn_combine_kernel(CombineK a) {
   for (int s = 0; s < kTopK; ++s) pi[s] = s_pos[sel * kTopK + s];
   // all split rows are loaded together (a missing split reads row 0 with weight 0)
   float2 ml[kTopK];
-  uint4 v[kTopK];
+  uint3 v[kTopK];
 #pragma unroll
   for (int s = 0; s < kTopK; ++s) {
     const int64_t r = (int64_t)max(pi[s], 0) * a.HP + hp;
     ml[s] = a.part_ml[r];
-    if constexpr (F12) {
-      const uint3 x = *reinterpret_cast<const uint3*>(reinterpret_cast<const uint8_t*>(a.part_o) +
-                                                      r * kRowBytesF12 + 12 * c);
-      v[s] = make_uint4(x.x, x.y, x.z, 0u);
-    } else {
-      v[s] = *reinterpret_cast<const uint4*>(a.part_o + r * kDim + 8 * c);
-    }
+    v[s] = *reinterpret_cast<const uint3*>(a.part_o + r * kRowBytes + 12 * c);
   }
   float M = -INFINITY;
 #pragma unroll
@@ -497,16 +480,7 @@ __global__ __launch_bounds__(1024) void attn_combine_kernel(CombineK a) {
     for (int s = 0; s < kTopK; ++s) {
       const float wgt = pi[s] >= 0 ? __builtin_amdgcn_exp2f(ml[s].x - M) : 0.f;
       float x[8];
-      if constexpr (F12) {
-        unpack8_f12(make_uint3(v[s].x, v[s].y, v[s].z), x);
-      } else {
-        const uint32_t wv[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          x[2 * k] = bf16_to_f32((uint16_t)(wv[k] & 0xFFFFu));
-          x[2 * k + 1] = bf16_to_f32((uint16_t)(wv[k] >> 16));
-        }
-      }
+      unpack8_f12(v[s], x);
 #pragma unroll
       for (int k = 0; k < 8; ++k) o[k] += wgt * x[k];
       L += wgt * ml[s].y;
@@ -542,7 +516,7 @@ static int64_t partial_rows(const msa_varlen_t* vl, int Hq, int n_sel, int topk)
 size_t attn_workspace_bytes(const msa_varlen_t* vl, int Hq, int Hkv, int n_sel, int topk) {
   (void)Hkv;
   const int64_t rows = partial_rows(vl, Hq, n_sel, topk);
-  return align_up((size_t)(rows * kDim * sizeof(uint16_t)), 256) +
+  return align_up((size_t)(rows * kRowBytes), 256) +
          align_up((size_t)(rows * sizeof(float2)), 256);
 }
 
@@ -567,19 +541,17 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   k.logit_scale_log2 = a.softmax_scale * kLog2e;
   k.q_scale = a.q_scale;
   k.k_scale = a.k_scale;
-  k.part_o = reinterpret_cast<uint16_t*>(a.workspace);
+  k.part_o = reinterpret_cast<uint8_t*>(a.workspace);
   k.part_ml = reinterpret_cast<float2*>(reinterpret_cast<uint8_t*>(a.workspace) +
-                                        align_up((size_t)(rows * kDim * sizeof(uint16_t)), 256));
+                                        align_up((size_t)(rows * kRowBytes), 256));
   k.trash = rows - 1;
   const int64_t max_work = L.max_items * k.GY;
-  bool f12 = false;   // the narrow kernel writes 12-bit partials
   if (max_work > 0) {
     // Rows per item from the host bound on entries per CSR row (total_q * topk
     // entries over total_rows rows, at most kAttnQC queries per item).
     const int64_t per_row = ceil_div((int64_t)a.vl.total_q * kTopK, std::max(a.vl.total_rows, 1));
     const bool wide = std::min<int64_t>(per_row, kAttnQC) * k.G >= 2 * kWaves * 16;
     const int per_cu = wide ? kBlocksWide : kBlocksNarrow;
-    f12 = !wide;
     const int64_t grid = std::min<int64_t>(max_work, (int64_t)device_cu_count() * per_cu);
     if (wide)
       hipLaunchKernelGGL(attn_partial_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, k);
@@ -605,12 +577,8 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   c.v_scale = a.v_scale;
   c.out = a.out;
   c.out_stride = a.out_stride;
-  if (f12)
-    hipLaunchKernelGGL(attn_combine_kernel<true>, dim3((unsigned)a.vl.total_q), dim3(a.Hq * 16), 0,
-                       stream, c);
-  else
-    hipLaunchKernelGGL(attn_combine_kernel<false>, dim3((unsigned)a.vl.total_q), dim3(a.Hq * 16), 0,
-                       stream, c);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)a.vl.total_q), dim3(a.Hq * 16), 0, stream,
+                     c);
   return hipGetLastError();
 }
 
