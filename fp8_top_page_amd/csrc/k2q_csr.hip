@@ -7,12 +7,14 @@
 // return_schedule=True) returns row_ptr, q_indices and a schedule).
 //
 // Deterministic without sorting: every row owns a bitmap over its request's
-// query slots, walked in order, so each row comes out ascending.  A row's bitmap
-// is cut into units of 64 words (2048 query slots); units are the grain of the
-// count, scan and fill passes, so long rows (a page chosen by thousands of
-// queries) are spread over many waves.
+// query slots, walked in order, so each row comes out ascending.  The row-major
+// bitmap is cut into units of 64 consecutive words (one per lane); rows are
+// padded so a unit holds whole short rows (decode: one word per row, 64 rows per
+// unit) or one 2048-slot piece of a long row (a page chosen by thousands of
+// queries is spread over many waves).  Units are the grain of the count, scan
+// and fill passes.
 //
-// Three launches on the caller's stream, no host sync:
+// Three launches on the caller's stream (four for large grids), no host sync:
 //   words  -- one block per (request, 32 query slots): sets the bits of those
 //             slots for every row of the request in LDS and writes the word
 //             column out (so the bitmap needs no clearing and no global
@@ -20,6 +22,7 @@
 //             the (query, slot) -> CSR row table (-1 for empty slots)
 //   count  -- one wave per unit: entries and attention items of the unit, and
 //             per-block totals
+//   (scan) -- large grids only: exclusive prefix sums of the block totals
 //   fill   -- per block: base offsets from the totals of earlier blocks, scan of
 //             its units, then one wave per unit (one lane per bitmap word)
 //             writes q_indices (ascending), each word's first CSR position,
@@ -137,24 +140,23 @@ __global__ __launch_bounds__(kThreads) void csr_words_kernel(WordsK a) {
   }
 }
 
+// A unit is 64 consecutive words (one per lane) of the row-major bitmap
+// [n_rows, words].  Rows hold a power of two of words up to 64, else a multiple
+// of 64, so a unit covers whole rows (64 / words of them) or a 64-word piece of
+// one row; a "piece" is the part of one row inside one unit, G = min(words, 64)
+// lanes.  Work items never cross pieces.
+__device__ __forceinline__ int piece_sum(int x, int G) {   // sum over aligned groups of G lanes
+  for (int m = 1; m < G; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
 struct CountK {
   const uint32_t* bitmap;
-  int64_t words;          // per row
-  int32_t units_per_row;
-  int64_t n_units;
-  int32_t* unit_cnt;
+  int64_t n_words;        // n_rows * words
+  int32_t G;              // lanes per piece
   int32_t* blk_tot;       // [n_blocks]: entries
   int32_t* blk_items;     // [n_blocks]: attention items
 };
-
-__device__ __forceinline__ int unit_popcount(const uint32_t* bitmap, int64_t words, int upr,
-                                             int64_t u, int lane, uint32_t* bits_out) {
-  const int64_t row = u / upr;
-  const int64_t w = (u % upr) * kUnitWords + lane;
-  const uint32_t bits = w < words ? bitmap[row * words + w] : 0u;
-  *bits_out = bits;
-  return __popc(bits);
-}
 
 __global__ __launch_bounds__(kThreads) void csr_count_kernel(CountK a) {
   __shared__ int s_tot[kThreads / 64], s_it[kThreads / 64];
@@ -163,19 +165,19 @@ __global__ __launch_bounds__(kThreads) void csr_count_kernel(CountK a) {
   uint32_t bits[kUnitsPerWave];
 #pragma unroll
   for (int k = 0; k < kUnitsPerWave; ++k) {   // all loads in flight together
-    const int64_t u = u0 + k;
-    bits[k] = 0u;
-    if (u < a.n_units) unit_popcount(a.bitmap, a.words, a.units_per_row, u, lane, &bits[k]);
+    const int64_t fw = (u0 + k) * kUnitWords + lane;
+    bits[k] = fw < a.n_words ? a.bitmap[fw] : 0u;
   }
   int tot = 0, its = 0;
 #pragma unroll
   for (int k = 0; k < kUnitsPerWave; ++k) {
-    const int64_t u = u0 + k;
-    const int c = wave_sum(__popc(bits[k]));
-    if (u < a.n_units && lane == 0) a.unit_cnt[u] = c;
+    const int c = __popc(bits[k]);
+    const int n = piece_sum(c, a.G);
     tot += c;
-    its += (c + kAttnQC - 1) / kAttnQC;
+    its += (lane & (a.G - 1)) == 0 ? (n + kAttnQC - 1) / kAttnQC : 0;
   }
+  tot = wave_sum(tot);
+  its = wave_sum(its);
   if (lane == 0) { s_tot[wave] = tot; s_it[wave] = its; }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -186,29 +188,74 @@ __global__ __launch_bounds__(kThreads) void csr_count_kernel(CountK a) {
   }
 }
 
+// Exclusive prefix sums of the count blocks' totals, in place: one block of
+// 1024 threads walks tiles of 1024 x kScanPer entries; thread t loads its
+// kScanPer consecutive entries together, the per-thread sums are scanned across
+// the block and each thread writes its entries' prefixes.  Used when the grid
+// is large enough that every fill block summing its predecessors would cost
+// more than this launch.
+constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 16;
+constexpr int kScanFrom = 8192;               // count/fill blocks from which the scan runs
+
+__global__ __launch_bounds__(kScanThreads) void csr_scan_kernel(int32_t* tot, int32_t* items,
+                                                                int64_t n) {
+  __shared__ int s_a[kScanThreads / 64], s_b[kScanThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int carry_a = 0, carry_b = 0;
+  for (int64_t t0 = 0; t0 < n; t0 += (int64_t)kScanThreads * kScanPer) {
+    const int64_t j0 = t0 + (int64_t)tid * kScanPer;
+    int va[kScanPer], vb[kScanPer];
+    int sa = 0, sb = 0;
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      const bool ok = j0 + k < n;
+      va[k] = ok ? tot[j0 + k] : 0;
+      vb[k] = ok ? items[j0 + k] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) { sa += va[k]; sb += vb[k]; }
+    const int ia = wave_inclusive_scan(sa), ib = wave_inclusive_scan(sb);
+    if (lane == 63) { s_a[wave] = ia; s_b[wave] = ib; }
+    __syncthreads();
+    int ra = carry_a + ia - sa, rb = carry_b + ib - sb;
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+      if (w < wave) { ra += s_a[w]; rb += s_b[w]; }
+      carry_a += s_a[w];
+      carry_b += s_b[w];
+    }
+    __syncthreads();                          // s_a / s_b are rewritten by the next tile
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      if (j0 + k < n) { tot[j0 + k] = ra; items[j0 + k] = rb; }
+      ra += va[k];
+      rb += vb[k];
+    }
+  }
+}
+
+constexpr int kLdsBatch = 1024;               // requests whose offsets the fill keeps in LDS
+
 struct FillK {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int32_t batch;
   const int32_t* block_table;
   int64_t bt_stride;
-  const int32_t* topk;
-  int64_t tq, th;
-  int32_t n_sel;
   int32_t total_rows;
   const int32_t* row_base;
   const uint32_t* bitmap;
-  int64_t words;
-  int32_t units_per_row;
-  int64_t n_units;
+  int64_t words;           // per row
+  int32_t G;               // lanes per piece
+  int64_t n_words;         // n_rows * words
   int64_t n_rows;
   int32_t n_blocks;
-  const int32_t* unit_cnt;
-  const int32_t* blk_tot;
+  const int32_t* blk_tot;  // per-block totals, or (prefixed) their exclusive prefix sums
   const int32_t* blk_items;
+  int32_t prefixed;
   int32_t* row_ptr;
   int32_t* q_indices;
-  int32_t* wbase;      // [n_rows, words]: CSR position of each word's first entry
+  int32_t* wbase;          // [n_rows, words]: CSR position of each word's first entry
   int4* items;
   int64_t max_items;
   Hdr* hdr;
@@ -216,40 +263,69 @@ struct FillK {
 
 __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
   __shared__ int s_red[2][kThreads / 64];
+  __shared__ int s_cnt[kUnitsPerBlock], s_itc[kUnitsPerBlock];
   __shared__ int s_pos[kUnitsPerBlock];     // first CSR position of each unit
   __shared__ int s_item[kUnitsPerBlock];    // first item index of each unit
+  __shared__ int s_rb[kLdsBatch + 1], s_cq[kLdsBatch + 1], s_ck[kLdsBatch + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int blk = blockIdx.x;
-  const int64_t u0 = (int64_t)blk * kUnitsPerBlock;
+  const bool lds_req = a.batch <= kLdsBatch;
+  const int G = a.G;
 
-  // entries and items of all earlier blocks
-  int base_e = 0, base_i = 0;
-  for (int j = tid; j < blk; j += kThreads) {
-    base_e += a.blk_tot[j];
-    base_i += a.blk_items[j];
+  uint32_t bits[kUnitsPerWave];
+#pragma unroll
+  for (int k = 0; k < kUnitsPerWave; ++k) {   // all loads in flight together
+    const int64_t fw = ((int64_t)blk * kUnitsPerBlock + wave * kUnitsPerWave + k) * kUnitWords + lane;
+    bits[k] = fw < a.n_words ? a.bitmap[fw] : 0u;
   }
-  base_e = wave_sum(base_e);
-  base_i = wave_sum(base_i);
-  if (lane == 0) { s_red[0][wave] = base_e; s_red[1][wave] = base_i; }
+  if (lds_req)
+    for (int i = tid; i <= a.batch; i += kThreads) {
+      s_rb[i] = a.row_base[i];
+      s_cq[i] = a.cu_q[i];
+      s_ck[i] = a.cu_k[i];
+    }
+
+  // entries and items of all earlier blocks (summed here for small grids)
+  int base_e = 0, base_i = 0;
+  if (a.prefixed) {
+    base_e = a.blk_tot[blk];
+    base_i = a.blk_items[blk];
+  } else {
+    for (int j = tid; j < blk; j += kThreads) {
+      base_e += a.blk_tot[j];
+      base_i += a.blk_items[j];
+    }
+    base_e = wave_sum(base_e);
+    base_i = wave_sum(base_i);
+    if (lane == 0) { s_red[0][wave] = base_e; s_red[1][wave] = base_i; }
+  }
+  // entries and items of this block's units
+#pragma unroll
+  for (int k = 0; k < kUnitsPerWave; ++k) {
+    const int c = __popc(bits[k]);
+    const int n = piece_sum(c, G);
+    const int it = (lane & (G - 1)) == 0 ? (n + kAttnQC - 1) / kAttnQC : 0;
+    const int tc = wave_sum(c), ti = wave_sum(it);
+    if (lane == 0) { s_cnt[wave * kUnitsPerWave + k] = tc; s_itc[wave * kUnitsPerWave + k] = ti; }
+  }
   __syncthreads();
-  base_e = 0;
-  base_i = 0;
-  for (int w = 0; w < kThreads / 64; ++w) { base_e += s_red[0][w]; base_i += s_red[1][w]; }
+  if (!a.prefixed) {
+    base_e = 0;
+    base_i = 0;
+    for (int w = 0; w < kThreads / 64; ++w) { base_e += s_red[0][w]; base_i += s_red[1][w]; }
+  }
 
   // scan of this block's units (one lane per unit)
   static_assert(kUnitsPerBlock <= 64, "one lane per unit in the block scan");
   if (wave == 0) {
-    const int64_t u = u0 + lane;
-    const bool mine = lane < kUnitsPerBlock && u < a.n_units;
-    const int c = mine ? a.unit_cnt[u] : 0;
-    const int it = (c + kAttnQC - 1) / kAttnQC;
+    const int c = lane < kUnitsPerBlock ? s_cnt[lane] : 0;
+    const int it = lane < kUnitsPerBlock ? s_itc[lane] : 0;
     const int ie = wave_inclusive_scan(c);
     const int ii = wave_inclusive_scan(it);
     if (lane < kUnitsPerBlock) {
       s_pos[lane] = base_e + ie - c;
       s_item[lane] = base_i + ii - it;
     }
-    if (mine && u % a.units_per_row == 0) a.row_ptr[u / a.units_per_row] = base_e + ie - c;
     if (blk == a.n_blocks - 1 && lane == 63) {
       a.row_ptr[a.n_rows] = base_e + ie;
       a.hdr->nnz = base_e + ie;
@@ -258,52 +334,58 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
   }
   __syncthreads();
 
-  uint32_t ubits[kUnitsPerWave];
-#pragma unroll
-  for (int k = 0; k < kUnitsPerWave; ++k) {   // all loads in flight together
-    const int64_t u = u0 + wave * kUnitsPerWave + k;
-    ubits[k] = 0u;
-    if (u < a.n_units) unit_popcount(a.bitmap, a.words, a.units_per_row, u, lane, &ubits[k]);
-  }
+  const int32_t* rbase = lds_req ? s_rb : a.row_base;
+  const int32_t* cq = lds_req ? s_cq : a.cu_q;
+  const int32_t* ck = lds_req ? s_ck : a.cu_k;
+  const int lead = lane & ~(G - 1);
 #pragma unroll
   for (int k = 0; k < kUnitsPerWave; ++k) {
     const int ku = wave * kUnitsPerWave + k;
-    const int64_t u = u0 + ku;
-    if (u >= a.n_units) break;
-    const int64_t row = u / a.units_per_row;
+    const int64_t fw = ((int64_t)blk * kUnitsPerBlock + ku) * kUnitWords + lane;
+    if (fw - lane >= a.n_words) break;
+    const bool valid = fw < a.n_words;
+    const int64_t row = fw / a.words;
+    const int64_t word = fw - row * a.words;
     const int g = (int)(row / a.total_rows);
-    const int64_t rr = row % a.total_rows;
-    const int b = find_request(a.row_base, a.batch, rr);
-    const int j = (int)(rr - a.row_base[b]);
-    const int64_t q_base = a.cu_q[b] + (u % a.units_per_row) * (kUnitWords * 32);
-    const int sk = a.cu_k[b + 1] - a.cu_k[b];
-    const int ctx = sk - (a.cu_q[b + 1] - a.cu_q[b]);
+    const int64_t rr = row - (int64_t)g * a.total_rows;
+    const int b = valid ? find_request(rbase, a.batch, rr) : 0;
+    const int j = (int)(rr - rbase[b]);
     // One lane per bitmap word: the word's first CSR position is the unit's
     // plus the bits of earlier words; the lane then writes the word's entries
     // in bit order (a wave-uniform loop as long as any lane has bits left).
-    const uint32_t bits = ubits[k];
-    const int c = __popc(bits);
+    const uint32_t bits_k = bits[k];
+    const int c = __popc(bits_k);
     const int incl = wave_inclusive_scan(c);
-    const int n = __shfl(incl, 63);
     int pos = s_pos[ku] + incl - c;
-    const int64_t wi = row * a.words + (u % a.units_per_row) * kUnitWords + lane;
-    if ((u % a.units_per_row) * kUnitWords + lane < a.words) a.wbase[wi] = pos;
-    uint32_t x = bits;
-    const int64_t q_word = q_base + lane * 32;
+    if (valid) {
+      a.wbase[fw] = pos;
+      if (word == 0) a.row_ptr[row] = pos;
+    }
+    // work items of the lane's piece: (row, first entry, count), lane t of the
+    // piece writing item t (a piece of G words yields at most G items)
+    const int n = piece_sum(c, G);
+    const int n_it = (n + kAttnQC - 1) / kAttnQC;
+    const int it = lane == lead ? n_it : 0;
+    const int iincl = wave_inclusive_scan(it);
+    const int p_pos = __shfl(pos, lead);
+    const int p_item = s_item[ku] + __shfl(iincl - it, lead);
+    uint32_t x = bits_k;
+    const int64_t q_word = cq[b] + word * 32;
     while (__builtin_amdgcn_ballot_w64(x != 0u) != 0) {
       if (x != 0u) {
         a.q_indices[pos++] = (int32_t)(q_word + __builtin_ctz(x));
         x &= x - 1u;
       }
     }
-    // work items of the unit: (row, first entry, count)
-    const int n_it = (n + kAttnQC - 1) / kAttnQC;
-    const int phys = n_it > 0 ? a.block_table[(int64_t)b * a.bt_stride + j] : 0;
-    for (int t = lane; t < n_it; t += 64) {
-      const int64_t idx = (int64_t)s_item[ku] + t;
+    const int t = lane - lead;
+    if (valid && t < n_it) {
+      const int64_t idx = (int64_t)p_item + t;
       if (idx < a.max_items) {
-        a.items[2 * idx] = make_int4(s_pos[ku] + t * kAttnQC, min(kAttnQC, n - t * kAttnQC), phys, g);
-        a.items[2 * idx + 1] = make_int4(ctx - a.cu_q[b] - j * kPage, sk - j * kPage, (int)row, b);
+        const int sk = ck[b + 1] - ck[b];
+        const int ctx = sk - (cq[b + 1] - cq[b]);
+        const int phys = a.block_table[(int64_t)b * a.bt_stride + j];
+        a.items[2 * idx] = make_int4(p_pos + t * kAttnQC, min(kAttnQC, n - t * kAttnQC), phys, g);
+        a.items[2 * idx + 1] = make_int4(ctx - cq[b] - j * kPage, sk - j * kPage, (int)row, b);
       }
     }
   }
@@ -314,19 +396,25 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
 SchedLayout sched_layout(const msa_varlen_t* vl, int n_sel, int topk) {
   SchedLayout L;
   L.n_rows = (int64_t)n_sel * vl->total_rows;
-  L.words_per_row = std::max<int64_t>(1, ceil_div(std::max(vl->max_seqlen_q, 1), 32));
-  L.units_per_row = ceil_div(L.words_per_row, kUnitWords);
-  L.n_units = L.n_rows * L.units_per_row;
+  // one bit per query slot; rows padded to a power of two of words up to 64,
+  // else to a multiple of 64, so bitmap units align with rows
+  const int64_t w = std::max<int64_t>(1, ceil_div(std::max(vl->max_seqlen_q, 1), 32));
+  int64_t wp = 1;
+  while (wp < w && wp < kUnitWords) wp <<= 1;
+  L.words_per_row = w <= kUnitWords ? wp : ceil_div(w, kUnitWords) * kUnitWords;
+  L.n_units = ceil_div(L.n_rows * L.words_per_row, kUnitWords);
   L.n_blocks = std::max<int64_t>(1, ceil_div(L.n_units, kUnitsPerBlock));
   L.inv_len = (int64_t)vl->total_q * n_sel * topk;
   L.word_chunks = std::max<int64_t>(1, ceil_div((int64_t)n_sel * std::max(vl->max_pages, 1), kWordRows));
   L.word_blocks = L.words_per_row * std::max(vl->batch, 0) * L.word_chunks;
-  // every unit holding c entries yields ceil(c / kAttnQC) items
-  L.max_items = ceil_div((int64_t)n_sel * vl->total_q * topk, kAttnQC) + L.n_units;
+  // a piece (a row's words inside one unit) holding c entries yields
+  // ceil(c / kAttnQC) items; only pieces with entries yield any
+  const int64_t entries = (int64_t)n_sel * vl->total_q * topk;
+  const int64_t pieces = L.n_rows * std::max<int64_t>(1, L.words_per_row / kUnitWords);
+  L.max_items = ceil_div(entries, kAttnQC) + std::min(entries, pieces);
   size_t off = 0;
   L.hdr = off;        off += sizeof(Hdr);
   L.row_base = off;   off += align_up(sizeof(int32_t) * (vl->batch + 1), 256);
-  L.unit_cnt = off;   off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.n_units), 256);
   L.blk_tot = off;    off += align_up(sizeof(int32_t) * 2 * L.n_blocks, 256);
   L.items = off;      off += align_up(2 * sizeof(int4) * std::max<int64_t>(1, L.max_items), 256);
   L.rowsel = off;     off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.inv_len), 256);
@@ -340,7 +428,6 @@ hipError_t launch_k2q_csr(const CsrArgs& a, hipStream_t stream) {
   const SchedLayout& L = a.L;
   Hdr* hdr = reinterpret_cast<Hdr*>(a.sched + L.hdr);
   int32_t* row_base = reinterpret_cast<int32_t*>(a.sched + L.row_base);
-  int32_t* unit_cnt = reinterpret_cast<int32_t*>(a.sched + L.unit_cnt);
   int32_t* blk_tot = reinterpret_cast<int32_t*>(a.sched + L.blk_tot);
   int32_t* blk_items = blk_tot + L.n_blocks;
   int4* items = reinterpret_cast<int4*>(a.sched + L.items);
@@ -356,14 +443,18 @@ hipError_t launch_k2q_csr(const CsrArgs& a, hipStream_t stream) {
                        wk);
   }
 
-  CountK cnt{bitmap, L.words_per_row, (int32_t)L.units_per_row, L.n_units, unit_cnt, blk_tot,
-             blk_items};
+  const int32_t G = (int32_t)std::min<int64_t>(L.words_per_row, kUnitWords);
+  const int64_t n_words = L.n_rows * L.words_per_row;
+  CountK cnt{bitmap, n_words, G, blk_tot, blk_items};
   hipLaunchKernelGGL(csr_count_kernel, dim3((unsigned)L.n_blocks), dim3(kThreads), 0, stream, cnt);
 
+  const int32_t prefixed = L.n_blocks >= kScanFrom ? 1 : 0;
+  if (prefixed)
+    hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, blk_tot, blk_items,
+                       L.n_blocks);
   FillK fk{a.vl.cu_seqlens_q, a.vl.cu_seqlens_k, a.vl.batch, a.vl.block_table,
-           a.vl.block_table_stride, a.topk, a.tq_stride, a.th_stride, a.n_sel,
-           a.vl.total_rows, row_base, bitmap, L.words_per_row, (int32_t)L.units_per_row,
-           L.n_units, L.n_rows, (int32_t)L.n_blocks, unit_cnt, blk_tot, blk_items, a.row_ptr,
+           a.vl.block_table_stride, a.vl.total_rows, row_base, bitmap, L.words_per_row, G,
+           n_words, L.n_rows, (int32_t)L.n_blocks, blk_tot, blk_items, prefixed, a.row_ptr,
            a.q_indices, wbase, items, L.max_items, hdr};
   hipLaunchKernelGGL(csr_fill_kernel, dim3((unsigned)L.n_blocks), dim3(kThreads), 0, stream, fk);
   return hipGetLastError();

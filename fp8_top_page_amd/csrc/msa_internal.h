@@ -68,11 +68,10 @@ constexpr int kAttnQC = 32;
 
 struct SchedLayout {
   // byte offsets inside the schedule buffer
-  size_t hdr, row_base, unit_cnt, blk_tot, items, rowsel, wbase, bitmap, total;
+  size_t hdr, row_base, blk_tot, items, rowsel, wbase, bitmap, total;
   int64_t n_rows;         // n_sel * total_rows
-  int64_t words_per_row;  // bitmap words per row (one bit per query slot of the request)
-  int64_t units_per_row;  // bitmap units (64 words) per row
-  int64_t n_units;
+  int64_t words_per_row;  // bitmap words per row (one bit per query slot, padded)
+  int64_t n_units;        // bitmap units (64 consecutive words of the row-major bitmap)
   int64_t n_blocks;       // count/fill blocks
   int64_t max_items;
   int64_t inv_len;        // total_q * n_sel * topk: entries of the (query, slot) -> row table

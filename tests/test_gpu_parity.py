@@ -21,7 +21,8 @@ from parity import (check_attention, check_csr, check_scores, check_selection_in
 
 pytestmark = pytest.mark.gpu
 
-SAMPLE = {"tiny_1k": None, "q128_kv32k": None, "fresh_32k": 48, "q2048_kv1m": 32, "ragged_b8": 48}
+SAMPLE = {"tiny_1k": None, "q128_kv32k": None, "fresh_32k": 48, "q2048_kv1m": 32, "ragged_b8": 48,
+          "decode_b16": 32}
 
 
 @functools.lru_cache(maxsize=1)
@@ -169,6 +170,26 @@ def test_per_kv_head_selection_and_random_topk():
     out = to_np(path.out.float()).reshape(inp.total_q, 16, 128)
     q = np.arange(0, inp.total_q, 7)
     check_attention(inp, sel, out, q, n_sel=2)
+
+
+def test_large_csr_grid_random_topk():
+    """A CSR large enough that its per-block totals go through the separate
+    prefix-scan launch (16384 queries of one request over 4160 pages, plus a
+    short second request): CSR bit-exact, attention on sampled queries."""
+    from fp8_top_page_amd.pipeline import DeviceBatch, MsaPath
+    inp = _small_inputs((16384, 100), (532480, 5000), 1, 8, 1, seed=12)
+    sel = workloads.random_topk(inp, n_sel=1, seed=5)
+    db = DeviceBatch.from_inputs(inp)
+    path = MsaPath(db)
+    path.topk.copy_(torch.from_numpy(sel))
+    print("\n[parity] large CSR grid: csr + attention", flush=True)
+    path.csr()
+    path.attend()
+    torch.cuda.synchronize()
+    check_csr(inp, sel[:, 0, :], to_np(path.row_ptr), to_np(path.q_indices))
+    out = to_np(path.out.float()).reshape(inp.total_q, 8, 128)
+    q = np.concatenate([np.arange(0, 16384, 1021), np.arange(16384, inp.total_q, 9)])
+    check_attention(inp, sel[:, 0, :], out, q)
 
 
 def test_block_table_permutation_is_bitwise_invariant():

@@ -83,11 +83,20 @@ def _build_workloads():
     ws["ragged_b8"] = Workload(
         "ragged_b8", 5, sq, sk, 2, 16, 2,
         description="8 requests, log-uniform prefixes in [512,150000], chunks in {512,2048,8192}")
+    # decode with speculative verification: eight new tokens per request (one
+    # decoded plus seven drafts) over a 128K-token context, the shape of the
+    # pages' decode-indexer table (16 and 64 requests, eight queries each)
+    ws["decode_b16"] = Workload(
+        "decode_b16", 6, (8,) * 16, (131072,) * 16, 1, 8, 1,
+        description="16 requests, 8 new tokens each after a 131064-token prefix (1024 pages)")
+    ws["decode_b64"] = Workload(
+        "decode_b64", 7, (8,) * 64, (131072,) * 64, 1, 8, 1,
+        description="64 requests, 8 new tokens each after a 131064-token prefix (1024 pages)")
     return ws
 
 
 WORKLOADS = _build_workloads()
-ORDER = ["tiny_1k", "q128_kv32k", "fresh_32k", "q2048_kv1m", "ragged_b8"]
+ORDER = ["tiny_1k", "q128_kv32k", "fresh_32k", "q2048_kv1m", "ragged_b8", "decode_b16"]
 
 
 def custom(name, seed, seqlen_q, seqlen_k, index_heads=1, q_heads=8, kv_heads=1,
