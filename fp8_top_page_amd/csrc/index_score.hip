@@ -14,11 +14,15 @@
 //    all query blocks see the same pages, three when they differ).  The scorer
 //    grid is sized from host-side upper bounds, and blocks past the device-side
 //    item count exit.
-//  * Scoring: tokens are the MFMA M axis, queries the N axis.  Each wave keeps
-//    the E4M3 fragments of 128/H queries (all H heads) in registers for the
-//    whole item; the index-K page (16 KiB) is staged once per block in LDS
-//    (double-buffered, padded rows) and read by all 8 waves.  The H head
-//    products chain into one accumulator (a contraction of length H*128).
+//  * Scoring: tokens are the MFMA M axis, queries the N axis.  Each of the 16
+//    waves keeps the E4M3 fragments of 64/H queries (all H heads) in registers
+//    for the whole item; index-K pages (16 KiB) stream into a ring of four LDS
+//    slots by direct global -> LDS copies and are read by every wave.  The H
+//    head products chain into one accumulator (a contraction of length H*128).
+//  * Decode-like batches (every request at most 64/H queries): one wave's
+//    queries are all there is, so the waves split each page instead: wave w
+//    scores a 16-token slice of one page for all the queries, and the slices'
+//    maxima are reduced through LDS.
 //  * Epilogue: each lane holds 4 consecutive tokens of one query per 16-token
 //    tile; the max over the page's 8 tiles is taken in registers, then across
 //    the 4 lane groups.  Scores of 4 consecutive pages are gathered so each
@@ -518,10 +522,209 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode-like batches: every request has at most 64/H queries, so every item
+// does and one wave's query tiles hold them all.  The 16 waves then split each
+// pair of pages (wave w: page p + w / 8, tokens 16 (w % 8) .. 16 (w % 8) + 15),
+// each with all the query tiles, and write per-query partial maxima to LDS;
+// wave 0 reduces a pair's 8 + 8 partials one step later (the partials are
+// double-buffered across the barrier) and keeps the score tile.
+// ---------------------------------------------------------------------------
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
+// l's bytes land at LDS byte address lds_addr + 16 l (lds_addr wave-uniform,
+// passed in M0).  Inline assembly keeps the copy out of the compiler's
+// wait-count bookkeeping, which cannot tell the ring slots apart and would
+// otherwise wait for every copy in flight before each LDS read; the kernel's own
+// vmcnt waits and barriers order copies and reads.  (Counters retire in issue
+// order, so copies the compiler does not know of only lengthen the waits it
+// places for other loads.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               ::"v"(src), "s"(lds_addr)
+               : "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS: the page ring, wave 0's score tile, the physical page ids and two
+// buffers of partial maxima [wave][query].
+template <int H>
+constexpr size_t score_pp_lds_bytes() {
+  return 4 * kLdsPage + (size_t)score_qtiles(H) * 16 * kSRow * sizeof(float) +
+         kMaxItemPages * sizeof(int) + 2 * kScoreWaves * score_qtiles(H) * 16 * sizeof(float);
+}
+
+template <int H>
+__global__ __launch_bounds__(kThreads) void index_score_pp_kernel(ScoreK a) {
+  constexpr int NQT = score_qtiles(H);
+  constexpr int kQ = NQT * 16;                    // query slots
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+  const int item = blockIdx.x;
+  if (item >= a.hdr->n_items) return;
+  const int4 it = a.items[item];
+  const int b = it.x, q_first = it.y, q_count = it.z, p0 = it.w;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  float* sbuf = reinterpret_cast<float*>(lds + 4 * kLdsPage);
+  int* s_phys = reinterpret_cast<int*>(lds + 4 * kLdsPage + kQ * kSRow * 4);
+  float* s_part = reinterpret_cast<float*>(s_phys + kMaxItemPages);
+
+  const int cq0 = a.cu_q[b];
+  const int sq = a.cu_q[b + 1] - cq0;
+  const int sk = a.cu_k[b + 1] - a.cu_k[b];
+  const int ctx = sk - sq;
+  const int pos_first = ctx + (q_first - cq0);
+  const int pos_last = pos_first + q_count - 1;
+  const int v_block = pos_last / kPage + 1;
+  const int p_end = min(min(p0 + a.hdr->pages_per_item, v_block), a.max_pages);
+  if (p0 >= p_end) return;
+  const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
+  for (int k = tid; k < p_end - p0; k += kThreads) {
+    const int phys = bt[p0 + k];
+    s_phys[k] = (phys < 0 || phys >= a.num_pages) ? 0 : phys;
+  }
+  __syncthreads();
+
+  // page ring: as in the prefill kernel, four slots, page p in slot p & 3
+  const int ld_row = wave * 8 + (lane >> 3);
+  const int ld_piece = (lane & 7) ^ ((ld_row >> 1) & 7);
+  const uint32_t lds_wave =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds + wave * 1024;
+  auto issue_page = [&](int p) {
+    const int phys = s_phys[min(p, p_end - 1) - p0];
+    const uint8_t* src = a.k_cache + (int64_t)phys * (kPage * kDim) + ld_row * kDim + ld_piece * 16;
+    copy16_to_lds(src, lds_wave + (uint32_t)((p & 3) * kLdsPage));
+  };
+  issue_page(p0);
+  issue_page(p0 + 1);
+  issue_page(p0 + 2);
+  issue_page(p0 + 3);
+
+  // every wave: the fragments of all the item's queries (tiles past them skipped)
+  v8i qf[NQT][H];
+  const int q_end = q_first + q_count;
+  const int nt = (q_count + 15) / 16;
+  const int my_q0 = q_first + col;
+  const int my_pos0 = ctx + (my_q0 - cq0);
+#pragma unroll
+  for (int n = 0; n < NQT; ++n) {
+    const int qi = my_q0 + n * 16;
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+      qf[n][h] = qi < q_end ? load_frag_global(a.q + (int64_t)qi * a.q_stride + h * kDim + grp * 32)
+                            : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  const float scale = (*a.q_scale) * (*a.k_scale);
+  const Swz swz = lane_swizzle(col, grp);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // partial maxima of page pw, tokens 16T .. 16T + 15, into dst[query]
+  auto partial = [&](int pw, int T, float* dst) {
+    const uint8_t* pg = lds + (pw & 3) * kLdsPage;
+    const v8i a_t = load_frag_swz(pg + (T * 16 + col) * kDim, swz);
+    const bool causal = (pw + 1) * kPage - 1 > pos_first;
+    const int tok0 = pw * kPage + T * 16 + grp * 4;        // token of acc[0] in this lane
+#pragma unroll
+    for (int n = 0; n < NQT; ++n) {
+      if (n >= nt) break;
+      v4f acc = mfma_e4m3(a_t, qf[n][0], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int h = 1; h < H; ++h) acc = mfma_e4m3(a_t, qf[n][h], acc);
+      float m;
+      if (causal) {
+        const int lim = my_pos0 + 16 * n;
+        m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, tok0 + i > lim ? -INFINITY : acc[i]);
+      } else {
+        m = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+      }
+      m = max_across_groups(m);
+      if ((n & 3) == grp) dst[n * 16 + col] = m;
+    }
+  };
+  // wave 0: score tile flush for pages [pg0, pg_hi), as in the prefill kernel
+  auto flush = [&](int pg0, int pg_hi) {
+#pragma unroll
+    for (int r = 0; r < NQT; ++r) {
+      const int ql = r * 16 + (lane >> 2);
+      const int c = (lane & 3) * 4;
+      const int qi = q_first + ql;
+      const int pos = ctx + (qi - cq0);
+      const int pp = pg0 + c;
+      const float* src = sbuf + ql * kSRow + c;
+      const float v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
+      if (qi < q_end) {
+        float* dst = a.scores + (int64_t)qi * a.ld + pp;
+        const int vis_end = min(pg_hi, pos / kPage + 1);
+        if (pp + 3 < vis_end) {
+          *reinterpret_cast<v4f*>(dst) = v4f{v0, v1, v2, v3};
+        } else {
+          if (pp + 0 < vis_end) dst[0] = v0;
+          if (pp + 1 < vis_end) dst[1] = v1;
+          if (pp + 2 < vis_end) dst[2] = v2;
+        }
+      }
+    }
+  };
+  // wave 0: page pr's score from its 8 partials (waves 8j .. 8j + 7 of src)
+  auto reduce = [&](int pr, int j, const float* src) {
+    const int pc = (pr - p0) & (kFlush - 1);
+    if (lane < kQ) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int T = 0; T < 8; ++T) m = fmaxf(m, src[(j * 8 + T) * kQ + lane]);
+      sbuf[lane * kSRow + pc] = m * scale;
+    }
+    if (pc == kFlush - 1 || pr == p_end - 1) flush(pr - pc, pr + 1);
+  };
+
+  // One step: partials of pages p, p + 1 (wave 0 also reduces the previous
+  // pair); wait for this wave's pieces of p + 2, p + 3; barrier; request
+  // p + 4, p + 5 into the slots of p, p + 1.
+  constexpr int kPartBuf = kScoreWaves * kQ;
+  int buf = 0;
+  for (int p = p0; p < p_end; p += 2) {
+    const int pw = p + (wave >> 3);
+    if (pw < p_end) partial(pw, wave & 7, s_part + buf * kPartBuf + wave * kQ);
+    if (wave == 0 && p > p0) {
+      reduce(p - 2, 0, s_part + (buf ^ 1) * kPartBuf);
+      reduce(p - 1, 1, s_part + (buf ^ 1) * kPartBuf);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (p + 2 < p_end) {
+      issue_page(p + 4);
+      issue_page(p + 5);
+    }
+    buf ^= 1;
+  }
+  if (wave == 0) {                    // the last pair
+    const int pl = p0 + (p_end - 1 - p0) / 2 * 2;
+    reduce(pl, 0, s_part + (buf ^ 1) * kPartBuf);
+    if (pl + 1 < p_end) reduce(pl + 1, 1, s_part + (buf ^ 1) * kPartBuf);
+  }
+}
+
 }  // namespace
 
 template <int H>
-hipError_t launch_scorer(dim3 grid, hipStream_t stream, const ScoreK& k) {
+hipError_t launch_scorer(dim3 grid, hipStream_t stream, const ScoreK& k, int max_seqlen_q) {
+  if (max_seqlen_q <= score_qtiles(H) * 16) {   // every item fits one wave's query tiles
+    constexpr size_t bytes = score_pp_lds_bytes<H>();
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&index_score_pp_kernel<H>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(index_score_pp_kernel<H>, grid, dim3(kThreads), bytes, stream, k);
+    return hipGetLastError();
+  }
   constexpr size_t bytes = score_lds_bytes<H>();
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&index_score_kernel<H>),
@@ -581,9 +784,9 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
   k.items = items;
   dim3 grid((unsigned)a.plan.max_items);
   switch (a.H) {
-    case 1: return launch_scorer<1>(grid, stream, k);
-    case 2: return launch_scorer<2>(grid, stream, k);
-    case 4: return launch_scorer<4>(grid, stream, k);
+    case 1: return launch_scorer<1>(grid, stream, k, a.vl.max_seqlen_q);
+    case 2: return launch_scorer<2>(grid, stream, k, a.vl.max_seqlen_q);
+    case 4: return launch_scorer<4>(grid, stream, k, a.vl.max_seqlen_q);
     default: return hipErrorInvalidValue;
   }
 }

@@ -88,6 +88,10 @@ def _small_inputs(seqlen_q, seqlen_k, H=1, Hq=8, Hkv=1, seed=11):
     ((1,), (1,), 1, 8, 1),                                   # one token
     ((129,), (257,), 4, 4, 4),                               # one q-head per KV head
     ((600, 70), (20000, 3000), 1, 32, 2),                    # 16 q-heads per KV head
+    # decode-like batches (at most 64 / H queries per request: page-parallel scoring)
+    ((64, 3, 50, 0), (9000, 200, 64, 500), 1, 8, 1),
+    ((32, 7, 1), (5000, 40, 70000), 2, 16, 2),
+    ((16, 9), (3000, 777), 4, 8, 4),
 ])
 def test_edge_shapes(sq, sk, H, Hq, Hkv):
     print(f"\n[parity] edge shape sq={sq} sk={sk} H={H} Hq={Hq} Hkv={Hkv}", flush=True)
