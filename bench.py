@@ -239,6 +239,15 @@ def main():
     score_us = float(mean_us[0])
     attn_us = float(mean_us[3])
     score_tflops = work["score_flops"] / (score_us * 1e-6) / 1e12
+    score_gbs = work["score_bytes"] / (score_us * 1e-6) / 1e9
+    # the scorer's bound: whichever peak its algorithmic work reaches first
+    # (MFMA for prefill chunks; HBM for decode-like batches of few queries)
+    if work["score_bytes"] / PEAK_HBM_GBS / 1e9 > work["score_flops"] / PEAK_FP8_TFLOPS / 1e12:
+        score_roof = {"bound": "hbm", "achieved": round(score_gbs, 1), "peak": PEAK_HBM_GBS,
+                      "unit": "GB/s", "frac": round(score_gbs / PEAK_HBM_GBS, 4)}
+    else:
+        score_roof = {"bound": "mfma", "achieved": round(score_tflops, 1), "peak": PEAK_FP8_TFLOPS,
+                      "unit": "TFLOP/s", "frac": round(score_tflops / PEAK_FP8_TFLOPS, 4)}
     attn_tflops = work["attn_flops"] / (attn_us * 1e-6) / 1e12
     result = {
         "metric": METRIC,
@@ -259,9 +268,8 @@ def main():
                    "q_heads": wl.q_heads, "kv_heads": wl.kv_heads, "page": 128, "head_dim": 128,
                    "topk": 16, "cache": "cold (1 GiB overwrite per step)" if args.cold
                    else "warm (steps back to back)"},
-        "roofline": {"bound": "mfma", "achieved": round(score_tflops, 1), "peak": PEAK_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(score_tflops / PEAK_FP8_TFLOPS, 4),
-                     "traffic": scorer_hbm_traffic(wl.name), "kernel": "index_score (plan + scorer)",
+        "roofline": {**score_roof, "traffic": scorer_hbm_traffic(wl.name),
+                     "kernel": "index_score (plan + scorer)",
                      "flops_per_launch": work["score_flops"],
                      "algorithmic_bytes_per_launch": work["score_bytes"],
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"},
