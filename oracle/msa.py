@@ -38,6 +38,11 @@ Pins (each function is checked by tests against something other than itself):
       explicit mask) when the selection covers every visible page, closed forms
       (constant V, one visible token, all-zero K gives the mean of V).
   round_bf16    -- torch's bfloat16 cast on random and tie values.
+  encode_e4m3 / quantize_e4m3 / insert_* -- every finite code round-trips,
+      midpoints between neighbouring codes go to the even code, values just off
+      a midpoint go to the nearer code, torch.float8_e4m3fn's CPU cast inside
+      its non-saturating range (|x| <= 464), saturation and NaN by the stated
+      rule, power-of-two scales exact; inserts against hand-placed rows.
 """
 from __future__ import annotations
 
@@ -81,6 +86,90 @@ _E4M3 = e4m3_table()
 def decode_e4m3(codes: np.ndarray) -> np.ndarray:
     """Decode E4M3 bytes to float64 (unscaled)."""
     return _E4M3[np.asarray(codes, dtype=np.uint8)]
+
+
+def encode_e4m3(x) -> np.ndarray:
+    """Nearest E4M3FN code of each value, ties to the even code, saturating.
+
+    Finite magnitudes at or above 448 and infinities give +-448 (0x7E / 0xFE),
+    NaN gives 0x7F, and the sign of zero is kept.  Otherwise, with a = |x|:
+    below the smallest normal 2^-6 the code counts multiples of 2^-9 (a
+    subnormal, m = round(a / 2^-9), m = 8 being the smallest normal); else
+    a = (1 + f) * 2^e with e = floor(log2 a), and the 3-bit mantissa is
+    round(f * 8), a carry to 8 moving to the next binade.  Rounding is half to
+    even (np.rint).
+    """
+    x = np.asarray(x, np.float64)
+    out = np.empty(x.shape, np.uint8)
+    flat, res = x.reshape(-1), out.reshape(-1)
+    for k, v in enumerate(flat):
+        if math.isnan(v):
+            res[k] = 0x7F
+            continue
+        sign = 0x80 if math.copysign(1.0, v) < 0 else 0
+        a = abs(v)
+        if a >= 448.0:
+            res[k] = sign | 0x7E
+            continue
+        if a < 2.0 ** -6:
+            m = int(np.rint(a / 2.0 ** -9))          # 0 .. 8; 8 is the smallest normal
+            res[k] = sign | m
+            continue
+        _, e2 = math.frexp(a)                        # a = f * 2^e2, f in [0.5, 1)
+        e = e2 - 1                                   # a in [2^e, 2^(e+1))
+        m = int(np.rint(a / 2.0 ** (e - 3))) - 8     # mantissa in eighths, 0 .. 8
+        if m == 8:
+            e, m = e + 1, 0
+        if e > 8 or (e == 8 and m == 7):             # past 448: saturate
+            res[k] = sign | 0x7E
+            continue
+        res[k] = sign | ((e + 7) << 3) | m
+    return out
+
+
+# ----------------------------------------------------------------------------
+# E4M3 quantisation and the paged cache write [P2 Overview: a fused insert
+# kernel writes the query in E4M3 and the new tokens' K|V into the packed cache
+# pages; P2 Details: the FP8 cache is written with unit scales; P2 script and
+# P4 forward: slot_mapping, one int64 cache slot per token]
+# ----------------------------------------------------------------------------
+def quantize_e4m3(x, scale) -> np.ndarray:
+    """E4M3 codes of x / scale: the quotient taken in float32 (one correctly
+    rounded division), then encode_e4m3.  x: float32 values (bf16 inputs are
+    widened to float32 exactly first)."""
+    q = np.asarray(x, np.float32) / np.float32(scale)
+    return encode_e4m3(q.astype(np.float64))
+
+
+def insert_index_k(k_cache, k, slot_mapping, scale):
+    """Write the index keys of new tokens into the paged index-K cache.
+
+    k_cache: [num_pages, 128, 128] uint8, updated in place.  k: [n, 128]
+    float32.  Token t with slot s = slot_mapping[t] >= 0 goes to row s % 128 of
+    page s // 128; tokens with s < 0 are skipped.
+    """
+    for t, s in enumerate(np.asarray(slot_mapping, np.int64)):
+        if s < 0:
+            continue
+        k_cache[s // PAGE, s % PAGE, :] = quantize_e4m3(k[t], scale)
+    return k_cache
+
+
+def insert_kv(kv_cache, k, v, slot_mapping, k_scale, v_scale):
+    """Write K and V of new tokens into the packed K|V cache.
+
+    kv_cache: [num_pages, Hkv, 128, 256] uint8, updated in place; K takes bytes
+    [..., :128] of a token's row and V bytes [..., 128:] ([P4] forward: the
+    packed page split).  k, v: [n, Hkv, 128] float32.  Token t with slot
+    s >= 0 goes to row s % 128 of page s // 128, every KV head; s < 0 skipped.
+    """
+    for t, s in enumerate(np.asarray(slot_mapping, np.int64)):
+        if s < 0:
+            continue
+        for h in range(k.shape[1]):
+            kv_cache[s // PAGE, h, s % PAGE, :HEAD_DIM] = quantize_e4m3(k[t, h], k_scale)
+            kv_cache[s // PAGE, h, s % PAGE, HEAD_DIM:] = quantize_e4m3(v[t, h], v_scale)
+    return kv_cache
 
 
 # ----------------------------------------------------------------------------
