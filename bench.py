@@ -150,6 +150,65 @@ def cpu_baseline(inp, budget_s):
                       f"float64 numpy oracle index scoring, {dt:.1f} s, scaled linearly by query count"}
 
 
+def time_insert(inp, db, steps, stream):
+    """The cache write for the workload's new tokens, bf16 sources: the index-K
+    insert and the packed K|V insert (every KV head), each launched `steps`
+    times back to back (one graph replay between two events).  Reported beside
+    the path, not in `value`.
+    Runs after the path is timed (it overwrites the new tokens' cache rows)."""
+    import numpy as np
+    import torch
+
+    from fp8_top_page_amd import msa_insert_index_k, msa_insert_kv
+    n = int(inp.total_q)
+    if n == 0:
+        return None
+    # slot of each new token: page pos // 128 of its request through the block table
+    cu_q, cu_k, bt = inp.cu_seqlens_q, inp.cu_seqlens_k, inp.block_table
+    slots = np.empty(n, np.int64)
+    for b in range(len(cu_q) - 1):
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        sk = int(cu_k[b + 1] - cu_k[b])
+        pos = np.arange(sk - (q1 - q0), sk)
+        slots[q0:q1] = bt[b, pos // 128].astype(np.int64) * 128 + pos % 128
+    g = torch.Generator(device="cuda").manual_seed(11)
+    k_idx = torch.randn(n, 128, generator=g, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn(n, db.Hkv, 128, generator=g, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn(n, db.Hkv, 128, generator=g, device="cuda", dtype=torch.bfloat16)
+    slot_t = torch.from_numpy(slots).cuda()
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    calls = [lambda: msa_insert_index_k(k_idx, slot_t, db.ik_scale, db.k_cache, db.num_pages),
+             lambda: msa_insert_kv(k, v, slot_t, one, one, db.kv, db.num_pages, db.Hkv)]
+    # the calls are small next to Python's per-call cost, so `steps` of them are
+    # captured in a HIP graph and one replay is timed
+    us = []
+    for c in calls:
+        for _ in range(3):
+            c()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(steps):
+                c()
+        graph.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us.append(e0.elapsed_time(e1) * 1e3 / steps)
+    # bytes: bf16 source read, E4M3 row written, the int64 slot
+    b_idx = n * (128 * 2 + 128 + 8)
+    b_kv = n * (db.Hkv * 2 * 128 * (2 + 1) + 8)
+    return {"tokens": n, "index_k_us": round(us[0], 2), "kv_us": round(us[1], 2),
+            "index_k_gbs": round(b_idx / (us[0] * 1e-6) / 1e9, 1),
+            "kv_gbs": round(b_kv / (us[1] * 1e-6) / 1e9, 1),
+            "kv_frac_hbm_peak": round(b_kv / (us[1] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "bytes_per_launch": {"index_k": b_idx, "kv": b_kv},
+            "source": "bf16 -> E4M3 through slot_mapping"}
+
+
 def main():
     args = parse()
     if args.copy_probe_mib:
@@ -236,6 +295,7 @@ def main():
 
     sel = path.topk[:, 0, :].cpu().numpy()
     work = algorithmic_work(inp, sel)
+    insert = time_insert(inp, db, args.steps, stream)
     score_us = float(mean_us[0])
     attn_us = float(mean_us[3])
     score_tflops = work["score_flops"] / (score_us * 1e-6) / 1e12
@@ -281,6 +341,7 @@ def main():
         "sparse_prefill_frac_hbm_peak": round(work["attn_bytes"] / (attn_us * 1e-6) / 1e9 /
                                               PEAK_HBM_GBS, 4),
         "topk_gbs": round(work["topk_bytes"] / (float(mean_us[1]) * 1e-6) / 1e9, 1),
+        "cache_insert": insert,
         "work": work,
         "context": {"note": "other hardware, per rank, cold L2; not a target",
                     "gb300_cute_scorer_us": 305, "rubin_cute_scorer_us": 174},

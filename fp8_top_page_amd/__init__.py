@@ -16,6 +16,7 @@ __all__ = [
     "MsaError", "Varlen", "lib", "msa_index_score", "msa_index_score_workspace_size",
     "msa_topk_select", "msa_build_k2q_csr", "msa_k2q_schedule_size", "msa_sparse_attn_prefill",
     "msa_sparse_attn_workspace_size", "msa_status_string", "msa_last_error", "msa_abi_version",
+    "msa_quantize_e4m3", "msa_insert_index_k", "msa_insert_kv",
     "LIB_PATH", "PAGE", "HEAD_DIM", "TOPK",
 ]
 
@@ -72,6 +73,15 @@ def lib():
                                               _c_p, _c_p, _c_i32, _c_p, _c_size, _c_i32, _c_f,
                                               _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_size, _c_p]
         L.msa_sparse_attn_prefill.restype = ctypes.c_int
+        L.msa_quantize_e4m3.argtypes = [_c_p, _c_i32, _c_i64, _c_i32, _c_i64, _c_p, _c_p, _c_i64,
+                                        _c_p]
+        L.msa_quantize_e4m3.restype = ctypes.c_int
+        L.msa_insert_index_k.argtypes = [_c_p, _c_i32, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_i32,
+                                         _c_p]
+        L.msa_insert_index_k.restype = ctypes.c_int
+        L.msa_insert_kv.argtypes = [_c_p, _c_p, _c_i32, _c_i64, _c_i32, _c_i64, _c_i64, _c_p, _c_p,
+                                    _c_p, _c_p, _c_i32, _c_p]
+        L.msa_insert_kv.restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
         L.msa_last_error.argtypes = []
@@ -192,3 +202,42 @@ def msa_sparse_attn_prefill(vl: Varlen, q, num_q_heads, kv_cache, num_pages, num
         out.stride(0), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check(st, "msa_sparse_attn_prefill")
+
+
+_DTYPES = {torch.bfloat16: 0, torch.float32: 1}     # MSA_DTYPE_BF16, MSA_DTYPE_F32
+
+
+def _src_dtype(t):
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"source must be bfloat16 or float32, got {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def msa_quantize_e4m3(src, scale, dst, stream=None):
+    """src: bf16/f32 [n, heads*128] (or [n, heads, 128]), rows contiguous; dst: uint8 same shape."""
+    n = src.shape[0]
+    inner = 1
+    for d in src.shape[1:]:
+        inner *= d
+    heads = max(1, inner // HEAD_DIM)
+    st = lib().msa_quantize_e4m3(_ptr(src), _src_dtype(src), n, heads, src.stride(0), _ptr(scale),
+                                 _ptr(dst), dst.stride(0), _stream(stream))
+    _check(st, "msa_quantize_e4m3")
+
+
+def msa_insert_index_k(k, slot_mapping, scale, k_cache, num_pages, stream=None):
+    """k: bf16/f32 [n_tokens, 128]; slot_mapping: int64 [n_tokens]; k_cache: uint8 [pages, 128, 128]."""
+    st = lib().msa_insert_index_k(_ptr(k), _src_dtype(k), k.shape[0], k.stride(0),
+                                  _ptr(slot_mapping), _ptr(scale), _ptr(k_cache), num_pages,
+                                  _stream(stream))
+    _check(st, "msa_insert_index_k")
+
+
+def msa_insert_kv(k, v, slot_mapping, k_scale, v_scale, kv_cache, num_pages, num_kv_heads,
+                  stream=None):
+    """k, v: bf16/f32 [n_tokens, Hkv, 128] (heads contiguous); kv_cache: uint8 [pages, Hkv, 128, 256]."""
+    st = lib().msa_insert_kv(_ptr(k), _ptr(v), _src_dtype(k), k.shape[0], num_kv_heads,
+                             k.stride(0), v.stride(0), _ptr(slot_mapping), _ptr(k_scale),
+                             _ptr(v_scale), _ptr(kv_cache), num_pages, _stream(stream))
+    _check(st, "msa_insert_kv")
+

@@ -13,7 +13,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
-SOURCES = ["msa_api.hip", "index_score.hip", "topk_select.hip", "k2q_csr.hip", "sparse_attn.hip"]
+SOURCES = ["msa_api.hip", "index_score.hip", "topk_select.hip", "k2q_csr.hip", "sparse_attn.hip",
+           "quantize_insert.hip"]
 ARCH = os.environ.get("MSA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

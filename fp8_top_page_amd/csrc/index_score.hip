@@ -318,13 +318,16 @@ __device__ __forceinline__ v8i load_frag_swz(const uint8_t* row, const Swz& z) {
 }
 
 // Max over one page's 128 tokens for every resident query tile.  A fragments
-// (16 tokens x 128 bytes) are read from LDS one tile ahead of their products.
+// (16 tokens x 128 bytes) are read from LDS one tile ahead of their products,
+// and the max of each product is taken one product later (after the next one
+// is issued), so the wave does not stall on the matrix-core latency.
 template <int H, int NQT>
 __device__ __forceinline__ void page_max(const uint8_t* __restrict__ pg, const v8i (&qf)[NQT][H],
                                          int col, const Swz& z, v4f (&rmax)[NQT]) {
 #pragma unroll
   for (int n = 0; n < NQT; ++n) rmax[n] = v4f{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   v8i a_cur = load_frag_swz(pg + col * kDim, z);
+  v4f prev;
 #pragma unroll
   for (int T = 0; T < 8; ++T) {
     v8i a_nxt;
@@ -334,11 +337,17 @@ __device__ __forceinline__ void page_max(const uint8_t* __restrict__ pg, const v
       v4f acc = mfma_e4m3(a_cur, qf[n][0], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int h = 1; h < H; ++h) acc = mfma_e4m3(a_cur, qf[n][h], acc);
+      if (T > 0 || n > 0) {
+        const int pn = n > 0 ? n - 1 : NQT - 1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rmax[n][i] = fmaxf(rmax[n][i], acc[i]);
+        for (int i = 0; i < 4; ++i) rmax[pn][i] = fmaxf(rmax[pn][i], prev[i]);
+      }
+      prev = acc;
     }
     if (T < 7) a_cur = a_nxt;
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rmax[NQT - 1][i] = fmaxf(rmax[NQT - 1][i], prev[i]);
 }
 
 // Same with the causal cut: token (16T + 4*grp + i) of the page counts for the

@@ -255,4 +255,132 @@ msa_status_t msa_sparse_attn_prefill(const msa_varlen_t* vl, const uint8_t* q, i
   return MSA_OK;
 }
 
+
+// ---- E4M3 quantisation and the paged cache write ---------------------------
+
+namespace {
+
+msa_status_t check_src(const void* p, int32_t dtype, int64_t stride, int64_t min_stride,
+                       const char* name) {
+  MSA_CHECK(dtype == MSA_DTYPE_BF16 || dtype == MSA_DTYPE_F32, MSA_ERR_UNSUPPORTED,
+            "%s: src_dtype must be MSA_DTYPE_BF16 or MSA_DTYPE_F32 (got %d)", name, dtype);
+  MSA_CHECK(p != nullptr, MSA_ERR_INVALID_ARGUMENT, "%s: NULL source", name);
+  MSA_CHECK(aligned(p, 16), MSA_ERR_INVALID_ARGUMENT, "%s: source must be 16-byte aligned", name);
+  MSA_CHECK(stride >= min_stride && stride % 8 == 0, MSA_ERR_INVALID_ARGUMENT,
+            "%s: stride (%lld) must be >= %lld elements and a multiple of 8", name,
+            (long long)stride, (long long)min_stride);
+  return MSA_OK;
+}
+
+msa_status_t run_quantize(const QuantArgs& q, void* stream, const char* name) {
+  msa_status_t st = check_device();
+  if (st != MSA_OK) return st;
+  hipError_t e = launch_quantize(q, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, name);
+  return MSA_OK;
+}
+
+constexpr int64_t kMaxQuantRows = (int64_t)UINT32_MAX * 16;   // grid x limit of the row kernel
+
+}  // namespace
+
+msa_status_t msa_quantize_e4m3(const void* src, int32_t src_dtype, int64_t n_rows, int32_t heads,
+                               int64_t src_stride, const float* scale, uint8_t* dst,
+                               int64_t dst_stride, void* stream) {
+  MSA_CHECK(n_rows >= 0 && heads >= 1, MSA_ERR_INVALID_ARGUMENT,
+            "msa_quantize_e4m3: n_rows must be >= 0 and heads >= 1");
+  MSA_CHECK(n_rows * heads <= kMaxQuantRows, MSA_ERR_UNSUPPORTED, "msa_quantize_e4m3: too many rows");
+  if (n_rows == 0) return MSA_OK;
+  msa_status_t st = check_src(src, src_dtype, src_stride, (int64_t)heads * kDim, "msa_quantize_e4m3");
+  if (st != MSA_OK) return st;
+  MSA_CHECK(scale && dst, MSA_ERR_INVALID_ARGUMENT, "msa_quantize_e4m3: NULL scale or dst");
+  MSA_CHECK(aligned(dst, 8) && dst_stride >= (int64_t)heads * kDim && dst_stride % 8 == 0,
+            MSA_ERR_INVALID_ARGUMENT,
+            "msa_quantize_e4m3: dst must be 8-byte aligned, dst_stride >= heads*128 and a multiple of 8");
+  QuantArgs q{};
+  q.n_parts = 1;
+  q.src[0] = q.src[1] = src;
+  q.scale[0] = q.scale[1] = scale;
+  q.dtype = src_dtype;
+  q.n_tokens = n_rows;
+  q.heads = heads;
+  q.src_tok_stride[0] = q.src_tok_stride[1] = src_stride;
+  q.src_head_stride = kDim;
+  q.dst = dst;
+  q.dst_tok_stride = dst_stride;
+  q.dst_head_stride = kDim;
+  return run_quantize(q, stream, "msa_quantize_e4m3");
+}
+
+msa_status_t msa_insert_index_k(const void* k, int32_t src_dtype, int64_t n_tokens,
+                                int64_t k_stride, const int64_t* slot_mapping, const float* scale,
+                                uint8_t* k_cache, int32_t num_pages, void* stream) {
+  MSA_CHECK(n_tokens >= 0, MSA_ERR_INVALID_ARGUMENT, "msa_insert_index_k: n_tokens must be >= 0");
+  MSA_CHECK(n_tokens <= kMaxQuantRows, MSA_ERR_UNSUPPORTED, "msa_insert_index_k: too many tokens");
+  if (n_tokens == 0) return MSA_OK;
+  msa_status_t st = check_src(k, src_dtype, k_stride, kDim, "msa_insert_index_k");
+  if (st != MSA_OK) return st;
+  MSA_CHECK(slot_mapping && scale && k_cache, MSA_ERR_INVALID_ARGUMENT,
+            "msa_insert_index_k: NULL slot_mapping, scale or k_cache");
+  MSA_CHECK(aligned(k_cache, 8) && num_pages >= 1, MSA_ERR_INVALID_ARGUMENT,
+            "msa_insert_index_k: k_cache must be 8-byte aligned and num_pages >= 1");
+  QuantArgs q{};
+  q.n_parts = 1;
+  q.src[0] = q.src[1] = k;
+  q.scale[0] = q.scale[1] = scale;
+  q.dtype = src_dtype;
+  q.n_tokens = n_tokens;
+  q.heads = 1;
+  q.src_tok_stride[0] = q.src_tok_stride[1] = k_stride;
+  q.src_head_stride = kDim;
+  q.slots = slot_mapping;
+  q.max_slot = (int64_t)num_pages * kPage;
+  q.dst = k_cache;
+  q.dst_page_stride = (int64_t)kPage * kDim;
+  q.dst_row_stride = kDim;
+  return run_quantize(q, stream, "msa_insert_index_k");
+}
+
+msa_status_t msa_insert_kv(const void* k, const void* v, int32_t src_dtype, int64_t n_tokens,
+                           int32_t num_kv_heads, int64_t k_stride, int64_t v_stride,
+                           const int64_t* slot_mapping, const float* k_scale,
+                           const float* v_scale, uint8_t* kv_cache, int32_t num_pages,
+                           void* stream) {
+  MSA_CHECK(n_tokens >= 0 && num_kv_heads >= 1, MSA_ERR_INVALID_ARGUMENT,
+            "msa_insert_kv: n_tokens must be >= 0 and num_kv_heads >= 1");
+  MSA_CHECK(n_tokens * num_kv_heads <= kMaxQuantRows, MSA_ERR_UNSUPPORTED,
+            "msa_insert_kv: too many rows");
+  if (n_tokens == 0) return MSA_OK;
+  const int64_t min_stride = (int64_t)num_kv_heads * kDim;
+  msa_status_t st = check_src(k, src_dtype, k_stride, min_stride, "msa_insert_kv (k)");
+  if (st != MSA_OK) return st;
+  st = check_src(v, src_dtype, v_stride, min_stride, "msa_insert_kv (v)");
+  if (st != MSA_OK) return st;
+  MSA_CHECK(slot_mapping && k_scale && v_scale && kv_cache, MSA_ERR_INVALID_ARGUMENT,
+            "msa_insert_kv: NULL slot_mapping, scale or kv_cache");
+  MSA_CHECK(aligned(kv_cache, 8) && num_pages >= 1, MSA_ERR_INVALID_ARGUMENT,
+            "msa_insert_kv: kv_cache must be 8-byte aligned and num_pages >= 1");
+  QuantArgs q{};
+  q.n_parts = 2;
+  q.src[0] = k;
+  q.src[1] = v;
+  q.scale[0] = k_scale;
+  q.scale[1] = v_scale;
+  q.col_off[0] = 0;
+  q.col_off[1] = kDim;
+  q.dtype = src_dtype;
+  q.n_tokens = n_tokens;
+  q.heads = num_kv_heads;
+  q.src_tok_stride[0] = k_stride;
+  q.src_tok_stride[1] = v_stride;
+  q.src_head_stride = kDim;
+  q.slots = slot_mapping;
+  q.max_slot = (int64_t)num_pages * kPage;
+  q.dst = kv_cache;
+  q.dst_page_stride = (int64_t)num_kv_heads * kPage * 2 * kDim;
+  q.dst_head_stride = (int64_t)kPage * 2 * kDim;
+  q.dst_row_stride = 2 * kDim;
+  return run_quantize(q, stream, "msa_insert_kv");
+}
+
 }  // extern "C"

@@ -115,6 +115,23 @@ struct AttnArgs {
 size_t attn_workspace_bytes(const msa_varlen_t* vl, int Hq, int Hkv, int n_sel, int topk);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);
 
+// ---- E4M3 quantisation / paged cache write ----------------------------------
+struct QuantArgs {
+  int n_parts;               // 1, or 2 (K and V of the packed cache)
+  const void* src[2];
+  const float* scale[2];
+  int64_t col_off[2];        // destination byte offset inside a row, per part
+  int dtype;
+  int64_t n_tokens;
+  int heads;
+  int64_t src_tok_stride[2], src_head_stride;   // elements
+  const int64_t* slots;      // nullptr: linear destination
+  int64_t max_slot;
+  uint8_t* dst;
+  int64_t dst_tok_stride, dst_page_stride, dst_head_stride, dst_row_stride;   // bytes
+};
+hipError_t launch_quantize(const QuantArgs& q, hipStream_t stream);
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -192,12 +192,59 @@ msa_status_t msa_sparse_attn_prefill(const msa_varlen_t* vl, const uint8_t* q, i
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * 5. E4M3 quantisation and the paged cache write: the step just before the
+ *    path ([P2] Overview: a fused insert kernel writes the query in E4M3 and
+ *    the new tokens' K|V into the packed cache pages; [P2] Details: the FP8
+ *    cache is written with unit scales; [P2] script and [P4] forward:
+ *    slot_mapping, one int64 cache slot per token).
+ *
+ * Every element becomes the E4M3 code nearest to x / scale, the quotient taken
+ * as one correctly rounded fp32 division, ties to the even code, saturating:
+ * finite values beyond +-448 and +-inf give +-448, NaN gives 0x7F, the sign of
+ * zero is kept.  (The pages state neither rounding nor overflow; this is the
+ * reading the library implements.)
+ *
+ *   src_dtype  MSA_DTYPE_BF16 or MSA_DTYPE_F32; source rows of 128 elements,
+ *              strides in elements, multiples of 8, base 16-byte aligned
+ *   scale      device fp32 scalar
+ *   slot_mapping  [n_tokens] int64: token t goes to row s % 128 of physical page
+ *              s / 128 (s = slot_mapping[t]); tokens with s < 0 are skipped, and
+ *              so are slots >= num_pages * 128.  Distinct tokens must have
+ *              distinct slots (otherwise which token's bytes land is unspecified).
+ *
+ * msa_quantize_e4m3: src [n_rows, heads, 128] -> dst [n_rows, heads, 128] E4M3,
+ *   dst row stride dst_stride bytes (>= heads * 128, multiple of 8, base 8-byte
+ *   aligned), heads contiguous.  For the attention and index queries.
+ * msa_insert_index_k: k [n_tokens, 128] (token stride k_stride) into
+ *   k_cache [num_pages, 128, 128] (the index-K layout of section 1).
+ * msa_insert_kv: k, v [n_tokens, Hkv, 128] (token strides k_stride / v_stride,
+ *   heads contiguous) into kv_cache [num_pages, Hkv, 128, 256]: K to bytes
+ *   [..., 0:128] and V to [..., 128:256] of the token's row (the packed page of
+ *   section 4), with k_scale and v_scale.
+ * Rows of the caches that no token maps to are left as they are.
+ * ------------------------------------------------------------------------- */
+typedef enum { MSA_DTYPE_BF16 = 0, MSA_DTYPE_F32 = 1 } msa_dtype_t;
+
+msa_status_t msa_quantize_e4m3(const void* src, int32_t src_dtype, int64_t n_rows,
+                               int32_t heads, int64_t src_stride, const float* scale,
+                               uint8_t* dst, int64_t dst_stride, void* stream);
+msa_status_t msa_insert_index_k(const void* k, int32_t src_dtype, int64_t n_tokens,
+                                int64_t k_stride, const int64_t* slot_mapping,
+                                const float* scale, uint8_t* k_cache, int32_t num_pages,
+                                void* stream);
+msa_status_t msa_insert_kv(const void* k, const void* v, int32_t src_dtype, int64_t n_tokens,
+                           int32_t num_kv_heads, int64_t k_stride, int64_t v_stride,
+                           const int64_t* slot_mapping, const float* k_scale,
+                           const float* v_scale, uint8_t* kv_cache, int32_t num_pages,
+                           void* stream);
+
+/* ---------------------------------------------------------------------------
  * Diagnostics.
  * ------------------------------------------------------------------------- */
 const char* msa_status_string(msa_status_t status);  /* static string */
 const char* msa_last_error(void);   /* thread-local detail of this thread's last failed call */
 int32_t msa_abi_version(void);      /* MSA_ABI_VERSION */
-#define MSA_ABI_VERSION 1
+#define MSA_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

@@ -137,7 +137,8 @@ def quantize_e4m3(x, scale) -> np.ndarray:
     """E4M3 codes of x / scale: the quotient taken in float32 (one correctly
     rounded division), then encode_e4m3.  x: float32 values (bf16 inputs are
     widened to float32 exactly first)."""
-    q = np.asarray(x, np.float32) / np.float32(scale)
+    with np.errstate(invalid="ignore", over="ignore"):     # inf / NaN inputs are expected
+        q = np.asarray(x, np.float32) / np.float32(scale)
     return encode_e4m3(q.astype(np.float64))
 
 

@@ -33,10 +33,11 @@ def test_library_exports_every_declared_symbol():
     assert names == sorted([
         "msa_index_score_workspace_size", "msa_index_score", "msa_topk_select",
         "msa_k2q_schedule_size", "msa_build_k2q_csr", "msa_sparse_attn_workspace_size",
-        "msa_sparse_attn_prefill", "msa_status_string", "msa_last_error", "msa_abi_version"]), names
+        "msa_sparse_attn_prefill", "msa_status_string", "msa_last_error", "msa_abi_version",
+        "msa_quantize_e4m3", "msa_insert_index_k", "msa_insert_kv"]), names
     for n in names:
         assert hasattr(L, n), n
-    assert msa.msa_abi_version() == 1
+    assert msa.msa_abi_version() == 2
 
 
 def test_status_strings():
@@ -176,3 +177,42 @@ def test_pipeline_marshalling_on_host_buffers():
                 step()
             except msa.MsaError as e:
                 assert e.status == NO_DEV, e
+
+
+def test_quantize_and_insert_validation():
+    L = msa.lib()
+    BF16, F32 = 0, 1
+    q = lambda src=FAKE, dt=BF16, n=4, heads=2, ss=256, sc=FAKE, dst=FAKE, ds=256: \
+        L.msa_quantize_e4m3(src, dt, n, heads, ss, sc, dst, ds, None)
+    assert q(n=0) == OK                       # nothing to do
+    assert q(dt=2) == UNSUPPORTED             # not bf16 / f32
+    assert q(n=-1) == INVALID
+    assert q(heads=0) == INVALID
+    assert q(src=None) == INVALID
+    assert q(src=FAKE + 8) == INVALID         # source not 16-byte aligned
+    assert q(ss=128) == INVALID               # < heads * 128
+    assert q(ss=260) == INVALID               # not a multiple of 8
+    assert q(sc=None) == INVALID
+    assert q(dst=FAKE + 4) == INVALID         # dst not 8-byte aligned
+    assert q(ds=200) == INVALID
+    if NO_GPU:                                # validation passes: only reachable without a GPU
+        assert q() == NO_DEV
+    ik = lambda k=FAKE, dt=F32, n=3, ks=128, slots=FAKE, sc=FAKE, cache=FAKE, pages=2: \
+        L.msa_insert_index_k(k, dt, n, ks, slots, sc, cache, pages, None)
+    assert ik(n=0) == OK
+    assert ik(ks=64) == INVALID
+    assert ik(slots=None) == INVALID
+    assert ik(pages=0) == INVALID
+    assert ik(dt=7) == UNSUPPORTED
+    if NO_GPU:
+        assert ik() == NO_DEV
+    kv = lambda k=FAKE, v=FAKE, dt=BF16, n=3, hkv=2, ks=256, vs=256, slots=FAKE, cache=FAKE, pages=2: \
+        L.msa_insert_kv(k, v, dt, n, hkv, ks, vs, slots, FAKE, FAKE, cache, pages, None)
+    assert kv(n=0) == OK
+    assert kv(hkv=0) == INVALID
+    assert kv(v=None) == INVALID
+    assert kv(vs=128) == INVALID              # < Hkv * 128
+    assert kv(cache=FAKE + 2) == INVALID
+    if NO_GPU:
+        assert kv() == NO_DEV
+
