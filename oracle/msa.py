@@ -38,6 +38,10 @@ Pins (each function is checked by tests against something other than itself):
       explicit mask) when the selection covers every visible page, closed forms
       (constant V, one visible token, all-zero K gives the mean of V).
   round_bf16    -- torch's bfloat16 cast on random and tie values.
+  e2m1_table / e8m0_value / decode_mxfp4 / encode_e2m1 / quantize_mxfp4 --
+      the E2M1 value list by hand (tests/golden), torch's E8M0 decode, every
+      code round-trips, ties to even, exact blocks reproduce their codes,
+      scale choice and saturation by worked values.
   encode_e4m3 / quantize_e4m3 / insert_* -- every finite code round-trips,
       midpoints between neighbouring codes go to the even code, values just off
       a midpoint go to the nearer code, torch.float8_e4m3fn's CPU cast inside
@@ -128,6 +132,107 @@ def encode_e4m3(x) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# MXFP4 index keys (OCP Microscaling MXFP4: blocks of 32 E2M1 elements sharing
+# one E8M0 power-of-two scale) -- the gfx950 analogue of the pages' 4-bit index
+# cache [P3 Details: NVFP4 index cache, FP8 query times FP4 key ("Q8KV4")]
+# ----------------------------------------------------------------------------
+class Mxfp4Keys:
+    """An MXFP4 index-K cache: data [num_pages, 128, 64] (element 2i of a row in
+    the low nibble of byte i, 2i + 1 in the high nibble) and scales
+    [num_pages, 128, 4] E8M0 (block k covers elements 32k .. 32k + 31)."""
+
+    def __init__(self, data, scales):
+        self.data = np.asarray(data, np.uint8)
+        self.scales = np.asarray(scales, np.uint8)
+
+
+def e2m1_table() -> np.ndarray:
+    """Value of each of the 16 E2M1 codes: sign = bit 3, exponent = bits 2..1
+    (bias 1), mantissa = bit 0; exponent 0 is subnormal m * 0.5, otherwise
+    (1 + m/2) * 2^(e-1).  No inf, no NaN; the largest magnitude is 6."""
+    vals = np.empty(16, np.float64)
+    for code in range(16):
+        sign = -1.0 if code & 8 else 1.0
+        e, m = (code >> 1) & 3, code & 1
+        vals[code] = sign * (m * 0.5 if e == 0 else (1.0 + m / 2.0) * 2.0 ** (e - 1))
+    return vals
+
+
+_E2M1 = e2m1_table()
+
+
+def e8m0_value(codes) -> np.ndarray:
+    """E8M0 scale codes: 2^(code - 127); 0xFF is NaN."""
+    c = np.asarray(codes, np.int64)
+    return np.where(c == 0xFF, np.nan, np.ldexp(1.0, c - 127))
+
+
+def decode_mxfp4(data, scales) -> np.ndarray:
+    """[..., 64] data bytes and [..., 4] scales -> [..., 128] float64 values."""
+    data = np.asarray(data, np.uint8)
+    codes = np.stack([data & 15, data >> 4], axis=-1).reshape(*data.shape[:-1], 2 * data.shape[-1])
+    blocks = _E2M1[codes].reshape(*data.shape[:-1], -1, 32)
+    out = blocks * e8m0_value(scales)[..., None]
+    return out.reshape(*data.shape[:-1], -1)
+
+
+def encode_e2m1(v) -> np.ndarray:
+    """Nearest E2M1 code of each value, ties to the even code (mantissa bit 0),
+    saturating at +-6; the sign of zero is kept."""
+    v = np.asarray(v, np.float64)
+    mags = _E2M1[:8]                                   # 0, .5, 1, 1.5, 2, 3, 4, 6
+    out = np.empty(v.shape, np.uint8)
+    flat, res = v.reshape(-1), out.reshape(-1)
+    for k, x in enumerate(flat):
+        sign = 8 if math.copysign(1.0, x) < 0 else 0
+        a = min(abs(x), 6.0)
+        d = np.abs(mags - a)
+        best = np.nonzero(d == d.min())[0]
+        code = int(best[0]) if len(best) == 1 else int(best[best % 2 == 0][0])
+        res[k] = sign | code
+    return out
+
+
+def quantize_mxfp4(x):
+    """MXFP4 of rows of 128 values (OCP Microscaling conversion): per block of
+    32, the shared exponent is floor(log2(max |v|)) - 2 (2 being the exponent of
+    E2M1's largest value, 6 = 1.5 * 2^2), clamped to [-127, 127] (a block of
+    zeros takes -127); elements are encode_e2m1(v / 2^exponent), which
+    saturates.  A block holding NaN gets scale 0xFF and zero elements.
+    Returns (data [..., 64], scales [..., 4])."""
+    x = np.asarray(x, np.float64)
+    lead = x.shape[:-1]
+    blocks = x.reshape(*lead, 4, 32)
+    scales = np.empty((*lead, 4), np.uint8)
+    codes = np.empty((*lead, 4, 32), np.uint8)
+    for idx in np.ndindex(*lead, 4):
+        blk = blocks[idx]
+        if np.isnan(blk).any():
+            scales[idx] = 0xFF
+            codes[idx] = 0
+            continue
+        amax = float(np.abs(blk).max())
+        e = -127 if amax == 0.0 else min(127, max(-127, math.frexp(amax)[1] - 1 - 2))
+        scales[idx] = e + 127
+        codes[idx] = encode_e2m1(np.ldexp(blk, -e))
+    c = codes.reshape(*lead, 64, 2)
+    data = (c[..., 0] | (c[..., 1] << 4)).astype(np.uint8)
+    return data, scales
+
+
+def insert_index_k_mxfp4(cache: Mxfp4Keys, k, slot_mapping):
+    """Write index keys of new tokens into an MXFP4 index cache (in place):
+    token t with slot s >= 0 goes to row s % 128 of page s // 128."""
+    for t, s in enumerate(np.asarray(slot_mapping, np.int64)):
+        if s < 0:
+            continue
+        d, sc = quantize_mxfp4(np.asarray(k[t], np.float32).astype(np.float64)[None])
+        cache.data[s // PAGE, s % PAGE] = d[0]
+        cache.scales[s // PAGE, s % PAGE] = sc[0]
+    return cache
+
+
+# ----------------------------------------------------------------------------
 # E4M3 quantisation and the paged cache write [P2 Overview: a fused insert
 # kernel writes the query in E4M3 and the new tokens' K|V into the packed cache
 # pages; P2 Details: the FP8 cache is written with unit scales; P2 script and
@@ -197,11 +302,15 @@ def query_positions(cu_q: np.ndarray, cu_k: np.ndarray):
 
 
 def _request_keys(k_cache, block_table, b, seqlen_k):
-    """Logical index-K rows [seqlen_k, 128] of request b, decoded (float64)."""
+    """Logical index-K rows [seqlen_k, 128] of request b, decoded (float64):
+    E4M3 bytes [num_pages, 128, 128], or an Mxfp4Keys cache."""
     n_pages = (seqlen_k + PAGE - 1) // PAGE
     phys = np.asarray(block_table[b, :n_pages], np.int64)
-    rows = decode_e4m3(k_cache[phys]).reshape(n_pages * PAGE, HEAD_DIM)
-    return rows[:seqlen_k]
+    if isinstance(k_cache, Mxfp4Keys):
+        rows = decode_mxfp4(k_cache.data[phys], k_cache.scales[phys])
+    else:
+        rows = decode_e4m3(k_cache[phys])
+    return rows.reshape(n_pages * PAGE, HEAD_DIM)[:seqlen_k]
 
 
 # ----------------------------------------------------------------------------
@@ -221,7 +330,8 @@ def index_scores(cu_q, cu_k, block_table, index_q, k_cache, q_scale, k_scale,
     128 B per token), read through the block table, and only causally visible
     tokens counted.  Pages j >= pos_i // 128 + 1 are not visible.
 
-    index_q: [total_q, H, 128] E4M3 bytes.  k_cache: [num_pages, 128, 128] bytes.
+    index_q: [total_q, H, 128] E4M3 bytes.  k_cache: [num_pages, 128, 128] E4M3
+    bytes, or an Mxfp4Keys cache (values = E2M1 element * 2^(scale - 127)).
     queries: optional list of global query indices (default: all).
     Returns [len(queries), width] with width = max pages per request by default.
     """
