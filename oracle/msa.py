@@ -198,7 +198,8 @@ def quantize_mxfp4(x):
     32, the shared exponent is floor(log2(max |v|)) - 2 (2 being the exponent of
     E2M1's largest value, 6 = 1.5 * 2^2), clamped to [-127, 127] (a block of
     zeros takes -127); elements are encode_e2m1(v / 2^exponent), which
-    saturates.  A block holding NaN gets scale 0xFF and zero elements.
+    saturates.  A block holding NaN or an infinity gets scale 0xFF (NaN) and
+    zero elements.
     Returns (data [..., 64], scales [..., 4])."""
     x = np.asarray(x, np.float64)
     lead = x.shape[:-1]
@@ -207,7 +208,7 @@ def quantize_mxfp4(x):
     codes = np.empty((*lead, 4, 32), np.uint8)
     for idx in np.ndindex(*lead, 4):
         blk = blocks[idx]
-        if np.isnan(blk).any():
+        if not np.isfinite(blk).all():
             scales[idx] = 0xFF
             codes[idx] = 0
             continue

@@ -63,6 +63,9 @@ def test_block_scale_choice_clamp_and_nan():
     nan_block[40] = np.nan
     d, s = oracle.quantize_mxfp4(nan_block.reshape(1, 128))
     assert s[0].tolist() == [0, 0xFF, 0, 0] and np.all(d[0, 16:32] == 0)
+    inf_block = np.concatenate([z + 1, z, z, z])
+    inf_block[3] = -np.inf
+    assert oracle.quantize_mxfp4(inf_block.reshape(1, 128))[1][0].tolist() == [0xFF, 0, 0, 0]
 
 
 def test_exact_blocks_reproduce_their_codes():
