@@ -16,7 +16,8 @@ __all__ = [
     "MsaError", "Varlen", "lib", "msa_index_score", "msa_index_score_workspace_size",
     "msa_topk_select", "msa_build_k2q_csr", "msa_k2q_schedule_size", "msa_sparse_attn_prefill",
     "msa_sparse_attn_workspace_size", "msa_status_string", "msa_last_error", "msa_abi_version",
-    "msa_quantize_e4m3", "msa_insert_index_k", "msa_insert_kv",
+    "msa_quantize_e4m3", "msa_insert_index_k", "msa_insert_kv", "msa_index_score_mxfp4",
+    "msa_insert_index_k_mxfp4",
     "LIB_PATH", "PAGE", "HEAD_DIM", "TOPK",
 ]
 
@@ -82,6 +83,12 @@ def lib():
         L.msa_insert_kv.argtypes = [_c_p, _c_p, _c_i32, _c_i64, _c_i32, _c_i64, _c_i64, _c_p, _c_p,
                                     _c_p, _c_p, _c_i32, _c_p]
         L.msa_insert_kv.restype = ctypes.c_int
+        L.msa_index_score_mxfp4.argtypes = [vp, _c_p, _c_i64, _c_i32, _c_p, _c_p, _c_i32, _c_p,
+                                            _c_p, _c_p, _c_i64, _c_p, _c_size, _c_p]
+        L.msa_index_score_mxfp4.restype = ctypes.c_int
+        L.msa_insert_index_k_mxfp4.argtypes = [_c_p, _c_i32, _c_i64, _c_i64, _c_p, _c_p, _c_p,
+                                               _c_i32, _c_p]
+        L.msa_insert_index_k_mxfp4.restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
         L.msa_last_error.argtypes = []
@@ -240,4 +247,22 @@ def msa_insert_kv(k, v, slot_mapping, k_scale, v_scale, kv_cache, num_pages, num
                              k.stride(0), v.stride(0), _ptr(slot_mapping), _ptr(k_scale),
                              _ptr(v_scale), _ptr(kv_cache), num_pages, _stream(stream))
     _check(st, "msa_insert_kv")
+
+
+def msa_index_score_mxfp4(vl: Varlen, q, num_index_heads, k_data, k_scales, num_pages, q_scale,
+                          k_scale, scores, workspace, stream=None):
+    """msa_index_score over MXFP4 keys: k_data uint8 [pages, 128, 64], k_scales uint8 [pages, 128, 4]."""
+    st = lib().msa_index_score_mxfp4(vl.ref, _ptr(q), q.stride(0), num_index_heads, _ptr(k_data),
+                                     _ptr(k_scales), num_pages, _ptr(q_scale), _ptr(k_scale),
+                                     _ptr(scores), scores.stride(0), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "msa_index_score_mxfp4")
+
+
+def msa_insert_index_k_mxfp4(k, slot_mapping, k_data, k_scales, num_pages, stream=None):
+    """k: bf16/f32 [n_tokens, 128]; k_data uint8 [pages, 128, 64]; k_scales uint8 [pages, 128, 4]."""
+    st = lib().msa_insert_index_k_mxfp4(_ptr(k), _src_dtype(k), k.shape[0], k.stride(0),
+                                        _ptr(slot_mapping), _ptr(k_data), _ptr(k_scales),
+                                        num_pages, _stream(stream))
+    _check(st, "msa_insert_index_k_mxfp4")
 

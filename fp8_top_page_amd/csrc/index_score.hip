@@ -66,6 +66,7 @@ struct ScoreK {
   int64_t ld;
   const ItemHdr* hdr;
   const int4* items;
+  const uint8_t* k_scales;   // MXFP4 keys: [num_pages, 128, 4] E8M0 block scales
 };
 
 // ---------------------------------------------------------------------------
@@ -317,6 +318,65 @@ __device__ __forceinline__ v8i load_frag_swz(const uint8_t* row, const Swz& z) {
   return r;
 }
 
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
+// l's bytes land at LDS byte address lds_addr + 16 l (lds_addr wave-uniform,
+// passed in M0).  Inline assembly keeps the copy out of the compiler's
+// wait-count bookkeeping, which cannot tell the ring slots apart and would
+// otherwise wait for every copy in flight before each LDS read; the kernel's own
+// vmcnt waits and barriers order copies and reads.  (Counters retire in issue
+// order, so copies the compiler does not know of only lengthen the waits it
+// places for other loads.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               ::"v"(src), "s"(lds_addr)
+               : "m0");
+}
+#pragma clang diagnostic pop
+
+// MXFP4 keys (E2M1 pairs, element 2i in the low nibble of byte i, and one E8M0
+// scale per 32-element block).  A page slot holds 128 rows of 64 bytes, the
+// 16-byte piece c of row t (one block) at position c ^ ((t >> 2) & 3) (rows
+// 4 apart share banks, so four consecutive row quads take four different
+// pieces), then the 512 scale bytes, 4 per row.  The scaled matrix-core op
+// (v_mfma_scale_f32_16x16x128_f8f6f4, A = E2M1, B = E4M3) pairs lane group g's
+// 32 nibbles (its A block) with query bytes [16g, 16g + 16) and
+// [64 + 16g, 80 + 16g) of the B lane group g, and multiplies the lane's A
+// products by 2^(scale - 127) (probed on gfx950; the upper four A registers are
+// not read).
+constexpr int kF4Data = kPage * 64;            // 8 KiB of E2M1 pairs per page
+constexpr int kF4Slot = kF4Data + kPage * 4;   // + 512 B of scales
+__device__ __forceinline__ int f4_piece(int col, int grp) {   // byte offset of the lane's piece
+  return 16 * (grp ^ ((col >> 2) & 3));
+}
+__device__ __forceinline__ v8i load_frag_f4(const uint8_t* row, int off) {
+  const uint4 x = *reinterpret_cast<const uint4*>(row + off);
+  v8i r;
+  r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
+  r[4] = x.x; r[5] = x.y; r[6] = x.z; r[7] = x.w;     // not read by the op
+  return r;
+}
+// Query fragment for MXFP4 keys: bytes [16g, 16g + 16) and [64 + 16g, 80 + 16g).
+__device__ __forceinline__ v8i load_qfrag_f4(const uint8_t* q, int grp) {
+  const uint4 x = *reinterpret_cast<const uint4*>(q + 16 * grp);
+  const uint4 y = *reinterpret_cast<const uint4*>(q + 64 + 16 * grp);
+  v8i r;
+  r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
+  r[4] = y.x; r[5] = y.y; r[6] = y.z; r[7] = y.w;
+  return r;
+}
+__device__ __forceinline__ v4f mfma_f4_e4m3(const v8i& a, const v8i& b, const v4f& c, int scale_a) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, scale_a, 0, 127);
+}
+// The lane's A fragment and scale of token tile T of an MXFP4 page slot.
+__device__ __forceinline__ v8i f4_frag(const uint8_t* pg, int T, int col, int off) {
+  return load_frag_f4(pg + (T * 16 + col) * 64, off);
+}
+__device__ __forceinline__ int f4_scale(const uint8_t* pg, int T, int col, int grp) {
+  return pg[kF4Data + (T * 16 + col) * 4 + grp];
+}
+
 // Max over one page's 128 tokens for every resident query tile.  A fragments
 // (16 tokens x 128 bytes) are read from LDS one tile ahead of their products,
 // and the max of each product is taken one product later (after the next one
@@ -378,19 +438,85 @@ __device__ __forceinline__ void page_max_causal(const uint8_t* __restrict__ pg,
   }
 }
 
+// The same two page maxima over an MXFP4 page slot (scaled matrix-core op).
+template <int H, int NQT>
+__device__ __forceinline__ void page_max_f4(const uint8_t* __restrict__ pg, const v8i (&qf)[NQT][H],
+                                            int col, int grp, int off, v4f (&rmax)[NQT]) {
+#pragma unroll
+  for (int n = 0; n < NQT; ++n) rmax[n] = v4f{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  v8i a_cur = f4_frag(pg, 0, col, off);
+  int s_cur = f4_scale(pg, 0, col, grp);
+  v4f prev;
+#pragma unroll
+  for (int T = 0; T < 8; ++T) {
+    v8i a_nxt;
+    int s_nxt = 0;
+    if (T < 7) {
+      a_nxt = f4_frag(pg, T + 1, col, off);
+      s_nxt = f4_scale(pg, T + 1, col, grp);
+    }
+#pragma unroll
+    for (int n = 0; n < NQT; ++n) {
+      v4f acc = mfma_f4_e4m3(a_cur, qf[n][0], v4f{0.f, 0.f, 0.f, 0.f}, s_cur);
+#pragma unroll
+      for (int h = 1; h < H; ++h) acc = mfma_f4_e4m3(a_cur, qf[n][h], acc, s_cur);
+      if (T > 0 || n > 0) {
+        const int pn = n > 0 ? n - 1 : NQT - 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rmax[pn][i] = fmaxf(rmax[pn][i], prev[i]);
+      }
+      prev = acc;
+    }
+    if (T < 7) {
+      a_cur = a_nxt;
+      s_cur = s_nxt;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rmax[NQT - 1][i] = fmaxf(rmax[NQT - 1][i], prev[i]);
+}
+
+template <int H, int NQT>
+__device__ __forceinline__ void page_max_causal_f4(const uint8_t* __restrict__ pg,
+                                                   const v8i (&qf)[NQT][H], int lim0, int col,
+                                                   int grp, int off, v4f (&rmax)[NQT]) {
+#pragma unroll
+  for (int n = 0; n < NQT; ++n) rmax[n] = v4f{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll 1
+  for (int T = 0; T < 8; ++T) {
+    const v8i a_cur = f4_frag(pg, T, col, off);
+    const int s_cur = f4_scale(pg, T, col, grp);
+#pragma unroll
+    for (int n = 0; n < NQT; ++n) {
+      v4f acc = mfma_f4_e4m3(a_cur, qf[n][0], v4f{0.f, 0.f, 0.f, 0.f}, s_cur);
+#pragma unroll
+      for (int h = 1; h < H; ++h) acc = mfma_f4_e4m3(a_cur, qf[n][h], acc, s_cur);
+      const int lim = lim0 + 16 * n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = (T * 16 + grp * 4 + i > lim) ? -INFINITY : acc[i];
+        rmax[n][i] = fmaxf(rmax[n][i], v);
+      }
+    }
+  }
+}
+
 // LDS per block: a ring of four index-K pages (two being scored, two being
 // filled), one private score tile per wave ([queries of the wave][kFlush pages],
 // rows padded to kSRow floats), and the item's physical page ids.
-template <int H>
+template <int H, int KF>
 constexpr size_t score_lds_bytes() {
-  return 4 * kLdsPage + (size_t)kScoreWaves * score_qtiles(H) * 16 * kSRow * sizeof(float) +
+  return 4 * (KF ? kF4Slot : kLdsPage) +
+         (size_t)kScoreWaves * score_qtiles(H) * 16 * kSRow * sizeof(float) +
          kMaxItemPages * sizeof(int);
 }
 
-template <int H>
+// KF: index-K format, 0 = E4M3 rows of 128 bytes, 1 = MXFP4.
+template <int H, int KF>
 __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
   constexpr int NQT = score_qtiles(H);   // 16-query tiles per wave
   static_assert(NQT >= 1, "at least one query tile per wave");
+  constexpr int kSlot = KF ? kF4Slot : kLdsPage;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int item = blockIdx.x;
@@ -400,8 +526,8 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  float* sbuf = reinterpret_cast<float*>(lds + 4 * kLdsPage) + wave * (NQT * 16 * kSRow);
-  int* s_phys = reinterpret_cast<int*>(lds + 4 * kLdsPage + kScoreWaves * NQT * 16 * kSRow * 4);
+  float* sbuf = reinterpret_cast<float*>(lds + 4 * kSlot) + wave * (NQT * 16 * kSRow);
+  int* s_phys = reinterpret_cast<int*>(lds + 4 * kSlot + kScoreWaves * NQT * 16 * kSRow * 4);
 
   const int cq0 = a.cu_q[b];
   const int sq = a.cu_q[b + 1] - cq0;
@@ -430,14 +556,28 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
   // slot is requested even past the item's end (page index clamped) so the
   // count of loads in flight is the same on every path.
   static_assert(kThreads == kPage * kDim / 16, "one 16-byte piece per thread and page");
-  const int ld_row = wave * 8 + (lane >> 3);
-  const int ld_piece = (lane & 7) ^ ((ld_row >> 1) & 7);
+  // MXFP4 pages: waves 0..7 copy the 8 KiB of E2M1 pairs (rows 16w .. 16w + 15),
+  // lanes 0..31 of wave 8 the 512 scale bytes; the other waves copy nothing.
+  const int ld_row = KF ? wave * 16 + (lane >> 2) : wave * 8 + (lane >> 3);
+  const int ld_piece = KF ? (lane & 3) ^ ((ld_row >> 2) & 3) : (lane & 7) ^ ((ld_row >> 1) & 7);
+  const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds + wave * 1024);
   auto issue_page = [&](int p) {
     const int phys = s_phys[min(p, p_end - 1) - p0];
-    const uint8_t* src = a.k_cache + (int64_t)phys * (kPage * kDim) + ld_row * kDim + ld_piece * 16;
-    __builtin_amdgcn_global_load_lds(
-        src, (__attribute__((address_space(3))) void*)(lds + (p & 3) * kLdsPage + wave * 1024), 16,
-        0, 0);
+    if constexpr (KF == 0) {
+      const uint8_t* src = a.k_cache + (int64_t)phys * (kPage * kDim) + ld_row * kDim + ld_piece * 16;
+      __builtin_amdgcn_global_load_lds(
+          src, (__attribute__((address_space(3))) void*)(lds + (p & 3) * kLdsPage + wave * 1024),
+          16, 0, 0);
+    } else {
+      if (wave < 8) {
+        copy16_to_lds(a.k_cache + (int64_t)phys * kF4Data + ld_row * 64 + ld_piece * 16,
+                      lds_wave + (uint32_t)((p & 3) * kSlot));
+      } else if (wave == 8 && lane < 32) {
+        copy16_to_lds(a.k_scales + (int64_t)phys * (kPage * 4) + lane * 16,
+                      lds_wave + (uint32_t)((p & 3) * kSlot + kF4Data - 8 * 1024));
+      }
+    }
   };
   issue_page(p0);
   issue_page(p0 + 1);
@@ -459,7 +599,11 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
 #pragma unroll
     for (int h = 0; h < H; ++h) {
       if (ok) {
-        qf[n][h] = load_frag_global(a.q + (int64_t)qi * a.q_stride + h * kDim + grp * 32);
+        const uint8_t* qrow = a.q + (int64_t)qi * a.q_stride + h * kDim;
+        if constexpr (KF == 0)
+          qf[n][h] = load_frag_global(qrow + grp * 32);
+        else
+          qf[n][h] = load_qfrag_f4(qrow, grp);
       } else {
         qf[n][h] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
       }
@@ -467,6 +611,7 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
   }
   const float scale = (*a.q_scale) * (*a.k_scale);
   const Swz swz = lane_swizzle(col, grp);
+  const int f4off = f4_piece(col, grp);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's page pieces have landed
   __syncthreads();
 
@@ -498,12 +643,19 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
   };
 
   auto score_page = [&](int p) {
-    const uint8_t* pg = lds + (p & 3) * kLdsPage;
+    const uint8_t* pg = lds + (p & 3) * kSlot;
     v4f rmax[NQT];
-    if ((p + 1) * kPage - 1 > pos_first)
-      page_max_causal<H, NQT>(pg, qf, my_pos0 - p * kPage, col, grp, swz, rmax);
-    else
-      page_max<H, NQT>(pg, qf, col, swz, rmax);
+    if constexpr (KF == 0) {
+      if ((p + 1) * kPage - 1 > pos_first)
+        page_max_causal<H, NQT>(pg, qf, my_pos0 - p * kPage, col, grp, swz, rmax);
+      else
+        page_max<H, NQT>(pg, qf, col, swz, rmax);
+    } else {
+      if ((p + 1) * kPage - 1 > pos_first)
+        page_max_causal_f4<H, NQT>(pg, qf, my_pos0 - p * kPage, col, grp, f4off, rmax);
+      else
+        page_max_f4<H, NQT>(pg, qf, col, grp, f4off, rmax);
+    }
     const int pc = (p - p0) & (kFlush - 1);    // tiles start at the item's first page
 #pragma unroll
     for (int n = 0; n < NQT; ++n) {
@@ -540,35 +692,20 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
 // double-buffered across the barrier) and keeps the score tile.
 // ---------------------------------------------------------------------------
 
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
-// l's bytes land at LDS byte address lds_addr + 16 l (lds_addr wave-uniform,
-// passed in M0).  Inline assembly keeps the copy out of the compiler's
-// wait-count bookkeeping, which cannot tell the ring slots apart and would
-// otherwise wait for every copy in flight before each LDS read; the kernel's own
-// vmcnt waits and barriers order copies and reads.  (Counters retire in issue
-// order, so copies the compiler does not know of only lengthen the waits it
-// places for other loads.)
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               ::"v"(src), "s"(lds_addr)
-               : "m0");
-}
-#pragma clang diagnostic pop
 
 // LDS: the page ring, wave 0's score tile, the physical page ids and two
 // buffers of partial maxima [wave][query].
-template <int H>
+template <int H, int KF>
 constexpr size_t score_pp_lds_bytes() {
-  return 4 * kLdsPage + (size_t)score_qtiles(H) * 16 * kSRow * sizeof(float) +
+  return 4 * (KF ? kF4Slot : kLdsPage) + (size_t)score_qtiles(H) * 16 * kSRow * sizeof(float) +
          kMaxItemPages * sizeof(int) + 2 * kScoreWaves * score_qtiles(H) * 16 * sizeof(float);
 }
 
-template <int H>
+template <int H, int KF>
 __global__ __launch_bounds__(kThreads) void index_score_pp_kernel(ScoreK a) {
   constexpr int NQT = score_qtiles(H);
   constexpr int kQ = NQT * 16;                    // query slots
+  constexpr int kSlot = KF ? kF4Slot : kLdsPage;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int item = blockIdx.x;
@@ -579,8 +716,8 @@ __global__ __launch_bounds__(kThreads) void index_score_pp_kernel(ScoreK a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  float* sbuf = reinterpret_cast<float*>(lds + 4 * kLdsPage);
-  int* s_phys = reinterpret_cast<int*>(lds + 4 * kLdsPage + kQ * kSRow * 4);
+  float* sbuf = reinterpret_cast<float*>(lds + 4 * kSlot);
+  int* s_phys = reinterpret_cast<int*>(lds + 4 * kSlot + kQ * kSRow * 4);
   float* s_part = reinterpret_cast<float*>(s_phys + kMaxItemPages);
 
   const int cq0 = a.cu_q[b];
@@ -600,14 +737,24 @@ __global__ __launch_bounds__(kThreads) void index_score_pp_kernel(ScoreK a) {
   __syncthreads();
 
   // page ring: as in the prefill kernel, four slots, page p in slot p & 3
-  const int ld_row = wave * 8 + (lane >> 3);
-  const int ld_piece = (lane & 7) ^ ((ld_row >> 1) & 7);
+  const int ld_row = KF ? wave * 16 + (lane >> 2) : wave * 8 + (lane >> 3);
+  const int ld_piece = KF ? (lane & 3) ^ ((ld_row >> 2) & 3) : (lane & 7) ^ ((ld_row >> 1) & 7);
   const uint32_t lds_wave =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds + wave * 1024;
   auto issue_page = [&](int p) {
     const int phys = s_phys[min(p, p_end - 1) - p0];
-    const uint8_t* src = a.k_cache + (int64_t)phys * (kPage * kDim) + ld_row * kDim + ld_piece * 16;
-    copy16_to_lds(src, lds_wave + (uint32_t)((p & 3) * kLdsPage));
+    if constexpr (KF == 0) {
+      const uint8_t* src = a.k_cache + (int64_t)phys * (kPage * kDim) + ld_row * kDim + ld_piece * 16;
+      copy16_to_lds(src, lds_wave + (uint32_t)((p & 3) * kLdsPage));
+    } else {
+      if (wave < 8) {
+        copy16_to_lds(a.k_cache + (int64_t)phys * kF4Data + ld_row * 64 + ld_piece * 16,
+                      lds_wave + (uint32_t)((p & 3) * kSlot));
+      } else if (wave == 8 && lane < 32) {
+        copy16_to_lds(a.k_scales + (int64_t)phys * (kPage * 4) + lane * 16,
+                      lds_wave + (uint32_t)((p & 3) * kSlot + kF4Data - 8 * 1024));
+      }
+    }
   };
   issue_page(p0);
   issue_page(p0 + 1);
@@ -624,27 +771,34 @@ __global__ __launch_bounds__(kThreads) void index_score_pp_kernel(ScoreK a) {
   for (int n = 0; n < NQT; ++n) {
     const int qi = my_q0 + n * 16;
 #pragma unroll
-    for (int h = 0; h < H; ++h)
-      qf[n][h] = qi < q_end ? load_frag_global(a.q + (int64_t)qi * a.q_stride + h * kDim + grp * 32)
-                            : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int h = 0; h < H; ++h) {
+      const uint8_t* qrow = a.q + (int64_t)qi * a.q_stride + h * kDim;
+      if constexpr (KF == 0)
+        qf[n][h] = qi < q_end ? load_frag_global(qrow + grp * 32) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      else
+        qf[n][h] = qi < q_end ? load_qfrag_f4(qrow, grp) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    }
   }
   const float scale = (*a.q_scale) * (*a.k_scale);
   const Swz swz = lane_swizzle(col, grp);
+  const int f4off = f4_piece(col, grp);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   // partial maxima of page pw, tokens 16T .. 16T + 15, into dst[query]
   auto partial = [&](int pw, int T, float* dst) {
-    const uint8_t* pg = lds + (pw & 3) * kLdsPage;
-    const v8i a_t = load_frag_swz(pg + (T * 16 + col) * kDim, swz);
+    const uint8_t* pg = lds + (pw & 3) * kSlot;
+    const v8i a_t = KF ? f4_frag(pg, T, col, f4off) : load_frag_swz(pg + (T * 16 + col) * kDim, swz);
+    const int sa = KF ? f4_scale(pg, T, col, grp) : 0;
     const bool causal = (pw + 1) * kPage - 1 > pos_first;
     const int tok0 = pw * kPage + T * 16 + grp * 4;        // token of acc[0] in this lane
 #pragma unroll
     for (int n = 0; n < NQT; ++n) {
       if (n >= nt) break;
-      v4f acc = mfma_e4m3(a_t, qf[n][0], v4f{0.f, 0.f, 0.f, 0.f});
+      v4f acc = KF ? mfma_f4_e4m3(a_t, qf[n][0], v4f{0.f, 0.f, 0.f, 0.f}, sa)
+                   : mfma_e4m3(a_t, qf[n][0], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int h = 1; h < H; ++h) acc = mfma_e4m3(a_t, qf[n][h], acc);
+      for (int h = 1; h < H; ++h) acc = KF ? mfma_f4_e4m3(a_t, qf[n][h], acc, sa) : mfma_e4m3(a_t, qf[n][h], acc);
       float m;
       if (causal) {
         const int lim = my_pos0 + 16 * n;
@@ -723,24 +877,34 @@ __global__ __launch_bounds__(kThreads) void index_score_pp_kernel(ScoreK a) {
 
 }  // namespace
 
-template <int H>
+template <int H, int KF>
 hipError_t launch_scorer(dim3 grid, hipStream_t stream, const ScoreK& k, int max_seqlen_q) {
   if (max_seqlen_q <= score_qtiles(H) * 16) {   // every item fits one wave's query tiles
-    constexpr size_t bytes = score_pp_lds_bytes<H>();
+    constexpr size_t bytes = score_pp_lds_bytes<H, KF>();
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&index_score_pp_kernel<H>),
+        reinterpret_cast<const void*>(&index_score_pp_kernel<H, KF>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(index_score_pp_kernel<H>, grid, dim3(kThreads), bytes, stream, k);
+    hipLaunchKernelGGL((index_score_pp_kernel<H, KF>), grid, dim3(kThreads), bytes, stream, k);
     return hipGetLastError();
   }
-  constexpr size_t bytes = score_lds_bytes<H>();
+  constexpr size_t bytes = score_lds_bytes<H, KF>();
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&index_score_kernel<H>),
+      reinterpret_cast<const void*>(&index_score_kernel<H, KF>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(index_score_kernel<H>, grid, dim3(kThreads), bytes, stream, k);
+  hipLaunchKernelGGL((index_score_kernel<H, KF>), grid, dim3(kThreads), bytes, stream, k);
   return hipGetLastError();
+}
+
+template <int KF>
+hipError_t launch_scorer_h(dim3 grid, hipStream_t stream, const ScoreK& k, int H, int max_seqlen_q) {
+  switch (H) {
+    case 1: return launch_scorer<1, KF>(grid, stream, k, max_seqlen_q);
+    case 2: return launch_scorer<2, KF>(grid, stream, k, max_seqlen_q);
+    case 4: return launch_scorer<4, KF>(grid, stream, k, max_seqlen_q);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 ScorePlan score_plan(const msa_varlen_t* vl, int H) {
@@ -791,13 +955,10 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
   k.ld = a.ld;
   k.hdr = hdr;
   k.items = items;
+  k.k_scales = a.k_scales;
   dim3 grid((unsigned)a.plan.max_items);
-  switch (a.H) {
-    case 1: return launch_scorer<1>(grid, stream, k, a.vl.max_seqlen_q);
-    case 2: return launch_scorer<2>(grid, stream, k, a.vl.max_seqlen_q);
-    case 4: return launch_scorer<4>(grid, stream, k, a.vl.max_seqlen_q);
-    default: return hipErrorInvalidValue;
-  }
+  if (a.k_scales) return launch_scorer_h<1>(grid, stream, k, a.H, a.vl.max_seqlen_q);   // MXFP4 keys
+  return launch_scorer_h<0>(grid, stream, k, a.H, a.vl.max_seqlen_q);
 }
 
 }  // namespace msa

@@ -96,11 +96,17 @@ size_t msa_index_score_workspace_size(const msa_varlen_t* vl, int32_t num_index_
   return score_plan(vl, num_index_heads).workspace_bytes;
 }
 
-msa_status_t msa_index_score(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
-                             int32_t num_index_heads, const uint8_t* k_cache, int32_t num_pages,
-                             const float* q_scale, const float* k_scale, float* scores,
-                             int64_t ld_scores, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by both key formats: k_scales == nullptr means E4M3 keys.
+msa_status_t index_score_impl(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
+                              int32_t num_index_heads, const uint8_t* k_cache,
+                              const uint8_t* k_scales, int32_t num_pages, const float* q_scale,
+                              const float* k_scale, float* scores, int64_t ld_scores,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              const char* name) {
   msa_status_t st = check_varlen(vl);
   if (st != MSA_OK) return st;
   const int H = num_index_heads;
@@ -113,6 +119,8 @@ msa_status_t msa_index_score(const msa_varlen_t* vl, const uint8_t* q, int64_t q
             "q_stride must be >= H*128 and a multiple of 16 (got %lld)", (long long)q_stride);
   MSA_CHECK(aligned(q, 16) && aligned(k_cache, 16), MSA_ERR_INVALID_ARGUMENT,
             "q and k_cache must be 16-byte aligned");
+  MSA_CHECK(!k_scales || aligned(k_scales, 16), MSA_ERR_INVALID_ARGUMENT,
+            "k_scales must be 16-byte aligned");
   MSA_CHECK(num_pages >= 1, MSA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
   MSA_CHECK(ld_scores >= vl->max_pages && ld_scores >= 1, MSA_ERR_INVALID_ARGUMENT,
             "ld_scores (%lld) < max_pages (%d)", (long long)ld_scores, vl->max_pages);
@@ -126,10 +134,37 @@ msa_status_t msa_index_score(const msa_varlen_t* vl, const uint8_t* q, int64_t q
   st = check_device();
   if (st != MSA_OK) return st;
   ScoreArgs a{*vl, q, q_stride, H, k_cache, num_pages, q_scale, k_scale,
-              scores, ld_scores, workspace, plan};
+              scores, ld_scores, workspace, plan, k_scales};
   hipError_t e = launch_index_score(a, reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "msa_index_score");
+  if (e != hipSuccess) return hip_fail(e, name);
   return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status_t msa_index_score(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
+                             int32_t num_index_heads, const uint8_t* k_cache, int32_t num_pages,
+                             const float* q_scale, const float* k_scale, float* scores,
+                             int64_t ld_scores, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return index_score_impl(vl, q, q_stride, num_index_heads, k_cache, nullptr, num_pages, q_scale,
+                          k_scale, scores, ld_scores, workspace, workspace_bytes, stream,
+                          "msa_index_score");
+}
+
+msa_status_t msa_index_score_mxfp4(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
+                                   int32_t num_index_heads, const uint8_t* k_data,
+                                   const uint8_t* k_scales, int32_t num_pages,
+                                   const float* q_scale, const float* k_scale, float* scores,
+                                   int64_t ld_scores, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  MSA_CHECK(k_scales != nullptr || !vl || vl->total_q == 0, MSA_ERR_INVALID_ARGUMENT,
+            "msa_index_score_mxfp4: k_scales is NULL");
+  return index_score_impl(vl, q, q_stride, num_index_heads, k_data, k_scales, num_pages, q_scale,
+                          k_scale, scores, ld_scores, workspace, workspace_bytes, stream,
+                          "msa_index_score_mxfp4");
 }
 
 // ---------------------------------------------------------------------------
@@ -381,6 +416,28 @@ msa_status_t msa_insert_kv(const void* k, const void* v, int32_t src_dtype, int6
   q.dst_head_stride = (int64_t)kPage * 2 * kDim;
   q.dst_row_stride = 2 * kDim;
   return run_quantize(q, stream, "msa_insert_kv");
+}
+
+msa_status_t msa_insert_index_k_mxfp4(const void* k, int32_t src_dtype, int64_t n_tokens,
+                                      int64_t k_stride, const int64_t* slot_mapping,
+                                      uint8_t* k_data, uint8_t* k_scales, int32_t num_pages,
+                                      void* stream) {
+  MSA_CHECK(n_tokens >= 0, MSA_ERR_INVALID_ARGUMENT, "msa_insert_index_k_mxfp4: n_tokens must be >= 0");
+  MSA_CHECK(n_tokens <= kMaxQuantRows, MSA_ERR_UNSUPPORTED, "msa_insert_index_k_mxfp4: too many tokens");
+  if (n_tokens == 0) return MSA_OK;
+  msa_status_t st = check_src(k, src_dtype, k_stride, kDim, "msa_insert_index_k_mxfp4");
+  if (st != MSA_OK) return st;
+  MSA_CHECK(slot_mapping && k_data && k_scales, MSA_ERR_INVALID_ARGUMENT,
+            "msa_insert_index_k_mxfp4: NULL slot_mapping, k_data or k_scales");
+  MSA_CHECK(aligned(k_data, 4) && num_pages >= 1, MSA_ERR_INVALID_ARGUMENT,
+            "msa_insert_index_k_mxfp4: k_data must be 4-byte aligned and num_pages >= 1");
+  st = check_device();
+  if (st != MSA_OK) return st;
+  Mx4Args q{k, src_dtype, n_tokens, k_stride, slot_mapping, (int64_t)num_pages * kPage, k_data,
+            k_scales};
+  hipError_t e = launch_insert_mxfp4(q, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "msa_insert_index_k_mxfp4");
+  return MSA_OK;
 }
 
 }  // extern "C"

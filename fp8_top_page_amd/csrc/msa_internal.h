@@ -40,7 +40,7 @@ struct ScoreArgs {
   const uint8_t* q;
   int64_t q_stride;
   int H;
-  const uint8_t* k_cache;
+  const uint8_t* k_cache;      // E4M3 rows [num_pages, 128, 128], or MXFP4 data [num_pages, 128, 64]
   int32_t num_pages;
   const float* q_scale;
   const float* k_scale;
@@ -48,6 +48,7 @@ struct ScoreArgs {
   int64_t ld;
   void* workspace;
   ScorePlan plan;
+  const uint8_t* k_scales;     // nullptr: E4M3 keys; else MXFP4 block scales [num_pages, 128, 4]
 };
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream);
 
@@ -131,6 +132,18 @@ struct QuantArgs {
   int64_t dst_tok_stride, dst_page_stride, dst_head_stride, dst_row_stride;   // bytes
 };
 hipError_t launch_quantize(const QuantArgs& q, hipStream_t stream);
+
+struct Mx4Args {             // MXFP4 index-key insert
+  const void* src;
+  int dtype;
+  int64_t n_tokens;
+  int64_t src_tok_stride;    // elements
+  const int64_t* slots;
+  int64_t max_slot;
+  uint8_t* data;             // [num_pages, 128, 64]
+  uint8_t* scales;           // [num_pages, 128, 4]
+};
+hipError_t launch_insert_mxfp4(const Mx4Args& q, hipStream_t stream);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

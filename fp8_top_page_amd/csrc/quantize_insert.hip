@@ -51,9 +51,9 @@ struct QuantK {
 };
 
 // Source element e of a row as fp32 (bf16 widens exactly).
-__device__ __forceinline__ void load8(const QuantK& a, const Part& p, int64_t src_off, float (&x)[8]) {
-  if (a.dtype == MSA_DTYPE_BF16) {
-    const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.src) + src_off);
+__device__ __forceinline__ void load8(int dtype, const void* src, int64_t src_off, float (&x)[8]) {
+  if (dtype == MSA_DTYPE_BF16) {
+    const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(src) + src_off);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -61,7 +61,7 @@ __device__ __forceinline__ void load8(const QuantK& a, const Part& p, int64_t sr
       x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
     }
   } else {
-    const float* f = reinterpret_cast<const float*>(p.src) + src_off;
+    const float* f = reinterpret_cast<const float*>(src) + src_off;
     const float4 u = *reinterpret_cast<const float4*>(f);
     const float4 v = *reinterpret_cast<const float4*>(f + 4);
     x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(QuantK a) {
       off = t * a.dst_tok_stride;
     }
     dst_off[r] = off + h * a.dst_head_stride + p.col_off + c0;
-    load8(a, p, t * p.src_tok_stride + h * a.src_head_stride + c0, x[r]);
+    load8(a.dtype, p.src, t * p.src_tok_stride + h * a.src_head_stride + c0, x[r]);
   }
   const float s = *p.scale;
   const uint32_t sb = __float_as_uint(s);
@@ -136,6 +136,68 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(QuantK a) {
 #pragma unroll
     for (int r = 0; r < kRowsPerGroup; ++r)
       if (dst_off[r] >= 0) *reinterpret_cast<uint2*>(a.dst + dst_off[r]) = encode8<false>(x[r], s, 0.f);
+  }
+}
+
+// ---- MXFP4 index keys --------------------------------------------------------
+// Row of 128 elements -> 4 blocks of 32 E2M1 codes sharing one E8M0 scale
+// (OCP Microscaling conversion): exponent = floor(log2(max |x|)) - 2, clamped
+// to [-127, 127] (-127 for a block of zeros); elements = nearest E2M1 of
+// x * 2^-exponent, ties to the even code, saturating at 6.  A block holding NaN
+// or an infinity gets scale 0xFF and zero elements.  A block is 4 lanes of the
+// row's 16; each lane writes its 8 codes as 4 bytes (element 2i low nibble),
+// the block's first lane its scale byte.
+struct Mx4K {
+  const void* src;
+  int dtype;
+  int64_t n_tokens;
+  int64_t src_tok_stride;    // elements
+  const int64_t* slots;
+  int64_t max_slot;
+  uint8_t* data;             // [num_pages, 128, 64]
+  uint8_t* scales;           // [num_pages, 128, 4]
+};
+
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                   : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.f ? 6u : 7u;
+  return c | (signbit(v) ? 8u : 0u);
+}
+
+__global__ __launch_bounds__(kThreads) void insert_mxfp4_kernel(Mx4K a) {
+  const int g = threadIdx.x >> 4, l16 = threadIdx.x & 15;
+  const int c0 = l16 * 8;
+#pragma unroll
+  for (int r = 0; r < kRowsPerGroup; ++r) {
+    const int64_t t = ((int64_t)blockIdx.x * kRowsPerGroup + r) * kGroups + g;   // group-uniform
+    if (t >= a.n_tokens) break;
+    const int64_t s = a.slots[t];
+    if (s < 0 || s >= a.max_slot) continue;          // padding token (or out of range): skipped
+    float x[8];
+    load8(a.dtype, a.src, t * a.src_tok_stride + c0, x);
+    float amax = 0.f;
+    bool bad = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      bad |= !isfinite(x[e]);
+      amax = fmaxf(amax, fabsf(x[e]));
+    }
+    // the block's 4 lanes (aligned within the 16-lane row)
+#pragma unroll
+    for (int m = 1; m < 4; m <<= 1) {
+      amax = fmaxf(amax, __shfl_xor(amax, m));
+      bad |= __shfl_xor((int)bad, m) != 0;
+    }
+    const int ex = amax == 0.f ? -127 : min(127, max(-127, ilogbf(amax) - 2));
+    uint32_t w = 0;
+    if (!bad) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w |= e2m1_code(ldexpf(x[e], -ex)) << (4 * e);
+    }
+    // slot s is row s % 128 of page s / 128, i.e. row s of the [pages * 128] rows
+    *reinterpret_cast<uint32_t*>(a.data + s * 64 + l16 * 4) = w;
+    if ((l16 & 3) == 0) a.scales[s * 4 + (l16 >> 2)] = bad ? (uint8_t)0xFF : (uint8_t)(ex + 127);
   }
 }
 
@@ -159,6 +221,14 @@ hipError_t launch_quantize(const QuantArgs& q, hipStream_t stream) {
   k.dst_row_stride = q.dst_row_stride;
   const dim3 grid((unsigned)ceil_div(n_rows, kRowsPerBlock), (unsigned)q.n_parts);
   hipLaunchKernelGGL(quantize_rows_kernel, grid, dim3(kThreads), 0, stream, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_insert_mxfp4(const Mx4Args& q, hipStream_t stream) {
+  if (q.n_tokens == 0) return hipSuccess;
+  Mx4K k{q.src, q.dtype, q.n_tokens, q.src_tok_stride, q.slots, q.max_slot, q.data, q.scales};
+  const dim3 grid((unsigned)ceil_div(q.n_tokens, kRowsPerBlock));
+  hipLaunchKernelGGL(insert_mxfp4_kernel, grid, dim3(kThreads), 0, stream, k);
   return hipGetLastError();
 }
 

@@ -7,7 +7,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (PAGE, TOPK, Varlen, msa_build_k2q_csr, msa_index_score,
+from . import (PAGE, TOPK, Varlen, msa_build_k2q_csr, msa_index_score, msa_index_score_mxfp4,
                msa_index_score_workspace_size, msa_k2q_schedule_size, msa_sparse_attn_prefill,
                msa_sparse_attn_workspace_size, msa_topk_select)
 
@@ -41,6 +41,7 @@ class DeviceBatch:
         self.vl = Varlen(self.cu_q, self.cu_k, self.block_table, total_q=self.total_q,
                          max_seqlen_q=self.max_seqlen_q, max_seqlen_k=self.max_seqlen_k,
                          total_rows=self.total_rows, max_pages=self.max_pages)
+        self.k_fp4 = None            # (data, scales) of MXFP4 index keys, if scored from those
         self.H = int(index_q.shape[1])
         self.index_q = _dev(np.asarray(index_q).reshape(index_q.shape[0], self.H * 128), device)
         self.k_cache = _dev(index_k_cache, device)
@@ -64,6 +65,10 @@ class DeviceBatch:
                    inp.index_k_cache, inp.index_q_scale, inp.index_k_scale, inp.attn_q,
                    inp.kv_cache, inp.attn_q_scale, inp.attn_k_scale, inp.attn_v_scale,
                    inp.softmax_scale, device)
+
+    def use_mxfp4_keys(self, data, scales):
+        """Score from MXFP4 index keys (uint8 [pages, 128, 64] and [pages, 128, 4])."""
+        self.k_fp4 = (_dev(data, self.device), _dev(scales, self.device))
 
 
 class MsaPath:
@@ -93,8 +98,12 @@ class MsaPath:
 
     def score(self, stream=None):
         db = self.db
-        msa_index_score(db.vl, db.index_q, db.H, db.k_cache, db.num_pages, db.iq_scale,
-                        db.ik_scale, self.scores, self.ws_score, stream)
+        if db.k_fp4 is not None:                  # MXFP4 index keys
+            msa_index_score_mxfp4(db.vl, db.index_q, db.H, db.k_fp4[0], db.k_fp4[1], db.num_pages,
+                                  db.iq_scale, db.ik_scale, self.scores, self.ws_score, stream)
+        else:
+            msa_index_score(db.vl, db.index_q, db.H, db.k_cache, db.num_pages, db.iq_scale,
+                            db.ik_scale, self.scores, self.ws_score, stream)
 
     def select(self, stream=None):
         assert self.n_sel == 1

@@ -239,12 +239,45 @@ msa_status_t msa_insert_kv(const void* k, const void* v, int32_t src_dtype, int6
                            void* stream);
 
 /* ---------------------------------------------------------------------------
+ * 6. MXFP4 index keys: the 4-bit analogue of the pages' NVFP4 index cache
+ *    ([P3] Details: FP8 query times FP4 key in the decode indexer), in the
+ *    format gfx950's matrix cores take natively (OCP Microscaling MXFP4).
+ *
+ * k_data   [num_pages, 128, 64]: a token's 128 key elements as E2M1 codes,
+ *          element 2i in the low nibble of byte i, 2i+1 in the high nibble
+ * k_scales [num_pages, 128, 4]: E8M0 scale of each 32-element block
+ *          (value 2^(code-127), 0xFF = NaN); key value = E2M1 element * 2^(code-127)
+ *
+ * msa_index_score_mxfp4: msa_index_score (section 1) over such keys, with the
+ *   same arguments, layouts and errors; k_scale stays a per-tensor factor.
+ *   k_data and k_scales 16-byte aligned.
+ * msa_insert_index_k_mxfp4: quantise rows of 128 elements (src as in section
+ *   5) per block of 32: exponent = floor(log2(max |x|)) - 2 clamped to
+ *   [-127, 127] (-127 for a block of zeros), elements = nearest E2M1 of
+ *   x * 2^-exponent, ties to even, saturating at +-6; a block holding NaN or
+ *   an infinity gets scale 0xFF and zero elements.  Token t goes to row s % 128
+ *   of page s / 128 of both arrays (s = slot_mapping[t]; s < 0 and
+ *   s >= num_pages*128 skipped).  (The Microscaling conversion rule; the pages
+ *   describe NVFP4, so this format is the reading the library implements.)
+ * ------------------------------------------------------------------------- */
+msa_status_t msa_index_score_mxfp4(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
+                                   int32_t num_index_heads, const uint8_t* k_data,
+                                   const uint8_t* k_scales, int32_t num_pages,
+                                   const float* q_scale, const float* k_scale, float* scores,
+                                   int64_t ld_scores, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+msa_status_t msa_insert_index_k_mxfp4(const void* k, int32_t src_dtype, int64_t n_tokens,
+                                      int64_t k_stride, const int64_t* slot_mapping,
+                                      uint8_t* k_data, uint8_t* k_scales, int32_t num_pages,
+                                      void* stream);
+
+/* ---------------------------------------------------------------------------
  * Diagnostics.
  * ------------------------------------------------------------------------- */
 const char* msa_status_string(msa_status_t status);  /* static string */
 const char* msa_last_error(void);   /* thread-local detail of this thread's last failed call */
 int32_t msa_abi_version(void);      /* MSA_ABI_VERSION */
-#define MSA_ABI_VERSION 2
+#define MSA_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

@@ -34,10 +34,11 @@ def test_library_exports_every_declared_symbol():
         "msa_index_score_workspace_size", "msa_index_score", "msa_topk_select",
         "msa_k2q_schedule_size", "msa_build_k2q_csr", "msa_sparse_attn_workspace_size",
         "msa_sparse_attn_prefill", "msa_status_string", "msa_last_error", "msa_abi_version",
-        "msa_quantize_e4m3", "msa_insert_index_k", "msa_insert_kv"]), names
+        "msa_quantize_e4m3", "msa_insert_index_k", "msa_insert_kv", "msa_index_score_mxfp4",
+        "msa_insert_index_k_mxfp4"]), names
     for n in names:
         assert hasattr(L, n), n
-    assert msa.msa_abi_version() == 2
+    assert msa.msa_abi_version() == 3
 
 
 def test_status_strings():
@@ -215,4 +216,27 @@ def test_quantize_and_insert_validation():
     assert kv(cache=FAKE + 2) == INVALID
     if NO_GPU:
         assert kv() == NO_DEV
+
+
+def test_mxfp4_validation():
+    L = msa.lib()
+    v = vl()
+    ws = L.msa_index_score_workspace_size(ctypes.byref(v), 1)
+    sc = lambda kd=FAKE, ks=FAKE, H=1: L.msa_index_score_mxfp4(
+        ctypes.byref(v), FAKE, 128 * H, H, kd, ks, 8, FAKE, FAKE, FAKE, 8, 0x100000, ws, None)
+    assert sc(ks=None) == INVALID
+    assert sc(ks=FAKE + 4) == INVALID         # scales not 16-byte aligned
+    assert sc(H=3) == UNSUPPORTED
+    if NO_GPU:
+        assert sc() == NO_DEV
+    ins = lambda k=FAKE, dt=0, n=5, ks=128, slots=FAKE, kd=FAKE, kscale=FAKE, pages=2: \
+        L.msa_insert_index_k_mxfp4(k, dt, n, ks, slots, kd, kscale, pages, None)
+    assert ins(n=0) == OK
+    assert ins(dt=3) == UNSUPPORTED
+    assert ins(ks=120) == INVALID
+    assert ins(kscale=None) == INVALID
+    assert ins(kd=FAKE + 2) == INVALID
+    assert ins(pages=0) == INVALID
+    if NO_GPU:
+        assert ins() == NO_DEV
 
