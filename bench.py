@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--cold", action="store_true",
                     help="overwrite a 1 GiB buffer before every step (outside the events)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--index-cache", choices=["e4m3", "mxfp4"], default="e4m3",
+                    help="index-K format the scorer reads (mxfp4: the workload's keys re-quantised "
+                         "on the device to E2M1 blocks with E8M0 scales)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -69,8 +72,9 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes": n, "repeats": 3}), flush=True)
 
 
-def algorithmic_work(inp, sel):
-    """FLOPs and bytes the path must do at minimum (see the design notes)."""
+def algorithmic_work(inp, sel, key_bytes=128.0):
+    """FLOPs and bytes the path must do at minimum (see the design notes);
+    key_bytes: index-K bytes per token (128 E4M3, 68 MXFP4)."""
     import numpy as np
     cu_q = np.asarray(inp.cu_seqlens_q, np.int64)
     cu_k = np.asarray(inp.cu_seqlens_k, np.int64)
@@ -85,7 +89,7 @@ def algorithmic_work(inp, sel):
     total_q = int(cu_q[-1])
     total_k = int(cu_k[-1])
     score_flops = 2.0 * 128 * H * pos_sum
-    score_bytes = 128.0 * total_k + 128.0 * H * total_q + 4.0 * vis_sum
+    score_bytes = key_bytes * total_k + 128.0 * H * total_q + 4.0 * vis_sum
     # attended tokens per query: selected pages, tokens <= pos
     req = np.repeat(np.arange(len(cu_q) - 1), np.diff(cu_q))
     ctx = (np.diff(cu_k) - np.diff(cu_q))[req]
@@ -233,6 +237,19 @@ def main():
     print(f"[bench] inputs for {wl.name} generated in {time.time() - t0:.1f} s", file=sys.stderr,
           flush=True)
     db = DeviceBatch.from_inputs(inp, dev)
+    if args.index_cache == "mxfp4":
+        # the same keys as MXFP4: decoded E4M3 values times their scale, re-quantised
+        # by the library's insert (every cache row, identity slots)
+        from fp8_top_page_amd import msa_insert_index_k_mxfp4
+        kf = db.k_cache.view(torch.float8_e4m3fn).float().reshape(-1, 128) * float(inp.index_k_scale)
+        data = torch.empty((db.num_pages, 128, 64), dtype=torch.uint8, device=dev)
+        scales = torch.empty((db.num_pages, 128, 4), dtype=torch.uint8, device=dev)
+        slots = torch.arange(kf.shape[0], dtype=torch.int64, device=dev)
+        msa_insert_index_k_mxfp4(kf, slots, data, scales, db.num_pages)
+        torch.cuda.synchronize()
+        del kf
+        db.k_fp4 = (data, scales)
+        db.ik_scale = torch.ones(1, dtype=torch.float32, device=dev)
     path = MsaPath(db)
     stream = torch.cuda.current_stream()
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.cold else None
@@ -294,7 +311,7 @@ def main():
           ", ".join(f"{n} {m:.1f} us" for n, m in zip(names, mean_us)), file=sys.stderr, flush=True)
 
     sel = path.topk[:, 0, :].cpu().numpy()
-    work = algorithmic_work(inp, sel)
+    work = algorithmic_work(inp, sel, 68.0 if args.index_cache == "mxfp4" else 128.0)
     insert = time_insert(inp, db, args.steps, stream)
     score_us = float(mean_us[0])
     attn_us = float(mean_us[3])
@@ -326,9 +343,11 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "seqlen_q": list(wl.seqlen_q),
                    "seqlen_k": list(wl.seqlen_k), "index_heads": wl.index_heads,
                    "q_heads": wl.q_heads, "kv_heads": wl.kv_heads, "page": 128, "head_dim": 128,
-                   "topk": 16, "cache": "cold (1 GiB overwrite per step)" if args.cold
+                   "topk": 16, "index_cache": args.index_cache,
+                   "cache": "cold (1 GiB overwrite per step)" if args.cold
                    else "warm (steps back to back)"},
-        "roofline": {**score_roof, "traffic": scorer_hbm_traffic(wl.name),
+        "roofline": {**score_roof,
+                     "traffic": scorer_hbm_traffic(wl.name) if args.index_cache == "e4m3" else None,
                      "kernel": "index_score (plan + scorer)",
                      "flops_per_launch": work["score_flops"],
                      "algorithmic_bytes_per_launch": work["score_bytes"],

@@ -695,9 +695,14 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
 
 // LDS: the page ring, wave 0's score tile, the physical page ids and two
 // buffers of partial maxima [wave][query].
+// MXFP4 pages are half the bytes, so their ring is twice as deep (8 slots) to
+// keep as many bytes in flight.
+template <int KF>
+constexpr int pp_ring() { return KF ? 8 : 4; }
+
 template <int H, int KF>
 constexpr size_t score_pp_lds_bytes() {
-  return 4 * (KF ? kF4Slot : kLdsPage) + (size_t)score_qtiles(H) * 16 * kSRow * sizeof(float) +
+  return pp_ring<KF>() * (KF ? kF4Slot : kLdsPage) + (size_t)score_qtiles(H) * 16 * kSRow * sizeof(float) +
          kMaxItemPages * sizeof(int) + 2 * kScoreWaves * score_qtiles(H) * 16 * sizeof(float);
 }
 
@@ -706,6 +711,8 @@ __global__ __launch_bounds__(kThreads) void index_score_pp_kernel(ScoreK a) {
   constexpr int NQT = score_qtiles(H);
   constexpr int kQ = NQT * 16;                    // query slots
   constexpr int kSlot = KF ? kF4Slot : kLdsPage;
+  constexpr int kRingN = pp_ring<KF>();
+  constexpr int kReducer = 0;        // the wave that reduces the partials and stores the scores
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int item = blockIdx.x;
@@ -716,8 +723,8 @@ __global__ __launch_bounds__(kThreads) void index_score_pp_kernel(ScoreK a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  float* sbuf = reinterpret_cast<float*>(lds + 4 * kSlot);
-  int* s_phys = reinterpret_cast<int*>(lds + 4 * kSlot + kQ * kSRow * 4);
+  float* sbuf = reinterpret_cast<float*>(lds + kRingN * kSlot);
+  int* s_phys = reinterpret_cast<int*>(lds + kRingN * kSlot + kQ * kSRow * 4);
   float* s_part = reinterpret_cast<float*>(s_phys + kMaxItemPages);
 
   const int cq0 = a.cu_q[b];
@@ -749,10 +756,10 @@ __global__ __launch_bounds__(kThreads) void index_score_pp_kernel(ScoreK a) {
     } else {
       if (wave < 8) {
         copy16_to_lds(a.k_cache + (int64_t)phys * kF4Data + ld_row * 64 + ld_piece * 16,
-                      lds_wave + (uint32_t)((p & 3) * kSlot));
+                      lds_wave + (uint32_t)((p & (kRingN - 1)) * kSlot));
       } else if (wave == 8 && lane < 32) {
         copy16_to_lds(a.k_scales + (int64_t)phys * (kPage * 4) + lane * 16,
-                      lds_wave + (uint32_t)((p & 3) * kSlot + kF4Data - 8 * 1024));
+                      lds_wave + (uint32_t)((p & (kRingN - 1)) * kSlot + kF4Data - 8 * 1024));
       }
     }
   };
@@ -784,10 +791,14 @@ __global__ __launch_bounds__(kThreads) void index_score_pp_kernel(ScoreK a) {
   const int f4off = f4_piece(col, grp);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  // a deeper ring fills up once the first four pages are in (the first step
+  // waits only for pages it has already waited for)
+#pragma unroll
+  for (int k = 4; k < kRingN; ++k) issue_page(p0 + k);
 
   // partial maxima of page pw, tokens 16T .. 16T + 15, into dst[query]
   auto partial = [&](int pw, int T, float* dst) {
-    const uint8_t* pg = lds + (pw & 3) * kSlot;
+    const uint8_t* pg = lds + (pw & (kRingN - 1)) * kSlot;
     const v8i a_t = KF ? f4_frag(pg, T, col, f4off) : load_frag_swz(pg + (T * 16 + col) * kDim, swz);
     const int sa = KF ? f4_scale(pg, T, col, grp) : 0;
     const bool causal = (pw + 1) * kPage - 1 > pos_first;
@@ -812,7 +823,7 @@ __global__ __launch_bounds__(kThreads) void index_score_pp_kernel(ScoreK a) {
       if ((n & 3) == grp) dst[n * 16 + col] = m;
     }
   };
-  // wave 0: score tile flush for pages [pg0, pg_hi), as in the prefill kernel
+  // the reducer wave: score tile flush for pages [pg0, pg_hi), as in the prefill kernel
   auto flush = [&](int pg0, int pg_hi) {
 #pragma unroll
     for (int r = 0; r < NQT; ++r) {
@@ -836,7 +847,7 @@ __global__ __launch_bounds__(kThreads) void index_score_pp_kernel(ScoreK a) {
       }
     }
   };
-  // wave 0: page pr's score from its 8 partials (waves 8j .. 8j + 7 of src)
+  // the reducer wave: page pr's score from its 8 partials (waves 8j .. 8j + 7 of src)
   auto reduce = [&](int pr, int j, const float* src) {
     const int pc = (pr - p0) & (kFlush - 1);
     if (lane < kQ) {
@@ -848,27 +859,28 @@ __global__ __launch_bounds__(kThreads) void index_score_pp_kernel(ScoreK a) {
     if (pc == kFlush - 1 || pr == p_end - 1) flush(pr - pc, pr + 1);
   };
 
-  // One step: partials of pages p, p + 1 (wave 0 also reduces the previous
-  // pair); wait for this wave's pieces of p + 2, p + 3; barrier; request
-  // p + 4, p + 5 into the slots of p, p + 1.
+  // One step: partials of pages p, p + 1 (the reducer also reduces the
+  // previous pair); wait for this wave's pieces of p + 2, p + 3 (copies retire
+  // in issue order and the kRingN - 4 pages after them were issued later);
+  // barrier; request p + kRingN, p + kRingN + 1 into the slots of p, p + 1.
   constexpr int kPartBuf = kScoreWaves * kQ;
   int buf = 0;
   for (int p = p0; p < p_end; p += 2) {
     const int pw = p + (wave >> 3);
     if (pw < p_end) partial(pw, wave & 7, s_part + buf * kPartBuf + wave * kQ);
-    if (wave == 0 && p > p0) {
+    if (wave == kReducer && p > p0) {
       reduce(p - 2, 0, s_part + (buf ^ 1) * kPartBuf);
       reduce(p - 1, 1, s_part + (buf ^ 1) * kPartBuf);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRingN - 4) : "memory");
     __syncthreads();
     if (p + 2 < p_end) {
-      issue_page(p + 4);
-      issue_page(p + 5);
+      issue_page(p + kRingN);
+      issue_page(p + kRingN + 1);
     }
     buf ^= 1;
   }
-  if (wave == 0) {                    // the last pair
+  if (wave == kReducer) {             // the last pair
     const int pl = p0 + (p_end - 1 - p0) / 2 * 2;
     reduce(pl, 0, s_part + (buf ^ 1) * kPartBuf);
     if (pl + 1 < p_end) reduce(pl + 1, 1, s_part + (buf ^ 1) * kPartBuf);
