@@ -67,8 +67,13 @@ class DeviceBatch:
                    inp.softmax_scale, device)
 
     def use_mxfp4_keys(self, data, scales):
-        """Score from MXFP4 index keys (uint8 [pages, 128, 64] and [pages, 128, 4])."""
-        self.k_fp4 = (_dev(data, self.device), _dev(scales, self.device))
+        """Score from MXFP4 index keys (uint8 [pages, 128, 64] and [pages, 128, 4]),
+        host arrays or device tensors."""
+        def on_dev(x):
+            if isinstance(x, torch.Tensor):
+                return x.to(self.device).contiguous()
+            return _dev(x, self.device)
+        self.k_fp4 = (on_dev(data), on_dev(scales))
 
 
 class MsaPath:
