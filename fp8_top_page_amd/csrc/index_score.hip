@@ -24,9 +24,11 @@
 //    scores a 16-token slice of one page for all the queries, and the slices'
 //    maxima are reduced through LDS.
 //  * Epilogue: each lane holds 4 consecutive tokens of one query per 16-token
-//    tile; the max over the page's 8 tiles is taken in registers, then across
-//    the 4 lane groups.  Scores of 4 consecutive pages are gathered so each
-//    store writes 16 contiguous bytes per query.
+//    tile; the max over the page's 8 tiles is taken in registers and the lane's
+//    partial max goes to an LDS tile (4 pages x 4 lane groups per query).  Every
+//    4 pages the tile is flushed: a lane maxes the 4 groups of one (query, page)
+//    pair, scales it and stores it, four lanes covering 16 contiguous bytes of a
+//    query's row.  (The cross-group max thus costs no lane exchanges per page.)
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -35,8 +37,9 @@ namespace {
 
 constexpr int kLdsPage = kPage * kDim;       // 16 KiB: 128 rows of 128 B, 16-byte pieces swizzled
 constexpr int kThreads = kScoreWaves * 64;
-constexpr int kFlush = 16;                   // pages per score-tile flush
+constexpr int kFlush = 16;                   // pages per score-tile flush (decode kernel)
 constexpr int kSRow = kFlush + 1;            // score-tile row stride in floats
+constexpr int kSRowG = 20;                   // prefill tile: 4 pages x 4 lane groups, padded
 constexpr int kMaxItemPages = 256;           // pages per work item, at most
 constexpr int kMinItemPages = 4;             // ... and at least (keeps score stores 16-byte aligned)
 constexpr int kPlanCUs = 256;                // compute units the item sizing aims to fill
@@ -502,12 +505,13 @@ __device__ __forceinline__ void page_max_causal_f4(const uint8_t* __restrict__ p
 }
 
 // LDS per block: a ring of four index-K pages (two being scored, two being
-// filled), one private score tile per wave ([queries of the wave][kFlush pages],
-// rows padded to kSRow floats), and the item's physical page ids.
+// filled), one private partial-max tile per wave ([queries of the wave][4 pages
+// x 4 lane groups], rows padded to kSRowG floats: 16-byte aligned, and the 64
+// lanes' writes fall in distinct banks), and the item's physical page ids.
 template <int H, int KF>
 constexpr size_t score_lds_bytes() {
   return 4 * (KF ? kF4Slot : kLdsPage) +
-         (size_t)kScoreWaves * score_qtiles(H) * 16 * kSRow * sizeof(float) +
+         (size_t)kScoreWaves * score_qtiles(H) * 16 * kSRowG * sizeof(float) +
          kMaxItemPages * sizeof(int);
 }
 
@@ -526,8 +530,8 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  float* sbuf = reinterpret_cast<float*>(lds + 4 * kSlot) + wave * (NQT * 16 * kSRow);
-  int* s_phys = reinterpret_cast<int*>(lds + 4 * kSlot + kScoreWaves * NQT * 16 * kSRow * 4);
+  float* sbuf = reinterpret_cast<float*>(lds + 4 * kSlot) + wave * (NQT * 16 * kSRowG);
+  int* s_phys = reinterpret_cast<int*>(lds + 4 * kSlot + kScoreWaves * NQT * 16 * kSRowG * 4);
 
   const int cq0 = a.cu_q[b];
   const int sq = a.cu_q[b + 1] - cq0;
@@ -615,29 +619,22 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's page pieces have landed
   __syncthreads();
 
-  // Flush the wave's score tile for pages [pg0, pg_hi): lane handles a
-  // (query, 4-page) piece; full pieces go out as one 16-byte store (pg0 is a
-  // multiple of 4: items start at multiples of the pages per item).
+  // Flush the wave's tile for pages [pg0, pg_hi) (pg0 a multiple of 4): the
+  // lane takes (query, page) pairs, maxes the four lane groups' partials, scales
+  // and stores; four consecutive lanes write four consecutive pages of a query.
   auto flush = [&](int pg0, int pg_hi) {
+    constexpr int kPairs = NQT * 16 * 4;
 #pragma unroll
-    for (int r = 0; r < NQT; ++r) {
-      const int ql = r * 16 + (lane >> 2);
-      const int c = (lane & 3) * 4;
+    for (int it = 0; it < kPairs / 64; ++it) {
+      const int k = it * 64 + lane;
+      const int ql = k >> 2, c = k & 3;
       const int qi = wave_q0 + ql;
-      const int pos = ctx + (qi - cq0);
       const int pp = pg0 + c;
-      const float* src = sbuf + ql * kSRow + c;
-      const float v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
+      const v4f g = *reinterpret_cast<const v4f*>(sbuf + ql * kSRowG + c * 4);
+      const float m = fmaxf(fmaxf(g[0], g[1]), fmaxf(g[2], g[3])) * scale;
       if (qi < q_end) {
-        float* dst = a.scores + (int64_t)qi * a.ld + pp;
-        const int vis_end = min(pg_hi, pos / kPage + 1);   // pages < vis_end are written
-        if (pp + 3 < vis_end) {
-          *reinterpret_cast<v4f*>(dst) = v4f{v0, v1, v2, v3};
-        } else {
-          if (pp + 0 < vis_end) dst[0] = v0;
-          if (pp + 1 < vis_end) dst[1] = v1;
-          if (pp + 2 < vis_end) dst[2] = v2;
-        }
+        const int pos = ctx + (qi - cq0);
+        if (pp < min(pg_hi, pos / kPage + 1)) a.scores[(int64_t)qi * a.ld + pp] = m;
       }
     }
   };
@@ -656,14 +653,13 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
       else
         page_max_f4<H, NQT>(pg, qf, col, grp, f4off, rmax);
     }
-    const int pc = (p - p0) & (kFlush - 1);    // tiles start at the item's first page
+    const int pc = (p - p0) & 3;               // tiles start at the item's first page
 #pragma unroll
     for (int n = 0; n < NQT; ++n) {
-      float m = fmaxf(fmaxf(rmax[n][0], rmax[n][1]), fmaxf(rmax[n][2], rmax[n][3]));
-      m = max_across_groups(m);
-      if ((n & 3) == grp) sbuf[(n * 16 + col) * kSRow + pc] = m * scale;
+      const float m = fmaxf(fmaxf(rmax[n][0], rmax[n][1]), fmaxf(rmax[n][2], rmax[n][3]));
+      sbuf[(n * 16 + col) * kSRowG + pc * 4 + grp] = m;
     }
-    if (pc == kFlush - 1 || p == p_end - 1) flush(p - pc, p + 1);
+    if (pc == 3 || p == p_end - 1) flush(p - pc, p + 1);
   };
 
   // One step: score pages p, p + 1; wait for this wave's pieces of p + 2, p + 3;
