@@ -9,11 +9,13 @@
 // Design (MI355X):
 //  * Planning: one small kernel turns cu_seqlens_q/k into a list of work items
 //    (request, block of queries, chunk of pages), causal-trimmed, in the
-//    workspace.  It first sums the visible pages of every query block and sizes
-//    the page chunks so the items about fill the GPU (one per compute unit when
-//    all query blocks see the same pages, three when they differ).  The scorer
-//    grid is sized from host-side upper bounds, and blocks past the device-side
-//    item count exit.
+//    workspace.  It first sums the visible pages of every query block, then
+//    tries six chunk sizes (about 1 to 6 items per compute unit) and keeps the
+//    one whose items finish first when dealt out in rounds of one per compute
+//    unit (each round as long as a full chunk plus the item's start-up), so a
+//    batch of uneven query blocks neither leaves a nearly empty last round nor
+//    pays many start-ups.  The scorer grid is sized from host-side upper
+//    bounds, and blocks past the device-side item count exit.
 //  * Scoring: tokens are the MFMA M axis, queries the N axis.  Each of the 16
 //    waves keeps the E4M3 fragments of 64/H queries (all H heads) in registers
 //    for the whole item; index-K pages (16 KiB) stream into a ring of four LDS
@@ -43,8 +45,7 @@ constexpr int kSRowG = 20;                   // prefill tile: 4 pages x 4 lane g
 constexpr int kMaxItemPages = 256;           // pages per work item, at most
 constexpr int kMinItemPages = 4;             // ... and at least (keeps score stores 16-byte aligned)
 constexpr int kPlanCUs = 256;                // compute units the item sizing aims to fill
-constexpr int kItemsUniform = kPlanCUs;      // item count aimed at when all q-blocks are alike
-constexpr int kItemsRagged = 3 * kPlanCUs;   // ... and otherwise
+constexpr int kPlanCands = 6;                // item sizes tried: about k rounds of kPlanCUs items, k = 1..6
 
 struct ItemHdr {
   int32_t n_items;
@@ -84,6 +85,57 @@ __device__ __forceinline__ int qblock_visible(int ctx, int qf, int qn) {
   return (ctx + qf + qn - 1) / kPage + 1;
 }
 
+// Candidate k of the pages per item: the w visible pages of all q-blocks cut
+// into about k * kPlanCUs chunks (a multiple of 4, within [kMinItemPages,
+// kMaxItemPages]).
+__device__ __forceinline__ int cand_pages(int64_t w, int k) {
+  const int64_t per = (int64_t)kPlanCUs * k;
+  const int64_t pc = ((w + per - 1) / per + 3) / 4 * 4;
+  return (int)min<int64_t>(kMaxItemPages, max<int64_t>(kMinItemPages, pc));
+}
+// Predicted run time of n items of at most pc pages, in fifths of a page: the
+// items run in rounds of kPlanCUs (one block per compute unit), each round as
+// long as a full item, whose start-up (query fragments, first page copies)
+// costs about 1.2 pages.  The plan keeps the candidate with the least.
+__device__ __forceinline__ int64_t cand_cost(int64_t n, int pc) {
+  return (n + kPlanCUs - 1) / kPlanCUs * (5 * (int64_t)pc + 6);
+}
+// Block-wide sums of per-thread values over W waves (result in every thread).
+template <int W, int N>
+__device__ __forceinline__ void block_sum(int (&x)[N], int (*s_red)[N]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += __shfl_xor(x[i], o);
+  if (lane == 0)
+#pragma unroll
+    for (int i = 0; i < N; ++i) s_red[wave][i] = x[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    x[i] = 0;
+    for (int k = 0; k < W; ++k) x[i] += s_red[k][i];
+  }
+  __syncthreads();
+}
+// Query blocks that all see about the same number of pages (every decode batch,
+// a short chunk over a long context) get about one item per compute unit; only
+// uneven batches weigh the candidates.
+__device__ __forceinline__ bool plan_uniform(int vmin, int vmax) { return (vmax - vmin) * 8 <= vmax; }
+
+// The candidate with the least predicted time (the smallest k on ties).
+__device__ __forceinline__ int best_pages(int64_t w, const int (&n)[kPlanCands]) {
+  int best = cand_pages(w, 1);
+  int64_t best_cost = cand_cost(n[0], best);
+  for (int k = 2; k <= kPlanCands; ++k) {
+    const int pc = cand_pages(w, k);
+    const int64_t c = cand_cost(n[k - 1], pc);
+    if (c < best_cost) { best_cost = c; best = pc; }
+  }
+  return best;
+}
+
 __global__ __launch_bounds__(256) void score_plan_kernel(const int32_t* __restrict__ cu_q,
                                                          const int32_t* __restrict__ cu_k, int B,
                                                          int qblock, int64_t max_items,
@@ -93,12 +145,13 @@ __global__ __launch_bounds__(256) void score_plan_kernel(const int32_t* __restri
   __shared__ int s_off[257];
   __shared__ int s_qf[256], s_qn[256];
   __shared__ int64_t running;
-  __shared__ int64_t s_w[4];
-  __shared__ int s_vmin[4], s_vmax[4];
-  __shared__ int s_pc;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  // pass 1: total and spread of the visible pages over all q-blocks
+  // pass 1: total and spread of the visible pages over all q-blocks; for
+  // uneven q-blocks also the chunk count of every candidate item size
+  __shared__ int64_t s_w[4];
+  __shared__ int s_vmin[4], s_vmax[4];
+  __shared__ int s_red[4][kPlanCands];
   int64_t w = 0;
   int vmin = INT32_MAX, vmax = 0;
   for (int b = 0; b < B; ++b) {
@@ -120,18 +173,31 @@ __global__ __launch_bounds__(256) void score_plan_kernel(const int32_t* __restri
   }
   if (lane == 0) { s_w[wave] = w; s_vmin[wave] = vmin; s_vmax[wave] = vmax; }
   __syncthreads();
-  if (tid == 0) {
-    int64_t tw = 0;
-    int lo = INT32_MAX, hi = 0;
-    for (int k = 0; k < 4; ++k) { tw += s_w[k]; lo = min(lo, s_vmin[k]); hi = max(hi, s_vmax[k]); }
-    const int64_t target = (hi - lo) * 8 <= hi ? kItemsUniform : kItemsRagged;
-    int64_t pc = (tw + target - 1) / target;
-    pc = (pc + 3) / 4 * 4;
-    s_pc = (int)min<int64_t>(kMaxItemPages, max<int64_t>(kMinItemPages, pc));
-    running = 0;
+  int64_t tw = 0;
+  int lo = INT32_MAX, hi = 0;
+  for (int k = 0; k < 4; ++k) { tw += s_w[k]; lo = min(lo, s_vmin[k]); hi = max(hi, s_vmax[k]); }
+  int pc_all = cand_pages(tw, 1);
+  if (!plan_uniform(lo, hi)) {
+    int cand[kPlanCands], n[kPlanCands] = {};
+#pragma unroll
+    for (int k = 0; k < kPlanCands; ++k) cand[k] = cand_pages(tw, k + 1);
+    for (int b = 0; b < B; ++b) {
+      const int sq = cu_q[b + 1] - cu_q[b];
+      const int ctx = (cu_k[b + 1] - cu_k[b]) - sq;
+      const int nqb = (sq + qblock - 1) / qblock;
+      for (int qb = tid; qb < nqb; qb += 256) {
+        const int qf = qb * qblock;
+        const int v = qblock_visible(ctx, qf, min(sq - qf, qblock));
+#pragma unroll
+        for (int k = 0; k < kPlanCands; ++k) n[k] += (v + cand[k] - 1) / cand[k];
+      }
+    }
+    block_sum<4>(n, s_red);
+    pc_all = best_pages(tw, n);
   }
+  if (tid == 0) running = 0;
   __syncthreads();
-  const int pc = s_pc;
+  const int pc = pc_all;
 
   // pass 2: emit
   for (int b = 0; b < B; ++b) {
@@ -197,6 +263,7 @@ __global__ __launch_bounds__(kPlanThreads) void score_plan_table_kernel(
   __shared__ int s_cnt[kW];
   __shared__ int64_t s_w[kW];
   __shared__ int s_lo[kW], s_hi[kW];
+  __shared__ int s_red[kW][kPlanCands];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   auto block_scan = [&](int x, int* total) {   // exclusive; adds the block total to *total
@@ -244,7 +311,8 @@ __global__ __launch_bounds__(kPlanThreads) void score_plan_table_kernel(
     return (s_ctx[b] + qf + *qn_out - 1) / kPage + 1;
   };
 
-  // pass 1: total and spread of v over all q-blocks -> pages per item
+  // pass 1: total and spread of v over all q-blocks; for uneven q-blocks also
+  // the chunk count of every candidate item size -> pages per item
   int64_t w = 0;
   int vmin = INT32_MAX, vmax = 0;
   for (int g = tid; g < G; g += kPlanThreads) {
@@ -264,10 +332,20 @@ __global__ __launch_bounds__(kPlanThreads) void score_plan_table_kernel(
   int64_t tw = 0;
   int lo = INT32_MAX, hi = 0;
   for (int k = 0; k < kW; ++k) { tw += s_w[k]; lo = min(lo, s_lo[k]); hi = max(hi, s_hi[k]); }
-  const int64_t target = (hi - lo) * 8 <= hi ? kItemsUniform : kItemsRagged;
-  int64_t pc64 = (tw + target - 1) / target;
-  pc64 = (pc64 + 3) / 4 * 4;
-  const int pc = (int)min<int64_t>(kMaxItemPages, max<int64_t>(kMinItemPages, pc64));
+  int pc = cand_pages(tw, 1);
+  if (!plan_uniform(lo, hi)) {
+    int cand[kPlanCands], n[kPlanCands] = {};
+#pragma unroll
+    for (int k = 0; k < kPlanCands; ++k) cand[k] = cand_pages(tw, k + 1);
+    for (int g = tid; g < G; g += kPlanThreads) {
+      int b, qf, qn;
+      const int v = visible(g, &b, &qf, &qn);
+#pragma unroll
+      for (int k = 0; k < kPlanCands; ++k) n[k] += (v + cand[k] - 1) / cand[k];
+    }
+    block_sum<kW>(n, s_red);
+    pc = best_pages(tw, n);
+  }
 
   // pass 2: page chunks per q-block, offsets
   int n_items = 0;
@@ -515,20 +593,23 @@ constexpr size_t score_lds_bytes() {
          kMaxItemPages * sizeof(int);
 }
 
+// One work item of the prefill scorer.  On return no copy into LDS is in
+// flight and every wave is past the item's last use of LDS.
 // KF: index-K format, 0 = E4M3 rows of 128 bytes, 1 = MXFP4.
 template <int H, int KF>
-__global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
+__device__ __forceinline__ void score_item(const ScoreK& a, int item, uint8_t* lds) {
   constexpr int NQT = score_qtiles(H);   // 16-query tiles per wave
   static_assert(NQT >= 1, "at least one query tile per wave");
   constexpr int kSlot = KF ? kF4Slot : kLdsPage;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  const int item = blockIdx.x;
-  if (item >= a.hdr->n_items) return;
   const int4 it = a.items[item];
   const int b = it.x, q_first = it.y, q_count = it.z, p0 = it.w;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The lane values below are recomputed per item (the empty asm hides that the
+  // thread index is loop-invariant), not kept live across the item loop.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   float* sbuf = reinterpret_cast<float*>(lds + 4 * kSlot) + wave * (NQT * 16 * kSRowG);
   int* s_phys = reinterpret_cast<int*>(lds + 4 * kSlot + kScoreWaves * NQT * 16 * kSRowG * 4);
@@ -679,6 +760,20 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
   }
 }
 
+// Persistent blocks (one per compute unit): block i takes items i, i + grid,
+// i + 2 grid, ... of the plan's list, so a grid sized for the host's upper bound
+// on the item count costs no dispatch rounds of empty blocks.  (Items of one
+// plan are about the same size; a shared counter handing out items dynamically
+// measured slower, its atomics serialising on one address.)
+template <int H, int KF, bool kDecode>
+__device__ __forceinline__ void take_items(const ScoreK& a, uint8_t* lds);
+
+template <int H, int KF>
+__global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  take_items<H, KF, false>(a, lds);
+}
+
 // ---------------------------------------------------------------------------
 // Decode-like batches: every request has at most 64/H queries, so every item
 // does and one wave's query tiles hold them all.  The 16 waves then split each
@@ -702,17 +797,15 @@ constexpr size_t score_pp_lds_bytes() {
          kMaxItemPages * sizeof(int) + 2 * kScoreWaves * score_qtiles(H) * 16 * sizeof(float);
 }
 
+// One work item of the decode scorer (same contract as score_item).
 template <int H, int KF>
-__global__ __launch_bounds__(kThreads) void index_score_pp_kernel(ScoreK a) {
+__device__ __forceinline__ void score_pp_item(const ScoreK& a, int item, uint8_t* lds) {
   constexpr int NQT = score_qtiles(H);
   constexpr int kQ = NQT * 16;                    // query slots
   constexpr int kSlot = KF ? kF4Slot : kLdsPage;
   constexpr int kRingN = pp_ring<KF>();
   constexpr int kReducer = 0;        // the wave that reduces the partials and stores the scores
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
-  const int item = blockIdx.x;
-  if (item >= a.hdr->n_items) return;
   const int4 it = a.items[item];
   const int b = it.x, q_first = it.y, q_count = it.z, p0 = it.w;
 
@@ -881,6 +974,27 @@ __global__ __launch_bounds__(kThreads) void index_score_pp_kernel(ScoreK a) {
     reduce(pl, 0, s_part + (buf ^ 1) * kPartBuf);
     if (pl + 1 < p_end) reduce(pl + 1, 1, s_part + (buf ^ 1) * kPartBuf);
   }
+  // copies requested past the item's end (clamped pages) land before the next
+  // item reuses the ring, and the reducer's LDS reads finish before its writes
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+template <int H, int KF>
+__global__ __launch_bounds__(kThreads) void index_score_pp_kernel(ScoreK a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  take_items<H, KF, true>(a, lds);
+}
+
+template <int H, int KF, bool kDecode>
+__device__ __forceinline__ void take_items(const ScoreK& a, uint8_t* lds) {
+  const int n_items = a.hdr->n_items;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    if constexpr (kDecode)
+      score_pp_item<H, KF>(a, item, lds);
+    else
+      score_item<H, KF>(a, item, lds);
+  }
 }
 
 }  // namespace
@@ -920,11 +1034,13 @@ ScorePlan score_plan(const msa_varlen_t* vl, int H) {
   const int qb = score_qblock(H);
   const int64_t qb_bound = ceil_div(vl->total_q, qb) + vl->batch;   // q-blocks, at most
   const int64_t max_pages = std::max<int32_t>(1, vl->max_pages);
-  // The device plan picks pages per item pc >= (sum of visible pages) / target,
-  // so sum over q-blocks of ceil(v / pc) <= target + q-blocks, unless pc hits
-  // kMaxItemPages, where it is at most q-blocks * (max_pages / kMaxItemPages + 1).
+  // The device plan picks pages per item pc >= (sum of visible pages) /
+  // (kPlanCands * kPlanCUs), so sum over q-blocks of ceil(v / pc) <=
+  // kPlanCands * kPlanCUs + q-blocks, unless pc hits kMaxItemPages, where it is
+  // at most q-blocks * (max_pages / kMaxItemPages + 1).
   p.pages_per_item = 0;   // chosen on the device
-  p.max_items = std::max<int64_t>(kItemsRagged, qb_bound * ceil_div(max_pages, kMaxItemPages)) +
+  p.max_items = std::max<int64_t>((int64_t)kPlanCands * kPlanCUs,
+                                  qb_bound * ceil_div(max_pages, kMaxItemPages)) +
                 qb_bound;
   p.workspace_bytes = sizeof(ItemHdr) + align_up((size_t)p.max_items * sizeof(int4), 256);
   return p;
@@ -964,7 +1080,8 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
   k.hdr = hdr;
   k.items = items;
   k.k_scales = a.k_scales;
-  dim3 grid((unsigned)a.plan.max_items);
+  // persistent blocks: one per compute unit (the kernels' LDS allows no more)
+  dim3 grid((unsigned)std::min<int64_t>(a.plan.max_items, device_cu_count()));
   if (a.k_scales) return launch_scorer_h<1>(grid, stream, k, a.H, a.vl.max_seqlen_q);   // MXFP4 keys
   return launch_scorer_h<0>(grid, stream, k, a.H, a.vl.max_seqlen_q);
 }

@@ -28,6 +28,9 @@ constexpr int kScoreQueriesPerWave = MSA_SCORE_QPW;
 constexpr int score_qtiles(int H) { return kScoreQueriesPerWave / 16 / H; }
 constexpr int score_qblock(int H) { return kScoreWaves * 16 * score_qtiles(H); }
 
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
 struct ScorePlan {
   int32_t pages_per_item;   // 0: chosen by the device plan
   int64_t max_items;        // host upper bound (grid size before padding)

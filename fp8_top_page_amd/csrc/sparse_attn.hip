@@ -494,6 +494,8 @@ __global__ __launch_bounds__(1024) void attn_combine_kernel(CombineK a) {
   *reinterpret_cast<uint2*>(dst + 16) = make_uint2(pack2_bf16(o[4], o[5]), pack2_bf16(o[6], o[7]));
 }
 
+}  // namespace
+
 int device_cu_count() {
   static int cache[64] = {0};
   int dev = 0;
@@ -505,8 +507,6 @@ int device_cu_count() {
   if (dev < 64) cache[dev] = n;
   return n;
 }
-
-}  // namespace
 
 // Partial rows: one per (CSR entry, head of its selection), plus one trash row.
 static int64_t partial_rows(const msa_varlen_t* vl, int Hq, int n_sel, int topk) {
