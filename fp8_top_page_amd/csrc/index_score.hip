@@ -26,11 +26,12 @@
 //    scores a 16-token slice of one page for all the queries, and the slices'
 //    maxima are reduced through LDS.
 //  * Epilogue: each lane holds 4 consecutive tokens of one query per 16-token
-//    tile; the max over the page's 8 tiles is taken in registers and the lane's
-//    partial max goes to an LDS tile (4 pages x 4 lane groups per query).  Every
-//    4 pages the tile is flushed: a lane maxes the 4 groups of one (query, page)
-//    pair, scales it and stores it, four lanes covering 16 contiguous bytes of a
-//    query's row.  (The cross-group max thus costs no lane exchanges per page.)
+//    tile; the max over the page's 8 tiles is taken in registers, one lane
+//    exchange folds the 4 lane groups into 2, and the two partial maxima go to
+//    an LDS tile (8 pages x 2 per query).  At the end of every group of 8 pages
+//    the tile is flushed: a lane maxes the 2 partials of each page of a (query,
+//    4-page) half group, scales them and stores them, two lanes covering the 32 contiguous bytes of a
+//    query's group (whole 32-byte write granules of HBM).
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -41,7 +42,7 @@ constexpr int kLdsPage = kPage * kDim;       // 16 KiB: 128 rows of 128 B, 16-by
 constexpr int kThreads = kScoreWaves * 64;
 constexpr int kFlush = 16;                   // pages per score-tile flush (decode kernel)
 constexpr int kSRow = kFlush + 1;            // score-tile row stride in floats
-constexpr int kSRowG = 20;                   // prefill tile: 4 pages x 4 lane groups, padded
+constexpr int kSRowG = 20;                   // prefill tile: 8 pages x 2 partials, padded (16-byte rows)
 constexpr int kMaxItemPages = 256;           // pages per work item, at most
 constexpr int kMinItemPages = 4;             // ... and at least (keeps score stores 16-byte aligned)
 constexpr int kPlanCUs = 256;                // compute units the item sizing aims to fill
@@ -583,9 +584,8 @@ __device__ __forceinline__ void page_max_causal_f4(const uint8_t* __restrict__ p
 }
 
 // LDS per block: a ring of four index-K pages (two being scored, two being
-// filled), one private partial-max tile per wave ([queries of the wave][4 pages
-// x 4 lane groups], rows padded to kSRowG floats: 16-byte aligned, and the 64
-// lanes' writes fall in distinct banks), and the item's physical page ids.
+// filled), one private partial-max tile per wave ([queries of the wave][8 pages
+// x 2 partials], rows padded to kSRowG floats), and the item's physical page ids.
 template <int H, int KF>
 constexpr size_t score_lds_bytes() {
   return 4 * (KF ? kF4Slot : kLdsPage) +
@@ -700,22 +700,32 @@ __device__ __forceinline__ void score_item(const ScoreK& a, int item, uint8_t* l
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's page pieces have landed
   __syncthreads();
 
-  // Flush the wave's tile for pages [pg0, pg_hi) (pg0 a multiple of 4): the
-  // lane takes (query, page) pairs, maxes the four lane groups' partials, scales
-  // and stores; four consecutive lanes write four consecutive pages of a query.
-  auto flush = [&](int pg0, int pg_hi) {
-    constexpr int kPairs = NQT * 16 * 4;
-#pragma unroll
-    for (int it = 0; it < kPairs / 64; ++it) {
-      const int k = it * 64 + lane;
-      const int ql = k >> 2, c = k & 3;
+  // Flush the wave's tile for pages [pg_lo, pg_hi) of the 8-page group that
+  // starts at pg0 (a multiple of 8): a lane takes a (query, 4-page) half group,
+  // maxes the two half-wave partials of each page, scales and stores the four
+  // scores as one 16-byte store when all four are to be written (two lanes
+  // cover the 32 contiguous bytes of a query's group).
+  auto flush = [&](int pg0, int pg_lo, int pg_hi) {
+    constexpr int kTasks = NQT * 16 * 2;
+    for (int t = lane; t < kTasks; t += 64) {
+      const int ql = t >> 1, h = t & 1;
       const int qi = wave_q0 + ql;
-      const int pp = pg0 + c;
-      const v4f g = *reinterpret_cast<const v4f*>(sbuf + ql * kSRowG + c * 4);
-      const float m = fmaxf(fmaxf(g[0], g[1]), fmaxf(g[2], g[3])) * scale;
+      const int pp = pg0 + 4 * h;
+      const v4f g0 = *reinterpret_cast<const v4f*>(sbuf + ql * kSRowG + 8 * h);
+      const v4f g1 = *reinterpret_cast<const v4f*>(sbuf + ql * kSRowG + 8 * h + 4);
+      const v4f m = v4f{fmaxf(g0[0], g0[1]), fmaxf(g0[2], g0[3]), fmaxf(g1[0], g1[1]),
+                        fmaxf(g1[2], g1[3])} * scale;
       if (qi < q_end) {
         const int pos = ctx + (qi - cq0);
-        if (pp < min(pg_hi, pos / kPage + 1)) a.scores[(int64_t)qi * a.ld + pp] = m;
+        const int hi = min(pg_hi, pos / kPage + 1);        // pages [pg_lo, hi) are written
+        float* dst = a.scores + (int64_t)qi * a.ld + pp;
+        if (pp >= pg_lo && pp + 4 <= hi) {
+          *reinterpret_cast<v4f*>(dst) = m;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (pp + j >= pg_lo && pp + j < hi) dst[j] = m[j];
+        }
       }
     }
   };
@@ -734,13 +744,15 @@ __device__ __forceinline__ void score_item(const ScoreK& a, int item, uint8_t* l
       else
         page_max_f4<H, NQT>(pg, qf, col, grp, f4off, rmax);
     }
-    const int pc = (p - p0) & 3;               // tiles start at the item's first page
+    const int pc = p & 7;                      // slot in the 8-page group
 #pragma unroll
     for (int n = 0; n < NQT; ++n) {
-      const float m = fmaxf(fmaxf(rmax[n][0], rmax[n][1]), fmaxf(rmax[n][2], rmax[n][3]));
-      sbuf[(n * 16 + col) * kSRowG + pc * 4 + grp] = m;
+      float m = fmaxf(fmaxf(rmax[n][0], rmax[n][1]), fmaxf(rmax[n][2], rmax[n][3]));
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+      m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));   // lane groups g and g ^ 2
+      if (grp < 2) sbuf[(n * 16 + col) * kSRowG + pc * 2 + grp] = m;
     }
-    if (pc == 3 || p == p_end - 1) flush(p - pc, p + 1);
+    if (pc == 7 || p == p_end - 1) flush(p - pc, max(p0, p - pc), p + 1);
   };
 
   // One step: score pages p, p + 1; wait for this wave's pieces of p + 2, p + 3;
