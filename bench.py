@@ -52,6 +52,11 @@ def parse():
                          "on the device to E2M1 blocks with E8M0 scales)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle sample")
+    ap.add_argument("--hbm-record", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                      "COPY_WRITE_CSV"),
+                    help="write profiles/index_score_<workload>_hbm.json and print the per-kernel "
+                         "byte table from four rocprofv3 counter_collection.csv files (FETCH_SIZE "
+                         "and WRITE_SIZE over this benchmark, then over --copy-probe-mib 1024)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB three times (the "
                          "reference kernel that scales HBM byte counters) and exit")
@@ -70,6 +75,77 @@ def copy_probe(mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": n, "repeats": 3}), flush=True)
+
+
+SCORER_SOURCES = ["fp8_top_page_amd/csrc/index_score.hip", "fp8_top_page_amd/csrc/msa_device.h",
+                  "fp8_top_page_amd/csrc/msa_internal.h"]
+
+
+def _sources_sha256(srcs):
+    import hashlib
+    h = hashlib.sha256()
+    for src in srcs:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    return h.hexdigest()
+
+
+def _counter_kib(csv_path):
+    """{short kernel name: [counter value in KiB per dispatch]} from a rocprofv3
+    counter_collection.csv (one counter per pass)."""
+    import csv
+    out = {}
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            name = name.replace("void ", "", 1).split("(msa::")[0].split("(at::")[0]
+            name = name.replace("msa::(anonymous namespace)::", "")
+            out.setdefault(name, []).append(float(row["Counter_Value"]))
+    return out
+
+
+def hbm_record(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mib=1024):
+    """HBM bytes per launch of every kernel of the path: the FETCH_SIZE and
+    WRITE_SIZE averages (KiB per dispatch), each scaled by actual / counted bytes
+    of a plain device copy of copy_mib MiB (the largest copy dispatches of the
+    probe run).  Writes the scorer's record (with the SHA-256 of its sources, so
+    it is void once they change) and prints a markdown table."""
+    import numpy as np
+    fetch, write = _counter_kib(fetch_csv), _counter_kib(write_csv)
+    cf = _counter_kib(copy_fetch_csv)["__amd_rocclr_copyBuffer"]
+    cw = _counter_kib(copy_write_csv)["__amd_rocclr_copyBuffer"]
+    copy_kib = copy_mib * 1024.0
+    f_factor = copy_kib / float(np.mean(sorted(cf)[-3:]))     # the three 1 GiB copies
+    w_factor = copy_kib / float(np.mean(sorted(cw)[-3:]))
+    scorer = "index_score_kernel<1, 0>"
+    rec = {
+        "kernel": scorer,
+        "workload": workload,
+        "fetch_bytes_counted": float(np.mean(fetch[scorer])) * 1024.0,
+        "write_bytes_counted": float(np.mean(write[scorer])) * 1024.0,
+        "fetch_factor": f_factor,
+        "write_factor": w_factor,
+    }
+    rec["hbm_bytes_per_launch"] = (rec["fetch_bytes_counted"] * f_factor +
+                                   rec["write_bytes_counted"] * w_factor)
+    rec["sources"] = SCORER_SOURCES
+    rec["sources_sha256"] = _sources_sha256(SCORER_SOURCES)
+    out = os.path.join(ROOT, "profiles", f"index_score_{workload}_hbm.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(f"copy calibration: FETCH_SIZE factor {f_factor:.3f}, WRITE_SIZE factor {w_factor:.3f}")
+    print("| kernel | launches | fetched MiB (scaled) | written MiB (scaled) |")
+    print("|---|---|---|---|")
+    rows = []
+    for k in fetch:
+        if k.startswith("__amd") or k.startswith("at::") or k.startswith("void at::"):
+            continue
+        fm = float(np.mean(fetch[k])) * f_factor / 1024.0
+        wm = float(np.mean(write.get(k, [0.0]))) * w_factor / 1024.0
+        rows.append((fm + wm, k, len(fetch[k]), fm, wm))
+    for _, k, n, fm, wm in sorted(rows, reverse=True):
+        print(f"| `{k}` | {n} | {fm:.1f} | {wm:.1f} |")
+    print(f"wrote {out}: {rec['hbm_bytes_per_launch'] / 1e6:.1f} MB per scorer launch")
 
 
 def algorithmic_work(inp, sel, key_bytes=128.0):
@@ -113,15 +189,11 @@ def scorer_hbm_traffic(workload):
     (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for a 1 GiB
     copy), or None when there is none for this workload or the scorer's sources
     have changed since the counters were taken."""
-    import hashlib
     f = os.path.join(ROOT, "profiles", f"index_score_{workload}_hbm.json")
     if not os.path.exists(f):
         return None
     rec = json.load(open(f))
-    h = hashlib.sha256()
-    for src in rec["sources"]:
-        h.update(open(os.path.join(ROOT, src), "rb").read())
-    if h.hexdigest() != rec["sources_sha256"]:
+    if _sources_sha256(rec["sources"]) != rec["sources_sha256"]:
         return None
     return int(round(rec["hbm_bytes_per_launch"]))
 
@@ -215,6 +287,9 @@ def time_insert(inp, db, steps, stream):
 
 def main():
     args = parse()
+    if args.hbm_record:
+        hbm_record(args.workload, *args.hbm_record)
+        return
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
         return
