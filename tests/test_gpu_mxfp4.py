@@ -75,6 +75,7 @@ def _run(inp, data, scales):
     ((64, 3, 50, 0), (9000, 200, 64, 500), 1, 8, 1),  # decode-like: page-parallel kernel
     ((32, 7, 1), (5000, 40, 70000), 2, 16, 2),
     ((16, 9), (3000, 777), 4, 8, 4),
+    ((8,) * 40, (12800,) * 40, 1, 8, 1),              # 280 items: several per scorer block
 ])
 def test_scores_from_mxfp4_keys(sq, sk, H, Hq, Hkv):
     print(f"\n[parity] mxfp4 keys sq={sq} sk={sk} H={H}", flush=True)

@@ -92,6 +92,10 @@ def _small_inputs(seqlen_q, seqlen_k, H=1, Hq=8, Hkv=1, seed=11):
     ((64, 3, 50, 0), (9000, 200, 64, 500), 1, 8, 1),
     ((32, 7, 1), (5000, 40, 70000), 2, 16, 2),
     ((16, 9), (3000, 777), 4, 8, 4),
+    # 40 decode requests of 100 pages plan 280 items of 16 pages: more items
+    # than scorer blocks, so blocks score several items in turn
+    ((8,) * 40, (12800,) * 40, 1, 8, 1),
+    ((4,) * 40, (12800,) * 40, 2, 16, 2),
 ])
 def test_edge_shapes(sq, sk, H, Hq, Hkv):
     print(f"\n[parity] edge shape sq={sq} sk={sk} H={H} Hq={Hq} Hkv={Hkv}", flush=True)
