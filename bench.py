@@ -295,7 +295,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              f"(the path is per tensor-parallel rank: see DESIGN.md on sharding)", file=sys.stderr)
+              f"(the path is one tensor-parallel rank's share; sharding across GPUs is not built)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
