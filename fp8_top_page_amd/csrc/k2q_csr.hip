@@ -26,7 +26,8 @@
 //   fill   -- per block: base offsets from the totals of earlier blocks, scan of
 //             its units, then one wave per unit (one lane per bitmap word)
 //             writes q_indices (ascending), each word's first CSR position,
-//             row_ptr and the work items of at most kAttnQC entries each:
+//             row_ptr and the work items of at most 32 or 64 entries each
+//             (64 when the rows average at least 64 queries):
 //               {first entry, count, physical page, selection head}
 //               {context - cu_seqlens_q[b] - 128 j, valid tokens of the page, row, request}
 //             (a query i of the item sees the page's tokens up to i + the first
@@ -156,6 +157,7 @@ struct CountK {
   int32_t G;              // lanes per piece
   int32_t* blk_tot;       // [n_blocks]: entries
   int32_t* blk_items;     // [n_blocks]: attention items
+  int32_t qc;             // queries per attention item, at most
 };
 
 __global__ __launch_bounds__(kThreads) void csr_count_kernel(CountK a) {
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void csr_count_kernel(CountK a) {
     const int c = __popc(bits[k]);
     const int n = piece_sum(c, a.G);
     tot += c;
-    its += (lane & (a.G - 1)) == 0 ? (n + kAttnQC - 1) / kAttnQC : 0;
+    its += (lane & (a.G - 1)) == 0 ? (n + a.qc - 1) / a.qc : 0;
   }
   tot = wave_sum(tot);
   its = wave_sum(its);
@@ -259,6 +261,7 @@ struct FillK {
   int4* items;
   int64_t max_items;
   Hdr* hdr;
+  int32_t qc;              // queries per attention item, at most
 };
 
 __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
@@ -304,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
   for (int k = 0; k < kUnitsPerWave; ++k) {
     const int c = __popc(bits[k]);
     const int n = piece_sum(c, G);
-    const int it = (lane & (G - 1)) == 0 ? (n + kAttnQC - 1) / kAttnQC : 0;
+    const int it = (lane & (G - 1)) == 0 ? (n + a.qc - 1) / a.qc : 0;
     const int tc = wave_sum(c), ti = wave_sum(it);
     if (lane == 0) { s_cnt[wave * kUnitsPerWave + k] = tc; s_itc[wave * kUnitsPerWave + k] = ti; }
   }
@@ -364,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
     // work items of the lane's piece: (row, first entry, count), lane t of the
     // piece writing item t (a piece of G words yields at most G items)
     const int n = piece_sum(c, G);
-    const int n_it = (n + kAttnQC - 1) / kAttnQC;
+    const int n_it = (n + a.qc - 1) / a.qc;
     const int it = lane == lead ? n_it : 0;
     const int iincl = wave_inclusive_scan(it);
     const int p_pos = __shfl(pos, lead);
@@ -384,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
         const int sk = ck[b + 1] - ck[b];
         const int ctx = sk - (cq[b + 1] - cq[b]);
         const int phys = a.block_table[(int64_t)b * a.bt_stride + j];
-        a.items[2 * idx] = make_int4(p_pos + t * kAttnQC, min(kAttnQC, n - t * kAttnQC), phys, g);
+        a.items[2 * idx] = make_int4(p_pos + t * a.qc, min(a.qc, n - t * a.qc), phys, g);
         a.items[2 * idx + 1] = make_int4(ctx - cq[b] - j * kPage, sk - j * kPage, (int)row, b);
       }
     }
@@ -408,10 +411,11 @@ SchedLayout sched_layout(const msa_varlen_t* vl, int n_sel, int topk) {
   L.word_chunks = std::max<int64_t>(1, ceil_div((int64_t)n_sel * std::max(vl->max_pages, 1), kWordRows));
   L.word_blocks = L.words_per_row * std::max(vl->batch, 0) * L.word_chunks;
   // a piece (a row's words inside one unit) holding c entries yields
-  // ceil(c / kAttnQC) items; only pieces with entries yield any
+  // ceil(c / item_q) items; only pieces with entries yield any
+  L.item_q = attn_item_queries(vl);
   const int64_t entries = (int64_t)n_sel * vl->total_q * topk;
   const int64_t pieces = L.n_rows * std::max<int64_t>(1, L.words_per_row / kUnitWords);
-  L.max_items = ceil_div(entries, kAttnQC) + std::min(entries, pieces);
+  L.max_items = ceil_div(entries, L.item_q) + std::min(entries, pieces);
   size_t off = 0;
   L.hdr = off;        off += sizeof(Hdr);
   L.row_base = off;   off += align_up(sizeof(int32_t) * (vl->batch + 1), 256);
@@ -445,7 +449,7 @@ hipError_t launch_k2q_csr(const CsrArgs& a, hipStream_t stream) {
 
   const int32_t G = (int32_t)std::min<int64_t>(L.words_per_row, kUnitWords);
   const int64_t n_words = L.n_rows * L.words_per_row;
-  CountK cnt{bitmap, n_words, G, blk_tot, blk_items};
+  CountK cnt{bitmap, n_words, G, blk_tot, blk_items, L.item_q};
   hipLaunchKernelGGL(csr_count_kernel, dim3((unsigned)L.n_blocks), dim3(kThreads), 0, stream, cnt);
 
   const int32_t prefixed = L.n_blocks >= kScanFrom ? 1 : 0;
@@ -455,7 +459,7 @@ hipError_t launch_k2q_csr(const CsrArgs& a, hipStream_t stream) {
   FillK fk{a.vl.cu_seqlens_q, a.vl.cu_seqlens_k, a.vl.batch, a.vl.block_table,
            a.vl.block_table_stride, a.vl.total_rows, row_base, bitmap, L.words_per_row, G,
            n_words, L.n_rows, (int32_t)L.n_blocks, blk_tot, blk_items, prefixed, a.row_ptr,
-           a.q_indices, wbase, items, L.max_items, hdr};
+           a.q_indices, wbase, items, L.max_items, hdr, L.item_q};
   hipLaunchKernelGGL(csr_fill_kernel, dim3((unsigned)L.n_blocks), dim3(kThreads), 0, stream, fk);
   return hipGetLastError();
 }

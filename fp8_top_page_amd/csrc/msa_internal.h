@@ -67,8 +67,8 @@ struct TopkArgs {
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 
 // ---- k2q CSR + attention schedule ----------------------------------------
-// Queries (CSR entries) per attention work item.
-constexpr int kAttnQC = 32;
+// Queries (CSR entries) per attention work item, at most.
+constexpr int kAttnQCMax = 64;
 
 struct SchedLayout {
   // byte offsets inside the schedule buffer
@@ -78,6 +78,7 @@ struct SchedLayout {
   int64_t n_units;        // bitmap units (64 consecutive words of the row-major bitmap)
   int64_t n_blocks;       // count/fill blocks
   int64_t max_items;
+  int32_t item_q;         // queries (CSR entries) per attention work item, at most
   int64_t inv_len;        // total_q * n_sel * topk: entries of the (query, slot) -> row table
   int64_t word_chunks;    // row chunks per (request, bitmap word) in the words pass
   int64_t word_blocks;    // blocks of the words pass
@@ -149,6 +150,15 @@ struct Mx4Args {             // MXFP4 index-key insert
 hipError_t launch_insert_mxfp4(const Mx4Args& q, hipStream_t stream);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// Queries per attention work item: 64 when the rows average at least that many
+// (long prefill chunks: each staged page serves more row tiles and is staged
+// half as often), else 32 (rows of a few queries, where a row of the local page
+// holds many more than the rest and longer items would finish last).
+inline int32_t attn_item_queries(const msa_varlen_t* vl) {
+  const int64_t per_row =
+      ceil_div((int64_t)vl->total_q * kTopK, vl->total_rows > 0 ? vl->total_rows : 1);
+  return per_row >= kAttnQCMax ? kAttnQCMax : 32;
+}
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace msa

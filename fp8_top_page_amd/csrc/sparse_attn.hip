@@ -10,7 +10,7 @@
 // combine.
 //
 // Page-major (k2q) design: a work item is (CSR row = one logical page of one
-// request, up to kAttnQC of the queries that selected it, one KV head).  The
+// request, up to 32 or 64 of the queries that selected it, one KV head).  The
 // block stages the page's K (token-major) and V (transposed, d-major) in LDS
 // once and every wave runs 16-row tiles of (query, q-head) rows against it:
 //   S^T = K Q^T           8 MFMA 16x16x128 (tokens on M, rows on N)
@@ -179,7 +179,7 @@ __device__ __forceinline__ void stage_page(const PageRegs& r, const Work& w, uin
       }
     }
   }
-  if (tid < kAttnQC) s_qi[tid] = r.qi;
+  if (tid < kAttnQCMax) s_qi[tid] = r.qi;
 }
 
 // The rows of NT consecutive 16-row tiles on one wave: lane (col, grp) of tile
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(kThreads, kWide ? kBlocksWide : kBlocksNarrow) void
     AttnK a) {
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[kPage * kRowB];
   __shared__ __attribute__((aligned(16))) uint8_t vt_lds[kDim * kRowB];
-  __shared__ int s_qi[kAttnQC];
+  __shared__ int s_qi[kAttnQCMax];
 
   const int n_items = *a.n_items;
   const int64_t n_work = (int64_t)n_items * a.GY;
@@ -548,9 +548,9 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   const int64_t max_work = L.max_items * k.GY;
   if (max_work > 0) {
     // Rows per item from the host bound on entries per CSR row (total_q * topk
-    // entries over total_rows rows, at most kAttnQC queries per item).
+    // entries over total_rows rows, at most L.item_q queries per item).
     const int64_t per_row = ceil_div((int64_t)a.vl.total_q * kTopK, std::max(a.vl.total_rows, 1));
-    const bool wide = std::min<int64_t>(per_row, kAttnQC) * k.G >= 2 * kWaves * 16;
+    const bool wide = std::min<int64_t>(per_row, L.item_q) * k.G >= 2 * kWaves * 16;
     const int per_cu = wide ? kBlocksWide : kBlocksNarrow;
     const int64_t grid = std::min<int64_t>(max_work, (int64_t)device_cu_count() * per_cu);
     if (wide)
