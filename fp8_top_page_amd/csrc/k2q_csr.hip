@@ -14,7 +14,8 @@
 // queries is spread over many waves).  Units are the grain of the count, scan
 // and fill passes.
 //
-// Three launches on the caller's stream (four for large grids), no host sync:
+// Three launches on the caller's stream (four for large grids, one more for
+// very long rows), no host sync:
 //   words  -- one block per (request, 32 query slots): sets the bits of those
 //             slots for every row of the request in LDS and writes the word
 //             column out (so the bitmap needs no clearing and no global
@@ -32,6 +33,8 @@
 //               {context - cu_seqlens_q[b] - 128 j, valid tokens of the page, row, request}
 //             (a query i of the item sees the page's tokens up to i + the first
 //             value; the physical page comes from the block table)
+//   (order) -- rows of >= 512 queries on average only: the items' order for
+//             the attention, sorted by the query range of their first query
 // The CSR position of (query i, slot s) is then the first position of i's word
 // in its row plus the set bits below i in that word; the attention's combine
 // computes it from the row table, the word positions and the bitmap.
@@ -394,6 +397,45 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
   }
 }
 
+// Attention item order for long rows: items sorted by the query range of
+// their first query (bucket = global query index >> shift), so that the
+// attention's resident blocks work on one range of queries at a time and
+// that range's query rows stay in cache while every page that any of them
+// selected is visited; within a bucket items keep about their list order
+// (rows ascending).  One block: histogram, scan, scatter of item indices.
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderKeys = 1024;
+
+__global__ __launch_bounds__(kOrderThreads) void item_order_kernel(const Hdr* __restrict__ hdr,
+                                                                   const int4* __restrict__ items,
+                                                                   const int32_t* __restrict__ q_indices,
+                                                                   int shift, int n_keys,
+                                                                   int64_t max_items,
+                                                                   int32_t* __restrict__ perm) {
+  __shared__ int s_cnt[kOrderKeys];
+  __shared__ int s_wave[kOrderThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = (int)min<int64_t>(hdr->n_items, max_items);
+  for (int k = tid; k < kOrderKeys; k += kOrderThreads) s_cnt[k] = 0;
+  __syncthreads();
+  auto key_of = [&](int i) {
+    return min(n_keys - 1, max(0, q_indices[items[2 * i].x] >> shift));
+  };
+  for (int i = tid; i < n; i += kOrderThreads) atomicAdd(&s_cnt[key_of(i)], 1);
+  __syncthreads();
+  // exclusive scan over the keys (one per thread)
+  const int c = s_cnt[tid];
+  const int incl = wave_inclusive_scan(c);
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  int off = 0;
+  for (int k = 0; k < wave; ++k) off += s_wave[k];
+  __syncthreads();
+  s_cnt[tid] = off + incl - c;
+  __syncthreads();
+  for (int i = tid; i < n; i += kOrderThreads) perm[atomicAdd(&s_cnt[key_of(i)], 1)] = i;
+}
+
 }  // namespace
 
 SchedLayout sched_layout(const msa_varlen_t* vl, int n_sel, int topk) {
@@ -416,11 +458,25 @@ SchedLayout sched_layout(const msa_varlen_t* vl, int n_sel, int topk) {
   const int64_t entries = (int64_t)n_sel * vl->total_q * topk;
   const int64_t pieces = L.n_rows * std::max<int64_t>(1, L.words_per_row / kUnitWords);
   L.max_items = ceil_div(entries, L.item_q) + std::min(entries, pieces);
+  // rows of at least 512 queries on average (a long fresh prefill): items in
+  // query-range order, ranges of 2048 queries (wider if there would be more
+  // than kOrderKeys); shorter rows lose more page reuse than they gain
+  L.order_shift = 0;
+  L.order_keys = 1;
+  const int64_t per_row =
+      ceil_div((int64_t)vl->total_q * topk, std::max<int64_t>(1, vl->total_rows));
+  if (L.item_q == kAttnQCMax && per_row >= 512 && L.max_items <= (int64_t)INT32_MAX) {
+    int shift = 11;
+    while ((std::max<int64_t>(vl->total_q, 1) >> shift) + 1 > kOrderKeys) ++shift;
+    L.order_shift = shift;
+    L.order_keys = (int32_t)((std::max<int64_t>(vl->total_q, 1) >> shift) + 1);
+  }
   size_t off = 0;
   L.hdr = off;        off += sizeof(Hdr);
   L.row_base = off;   off += align_up(sizeof(int32_t) * (vl->batch + 1), 256);
   L.blk_tot = off;    off += align_up(sizeof(int32_t) * 2 * L.n_blocks, 256);
   L.items = off;      off += align_up(2 * sizeof(int4) * std::max<int64_t>(1, L.max_items), 256);
+  L.perm = off;       off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.max_items), 256);
   L.rowsel = off;     off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.inv_len), 256);
   L.wbase = off;      off += align_up(sizeof(int32_t) * L.n_rows * L.words_per_row, 256);
   L.bitmap = off;     off += align_up(sizeof(uint32_t) * L.n_rows * L.words_per_row, 256);
@@ -461,6 +517,10 @@ hipError_t launch_k2q_csr(const CsrArgs& a, hipStream_t stream) {
            n_words, L.n_rows, (int32_t)L.n_blocks, blk_tot, blk_items, prefixed, a.row_ptr,
            a.q_indices, wbase, items, L.max_items, hdr, L.item_q};
   hipLaunchKernelGGL(csr_fill_kernel, dim3((unsigned)L.n_blocks), dim3(kThreads), 0, stream, fk);
+  if (L.order_shift > 0)
+    hipLaunchKernelGGL(item_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, hdr, items,
+                       a.q_indices, L.order_shift, L.order_keys, L.max_items,
+                       reinterpret_cast<int32_t*>(a.sched + L.perm));
   return hipGetLastError();
 }
 

@@ -72,13 +72,15 @@ constexpr int kAttnQCMax = 64;
 
 struct SchedLayout {
   // byte offsets inside the schedule buffer
-  size_t hdr, row_base, blk_tot, items, rowsel, wbase, bitmap, total;
+  size_t hdr, row_base, blk_tot, items, perm, rowsel, wbase, bitmap, total;
   int64_t n_rows;         // n_sel * total_rows
   int64_t words_per_row;  // bitmap words per row (one bit per query slot, padded)
   int64_t n_units;        // bitmap units (64 consecutive words of the row-major bitmap)
   int64_t n_blocks;       // count/fill blocks
   int64_t max_items;
   int32_t item_q;         // queries (CSR entries) per attention work item, at most
+  int32_t order_shift;    // items taken in order of (first query >> order_shift); 0: list order
+  int32_t order_keys;     // distinct keys of that order
   int64_t inv_len;        // total_q * n_sel * topk: entries of the (query, slot) -> row table
   int64_t word_chunks;    // row chunks per (request, bitmap word) in the words pass
   int64_t word_blocks;    // blocks of the words pass

@@ -53,6 +53,7 @@ struct AttnK {
   int32_t num_pages, Hkv;
   const int32_t* q_indices;
   const int4* items;
+  const int32_t* perm;             // order in which the items are taken, or nullptr: list order
   const int32_t* n_items;
   float logit_scale_log2;          // softmax_scale * log2(e)
   const float* q_scale;
@@ -377,18 +378,40 @@ __global__ __launch_bounds__(kThreads, kWide ? kBlocksWide : kBlocksNarrow) void
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: loops below do not diverge
   const float zscale = a.logit_scale_log2 * (a.q_scale ? *a.q_scale : 1.f) *
                        (a.k_scale ? *a.k_scale : 1.f);
-  // metadata of work index x (clamped to the last item, so the load is always valid)
+  // item of work index x (clamped to the last item, so the loads are always
+  // valid), through the order table when there is one
   auto item_of = [&](int64_t x) -> int64_t {
     const int64_t it = x / a.GY;
-    return it < n_items - 1 ? it : (int64_t)(n_items - 1);
+    const int64_t c = it < n_items - 1 ? it : (int64_t)(n_items - 1);
+    if constexpr (kWide) {                   // only long rows are ordered
+      if (a.perm) return (int64_t)a.perm[c];
+    }
+    return c;
   };
 
-  // prologue: the first item's page in registers, the second item's metadata in flight
-  Work cur = decode_work(a, w, a.items[2 * item_of(w)], a.items[2 * item_of(w) + 1]);
+  // prologue: the first item's page in registers, the second item's metadata in
+  // flight.  With an order table (wide kernel), the item index of the one after
+  // that is known too: a table lookup is made one work step before the item's
+  // metadata is requested, so requesting it never waits on a load issued after
+  // a page fetch.  (The narrow kernel keeps the plain sequence: the ordered one
+  // compiled to a slower schedule there.)
+  Work cur;
   PageRegs pr;
-  fetch_page(pr, a, cur, tid);
-  int4 mx = a.items[2 * item_of(w + gridDim.x)];
-  int4 my = a.items[2 * item_of(w + gridDim.x) + 1];
+  int4 mx, my;
+  int64_t i_nn = 0;
+  if constexpr (kWide) {
+    const int64_t i0 = item_of(w), i1 = item_of(w + gridDim.x);
+    i_nn = item_of(w + 2 * (int64_t)gridDim.x);
+    cur = decode_work(a, w, a.items[2 * i0], a.items[2 * i0 + 1]);
+    mx = a.items[2 * i1];
+    my = a.items[2 * i1 + 1];
+    fetch_page(pr, a, cur, tid);
+  } else {
+    cur = decode_work(a, w, a.items[2 * item_of(w)], a.items[2 * item_of(w) + 1]);
+    fetch_page(pr, a, cur, tid);
+    mx = a.items[2 * item_of(w + gridDim.x)];
+    my = a.items[2 * item_of(w + gridDim.x) + 1];
+  }
 
   for (;;) {
     __syncthreads();                         // the previous item is done with LDS
@@ -401,8 +424,14 @@ __global__ __launch_bounds__(kThreads, kWide ? kBlocksWide : kBlocksNarrow) void
     const Work nxt = has_next ? decode_work(a, wn, mx, my) : cur;
     auto prefetch = [&]() {
       fetch_page(pr, a, nxt, tid);
-      mx = a.items[2 * item_of(wn + gridDim.x)];
-      my = a.items[2 * item_of(wn + gridDim.x) + 1];
+      if constexpr (kWide) {
+        mx = a.items[2 * i_nn];
+        my = a.items[2 * i_nn + 1];
+        i_nn = item_of(wn + 2 * (int64_t)gridDim.x);
+      } else {
+        mx = a.items[2 * item_of(wn + gridDim.x)];
+        my = a.items[2 * item_of(wn + gridDim.x) + 1];
+      }
     };
     const int n_tiles = (cur.count * a.G + 15) >> 4;
     if (!kWide)
@@ -537,6 +566,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   k.Hkv = a.Hkv;
   k.q_indices = a.q_indices;
   k.items = reinterpret_cast<const int4*>(a.sched + L.items);
+  k.perm = L.order_shift > 0 ? reinterpret_cast<const int32_t*>(a.sched + L.perm) : nullptr;
   k.n_items = reinterpret_cast<const int32_t*>(a.sched + L.hdr);
   k.logit_scale_log2 = a.softmax_scale * kLog2e;
   k.q_scale = a.q_scale;
