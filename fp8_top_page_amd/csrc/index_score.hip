@@ -494,27 +494,39 @@ __device__ __forceinline__ void page_max(const uint8_t* __restrict__ pg, const v
 
 // Same with the causal cut: token (16T + 4*grp + i) of the page counts for the
 // query in lane column n only if it is <= lim0 + 16n (lim0 = last visible token
-// of the wave's first query tile, consecutive queries are consecutive positions).
-// Used only on the few pages that cross a query's position; not unrolled over T.
+// of the lane's query in tile 0; consecutive queries are consecutive
+// positions).  L0 (wave-uniform) is the limit of the wave's first query, so the
+// limits of tile n span [L0 + 16n, L0 + 16n + 15]: token tiles past all of them
+// are skipped, tiles below all of them take the plain max, and only the tiles
+// that straddle them are masked element by element.  Used only on the few
+// pages that cross a query's position.
 template <int H, int NQT>
 __device__ __forceinline__ void page_max_causal(const uint8_t* __restrict__ pg,
-                                                const v8i (&qf)[NQT][H], int lim0, int col,
+                                                const v8i (&qf)[NQT][H], int lim0, int L0, int col,
                                                 int grp, const Swz& z, v4f (&rmax)[NQT]) {
 #pragma unroll
   for (int n = 0; n < NQT; ++n) rmax[n] = v4f{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll 1
+#pragma unroll
   for (int T = 0; T < 8; ++T) {
+    if (16 * T > L0 + NQT * 16 - 1) break;          // masked for every query of the wave
     const v8i a_cur = load_frag_swz(pg + (T * 16 + col) * kDim, z);
 #pragma unroll
     for (int n = 0; n < NQT; ++n) {
+      const int lo = L0 + 16 * n;                    // least limit of the tile's queries
+      if (16 * T > lo + 15) continue;                // masked for every query of the tile
       v4f acc = mfma_e4m3(a_cur, qf[n][0], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int h = 1; h < H; ++h) acc = mfma_e4m3(a_cur, qf[n][h], acc);
-      const int lim = lim0 + 16 * n;
+      if (16 * T + 15 <= lo) {                       // visible to every query of the tile
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = (T * 16 + grp * 4 + i > lim) ? -INFINITY : acc[i];
-        rmax[n][i] = fmaxf(rmax[n][i], v);
+        for (int i = 0; i < 4; ++i) rmax[n][i] = fmaxf(rmax[n][i], acc[i]);
+      } else {
+        const int lim = lim0 + 16 * n;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = (T * 16 + grp * 4 + i > lim) ? -INFINITY : acc[i];
+          rmax[n][i] = fmaxf(rmax[n][i], v);
+        }
       }
     }
   }
@@ -560,24 +572,32 @@ __device__ __forceinline__ void page_max_f4(const uint8_t* __restrict__ pg, cons
 
 template <int H, int NQT>
 __device__ __forceinline__ void page_max_causal_f4(const uint8_t* __restrict__ pg,
-                                                   const v8i (&qf)[NQT][H], int lim0, int col,
-                                                   int grp, int off, v4f (&rmax)[NQT]) {
+                                                   const v8i (&qf)[NQT][H], int lim0, int L0,
+                                                   int col, int grp, int off, v4f (&rmax)[NQT]) {
 #pragma unroll
   for (int n = 0; n < NQT; ++n) rmax[n] = v4f{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll 1
+#pragma unroll
   for (int T = 0; T < 8; ++T) {
+    if (16 * T > L0 + NQT * 16 - 1) break;
     const v8i a_cur = f4_frag(pg, T, col, off);
     const int s_cur = f4_scale(pg, T, col, grp);
 #pragma unroll
     for (int n = 0; n < NQT; ++n) {
+      const int lo = L0 + 16 * n;
+      if (16 * T > lo + 15) continue;
       v4f acc = mfma_f4_e4m3(a_cur, qf[n][0], v4f{0.f, 0.f, 0.f, 0.f}, s_cur);
 #pragma unroll
       for (int h = 1; h < H; ++h) acc = mfma_f4_e4m3(a_cur, qf[n][h], acc, s_cur);
-      const int lim = lim0 + 16 * n;
+      if (16 * T + 15 <= lo) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = (T * 16 + grp * 4 + i > lim) ? -INFINITY : acc[i];
-        rmax[n][i] = fmaxf(rmax[n][i], v);
+        for (int i = 0; i < 4; ++i) rmax[n][i] = fmaxf(rmax[n][i], acc[i]);
+      } else {
+        const int lim = lim0 + 16 * n;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = (T * 16 + grp * 4 + i > lim) ? -INFINITY : acc[i];
+          rmax[n][i] = fmaxf(rmax[n][i], v);
+        }
       }
     }
   }
@@ -677,6 +697,7 @@ __device__ __forceinline__ void score_item(const ScoreK& a, int item, uint8_t* l
   const bool wave_active = wave_q0 < q_end;
   const int my_q0 = wave_q0 + col;              // query of this lane in tile n: my_q0 + 16n
   const int my_pos0 = ctx + (my_q0 - cq0);      // its position: my_pos0 + 16n
+  const int wave_pos0 = ctx + (wave_q0 - cq0);  // position of the wave's first query
 #pragma unroll
   for (int n = 0; n < NQT; ++n) {
     const int qi = my_q0 + n * 16;
@@ -735,12 +756,14 @@ __device__ __forceinline__ void score_item(const ScoreK& a, int item, uint8_t* l
     v4f rmax[NQT];
     if constexpr (KF == 0) {
       if ((p + 1) * kPage - 1 > pos_first)
-        page_max_causal<H, NQT>(pg, qf, my_pos0 - p * kPage, col, grp, swz, rmax);
+        page_max_causal<H, NQT>(pg, qf, my_pos0 - p * kPage, wave_pos0 - p * kPage, col, grp, swz,
+                                rmax);
       else
         page_max<H, NQT>(pg, qf, col, swz, rmax);
     } else {
       if ((p + 1) * kPage - 1 > pos_first)
-        page_max_causal_f4<H, NQT>(pg, qf, my_pos0 - p * kPage, col, grp, f4off, rmax);
+        page_max_causal_f4<H, NQT>(pg, qf, my_pos0 - p * kPage, wave_pos0 - p * kPage, col, grp,
+                                   f4off, rmax);
       else
         page_max_f4<H, NQT>(pg, qf, col, grp, f4off, rmax);
     }
