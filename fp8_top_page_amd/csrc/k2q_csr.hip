@@ -34,7 +34,8 @@
 //             (a query i of the item sees the page's tokens up to i + the first
 //             value; the physical page comes from the block table)
 //   (order) -- rows of >= 512 queries on average only: the items' order for
-//             the attention, sorted by the query range of their first query
+//             the attention, sorted by the query range of their piece (a key
+//             the fill writes per item)
 // The CSR position of (query i, slot s) is then the first position of i's word
 // in its row plus the set bits below i in that word; the attention's combine
 // computes it from the row table, the word positions and the bitmap.
@@ -265,6 +266,8 @@ struct FillK {
   int64_t max_items;
   Hdr* hdr;
   int32_t qc;              // queries per attention item, at most
+  int32_t order_shift;     // > 0: write each item's order key (query range of its piece)
+  int32_t* okey;
 };
 
 __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
@@ -384,6 +387,7 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
       }
     }
     const int t = lane - lead;
+    const int64_t q_piece = __shfl(q_word, lead);   // first query slot of the piece
     if (valid && t < n_it) {
       const int64_t idx = (int64_t)p_item + t;
       if (idx < a.max_items) {
@@ -392,25 +396,24 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
         const int phys = a.block_table[(int64_t)b * a.bt_stride + j];
         a.items[2 * idx] = make_int4(p_pos + t * a.qc, min(a.qc, n - t * a.qc), phys, g);
         a.items[2 * idx + 1] = make_int4(ctx - cq[b] - j * kPage, sk - j * kPage, (int)row, b);
+        if (a.order_shift > 0) a.okey[idx] = (int32_t)(q_piece >> a.order_shift);
       }
     }
   }
 }
 
-// Attention item order for long rows: items sorted by the query range of
-// their first query (bucket = global query index >> shift), so that the
-// attention's resident blocks work on one range of queries at a time and
-// that range's query rows stay in cache while every page that any of them
-// selected is visited; within a bucket items keep about their list order
-// (rows ascending).  One block: histogram, scan, scatter of item indices.
+// Attention item order for very long rows: items sorted by the query range of
+// their piece (key = first query slot of the piece >> shift, written by the
+// fill), so that the attention's resident blocks work on one range of queries
+// at a time and that range's query rows stay in cache while every page that
+// any of them selected is visited; within a bucket items keep about their list
+// order (rows ascending).  One block: histogram, scan, scatter of item indices.
 constexpr int kOrderThreads = 1024;
 constexpr int kOrderKeys = 1024;
 
 __global__ __launch_bounds__(kOrderThreads) void item_order_kernel(const Hdr* __restrict__ hdr,
-                                                                   const int4* __restrict__ items,
-                                                                   const int32_t* __restrict__ q_indices,
-                                                                   int shift, int n_keys,
-                                                                   int64_t max_items,
+                                                                   const int32_t* __restrict__ okey,
+                                                                   int n_keys, int64_t max_items,
                                                                    int32_t* __restrict__ perm) {
   __shared__ int s_cnt[kOrderKeys];
   __shared__ int s_wave[kOrderThreads / 64];
@@ -418,9 +421,7 @@ __global__ __launch_bounds__(kOrderThreads) void item_order_kernel(const Hdr* __
   const int n = (int)min<int64_t>(hdr->n_items, max_items);
   for (int k = tid; k < kOrderKeys; k += kOrderThreads) s_cnt[k] = 0;
   __syncthreads();
-  auto key_of = [&](int i) {
-    return min(n_keys - 1, max(0, q_indices[items[2 * i].x] >> shift));
-  };
+  auto key_of = [&](int i) { return min(n_keys - 1, max(0, okey[i])); };
   for (int i = tid; i < n; i += kOrderThreads) atomicAdd(&s_cnt[key_of(i)], 1);
   __syncthreads();
   // exclusive scan over the keys (one per thread)
@@ -476,6 +477,7 @@ SchedLayout sched_layout(const msa_varlen_t* vl, int n_sel, int topk) {
   L.row_base = off;   off += align_up(sizeof(int32_t) * (vl->batch + 1), 256);
   L.blk_tot = off;    off += align_up(sizeof(int32_t) * 2 * L.n_blocks, 256);
   L.items = off;      off += align_up(2 * sizeof(int4) * std::max<int64_t>(1, L.max_items), 256);
+  L.okey = off;       off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.max_items), 256);
   L.perm = off;       off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.max_items), 256);
   L.rowsel = off;     off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.inv_len), 256);
   L.wbase = off;      off += align_up(sizeof(int32_t) * L.n_rows * L.words_per_row, 256);
@@ -515,12 +517,13 @@ hipError_t launch_k2q_csr(const CsrArgs& a, hipStream_t stream) {
   FillK fk{a.vl.cu_seqlens_q, a.vl.cu_seqlens_k, a.vl.batch, a.vl.block_table,
            a.vl.block_table_stride, a.vl.total_rows, row_base, bitmap, L.words_per_row, G,
            n_words, L.n_rows, (int32_t)L.n_blocks, blk_tot, blk_items, prefixed, a.row_ptr,
-           a.q_indices, wbase, items, L.max_items, hdr, L.item_q};
+           a.q_indices, wbase, items, L.max_items, hdr, L.item_q, L.order_shift,
+           reinterpret_cast<int32_t*>(a.sched + L.okey)};
   hipLaunchKernelGGL(csr_fill_kernel, dim3((unsigned)L.n_blocks), dim3(kThreads), 0, stream, fk);
   if (L.order_shift > 0)
-    hipLaunchKernelGGL(item_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, hdr, items,
-                       a.q_indices, L.order_shift, L.order_keys, L.max_items,
-                       reinterpret_cast<int32_t*>(a.sched + L.perm));
+    hipLaunchKernelGGL(item_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, hdr,
+                       reinterpret_cast<const int32_t*>(a.sched + L.okey), L.order_keys,
+                       L.max_items, reinterpret_cast<int32_t*>(a.sched + L.perm));
   return hipGetLastError();
 }
 

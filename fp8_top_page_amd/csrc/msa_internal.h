@@ -72,7 +72,7 @@ constexpr int kAttnQCMax = 64;
 
 struct SchedLayout {
   // byte offsets inside the schedule buffer
-  size_t hdr, row_base, blk_tot, items, perm, rowsel, wbase, bitmap, total;
+  size_t hdr, row_base, blk_tot, items, okey, perm, rowsel, wbase, bitmap, total;
   int64_t n_rows;         // n_sel * total_rows
   int64_t words_per_row;  // bitmap words per row (one bit per query slot, padded)
   int64_t n_units;        // bitmap units (64 consecutive words of the row-major bitmap)
