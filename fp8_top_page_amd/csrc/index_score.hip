@@ -14,13 +14,16 @@
 //    one whose items finish first when dealt out in rounds of one per compute
 //    unit (each round as long as a full chunk plus the item's start-up), so a
 //    batch of uneven query blocks neither leaves a nearly empty last round nor
-//    pays many start-ups.  The scorer grid is sized from host-side upper
-//    bounds, and blocks past the device-side item count exit.
+//    pays many start-ups.  One persistent scorer block per compute unit strides
+//    over the items (the item count is known only on the device).
 //  * Scoring: tokens are the MFMA M axis, queries the N axis.  Each of the 16
 //    waves keeps the E4M3 fragments of 64/H queries (all H heads) in registers
 //    for the whole item; index-K pages (16 KiB) stream into a ring of four LDS
 //    slots by direct global -> LDS copies and are read by every wave.  The H
 //    head products chain into one accumulator (a contraction of length H*128).
+//    On the few pages that cross a query's position, token tiles every query
+//    of a tile has passed take the plain max, tiles none of them reaches are
+//    skipped, and only the tiles in between are masked.
 //  * Decode-like batches (every request at most 64/H queries): one wave's
 //    queries are all there is, so the waves split each page instead: wave w
 //    scores a 16-token slice of one page for all the queries, and the slices'
@@ -30,8 +33,9 @@
 //    exchange folds the 4 lane groups into 2, and the two partial maxima go to
 //    an LDS tile (8 pages x 2 per query).  At the end of every group of 8 pages
 //    the tile is flushed: a lane maxes the 2 partials of each page of a (query,
-//    4-page) half group, scales them and stores them, two lanes covering the 32 contiguous bytes of a
-//    query's group (whole 32-byte write granules of HBM).
+//    4-page) half group, scales them and stores them, two lanes covering the
+//    32 contiguous bytes of a query's group (whole 32-byte write granules of
+//    HBM).
 #include "msa_device.h"
 #include "msa_internal.h"
 
