@@ -221,8 +221,18 @@ def cpu_baseline(inp, budget_s):
         threads = max((d.get("num_threads") or 1) for d in info) if info else 1
     except Exception:
         threads = os.cpu_count()
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(dt / done * inp.total_q * 1e6, 1), "unit": "us/layer (index scoring)",
-            "cores": int(threads or 1), "kind": "oracle",
+            "cores": int(threads or 1), "kind": "oracle", "cpu_model": cpu_model,
+            "host_cpus": os.cpu_count(),
             "sample": f"{done} of {inp.total_q} queries of {inp.wl.name} (random, chunks of 64), "
                       f"float64 numpy oracle index scoring, {dt:.1f} s, scaled linearly by query count"}
 
