@@ -48,13 +48,14 @@ constexpr int kFlush = 16;                   // pages per score-tile flush (deco
 constexpr int kSRow = kFlush + 1;            // score-tile row stride in floats
 constexpr int kSRowG = 20;                   // prefill tile: 8 pages x 2 partials, padded (16-byte rows)
 constexpr int kMaxItemPages = 256;           // pages per work item, at most
-constexpr int kMinItemPages = 4;             // ... and at least (keeps score stores 16-byte aligned)
+constexpr int kMinItemPages = 4;             // ... and at least
 constexpr int kPlanCUs = 256;                // compute units the item sizing aims to fill
-constexpr int kPlanCands = 6;                // item sizes tried: about k rounds of kPlanCUs items, k = 1..6
+constexpr int kPlanRounds = 6;               // item sizes for about k rounds of kPlanCUs items, k = 1..6,
+constexpr int kPlanCands = kPlanRounds + 3;   // and three sizes at and just above one round's
 
 struct ItemHdr {
   int32_t n_items;
-  int32_t pages_per_item;                    // chosen by the plan, multiple of 4
+  int32_t pages_per_item;                    // chosen by the plan (a multiple of 4 for the decode kernel)
   int32_t pad[62];
 };
 
@@ -90,13 +91,28 @@ __device__ __forceinline__ int qblock_visible(int ctx, int qf, int qn) {
   return (ctx + qf + qn - 1) / kPage + 1;
 }
 
-// Candidate k of the pages per item: the w visible pages of all q-blocks cut
-// into about k * kPlanCUs chunks (a multiple of 4, within [kMinItemPages,
-// kMaxItemPages]).
-__device__ __forceinline__ int cand_pages(int64_t w, int k) {
+// Pages per item for about k rounds of kPlanCUs items: the w visible pages of
+// all q-blocks cut into k * kPlanCUs chunks, rounded up to a multiple of round,
+// within [kMinItemPages, kMaxItemPages].
+__device__ __forceinline__ int cand_pages(int64_t w, int k, int round) {
   const int64_t per = (int64_t)kPlanCUs * k;
-  const int64_t pc = ((w + per - 1) / per + 3) / 4 * 4;
+  const int64_t pc = ((w + per - 1) / per + round - 1) / round * round;
   return (int)min<int64_t>(kMaxItemPages, max<int64_t>(kMinItemPages, pc));
+}
+// The candidates: the k = 1..kPlanRounds sizes as multiples of 4, then three
+// sizes at and just above one round's: ceil(w / kPlanCUs) + 0, 1, 2 pages (the
+// remainder chunks of uneven q-blocks often push a size just past one round,
+// and a slightly larger chunk keeps it in one).  align = 4 (the decode kernel,
+// whose score flush is 16-byte aligned relative to an item's first page) keeps
+// every size a multiple of 4: the last three become the one-round size + 4, 8,
+// 12.  The prefill kernel's flush follows absolute 8-page groups: align = 1.
+__device__ __forceinline__ void plan_candidates(int64_t w, int align, int (&cand)[kPlanCands]) {
+#pragma unroll
+  for (int k = 0; k < kPlanRounds; ++k) cand[k] = cand_pages(w, k + 1, 4);
+  const int one = cand_pages(w, 1, align);
+#pragma unroll
+  for (int j = 0; j < kPlanCands - kPlanRounds; ++j)
+    cand[kPlanRounds + j] = min(kMaxItemPages, one + (align == 1 ? j : 4 * (j + 1)));
 }
 // Predicted run time of n items of at most pc pages, in fifths of a page: the
 // items run in rounds of kPlanCUs (one block per compute unit), each round as
@@ -129,21 +145,20 @@ __device__ __forceinline__ void block_sum(int (&x)[N], int (*s_red)[N]) {
 // uneven batches weigh the candidates.
 __device__ __forceinline__ bool plan_uniform(int vmin, int vmax) { return (vmax - vmin) * 8 <= vmax; }
 
-// The candidate with the least predicted time (the smallest k on ties).
-__device__ __forceinline__ int best_pages(int64_t w, const int (&n)[kPlanCands]) {
-  int best = cand_pages(w, 1);
+// The candidate with the least predicted time (the first one on ties).
+__device__ __forceinline__ int best_pages(const int (&cand)[kPlanCands], const int (&n)[kPlanCands]) {
+  int best = cand[0];
   int64_t best_cost = cand_cost(n[0], best);
-  for (int k = 2; k <= kPlanCands; ++k) {
-    const int pc = cand_pages(w, k);
-    const int64_t c = cand_cost(n[k - 1], pc);
-    if (c < best_cost) { best_cost = c; best = pc; }
+  for (int k = 1; k < kPlanCands; ++k) {
+    const int64_t c = cand_cost(n[k], cand[k]);
+    if (c < best_cost) { best_cost = c; best = cand[k]; }
   }
   return best;
 }
 
 __global__ __launch_bounds__(256) void score_plan_kernel(const int32_t* __restrict__ cu_q,
                                                          const int32_t* __restrict__ cu_k, int B,
-                                                         int qblock, int64_t max_items,
+                                                         int qblock, int align, int64_t max_items,
                                                          ItemHdr* __restrict__ hdr,
                                                          int4* __restrict__ items) {
   __shared__ int wave_tot[4];
@@ -181,11 +196,10 @@ __global__ __launch_bounds__(256) void score_plan_kernel(const int32_t* __restri
   int64_t tw = 0;
   int lo = INT32_MAX, hi = 0;
   for (int k = 0; k < 4; ++k) { tw += s_w[k]; lo = min(lo, s_vmin[k]); hi = max(hi, s_vmax[k]); }
-  int pc_all = cand_pages(tw, 1);
+  int pc_all = cand_pages(tw, 1, 4);
   if (!plan_uniform(lo, hi)) {
     int cand[kPlanCands], n[kPlanCands] = {};
-#pragma unroll
-    for (int k = 0; k < kPlanCands; ++k) cand[k] = cand_pages(tw, k + 1);
+    plan_candidates(tw, align, cand);
     for (int b = 0; b < B; ++b) {
       const int sq = cu_q[b + 1] - cu_q[b];
       const int ctx = (cu_k[b + 1] - cu_k[b]) - sq;
@@ -198,7 +212,7 @@ __global__ __launch_bounds__(256) void score_plan_kernel(const int32_t* __restri
       }
     }
     block_sum<4>(n, s_red);
-    pc_all = best_pages(tw, n);
+    pc_all = best_pages(cand, n);
   }
   if (tid == 0) running = 0;
   __syncthreads();
@@ -261,7 +275,7 @@ constexpr int kPlanMaxG = 4096;
 
 __global__ __launch_bounds__(kPlanThreads) void score_plan_table_kernel(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int B, int qblock,
-    int64_t max_items, ItemHdr* __restrict__ hdr, int4* __restrict__ items) {
+    int align, int64_t max_items, ItemHdr* __restrict__ hdr, int4* __restrict__ items) {
   constexpr int kW = kPlanThreads / 64;
   __shared__ int s_q0[kPlanMaxB], s_sq[kPlanMaxB], s_ctx[kPlanMaxB], s_qbase[kPlanMaxB + 1];
   __shared__ int s_first[kPlanMaxG + 1];
@@ -337,11 +351,10 @@ __global__ __launch_bounds__(kPlanThreads) void score_plan_table_kernel(
   int64_t tw = 0;
   int lo = INT32_MAX, hi = 0;
   for (int k = 0; k < kW; ++k) { tw += s_w[k]; lo = min(lo, s_lo[k]); hi = max(hi, s_hi[k]); }
-  int pc = cand_pages(tw, 1);
+  int pc = cand_pages(tw, 1, 4);
   if (!plan_uniform(lo, hi)) {
     int cand[kPlanCands], n[kPlanCands] = {};
-#pragma unroll
-    for (int k = 0; k < kPlanCands; ++k) cand[k] = cand_pages(tw, k + 1);
+    plan_candidates(tw, align, cand);
     for (int g = tid; g < G; g += kPlanThreads) {
       int b, qf, qn;
       const int v = visible(g, &b, &qf, &qn);
@@ -349,7 +362,7 @@ __global__ __launch_bounds__(kPlanThreads) void score_plan_table_kernel(
       for (int k = 0; k < kPlanCands; ++k) n[k] += (v + cand[k] - 1) / cand[k];
     }
     block_sum<kW>(n, s_red);
-    pc = best_pages(tw, n);
+    pc = best_pages(cand, n);
   }
 
   // pass 2: page chunks per q-block, offsets
@@ -1074,11 +1087,11 @@ ScorePlan score_plan(const msa_varlen_t* vl, int H) {
   const int64_t qb_bound = ceil_div(vl->total_q, qb) + vl->batch;   // q-blocks, at most
   const int64_t max_pages = std::max<int32_t>(1, vl->max_pages);
   // The device plan picks pages per item pc >= (sum of visible pages) /
-  // (kPlanCands * kPlanCUs), so sum over q-blocks of ceil(v / pc) <=
-  // kPlanCands * kPlanCUs + q-blocks, unless pc hits kMaxItemPages, where it is
+  // (kPlanRounds * kPlanCUs), so sum over q-blocks of ceil(v / pc) <=
+  // kPlanRounds * kPlanCUs + q-blocks, unless pc hits kMaxItemPages, where it is
   // at most q-blocks * (max_pages / kMaxItemPages + 1).
   p.pages_per_item = 0;   // chosen on the device
-  p.max_items = std::max<int64_t>((int64_t)kPlanCands * kPlanCUs,
+  p.max_items = std::max<int64_t>((int64_t)kPlanRounds * kPlanCUs,
                                   qb_bound * ceil_div(max_pages, kMaxItemPages)) +
                 qb_bound;
   p.workspace_bytes = sizeof(ItemHdr) + align_up((size_t)p.max_items * sizeof(int4), 256);
@@ -1090,15 +1103,17 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
   ItemHdr* hdr = reinterpret_cast<ItemHdr*>(a.workspace);
   int4* items = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(a.workspace) + sizeof(ItemHdr));
   const int qb = score_qblock(a.H);
+  // chunk alignment: 4 pages when the decode kernel runs (see cand_pages)
+  const int align = a.vl.max_seqlen_q <= score_qtiles(a.H) * 16 ? 4 : 1;
   // one request: the 256-thread kernel has less to set up; batches: the table kernel
   if (a.vl.batch > 1 && a.vl.batch <= kPlanMaxB &&
       ceil_div(a.vl.total_q, qb) + a.vl.batch <= kPlanMaxG)
     hipLaunchKernelGGL(score_plan_table_kernel, dim3(1), dim3(kPlanThreads), 0, stream,
-                       a.vl.cu_seqlens_q, a.vl.cu_seqlens_k, a.vl.batch, qb, a.plan.max_items, hdr,
-                       items);
+                       a.vl.cu_seqlens_q, a.vl.cu_seqlens_k, a.vl.batch, qb, align, a.plan.max_items,
+                       hdr, items);
   else
     hipLaunchKernelGGL(score_plan_kernel, dim3(1), dim3(256), 0, stream, a.vl.cu_seqlens_q,
-                       a.vl.cu_seqlens_k, a.vl.batch, qb, a.plan.max_items, hdr, items);
+                       a.vl.cu_seqlens_k, a.vl.batch, qb, align, a.plan.max_items, hdr, items);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   ScoreK k;
