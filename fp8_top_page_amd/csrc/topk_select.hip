@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkK a) {
   uint32_t tw = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t t = tw | (1u << bit);
-    if (__popcll(__ballot(m >= t)) >= ksel) tw = t;
+    if ((int)__popcll(__ballot(m >= t)) >= ksel) tw = t;
   }
   if (lane == 0) wave_tau[wave] = tw;
   if (tid == 0) n_cand = 0;
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(kBlock) void topk_wave_kernel(TopkK a) {
   uint32_t tau = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t t = tau | (1u << bit);
-    if (__popcll(__ballot(m >= t)) >= ksel) tau = t;
+    if ((int)__popcll(__ballot(m >= t)) >= ksel) tau = t;
   }
 
   // every candidate key >= tau goes to the list (at most 64 * KPT of them);
