@@ -239,28 +239,24 @@ def make_inputs(wl: Workload, attention: bool = True) -> Inputs:
 
 
 def random_topk(inp: Inputs, n_sel: int, seed: int) -> np.ndarray:
-    """Random causal top-16 with the local page forced, in the style of the
-    E4M3-query prefill benchmark's case(): local page first, future pages never,
-    -1 padding.  Returns [total_q, n_sel, 16] int32."""
-    g = torch.Generator().manual_seed(seed)
+    """A random causal selection obeying the rule of the E4M3-query prefill
+    benchmark (vLLM PR 60684, Validation): slot 0 holds the query's own
+    (local) page, the next min(16, v) - 1 slots hold distinct older visible
+    pages drawn uniformly without replacement, in random order, and the
+    remaining slots are -1 (v = visible pages of the query).  One selection
+    per selection head.  Returns [total_q, n_sel, 16] int32."""
+    rng = np.random.default_rng(seed)
     total_q = inp.total_q
     out = np.full((total_q, n_sel, TOPK), -1, np.int32)
-    cu_q, cu_k = inp.cu_seqlens_q, inp.cu_seqlens_k
+    cu_q = np.asarray(inp.cu_seqlens_q, np.int64)
+    cu_k = np.asarray(inp.cu_seqlens_k, np.int64)
     for b in range(len(cu_q) - 1):
-        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
-        n = q1 - q0
-        if n == 0:
-            continue
-        sk = int(cu_k[b + 1] - cu_k[b])
-        pos = torch.arange(sk - n, sk)
-        visible = pos // PAGE + 1
-        vmax = int(visible.max())
-        r = torch.rand(n, n_sel, vmax, generator=g)
-        ar = torch.arange(vmax)
-        r = torch.where(ar < visible[:, None, None] - 1, r, torch.tensor(-1.0))
-        r = torch.where(ar == visible[:, None, None] - 1, torch.tensor(2.0), r)
-        k = min(TOPK, vmax)
-        val, idx = r.topk(k, dim=-1)
-        sel = torch.where(val >= 0, idx, torch.tensor(-1)).int().numpy()
-        out[q0:q1, :, :k] = sel
+        first_new = int(cu_k[b + 1] - cu_k[b]) - int(cu_q[b + 1] - cu_q[b])
+        for i in range(int(cu_q[b]), int(cu_q[b + 1])):
+            own = (first_new + i - int(cu_q[b])) // PAGE     # the query's page
+            n_old = min(TOPK - 1, own)                         # older pages to draw
+            for g in range(n_sel):
+                out[i, g, 0] = own
+                if n_old:
+                    out[i, g, 1:1 + n_old] = rng.choice(own, size=n_old, replace=False)
     return out
