@@ -58,10 +58,26 @@ def parse():
                     help="write profiles/index_score_<workload>_hbm.json and print the per-kernel "
                          "byte table from four rocprofv3 counter_collection.csv files (FETCH_SIZE "
                          "and WRITE_SIZE over this benchmark, then over --copy-probe-mib 1024)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only build and run the fp8 matrix-core ceiling program (mfma_ceiling.hip "
+                         "beside this file; not part of the library) and exit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB three times (the "
                          "reference kernel that scales HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def mfma_ceiling():
+    """Build mfma_ceiling.hip (beside this file) into _build/ and run it: the fp8
+    matrix-core rate of three instruction mixes on constant and random E4M3
+    operands, the practical ceiling the scorer's roofline fraction is read against."""
+    import subprocess
+    from fp8_top_page_amd import build as b
+    os.makedirs(b.BUILD, exist_ok=True)
+    exe = os.path.join(b.BUILD, "mfma_ceiling")
+    cmd = [b.HIPCC, *b.FLAGS, os.path.join(ROOT, "mfma_ceiling.hip"), "-o", exe]
+    subprocess.run(cmd, check=True)
+    sys.exit(subprocess.run([exe]).returncode)
 
 
 def copy_probe(mib):
@@ -300,6 +316,9 @@ def main():
     args = parse()
     if args.hbm_record:
         hbm_record(args.workload, *args.hbm_record)
+        return
+    if args.mfma_ceiling:
+        mfma_ceiling()
         return
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)

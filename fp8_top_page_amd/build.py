@@ -13,9 +13,6 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
-# measurement program (not linked into the library): fp8 matrix-core rate of three instruction mixes
-PROBE_SRC = "mfma_ceiling.hip"
-PROBE = os.path.join(PKG, "mfma_ceiling")
 SOURCES = ["msa_api.hip", "index_score.hip", "topk_select.hip", "k2q_csr.hip", "sparse_attn.hip",
            "quantize_insert.hip"]
 ARCH = os.environ.get("MSA_OFFLOAD_ARCH", "gfx950")
@@ -47,13 +44,8 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
-    cmd = [HIPCC, *FLAGS, os.path.join(CSRC, PROBE_SRC), "-o", PROBE + ".tmp"]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stdout}\n{r.stderr}")
-    os.replace(PROBE + ".tmp", PROBE)
     if verbose:
-        print("built", LIB, "and", PROBE)
+        print("built", LIB)
     return LIB
 
 
