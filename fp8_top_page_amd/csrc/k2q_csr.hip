@@ -71,10 +71,14 @@ struct WordsK {
   int64_t words;          // per row
   int32_t* rowsel;        // [total_q, n_sel, 16]: CSR row of each selected page, or -1
   int32_t n_chunks;       // blocks per (request, word): ceil(n_sel * max_pages / kWordRows)
+  int32_t max_pages;
 };
 
-__device__ __forceinline__ int request_pages(const int32_t* cu_k, int b) {
-  return (cu_k[b + 1] - cu_k[b] + kPage - 1) / kPage;
+// Pages of request b, clamped to max_pages (device data contradicting the
+// host-side sizes must not move a write past the bitmap or a read past the
+// request's block-table row).
+__device__ __forceinline__ int request_pages(const int32_t* cu_k, int b, int max_pages) {
+  return min(max((cu_k[b + 1] - cu_k[b] + kPage - 1) / kPage, 0), max_pages);
 }
 
 // Block ((b * words) + w) * n_chunks + c: query slots 32w .. 32w+31 of request b,
@@ -86,14 +90,14 @@ __global__ __launch_bounds__(kThreads) void csr_words_kernel(WordsK a) {
   const int64_t bw = blockIdx.x / a.n_chunks;
   const int c = (int)(blockIdx.x % a.n_chunks);
   const int b = (int)(bw / a.words), w = (int)(bw % a.words);
-  const int pages = request_pages(a.cu_k, b);
+  const int pages = request_pages(a.cu_k, b, a.max_pages);
   const int rows = a.n_sel * pages;
   const int r0 = c * kWordRows;
   if (r0 >= rows && c > 0) return;
 
   // rows of earlier requests
   int part = 0;
-  for (int k = tid; k < b; k += kThreads) part += request_pages(a.cu_k, k);
+  for (int k = tid; k < b; k += kThreads) part += request_pages(a.cu_k, k, a.max_pages);
   part = wave_sum(part);
   if (lane == 0) s_red[wave] = part;
   __syncthreads();
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void csr_words_kernel(WordsK a) {
       const int g = (e % per_q) / kTopK, sl = e % kTopK;
       const int j = a.topk[(int64_t)(q0 + local) * a.tq + (int64_t)g * a.th + sl];
       a.rowsel[(int64_t)(q0 + local) * per_q + e % per_q] =
-          (j < 0 || j >= pages) ? -1 : g * a.total_rows + base + j;
+          (j < 0 || j >= pages || base + j >= a.total_rows) ? -1 : g * a.total_rows + base + j;
     }
     // the last request's blocks also clear any rows past the requests' pages
     if (b == a.batch - 1) {
@@ -134,14 +138,15 @@ __global__ __launch_bounds__(kThreads) void csr_words_kernel(WordsK a) {
     const int local = 32 * w + ql;
     if (local >= sq) continue;
     const int j = a.topk[(int64_t)(q0 + local) * a.tq + (int64_t)g * a.th + sl];
-    if (j < 0 || j >= pages) continue;
+    if (j < 0 || j >= pages || base + j >= a.total_rows) continue;
     const int r = g * pages + j - r0;
     if (r >= 0 && r < n_r) atomicOr(&s_bits[r], 1u << ql);
   }
   __syncthreads();
   for (int k = tid; k < n_r; k += kThreads) {
     const int r = r0 + k, g = r / pages, j = r - g * pages;
-    a.bitmap[((int64_t)g * a.total_rows + base + j) * a.words + w] = s_bits[k];
+    if (base + j < a.total_rows)
+      a.bitmap[((int64_t)g * a.total_rows + base + j) * a.words + w] = s_bits[k];
   }
 }
 
@@ -268,6 +273,7 @@ struct FillK {
   int32_t qc;              // queries per attention item, at most
   int32_t order_shift;     // > 0: write each item's order key (query range of its piece)
   int32_t* okey;
+  int32_t max_pages;
 };
 
 __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
@@ -358,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
     const int g = (int)(row / a.total_rows);
     const int64_t rr = row - (int64_t)g * a.total_rows;
     const int b = valid ? find_request(rbase, a.batch, rr) : 0;
-    const int j = (int)(rr - rbase[b]);
+    const int j = min(max((int)(rr - rbase[b]), 0), a.max_pages - 1);
     // One lane per bitmap word: the word's first CSR position is the unit's
     // plus the bits of earlier words; the lane then writes the word's entries
     // in bit order (a wave-uniform loop as long as any lane has bits left).
@@ -500,7 +506,7 @@ hipError_t launch_k2q_csr(const CsrArgs& a, hipStream_t stream) {
   if (a.vl.batch > 0 && L.words_per_row > 0) {
     WordsK wk{a.vl.cu_seqlens_q, a.vl.cu_seqlens_k, a.vl.batch, a.topk, a.tq_stride, a.th_stride,
               a.n_sel, a.vl.total_rows, row_base, bitmap, L.words_per_row, rowsel,
-              (int32_t)L.word_chunks};
+              (int32_t)L.word_chunks, std::max(a.vl.max_pages, 1)};
     hipLaunchKernelGGL(csr_words_kernel, dim3((unsigned)L.word_blocks), dim3(kThreads), 0, stream,
                        wk);
   }
@@ -518,7 +524,7 @@ hipError_t launch_k2q_csr(const CsrArgs& a, hipStream_t stream) {
            a.vl.block_table_stride, a.vl.total_rows, row_base, bitmap, L.words_per_row, G,
            n_words, L.n_rows, (int32_t)L.n_blocks, blk_tot, blk_items, prefixed, a.row_ptr,
            a.q_indices, wbase, items, L.max_items, hdr, L.item_q, L.order_shift,
-           reinterpret_cast<int32_t*>(a.sched + L.okey)};
+           reinterpret_cast<int32_t*>(a.sched + L.okey), std::max(a.vl.max_pages, 1)};
   hipLaunchKernelGGL(csr_fill_kernel, dim3((unsigned)L.n_blocks), dim3(kThreads), 0, stream, fk);
   if (L.order_shift > 0)
     hipLaunchKernelGGL(item_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, hdr,
