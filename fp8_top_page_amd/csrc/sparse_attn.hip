@@ -478,7 +478,10 @@ __global__ __launch_bounds__(1024) void attn_combine_kernel(CombineK a) {
   if (t < a.n_sel * kTopK) {
     const int b = find_request(a.cu_q, a.batch, i);
     const int local = (int)(i - a.cu_q[b]);
-    const int r = a.rowsel[i * a.n_sel * kTopK + t];
+    const int32_t* rs = a.rowsel + i * a.n_sel * kTopK;
+    int r = rs[t];
+    // a page listed twice in one selection is one CSR entry: merged once
+    for (int u = t - t % kTopK; u < t; ++u) r = rs[u] == r ? -1 : r;
     int p = -1;
     if (r >= 0) {
       const int64_t wi = (int64_t)r * a.words + (local >> 5);

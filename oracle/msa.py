@@ -415,7 +415,8 @@ def k2q_csr(cu_q, cu_k, topk_idx, total_rows=None):
     row(b, j) = sum_{b' < b} ceil(seqlen_k_b' / 128) + j, so there are
     total_kv_blocks rows per selection head; selection head g owns rows
     g * total_rows + row.  Each row lists the global indices of the queries
-    that selected it, ascending.
+    whose selection contains its page, ascending, each once (a page listed
+    twice in one selection is still one entry).
 
     topk_idx: [total_q, n_sel, K] int (logical pages, -1 = none).
     Returns (row_ptr [n_sel * total_rows + 1] int32, q_indices [nnz] int32).
@@ -433,10 +434,8 @@ def k2q_csr(cu_q, cu_k, topk_idx, total_rows=None):
     for i in range(topk_idx.shape[0]):           # ascending query order
         b = req[i]
         for g in range(n_sel):
-            for j in topk_idx[i, g]:
-                if j < 0:
-                    continue
-                rows[g * total_rows + row_base[b] + int(j)].append(i)
+            for j in dict.fromkeys(int(x) for x in topk_idx[i, g] if x >= 0):
+                rows[g * total_rows + row_base[b] + j].append(i)
     counts = np.array([len(r) for r in rows], np.int64)
     row_ptr = np.zeros(len(rows) + 1, np.int64)
     row_ptr[1:] = np.cumsum(counts)
@@ -457,7 +456,9 @@ def sparse_attention(cu_q, cu_k, block_table, q, kv_cache, topk_idx, softmax_sca
 
     For query i, q-head hq and KV head g = hq // (Hq // Hkv), the attended
     tokens are those of the selected pages (selection head g, or the single
-    shared selection when topk_idx has one head) at positions <= pos_i:
+    shared selection when topk_idx has one head) at positions <= pos_i.  The
+    selection is a set of pages: a page listed twice contributes its tokens
+    once.
 
         z_t = softmax_scale * q_scale * k_scale * sum_d q[i,hq,d] * K[t,g,d]
         out = v_scale * sum_t softmax(z)_t * V[t,g,:]
@@ -482,10 +483,7 @@ def sparse_attention(cu_q, cu_k, block_table, q, kv_cache, topk_idx, softmax_sca
         for g in range(Hkv):
             sel = topk_idx[i, g if n_sel > 1 else 0]
             tok_k, tok_v = [], []
-            for j in sel:
-                if j < 0:
-                    continue
-                j = int(j)
+            for j in dict.fromkeys(int(x) for x in sel if x >= 0):      # distinct pages
                 n_vis = min(PAGE, int(pos[i]) - PAGE * j + 1, int(seqlen_k[b]) - PAGE * j)
                 if n_vis <= 0:
                     continue

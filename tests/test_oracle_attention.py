@@ -116,3 +116,19 @@ def test_per_kv_head_selection():
     shared1 = oracle.sparse_attention(cu_q, cu_k, bt, q, kv, sel[:, 1:], 0.1)
     assert np.array_equal(out[:, :2], shared0[:, :2])   # heads 0,1 -> KV head 0 -> selection 0
     assert np.array_equal(out[:, 2:], shared1[:, 2:])   # heads 2,3 -> KV head 1 -> selection 1
+
+
+def test_page_listed_twice_counts_once():
+    """The selection is a set: repeating a page in a query's slots attends to its
+    tokens once, so the output equals that of the selection without the repeat."""
+    rng, cu_q, cu_k, bt, q, kv, kv_rows = _setup([6], [1500], 8, 1, seed=9)
+    _, pos = oracle.query_positions(cu_q, cu_k)
+    sel = np.full((6, 1, 16), -1, np.int32)
+    dup = sel.copy()
+    for i in range(6):
+        v = int(pos[i] // PAGE + 1)
+        sel[i, 0, :3] = [v - 1, 0, 2]
+        dup[i, 0, :6] = [v - 1, 0, 2, 0, v - 1, 2]
+    a = oracle.sparse_attention(cu_q, cu_k, bt, q, kv, sel, 0.1, 0.5)
+    b = oracle.sparse_attention(cu_q, cu_k, bt, q, kv, dup, 0.1, 0.5)
+    assert np.array_equal(a, b)

@@ -102,3 +102,18 @@ def test_csr_is_transpose_of_selection():
         for i in range(90):
             r = base[req[i]] + pos[i] // PAGE
             assert i in qidx[row_ptr[r]:row_ptr[r + 1]].tolist()
+
+
+def test_csr_lists_a_query_once_per_row():
+    """A page listed twice in one selection is one CSR entry: the rows of a
+    selection with repeats equal the brute-force rows of the distinct pages."""
+    cu_q = np.array([0, 4], np.int32)
+    cu_k = np.array([0, 1000], np.int32)
+    sel = np.full((4, 1, 16), -1, np.int32)
+    sel[0, 0, :5] = [5, 1, 1, 5, 3]
+    sel[1, 0, :3] = [5, 5, 5]
+    sel[2, 0, :4] = [7, 0, 7, 0]
+    sel[3, 0, :2] = [7, 2]
+    row_ptr, qidx = oracle.k2q_csr(cu_q, cu_k, sel, 8)
+    rows = [qidx[row_ptr[r]:row_ptr[r + 1]].tolist() for r in range(8)]
+    assert rows == [[2], [0], [3], [0], [], [0, 1], [], [2, 3]]
