@@ -65,6 +65,21 @@ def sample_queries(inp, n, seed=0):
     return np.array(sorted(pick), np.int64)
 
 
+def spread_queries(inp, n, seed=0):
+    """About n queries spread over the whole batch: the deterministic sample of
+    sample_queries plus one query drawn at random from each of n equal slices of
+    the query index range, so every scorer q-block and every query range of the
+    attention's item order holds sampled queries."""
+    total = inp.total_q
+    pick = set(sample_queries(inp, 0, seed).tolist())
+    rng = np.random.default_rng(seed + 1)
+    edges = np.linspace(0, total, num=min(n, total) + 1).astype(np.int64)
+    for a, b in zip(edges[:-1], edges[1:]):
+        if b > a:
+            pick.add(int(rng.integers(a, b)))
+    return np.array(sorted(pick), np.int64)
+
+
 def check_scores(inp, gpu_scores, queries, ref=None):
     """R1 on the visible entries of the sampled queries; unwritten entries stay NaN."""
     if ref is None:

@@ -2,9 +2,12 @@
 
 Workloads are the five seeded synthetic batches (tiny 1K prefill, 128 queries
 over a 32K prefix, fresh 32K prefill, 2048 queries over a 1M-token KV, ragged
-batch of 8).  Small batches are compared on every query; the large ones on
-every query for the integer steps and on a deterministic sample of queries for
-scores and attention.
+batch of 8) and a decode batch.  Scores, the selection (exact on the GPU's own
+scores, and against the oracle end to end up to near-tie swaps) and the CSR
+are compared on every query of every workload.  Attention is compared on every
+query of the small batches and on at least 2048 queries of the large ones,
+spread so that every scorer q-block and every query range of the attention's
+item order is sampled.
 """
 import functools
 import sys
@@ -17,12 +20,13 @@ import oracle
 import workloads
 from parity import (check_attention, check_csr, check_scores, check_selection_invariants,
                     check_topk_exact_on_gpu_scores, check_topk_vs_reference, run_path,
-                    sample_queries, to_np)
+                    spread_queries, to_np)
 
 pytestmark = pytest.mark.gpu
 
-SAMPLE = {"tiny_1k": None, "q128_kv32k": None, "fresh_32k": 48, "q2048_kv1m": 32, "ragged_b8": 48,
-          "decode_b16": 32}
+# attention queries per workload (None: every query)
+ATTN_SAMPLE = {"tiny_1k": None, "q128_kv32k": None, "fresh_32k": 2048, "q2048_kv1m": None,
+               "ragged_b8": 2048, "decode_b16": None}
 
 
 @functools.lru_cache(maxsize=1)
@@ -39,18 +43,20 @@ def test_workload_parity(name):
     sel = to_np(path.topk)[:, 0, :]
     row_ptr, q_idx = to_np(path.row_ptr), to_np(path.q_indices)
     out = to_np(path.out.float()).reshape(inp.total_q, -1, 128)
-    n = SAMPLE[name]
-    queries = np.arange(inp.total_q) if n is None else sample_queries(inp, n)
+    queries = np.arange(inp.total_q)
 
     ref_scores, worst = check_scores(inp, scores, queries)
-    print(f"[parity] {name}: scores ok on {len(queries)} queries (worst err/tol {worst:.3f})", flush=True)
+    print(f"[parity] {name}: scores ok on all {len(queries)} queries (worst err/tol {worst:.3f})",
+          flush=True)
     check_selection_invariants(inp, sel)
     check_topk_exact_on_gpu_scores(inp, scores, sel)
     swaps = check_topk_vs_reference(inp, sel, ref_scores, queries)
+    del ref_scores
     print(f"[parity] {name}: selection exact on GPU scores; {swaps} near-tie swaps vs oracle", flush=True)
     check_csr(inp, sel, row_ptr, q_idx)
     print(f"[parity] {name}: CSR bit-exact ({int(row_ptr[-1])} entries)", flush=True)
-    att_q = queries if n is None or len(queries) <= 64 else queries[:64]
+    n = ATTN_SAMPLE[name]
+    att_q = queries if n is None else spread_queries(inp, n)
     frac, mx = check_attention(inp, sel, out, att_q)
     print(f"[parity] {name}: attention ok on {len(att_q)} queries (frac {frac:.2e}, max {mx:.4f})",
           flush=True)
@@ -162,6 +168,43 @@ def test_topk_exact_ties_take_lower_pages():
         check_topk_exact_on_gpu_scores(meta, s, to_np(out))
 
 
+@pytest.mark.parametrize("kind", ["random", "levels", "late_top"])
+def test_topk_rows_longer_than_one_chunk(kind):
+    """Rows of more candidate pages than the block kernel holds in registers at
+    once (8192): requests of 11,719 and 20,313 pages, so the selection runs its
+    chunked passes (one, two and three re-reads of the row).  Random rows,
+    rows of four score levels (many exact ties, more candidates than the LDS
+    list holds) and rows whose best pages all lie past the first chunk; the
+    result must equal the oracle's selection on the same scores."""
+    from types import SimpleNamespace
+    from fp8_top_page_amd import msa_topk_select
+    from fp8_top_page_amd.pipeline import DeviceBatch
+    print(f"\n[parity] top-k over several chunks: {kind}", flush=True)
+    sq, sk = np.array([16, 8]), np.array([1_500_000, 2_600_000])
+    cu_q = np.concatenate([[0], np.cumsum(sq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(sk)]).astype(np.int32)
+    pages = (sk + 127) // 128
+    bt = np.zeros((2, pages.max()), np.int32)               # never read by the selection
+    db = DeviceBatch(cu_q, cu_k, bt, np.zeros((24, 1, 128), np.uint8),
+                     np.zeros((1, 128, 128), np.uint8), 1.0, 1.0)
+    meta = SimpleNamespace(cu_seqlens_q=cu_q, cu_seqlens_k=cu_k, total_q=24)
+    rng = np.random.default_rng(7)
+    ld = (db.max_pages + 3) // 4 * 4
+    if kind == "random":
+        s = rng.standard_normal((24, ld)).astype(np.float32)
+    elif kind == "levels":
+        s = rng.integers(0, 4, size=(24, ld)).astype(np.float32)
+    else:
+        s = rng.standard_normal((24, ld)).astype(np.float32)
+        s[:, 8192:] += 10.0
+        s[:, 8192 + 3000:8192 + 3040] += 20.0               # the winners, two chunks in
+    st = torch.from_numpy(s).cuda()
+    out = torch.full((24, 16), -7, dtype=torch.int32, device="cuda")
+    msa_topk_select(db.vl, st, 16, 1, out)
+    torch.cuda.synchronize()
+    check_topk_exact_on_gpu_scores(meta, s, to_np(out))
+
+
 def test_per_kv_head_selection_and_random_topk():
     """One selection per KV head, drawn like the benchmark script's case():
     CSR and attention against the oracle on that selection."""
@@ -178,6 +221,26 @@ def test_per_kv_head_selection_and_random_topk():
     out = to_np(path.out.float()).reshape(inp.total_q, 16, 128)
     q = np.arange(0, inp.total_q, 7)
     check_attention(inp, sel, out, q, n_sel=2)
+
+
+def test_page_listed_twice_is_merged_once():
+    """The C ABI takes any selection: one that repeats a page in a query's slots
+    must give the CSR of its distinct pages (each query once per row) and
+    attention over each page's tokens once, as the oracle computes."""
+    from fp8_top_page_amd.pipeline import DeviceBatch, MsaPath
+    inp = _small_inputs((300, 40), (6000, 900), 1, 8, 1, seed=14)
+    sel = workloads.random_topk(inp, n_sel=1, seed=9)
+    sel[:, 0, 15] = sel[:, 0, 1]                 # slot 15 repeats slot 1 (or stays -1)
+    sel[:, 0, 14] = np.where(sel[:, 0, 14] >= 0, sel[:, 0, 0], -1)   # and the local page
+    db = DeviceBatch.from_inputs(inp)
+    path = MsaPath(db)
+    path.topk.copy_(torch.from_numpy(sel))
+    path.csr()
+    path.attend()
+    torch.cuda.synchronize()
+    check_csr(inp, sel[:, 0, :], to_np(path.row_ptr), to_np(path.q_indices))
+    out = to_np(path.out.float()).reshape(inp.total_q, 8, 128)
+    check_attention(inp, sel[:, 0, :], out, np.arange(inp.total_q))
 
 
 def test_large_csr_grid_random_topk():
