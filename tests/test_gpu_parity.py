@@ -118,6 +118,44 @@ def test_edge_shapes(sq, sk, H, Hq, Hkv):
     check_attention(inp, sel, to_np(path.out.float()).reshape(inp.total_q, Hq, 128), queries)
 
 
+@pytest.mark.parametrize("sq,sk,H,Hq,Hkv", [
+    ((1500, 700), (40000, 9000), 2, 32, 2),     # 16 q-heads per KV head
+    ((1200, 0, 300), (30000, 500, 300), 4, 16, 4),   # 4 per KV head, an empty request
+    ((1030,), (70000,), 1, 4, 4),               # one q-head per KV head
+])
+def test_head_groupings_large_batches(sq, sk, H, Hq, Hkv):
+    """Batches of more than 1000 queries with other q-head groupings than the
+    workloads' (16, 4 and 1 q-heads per KV head) and an empty request: the
+    whole path against the oracle on every query."""
+    print(f"\n[parity] head grouping sq={sq} sk={sk} H={H} Hq={Hq} Hkv={Hkv}", flush=True)
+    inp = _small_inputs(sq, sk, H, Hq, Hkv, seed=31)
+    path = run_path(inp)
+    sel = to_np(path.topk)[:, 0, :]
+    check_selection_invariants(inp, sel)
+    check_csr(inp, sel, to_np(path.row_ptr), to_np(path.q_indices))
+    check_attention(inp, sel, to_np(path.out.float()).reshape(inp.total_q, Hq, 128),
+                    np.arange(inp.total_q))
+
+
+def test_per_kv_head_selection_with_repeats_large():
+    """One selection per KV head over 1300 queries, some slots repeating a
+    page: each (query, KV head) attends to its own distinct pages once."""
+    from fp8_top_page_amd.pipeline import DeviceBatch, MsaPath
+    inp = _small_inputs((900, 400), (12000, 5000), 1, 16, 2, seed=19)
+    sel = workloads.random_topk(inp, n_sel=2, seed=4)
+    sel[:, 1, 15] = sel[:, 1, 2]
+    sel[:, 0, 13] = np.where(sel[:, 0, 13] >= 0, sel[:, 0, 0], -1)
+    db = DeviceBatch.from_inputs(inp)
+    path = MsaPath(db, n_sel=2)
+    path.topk.copy_(torch.from_numpy(sel))
+    path.csr()
+    path.attend()
+    torch.cuda.synchronize()
+    check_csr(inp, sel, to_np(path.row_ptr), to_np(path.q_indices), n_sel=2)
+    out = to_np(path.out.float()).reshape(inp.total_q, 16, 128)
+    check_attention(inp, sel, out, np.arange(inp.total_q), n_sel=2)
+
+
 def test_empty_batch_is_a_no_op():
     inp = _small_inputs((0, 0), (300, 128))
     path = run_path(inp)
