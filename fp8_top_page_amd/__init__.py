@@ -17,7 +17,7 @@ __all__ = [
     "msa_topk_select", "msa_build_k2q_csr", "msa_k2q_schedule_size", "msa_sparse_attn_prefill",
     "msa_sparse_attn_workspace_size", "msa_status_string", "msa_last_error", "msa_abi_version",
     "msa_quantize_e4m3", "msa_insert_index_k", "msa_insert_kv", "msa_index_score_mxfp4",
-    "msa_insert_index_k_mxfp4",
+    "msa_insert_index_k_mxfp4", "msa_index_score_noalloc",
     "LIB_PATH", "PAGE", "HEAD_DIM", "TOPK",
 ]
 
@@ -89,6 +89,9 @@ def lib():
         L.msa_insert_index_k_mxfp4.argtypes = [_c_p, _c_i32, _c_i64, _c_i64, _c_p, _c_p, _c_p,
                                                _c_i32, _c_p]
         L.msa_insert_index_k_mxfp4.restype = ctypes.c_int
+        L.msa_index_score_noalloc.argtypes = [vp, _c_p, _c_i64, _c_i32, _c_p, _c_i32, _c_p, _c_p,
+                                              _c_p, _c_i64, _c_p]
+        L.msa_index_score_noalloc.restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
         L.msa_last_error.argtypes = []
@@ -266,3 +269,12 @@ def msa_insert_index_k_mxfp4(k, slot_mapping, k_data, k_scales, num_pages, strea
                                         num_pages, _stream(stream))
     _check(st, "msa_insert_index_k_mxfp4")
 
+
+
+def msa_index_score_noalloc(vl: Varlen, q, num_index_heads, k_cache, num_pages, q_scale, k_scale,
+                            scores, stream=None):
+    """msa_index_score with the library's built-in work-list buffer (no workspace)."""
+    st = lib().msa_index_score_noalloc(vl.ref, _ptr(q), q.stride(0), num_index_heads, _ptr(k_cache),
+                                       num_pages, _ptr(q_scale), _ptr(k_scale), _ptr(scores),
+                                       scores.stride(0), _stream(stream))
+    _check(st, "msa_index_score_noalloc")

@@ -8,6 +8,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "msa_internal.h"
 
@@ -152,6 +153,71 @@ msa_status_t msa_index_score(const msa_varlen_t* vl, const uint8_t* q, int64_t q
   return index_score_impl(vl, q, q_stride, num_index_heads, k_cache, nullptr, num_pages, q_scale,
                           k_scale, scores, ld_scores, workspace, workspace_bytes, stream,
                           "msa_index_score");
+}
+
+// ---- index scoring without allocation ---------------------------------------
+// The scorer's work list (a header and one 16-byte item per planned work item)
+// lives in this file-scope device array instead of a caller workspace.  Each
+// GPU holds its own copy until the process ends.  Host code never uses the
+// array's name as an address: its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and kept per device.
+}  // extern "C"
+
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+msa_status_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "msa_index_score_noalloc: hipGetDevice");
+  MSA_CHECK(dev >= 0 && dev < kMaxDevices, MSA_ERR_UNSUPPORTED,
+            "msa_index_score_noalloc: device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "msa_index_score_noalloc: hipGetSymbolAddress(scratch)");
+    MSA_CHECK(p != nullptr, MSA_ERR_HIP, "msa_index_score_noalloc: scratch has no device address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status_t msa_index_score_noalloc(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
+                                     int32_t num_index_heads, const uint8_t* k_cache,
+                                     int32_t num_pages, const float* q_scale,
+                                     const float* k_scale, float* scores, int64_t ld_scores,
+                                     void* stream) {
+  msa_status_t st = check_varlen(vl);
+  if (st != MSA_OK) return st;
+  const int H = num_index_heads;
+  MSA_CHECK(H == 1 || H == 2 || H == 4, MSA_ERR_UNSUPPORTED,
+            "num_index_heads must be 1, 2 or 4 (got %d)", H);
+  if (vl->total_q == 0) return MSA_OK;
+  const size_t need = score_plan(vl, H).workspace_bytes;
+  MSA_CHECK(need <= kNoAllocScratchBytes, MSA_ERR_UNSUPPORTED,
+            "msa_index_score_noalloc: the batch needs %zu bytes of work list, the built-in scratch "
+            "holds %zu; use msa_index_score with a workspace", need, kNoAllocScratchBytes);
+  st = check_device();
+  if (st != MSA_OK) return st;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != MSA_OK) return st;
+  return index_score_impl(vl, q, q_stride, num_index_heads, k_cache, nullptr, num_pages, q_scale,
+                          k_scale, scores, ld_scores, ws, kNoAllocScratchBytes, stream,
+                          "msa_index_score_noalloc");
 }
 
 msa_status_t msa_index_score_mxfp4(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,

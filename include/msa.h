@@ -272,6 +272,29 @@ msa_status_t msa_insert_index_k_mxfp4(const void* k, int32_t src_dtype, int64_t 
                                       void* stream);
 
 /* ---------------------------------------------------------------------------
+ * 7. Index scoring without allocation.  For callers that cannot allocate or
+ *    provide device memory (code under HIP graph capture that must not add
+ *    allocations, serving loops and harnesses that forbid allocation): exactly
+ *    msa_index_score (section 1), same arguments, layouts, results and errors,
+ *    except that the scorer's work list lives in a buffer built into the
+ *    library instead of a caller workspace.
+ *
+ * The built-in buffer holds 1 MiB per GPU (kept until the process ends); a
+ * batch whose work list needs more (msa_index_score_workspace_size(vl, H) >
+ * 1048576, i.e. hundreds of thousands of queries) is rejected with
+ * MSA_ERR_UNSUPPORTED before anything is launched.  Nothing is allocated:
+ * the buffer's device address is looked up on the first call on each device.
+ * Every call on one GPU shares that GPU's buffer, so calls that overlap in
+ * time on one GPU (other streams, other host threads) race and must be
+ * ordered by the caller; consecutive calls on one stream are safe.
+ * ------------------------------------------------------------------------- */
+msa_status_t msa_index_score_noalloc(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
+                                     int32_t num_index_heads, const uint8_t* k_cache,
+                                     int32_t num_pages, const float* q_scale,
+                                     const float* k_scale, float* scores, int64_t ld_scores,
+                                     void* stream);
+
+/* ---------------------------------------------------------------------------
  * Diagnostics.
  * ------------------------------------------------------------------------- */
 const char* msa_status_string(msa_status_t status);  /* static string */

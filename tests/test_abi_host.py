@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
         "msa_k2q_schedule_size", "msa_build_k2q_csr", "msa_sparse_attn_workspace_size",
         "msa_sparse_attn_prefill", "msa_status_string", "msa_last_error", "msa_abi_version",
         "msa_quantize_e4m3", "msa_insert_index_k", "msa_insert_kv", "msa_index_score_mxfp4",
-        "msa_insert_index_k_mxfp4"]), names
+        "msa_insert_index_k_mxfp4", "msa_index_score_noalloc"]), names
     for n in names:
         assert hasattr(L, n), n
     assert msa.msa_abi_version() == 3
@@ -240,3 +240,24 @@ def test_mxfp4_validation():
     if NO_GPU:
         assert ins() == NO_DEV
 
+
+
+def test_noalloc_scoring_validation():
+    """The no-allocation scorer: the same argument checks as msa_index_score,
+    and batches whose work list exceeds its 1 MiB built-in buffer are rejected
+    on the host, before any device call."""
+    L = msa.lib()
+
+    def na(v, H=1):
+        return L.msa_index_score_noalloc(ctypes.byref(v), FAKE, 128 * H, H, FAKE, 8, FAKE, FAKE,
+                                         FAKE, 8, None)
+    assert L.msa_index_score_noalloc(None, FAKE, 128, 1, FAKE, 8, FAKE, FAKE, FAKE, 8, None) == INVALID
+    assert na(vl(), H=3) == UNSUPPORTED
+    assert na(vl(total_q=0)) == OK
+    big = vl(batch=4096, total_q=1 << 22, max_q=1024, max_k=1 << 20, rows=4096 * 8192,
+             max_pages=8192, stride=8192)
+    assert L.msa_index_score_workspace_size(ctypes.byref(big), 1) > 1 << 20
+    assert na(big) == UNSUPPORTED
+    assert "built-in scratch" in msa.msa_last_error()
+    if NO_GPU:
+        assert na(vl()) == NO_DEV
