@@ -319,7 +319,7 @@ def _request_keys(k_cache, block_table, b, seqlen_k):
 # page per query; score-only plan(..., score_out=) / run_scores()]
 # ----------------------------------------------------------------------------
 def index_scores(cu_q, cu_k, block_table, index_q, k_cache, q_scale, k_scale,
-                 queries=None, width=None):
+                 queries=None, width=None, per_head=False):
     """Page scores s(i, j), float64, -inf where page j is not visible to query i.
 
     The pages do not state the reduction over a page's tokens or over index
@@ -335,6 +335,14 @@ def index_scores(cu_q, cu_k, block_table, index_q, k_cache, q_scale, k_scale,
     bytes, or an Mxfp4Keys cache (values = E2M1 element * 2^(scale - 127)).
     queries: optional list of global query indices (default: all).
     Returns [len(queries), width] with width = max pages per request by default.
+
+    per_head=True is the other reading of how selections map to KV heads (the
+    top-k buffer is [total_q, H, 16], one selection per KV head, API docs,
+    MiniMaxM3SparseMSAImpl.forward): index head h is scored alone,
+
+        s_h(i, j) = q_scale * k_scale * max_{t in page j, t <= pos_i} sum_d q[i,h,d] * k[t,d]
+
+    and the result is [len(queries), H, width].
     """
     cu_q = np.asarray(cu_q, np.int64)
     cu_k = np.asarray(cu_k, np.int64)
@@ -346,7 +354,8 @@ def index_scores(cu_q, cu_k, block_table, index_q, k_cache, q_scale, k_scale,
     seqlen_k = np.diff(cu_k)
     if width is None:
         width = int(((seqlen_k + PAGE - 1) // PAGE).max()) if len(seqlen_k) else 0
-    out = np.full((len(queries), width), -np.inf, np.float64)
+    H = np.asarray(index_q).shape[1]
+    out = np.full((len(queries), H, width) if per_head else (len(queries), width), -np.inf, np.float64)
     scale = float(q_scale) * float(k_scale)
     for b in np.unique(req[queries]) if len(queries) else []:
         sel = np.nonzero(req[queries] == b)[0]
@@ -358,16 +367,22 @@ def index_scores(cu_q, cu_k, block_table, index_q, k_cache, q_scale, k_scale,
             last = int(pos[qi].max())
             kk = keys[:last + 1]                                          # [T, 128]
             qq = decode_e4m3(index_q[qi])                                 # [n, H, 128]
-            dots = np.zeros((kk.shape[0], len(qi)), np.float64)
-            for h in range(qq.shape[1]):                                  # sum over index heads
-                dots += kk @ qq[:, h, :].T
             t = np.arange(kk.shape[0])[:, None]
-            dots[t > pos[qi][None, :]] = -np.inf                          # causal: t <= pos_i
             n_pages = (kk.shape[0] + PAGE - 1) // PAGE
-            padded = np.full((n_pages * PAGE, len(qi)), -np.inf)
-            padded[:kk.shape[0]] = dots
-            page_max = padded.reshape(n_pages, PAGE, len(qi)).max(axis=1)  # [pages, n]
-            out[rows, :n_pages] = (page_max * scale).T
+            # summed: one dot product over all index heads; per head: one per head
+            groups = [[h] for h in range(qq.shape[1])] if per_head else [range(qq.shape[1])]
+            for gi, heads in enumerate(groups):
+                dots = np.zeros((kk.shape[0], len(qi)), np.float64)
+                for h in heads:
+                    dots += kk @ qq[:, h, :].T
+                dots[t > pos[qi][None, :]] = -np.inf                      # causal: t <= pos_i
+                padded = np.full((n_pages * PAGE, len(qi)), -np.inf)
+                padded[:kk.shape[0]] = dots
+                page_max = padded.reshape(n_pages, PAGE, len(qi)).max(axis=1)   # [pages, n]
+                if per_head:
+                    out[rows, gi, :n_pages] = (page_max * scale).T
+                else:
+                    out[rows, :n_pages] = (page_max * scale).T
     return out
 
 

@@ -38,8 +38,19 @@ def test_hand_case_golden():
         assert sc[pos, page] == exp, (pos, page, sc[pos, page], exp)
 
 
-def _brute_scores(cu_q, cu_k, bt, q, kc, qs, ks):
-    """Per-token Python loops; decode through torch's float8 cast (not the oracle table)."""
+def test_hand_case_per_head_golden():
+    """The per-head reading (each index head scored alone) on the same hand case."""
+    spec, args = _hand_case()
+    sc = oracle.index_scores(*args, per_head=True)
+    assert sc.shape[1] == 2
+    for pos, page, head, val in spec["per_head_expected"]:
+        exp = -np.inf if val == "-inf" else float(val)
+        assert sc[pos, head, page] == exp, (pos, page, head, sc[pos, head, page], exp)
+
+
+def _brute_scores(cu_q, cu_k, bt, q, kc, qs, ks, per_head=False):
+    """Per-token Python loops; decode through torch's float8 cast (not the oracle table).
+    per_head: one score per (query, index head, page), no sum over heads."""
     dec = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e4m3fn).double().tolist()
     out = {}
     for b in range(len(cu_q) - 1):
@@ -49,15 +60,16 @@ def _brute_scores(cu_q, cu_k, bt, q, kc, qs, ks):
             pos = sk - sq + qi
             qv = [dec(q[i, h]) for h in range(q.shape[1])]
             for j in range(pos // PAGE + 1):
-                best = None
-                for t in range(PAGE * j, min(PAGE * j + PAGE, pos + 1)):
-                    kv = dec(kc[bt[b, j], t - PAGE * j])
-                    acc = 0.0
-                    for h in range(len(qv)):
-                        for d in range(D):
-                            acc += qv[h][d] * kv[d]
-                    best = acc if best is None else max(best, acc)
-                out[(i, j)] = best * qs * ks
+                for hs in ([[h] for h in range(len(qv))] if per_head else [range(len(qv))]):
+                    best = None
+                    for t in range(PAGE * j, min(PAGE * j + PAGE, pos + 1)):
+                        kv = dec(kc[bt[b, j], t - PAGE * j])
+                        acc = 0.0
+                        for h in hs:
+                            for d in range(D):
+                                acc += qv[h][d] * kv[d]
+                        best = acc if best is None else max(best, acc)
+                    out[(i, hs[0], j) if per_head else (i, j)] = best * qs * ks
     return out
 
 
@@ -134,3 +146,39 @@ def test_planted_mistakes_are_caught(monkeypatch):
     q_one_head = q[:, :1].copy()                # drop head 1
     sc = oracle.index_scores(cu_q, cu_k, bt, q_one_head, kc, qs, ks)
     assert sc[255, 1] != 0.5 and sc[100, 0] != 0.375
+
+
+@pytest.mark.parametrize("H", [2, 4])
+def test_per_head_brute_force_tiny(H):
+    rng = np.random.default_rng(20 + H)
+    cu_q, cu_k, bt, num_pages = varlen([4, 3], [190, 140], spare=1, seed=H)
+    total_q, total_k = int(cu_q[-1]), int(cu_k[-1])
+    q = random_codes(rng, (total_q, H, D))
+    rows = random_codes(rng, (total_k, D))
+    kc = scatter_pages(rows, cu_k, bt, num_pages, (D,))
+    sc = oracle.index_scores(cu_q, cu_k, bt, q, kc, 0.75, 1.5, per_head=True)
+    ref = _brute_scores(cu_q, cu_k, bt, q, kc, 0.75, 1.5, per_head=True)
+    assert sc.shape[:2] == (total_q, H)
+    for (i, h, j), v in ref.items():
+        assert sc[i, h, j] == pytest.approx(v, rel=1e-12, abs=1e-12), (i, h, j)
+    assert np.isfinite(sc).sum() == len(ref)
+
+
+def test_per_head_special_cases():
+    """One index head: per head equals summed.  A query whose other heads are
+    zero: its scores for the non-zero head equal the summed scores, and the zero
+    heads score exactly 0 on every visible page."""
+    rng = np.random.default_rng(8)
+    cu_q, cu_k, bt, num_pages = varlen([20, 9], [600, 300], seed=5)
+    rows = random_codes(rng, (int(cu_k[-1]), D))
+    kc = scatter_pages(rows, cu_k, bt, num_pages, (D,))
+    q1 = random_codes(rng, (int(cu_q[-1]), 1, D))
+    assert np.array_equal(oracle.index_scores(cu_q, cu_k, bt, q1, kc, 0.5, 2.0, per_head=True)[:, 0],
+                          oracle.index_scores(cu_q, cu_k, bt, q1, kc, 0.5, 2.0))
+    q3 = np.zeros((int(cu_q[-1]), 3, D), np.uint8)
+    q3[:, 1] = q1[:, 0]
+    ph = oracle.index_scores(cu_q, cu_k, bt, q3, kc, 0.5, 2.0, per_head=True)
+    summed = oracle.index_scores(cu_q, cu_k, bt, q3, kc, 0.5, 2.0)
+    assert np.array_equal(ph[:, 1], summed)
+    vis = np.isfinite(summed)
+    assert np.all(ph[:, 0][vis] == 0.0) and np.all(ph[:, 2][vis] == 0.0)
