@@ -17,7 +17,7 @@ __all__ = [
     "msa_topk_select", "msa_build_k2q_csr", "msa_k2q_schedule_size", "msa_sparse_attn_prefill",
     "msa_sparse_attn_workspace_size", "msa_status_string", "msa_last_error", "msa_abi_version",
     "msa_quantize_e4m3", "msa_insert_index_k", "msa_insert_kv", "msa_index_score_mxfp4",
-    "msa_insert_index_k_mxfp4", "msa_index_score_noalloc",
+    "msa_insert_index_k_mxfp4", "msa_index_score_noalloc", "msa_index_score_per_head",
     "LIB_PATH", "PAGE", "HEAD_DIM", "TOPK",
 ]
 
@@ -89,6 +89,9 @@ def lib():
         L.msa_insert_index_k_mxfp4.argtypes = [_c_p, _c_i32, _c_i64, _c_i64, _c_p, _c_p, _c_p,
                                                _c_i32, _c_p]
         L.msa_insert_index_k_mxfp4.restype = ctypes.c_int
+        L.msa_index_score_per_head.argtypes = [vp, _c_p, _c_i64, _c_i32, _c_p, _c_i32, _c_p, _c_p,
+                                               _c_p, _c_i64, _c_i64, _c_p, _c_size, _c_p]
+        L.msa_index_score_per_head.restype = ctypes.c_int
         L.msa_index_score_noalloc.argtypes = [vp, _c_p, _c_i64, _c_i32, _c_p, _c_i32, _c_p, _c_p,
                                               _c_p, _c_i64, _c_p]
         L.msa_index_score_noalloc.restype = ctypes.c_int
@@ -278,3 +281,15 @@ def msa_index_score_noalloc(vl: Varlen, q, num_index_heads, k_cache, num_pages, 
                                        num_pages, _ptr(q_scale), _ptr(k_scale), _ptr(scores),
                                        scores.stride(0), _stream(stream))
     _check(st, "msa_index_score_noalloc")
+
+
+def msa_index_score_per_head(vl: Varlen, q, num_index_heads, k_cache, num_pages, q_scale, k_scale,
+                             scores, workspace, stream=None):
+    """Per-index-head scores: scores f32 [total_q, H, ld] (query stride scores.stride(0), head
+    stride scores.stride(1))."""
+    st = lib().msa_index_score_per_head(vl.ref, _ptr(q), q.stride(0), num_index_heads,
+                                        _ptr(k_cache), num_pages, _ptr(q_scale), _ptr(k_scale),
+                                        _ptr(scores), scores.stride(0), scores.stride(1),
+                                        _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                        _stream(stream))
+    _check(st, "msa_index_score_per_head")

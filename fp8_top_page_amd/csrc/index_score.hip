@@ -1098,8 +1098,34 @@ ScorePlan score_plan(const msa_varlen_t* vl, int H) {
   return p;
 }
 
+// The device plan (work list of a.H-head q-blocks) into the workspace, then the
+// scorer over (q, scores); per-head scoring runs the single-head scorer once per
+// head over the same plan.
+static hipError_t launch_plan(const ScoreArgs& a, hipStream_t stream);
+static hipError_t launch_scorer_pass(const ScoreArgs& a, const uint8_t* q, float* scores,
+                                     hipStream_t stream);
+
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
   if (a.vl.total_q == 0) return hipSuccess;
+  hipError_t e = launch_plan(a, stream);
+  if (e != hipSuccess) return e;
+  return launch_scorer_pass(a, a.q, a.scores, stream);
+}
+
+hipError_t launch_index_score_heads(const ScoreArgs& a, int64_t head_stride, hipStream_t stream) {
+  if (a.vl.total_q == 0) return hipSuccess;
+  ScoreArgs one = a;
+  one.H = 1;                                  // every pass scores one index head
+  hipError_t e = launch_plan(one, stream);
+  if (e != hipSuccess) return e;
+  for (int h = 0; h < a.H; ++h) {
+    e = launch_scorer_pass(one, a.q + (int64_t)h * kDim, a.scores + (int64_t)h * head_stride, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+static hipError_t launch_plan(const ScoreArgs& a, hipStream_t stream) {
   ItemHdr* hdr = reinterpret_cast<ItemHdr*>(a.workspace);
   int4* items = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(a.workspace) + sizeof(ItemHdr));
   const int qb = score_qblock(a.H);
@@ -1114,8 +1140,13 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
   else
     hipLaunchKernelGGL(score_plan_kernel, dim3(1), dim3(256), 0, stream, a.vl.cu_seqlens_q,
                        a.vl.cu_seqlens_k, a.vl.batch, qb, align, a.plan.max_items, hdr, items);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+static hipError_t launch_scorer_pass(const ScoreArgs& a, const uint8_t* q, float* scores,
+                                     hipStream_t stream) {
+  ItemHdr* hdr = reinterpret_cast<ItemHdr*>(a.workspace);
+  int4* items = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(a.workspace) + sizeof(ItemHdr));
   ScoreK k;
   k.cu_q = a.vl.cu_seqlens_q;
   k.cu_k = a.vl.cu_seqlens_k;
@@ -1124,12 +1155,12 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
   k.batch = a.vl.batch;
   k.num_pages = a.num_pages;
   k.max_pages = a.vl.max_pages;
-  k.q = a.q;
+  k.q = q;
   k.q_stride = a.q_stride;
   k.k_cache = a.k_cache;
   k.q_scale = a.q_scale;
   k.k_scale = a.k_scale;
-  k.scores = a.scores;
+  k.scores = scores;
   k.ld = a.ld;
   k.hdr = hdr;
   k.items = items;

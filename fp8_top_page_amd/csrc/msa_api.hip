@@ -102,12 +102,14 @@ size_t msa_index_score_workspace_size(const msa_varlen_t* vl, int32_t num_index_
 namespace {
 
 // Shared by both key formats: k_scales == nullptr means E4M3 keys.
+// head_stride < 0: scores summed over the index heads (one row per query);
+// otherwise one row per (query, head), head h's row at h * head_stride.
 msa_status_t index_score_impl(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
                               int32_t num_index_heads, const uint8_t* k_cache,
                               const uint8_t* k_scales, int32_t num_pages, const float* q_scale,
                               const float* k_scale, float* scores, int64_t ld_scores,
                               void* workspace, size_t workspace_bytes, void* stream,
-                              const char* name) {
+                              const char* name, int64_t head_stride = -1) {
   msa_status_t st = check_varlen(vl);
   if (st != MSA_OK) return st;
   const int H = num_index_heads;
@@ -128,7 +130,15 @@ msa_status_t index_score_impl(const msa_varlen_t* vl, const uint8_t* q, int64_t 
   MSA_CHECK(ld_scores % 4 == 0 && aligned(scores, 16), MSA_ERR_INVALID_ARGUMENT,
             "ld_scores must be a multiple of 4 and scores 16-byte aligned");
   MSA_CHECK(aligned(workspace, 16), MSA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
-  const ScorePlan plan = score_plan(vl, H);
+  if (head_stride >= 0) {
+    MSA_CHECK(head_stride >= vl->max_pages && head_stride % 4 == 0, MSA_ERR_INVALID_ARGUMENT,
+              "head_stride (%lld) must be >= max_pages (%d) and a multiple of 4",
+              (long long)head_stride, vl->max_pages);
+    MSA_CHECK(ld_scores >= (int64_t)(H - 1) * head_stride + vl->max_pages, MSA_ERR_INVALID_ARGUMENT,
+              "ld_scores (%lld) cannot hold %d head rows of stride %lld", (long long)ld_scores, H,
+              (long long)head_stride);
+  }
+  const ScorePlan plan = score_plan(vl, head_stride >= 0 ? 1 : H);
   MSA_CHECK(workspace_bytes >= plan.workspace_bytes, MSA_ERR_WORKSPACE_TOO_SMALL,
             "workspace has %zu bytes, needs %zu", workspace_bytes, plan.workspace_bytes);
   MSA_CHECK(plan.max_items < (int64_t)INT32_MAX, MSA_ERR_UNSUPPORTED, "batch too large");
@@ -136,7 +146,9 @@ msa_status_t index_score_impl(const msa_varlen_t* vl, const uint8_t* q, int64_t 
   if (st != MSA_OK) return st;
   ScoreArgs a{*vl, q, q_stride, H, k_cache, num_pages, q_scale, k_scale,
               scores, ld_scores, workspace, plan, k_scales};
-  hipError_t e = launch_index_score(a, reinterpret_cast<hipStream_t>(stream));
+  hipError_t e = head_stride >= 0
+                     ? launch_index_score_heads(a, head_stride, reinterpret_cast<hipStream_t>(stream))
+                     : launch_index_score(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, name);
   return MSA_OK;
 }
@@ -218,6 +230,17 @@ msa_status_t msa_index_score_noalloc(const msa_varlen_t* vl, const uint8_t* q, i
   return index_score_impl(vl, q, q_stride, num_index_heads, k_cache, nullptr, num_pages, q_scale,
                           k_scale, scores, ld_scores, ws, kNoAllocScratchBytes, stream,
                           "msa_index_score_noalloc");
+}
+
+msa_status_t msa_index_score_per_head(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
+                                      int32_t num_index_heads, const uint8_t* k_cache,
+                                      int32_t num_pages, const float* q_scale,
+                                      const float* k_scale, float* scores, int64_t ld_scores,
+                                      int64_t head_stride, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  return index_score_impl(vl, q, q_stride, num_index_heads, k_cache, nullptr, num_pages, q_scale,
+                          k_scale, scores, ld_scores, workspace, workspace_bytes, stream,
+                          "msa_index_score_per_head", head_stride);
 }
 
 msa_status_t msa_index_score_mxfp4(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,

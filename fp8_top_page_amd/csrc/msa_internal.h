@@ -54,6 +54,9 @@ struct ScoreArgs {
   const uint8_t* k_scales;     // nullptr: E4M3 keys; else MXFP4 block scales [num_pages, 128, 4]
 };
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream);
+// Per-index-head scores: a.H single-head passes over one single-head plan,
+// head h's scores at a.scores + h * head_stride (a.plan must be score_plan(vl, 1)).
+hipError_t launch_index_score_heads(const ScoreArgs& a, int64_t head_stride, hipStream_t stream);
 
 // ---- top-k ---------------------------------------------------------------
 struct TopkArgs {

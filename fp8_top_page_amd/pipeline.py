@@ -8,8 +8,8 @@ import numpy as np
 import torch
 
 from . import (PAGE, TOPK, Varlen, msa_build_k2q_csr, msa_index_score, msa_index_score_mxfp4,
-               msa_index_score_workspace_size, msa_k2q_schedule_size, msa_sparse_attn_prefill,
-               msa_sparse_attn_workspace_size, msa_topk_select)
+               msa_index_score_per_head, msa_index_score_workspace_size, msa_k2q_schedule_size,
+               msa_sparse_attn_prefill, msa_sparse_attn_workspace_size, msa_topk_select)
 
 
 def _dev(x, device, dtype=None):
@@ -77,16 +77,27 @@ class DeviceBatch:
 
 
 class MsaPath:
-    """Outputs and workspaces for one batch; run the four calls in order."""
+    """Outputs and workspaces for one batch; run the four calls in order.
 
-    def __init__(self, db: DeviceBatch, n_local: int = 1, n_sel: int = 1, score_fill=float("nan")):
+    per_head=True: each index head h scores alone and selects the pages of KV
+    head h (scores [total_q, H, ld], top-k [total_q, H, 16], one CSR per KV
+    head); it needs H == num_kv_heads."""
+
+    def __init__(self, db: DeviceBatch, n_local: int = 1, n_sel: int = 1, score_fill=float("nan"),
+                 per_head: bool = False):
         self.db = db
         self.n_local = n_local
+        self.per_head = per_head
+        if per_head:
+            n_sel = db.H
+            if db.attn_q is not None and db.Hkv != db.H:
+                raise ValueError("per-head selection needs as many index heads as KV heads")
         self.n_sel = n_sel
         dev = db.device
         vl = db.vl
         self.ld = (db.max_pages + 3) // 4 * 4
-        self.scores = torch.full((db.total_q, self.ld), score_fill, dtype=torch.float32, device=dev)
+        shape = (db.total_q, db.H, self.ld) if per_head else (db.total_q, self.ld)
+        self.scores = torch.full(shape, score_fill, dtype=torch.float32, device=dev)
         self.ws_score = torch.empty(max(msa_index_score_workspace_size(vl, db.H), 256),
                                     dtype=torch.uint8, device=dev)
         self.topk = torch.full((db.total_q, n_sel, TOPK), -7, dtype=torch.int32, device=dev)
@@ -103,7 +114,10 @@ class MsaPath:
 
     def score(self, stream=None):
         db = self.db
-        if db.k_fp4 is not None:                  # MXFP4 index keys
+        if self.per_head:
+            msa_index_score_per_head(db.vl, db.index_q, db.H, db.k_cache, db.num_pages,
+                                     db.iq_scale, db.ik_scale, self.scores, self.ws_score, stream)
+        elif db.k_fp4 is not None:                # MXFP4 index keys
             msa_index_score_mxfp4(db.vl, db.index_q, db.H, db.k_fp4[0], db.k_fp4[1], db.num_pages,
                                   db.iq_scale, db.ik_scale, self.scores, self.ws_score, stream)
         else:
@@ -111,8 +125,12 @@ class MsaPath:
                             db.ik_scale, self.scores, self.ws_score, stream)
 
     def select(self, stream=None):
-        assert self.n_sel == 1
-        msa_topk_select(self.db.vl, self.scores, TOPK, self.n_local, self.topk[:, 0, :], stream)
+        if self.per_head:                         # one selection per (query, index head)
+            for h in range(self.db.H):
+                msa_topk_select(self.db.vl, self.scores[:, h, :], TOPK, self.n_local,
+                                self.topk[:, h, :], stream)
+        else:
+            msa_topk_select(self.db.vl, self.scores, TOPK, self.n_local, self.topk[:, 0, :], stream)
 
     def csr(self, stream=None, topk=None):
         t = self.topk if topk is None else topk

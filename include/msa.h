@@ -110,6 +110,34 @@ msa_status_t msa_index_score(const msa_varlen_t* vl, const uint8_t* q, int64_t q
                              size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * 1b. Per-index-head scores: the reading in which index head h selects the
+ *     pages of KV head h ([P4] forward: the top-k buffer is [total_q, H, 16],
+ *     viewed per KV head; [P2] script: an independent selection per KV head).
+ *     The pages leave open how head h's score is formed; here each index head
+ *     is scored alone, with no sum over heads:
+ *
+ *   scores[i * ld_scores + h * head_stride + j] =
+ *       q_scale * k_scale * max_{t in page j, t <= pos_i} sum_{d < 128} q[i,h,d] * k[block_table[b,j], t % 128, d]
+ *
+ * for h < H and every visible page j < v_i; entries j >= v_i are NOT written.
+ * Arguments and errors as msa_index_score, plus
+ *   head_stride  floats between the rows of consecutive heads of one query:
+ *                >= max_pages and a multiple of 4; ld_scores >= (H-1)*head_stride + max_pages
+ *   workspace    >= msa_index_score_workspace_size(vl, 1) bytes (the plan is
+ *                that of one index head; the size for H heads is also enough)
+ * The index-K cache is read once per index head (H scorer passes over one
+ * plan); select per head with msa_topk_select on each head's rows (scores +
+ * h*head_stride, row stride ld_scores, output topk_idx + h*16 with
+ * topk_stride = H*16), then build the CSR with n_sel_heads = H = num_kv_heads.
+ * ------------------------------------------------------------------------- */
+msa_status_t msa_index_score_per_head(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
+                                      int32_t num_index_heads, const uint8_t* k_cache,
+                                      int32_t num_pages, const float* q_scale,
+                                      const float* k_scale, float* scores, int64_t ld_scores,
+                                      int64_t head_stride, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/* ---------------------------------------------------------------------------
  * 2. Top-k page selection  ([P1] "Native Top16"; [P2] Validation, benchmark
  *    script case(): local page = visible - 1 always kept, future pages never
  *    chosen, k = min(16, visible), -1 padding.)

@@ -29,9 +29,9 @@ ATTN_FRAC = 1e-4
 ATTN_MAX = 0.25
 
 
-def run_path(inp, n_local=1, device="cuda"):
+def run_path(inp, n_local=1, device="cuda", per_head=False):
     db = DeviceBatch.from_inputs(inp, device)
-    path = MsaPath(db, n_local=n_local)
+    path = MsaPath(db, n_local=n_local, per_head=per_head)
     path.run()
     torch.cuda.synchronize()
     return path

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
         "msa_k2q_schedule_size", "msa_build_k2q_csr", "msa_sparse_attn_workspace_size",
         "msa_sparse_attn_prefill", "msa_status_string", "msa_last_error", "msa_abi_version",
         "msa_quantize_e4m3", "msa_insert_index_k", "msa_insert_kv", "msa_index_score_mxfp4",
-        "msa_insert_index_k_mxfp4", "msa_index_score_noalloc"]), names
+        "msa_insert_index_k_mxfp4", "msa_index_score_noalloc", "msa_index_score_per_head"]), names
     for n in names:
         assert hasattr(L, n), n
     assert msa.msa_abi_version() == 3
@@ -261,3 +261,19 @@ def test_noalloc_scoring_validation():
     assert "built-in scratch" in msa.msa_last_error()
     if NO_GPU:
         assert na(vl()) == NO_DEV
+
+
+def test_per_head_scoring_validation():
+    L = msa.lib()
+
+    def ph(v, H=2, ld=16, hs=8, ws=1 << 20):
+        return L.msa_index_score_per_head(ctypes.byref(v), FAKE, 128 * H, H, FAKE, 8, FAKE, FAKE,
+                                          FAKE, ld, hs, 0x100000, ws, None)
+    assert ph(vl(), H=3) == UNSUPPORTED
+    assert ph(vl(), hs=6) == INVALID              # head stride not a multiple of 4
+    assert ph(vl(), hs=4) == INVALID              # head stride < max_pages
+    assert ph(vl(), ld=12) == INVALID             # ld cannot hold 2 heads of stride 8
+    assert ph(vl(), ws=16) == WS_SMALL
+    assert ph(vl(total_q=0)) == OK
+    if NO_GPU:
+        assert ph(vl()) == NO_DEV

@@ -156,6 +156,35 @@ def test_per_kv_head_selection_with_repeats_large():
     check_attention(inp, sel, out, np.arange(inp.total_q), n_sel=2)
 
 
+@pytest.mark.parametrize("sq,sk,H", [
+    ((300, 40), (9000, 700), 2),
+    ((1200,), (30000,), 4),
+    ((8,) * 20, (12800,) * 20, 2),              # decode-like: page-parallel scorer
+])
+def test_per_index_head_selection(sq, sk, H):
+    """Index head h scores alone (no head sum) and selects the pages of KV head
+    h: per-head scores, per-head top-k, one CSR per KV head and attention
+    against the oracle's per-head reading on every query."""
+    print(f"\n[parity] per-head selection sq={sq} sk={sk} H=Hkv={H}", flush=True)
+    inp = _small_inputs(sq, sk, H, 8 * H, H, seed=23)
+    path = run_path(inp, per_head=True)
+    scores = to_np(path.scores)                          # [total_q, H, ld]
+    sel = to_np(path.topk)                               # [total_q, H, 16]
+    queries = np.arange(inp.total_q)
+    ref = oracle.index_scores(inp.cu_seqlens_q, inp.cu_seqlens_k, inp.block_table, inp.index_q,
+                              inp.index_k_cache, inp.index_q_scale, inp.index_k_scale,
+                              per_head=True)
+    for h in range(H):
+        check_scores(inp, scores[:, h, :], queries, ref=ref[:, h, :])
+        check_selection_invariants(inp, sel[:, h, :])
+        check_topk_exact_on_gpu_scores(inp, scores[:, h, :], sel[:, h, :])
+        check_topk_vs_reference(inp, sel[:, h, :], ref[:, h, :], queries)
+    assert any(not np.array_equal(sel[:, 0], sel[:, h]) for h in range(1, H)), "heads selected alike"
+    check_csr(inp, sel, to_np(path.row_ptr), to_np(path.q_indices), n_sel=H)
+    check_attention(inp, sel, to_np(path.out.float()).reshape(inp.total_q, 8 * H, 128), queries,
+                    n_sel=H)
+
+
 def test_empty_batch_is_a_no_op():
     inp = _small_inputs((0, 0), (300, 128))
     path = run_path(inp)
