@@ -47,6 +47,9 @@ class Workload:
     shift_fraction: float = 0.0  # fraction of tokens shifted along one direction
     shift_sigmas: float = 3.0
     description: str = ""
+    # attention-only stand-in: the selection is drawn at random by the rule of the
+    # pages' E4M3-query prefill benchmark (random_topk, one selection per KV head)
+    random_selection: bool = False
 
     @property
     def batch(self) -> int:
@@ -92,10 +95,24 @@ def _build_workloads():
     ws["decode_b64"] = Workload(
         "decode_b64", 7, (8,) * 64, (131072,) * 64, 1, 8, 1,
         description="64 requests, 8 new tokens each after a 131064-token prefix (1024 pages)")
+    # The five attention shapes of the E4M3-query prefill benchmark (vLLM PR
+    # 60684, Validation): (q-heads, KV heads, new tokens, cached context), one
+    # request, random top-16 per KV head with the local page kept; the timed unit
+    # there is the CSR build + attention + combine.  Index inputs are minimal
+    # (one head) and unused.
+    for k, (hq, hkv, q_len, ctx) in enumerate([(16, 1, 8192, 0), (16, 1, 8192, 32768),
+                                               (16, 1, 16384, 114688), (64, 4, 8192, 0),
+                                               (64, 4, 8192, 32768)]):
+        name = f"p2_h{hq}x{hkv}_q{q_len // 1024}k_c{ctx // 1024}k"
+        ws[name] = Workload(
+            name, 100 + k, (q_len,), (ctx + q_len,), 1, hq, hkv, random_selection=True,
+            description=f"attention stand-in: {hq} q-heads / {hkv} KV heads, {q_len} new tokens "
+                        f"after {ctx} cached, random top-16 per KV head")
     return ws
 
 
 WORKLOADS = _build_workloads()
+P2_SHAPES = [n for n in WORKLOADS if n.startswith("p2_")]
 ORDER = ["tiny_1k", "q128_kv32k", "fresh_32k", "q2048_kv1m", "ragged_b8", "decode_b16"]
 
 
