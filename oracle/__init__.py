@@ -9,5 +9,5 @@ from .msa import (  # noqa: F401
     topk_select, k2q_csr, sparse_attention, round_bf16, bf16_bits_to_float,
     encode_e4m3, quantize_e4m3, insert_index_k, insert_kv,
     Mxfp4Keys, e2m1_table, e8m0_value, decode_mxfp4, encode_e2m1, quantize_mxfp4,
-    insert_index_k_mxfp4,
+    insert_index_k_mxfp4, Mxfp4KV, mxfp4_staged_table, mxfp4_kv_as_e4m3,
 )

@@ -42,6 +42,11 @@ Pins (each function is checked by tests against something other than itself):
       the E2M1 value list by hand (tests/golden), torch's E8M0 decode, every
       code round-trips, ties to even, exact blocks reproduce their codes,
       scale choice and saturation by worked values.
+  mxfp4_staged_table / mxfp4_kv_as_e4m3 -- hand-worked (code, scale) codes
+      (tests/golden), torch's float8_e4m3fn cast of every clamped product, exact
+      agreement with decode_mxfp4 wherever the products are E4M3 values, element
+      placement by hand-placed bytes, and attention over it equal to dense
+      attention over decode_mxfp4 values.
   encode_e4m3 / quantize_e4m3 / insert_* -- every finite code round-trips,
       midpoints between neighbouring codes go to the even code, values just off
       a midpoint go to the nearer code, torch.float8_e4m3fn's CPU cast inside
@@ -231,6 +236,47 @@ def insert_index_k_mxfp4(cache: Mxfp4Keys, k, slot_mapping):
         cache.data[s // PAGE, s % PAGE] = d[0]
         cache.scales[s // PAGE, s % PAGE] = sc[0]
     return cache
+
+
+# ----------------------------------------------------------------------------
+# MXFP4 K|V pages read through E4M3 [P2 Details: with an E4M3 query the 4-bit
+# K|V kernel turns each code times its block scale into E4M3 before the FP8
+# products, and applies the K global scale to the scores and the V global scale
+# to the output; the reference of its test is the cache as that kernel reads
+# it.  Here the 4-bit format is MXFP4, the one gfx950's matrix cores take.]
+# ----------------------------------------------------------------------------
+class Mxfp4KV:
+    """An MXFP4 K|V cache: data [num_pages, Hkv, 128, 128] (bytes 0..63 hold the
+    token's 128 K elements, bytes 64..127 its 128 V elements, element 2i in the
+    low nibble of byte i as in Mxfp4Keys) and scales [num_pages, Hkv, 128, 8]
+    E8M0 (bytes 0..3: the K blocks of 32 elements, 4..7: the V blocks)."""
+
+    def __init__(self, data, scales):
+        self.data = np.asarray(data, np.uint8)
+        self.scales = np.asarray(scales, np.uint8)
+
+
+def mxfp4_staged_table() -> np.ndarray:
+    """[256, 16] E4M3 code of (E2M1 code value) x 2^(scale - 127) for every
+    (scale, code), rounded by encode_e4m3 (nearest, ties to even, saturating at
+    448); the NaN scale 0xFF gives NaN codes."""
+    t = np.empty((256, 16), np.uint8)
+    for sc in range(256):
+        t[sc] = encode_e4m3(_E2M1 * e8m0_value(sc))
+    return t
+
+
+_STAGED = mxfp4_staged_table()
+
+
+def mxfp4_kv_as_e4m3(data, scales) -> np.ndarray:
+    """The E4M3 K|V cache [..., 256] (K = [..., :128], V = [..., 128:]) that the
+    attention reads from MXFP4 K|V rows: data [..., 128], scales [..., 8]."""
+    data = np.asarray(data, np.uint8)
+    scales = np.asarray(scales, np.uint8)
+    codes = np.stack([data & 15, data >> 4], axis=-1).reshape(*data.shape[:-1], 2 * data.shape[-1])
+    block = np.repeat(scales, 32, axis=-1)            # element j belongs to block j // 32
+    return _STAGED[block, codes]
 
 
 # ----------------------------------------------------------------------------

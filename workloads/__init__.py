@@ -13,6 +13,9 @@ Formats (MiniMax-M3 MSA pages):
   * attention query [total_q, Hq, 128] E4M3 bytes, q_scale 0.5
   * K|V cache [num_pages, Hkv, 128, 256] E4M3 bytes, K = [..., :128],
     V = [..., 128:], unit scales (E4M3-query prefill page, benchmark script)
+  * MXFP4 K|V cache (kv_mxfp4): data [num_pages, Hkv, 128, 128] (K codes in
+    bytes 0..63, V codes in 64..127, two 4-bit codes per byte) and E8M0 block
+    scales [num_pages, Hkv, 128, 8] (K blocks 0..3, V blocks 4..7)
   * cu_seqlens_q / cu_seqlens_k [B+1] int32, block_table [B, max_pages] int32
     padded with -1.  New tokens are the last seqlen_q positions of each request.
 
@@ -277,3 +280,24 @@ def random_topk(inp: Inputs, n_sel: int, seed: int) -> np.ndarray:
                 if n_old:
                     out[i, g, 1:1 + n_old] = rng.choice(own, size=n_old, replace=False)
     return out
+
+
+def kv_mxfp4(inp: Inputs, seed: int, scale_lo: int = 124, scale_hi: int = 126):
+    """Random MXFP4 K|V pages for the attention of inp's batch: uniform 4-bit
+    codes and E8M0 block scales drawn uniformly from [scale_lo, scale_hi] (so
+    elements reach 6 * 2^(scale_hi - 127)).  Token rows outside every request
+    (unused rows of partial pages, spare pages) get the NaN scale 0xFF, so that
+    a read outside the visible range shows up as NaN.
+    Returns (data [num_pages, Hkv, 128, 128], scales [num_pages, Hkv, 128, 8])."""
+    rng = np.random.default_rng(seed)
+    hkv = inp.wl.kv_heads
+    data = rng.integers(0, 256, (inp.num_pages, hkv, PAGE, 128), dtype=np.uint8)
+    scales = rng.integers(scale_lo, scale_hi + 1, (inp.num_pages, hkv, PAGE, 8), dtype=np.uint8)
+    valid = np.zeros((inp.num_pages, PAGE), bool)
+    cu_k = np.asarray(inp.cu_seqlens_k, np.int64)
+    for b in range(len(cu_k) - 1):
+        n = int(cu_k[b + 1] - cu_k[b])
+        for j in range((n + PAGE - 1) // PAGE):
+            valid[inp.block_table[b, j], :min(PAGE, n - j * PAGE)] = True
+    scales.transpose(0, 2, 1, 3)[~valid] = 0xFF      # [pages, 128, Hkv, 8] view
+    return data, scales
