@@ -48,6 +48,9 @@ def parse():
                     help="per-index-head selection (each index head scores alone and selects the "
                          "pages of its KV head)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv-cache", choices=["e4m3", "mxfp4"], default="e4m3",
+                    help="K|V page format the attention reads (mxfp4: seeded random MXFP4 codes "
+                         "and block scales, read as E4M3)")
     ap.add_argument("--index-cache", choices=["e4m3", "mxfp4"], default="e4m3",
                     help="index-K format the scorer reads (mxfp4: the workload's keys re-quantised "
                          "on the device to E2M1 blocks with E8M0 scales)")
@@ -241,12 +244,13 @@ def hbm_record(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, c
     print(f"wrote {out}: {rec['hbm_bytes_per_launch'] / 1e6:.1f} MB per scorer launch")
 
 
-def algorithmic_work(inp, sel, key_bytes=128.0, per_head=False):
+def algorithmic_work(inp, sel, key_bytes=128.0, per_head=False, kv_page_bytes=32768.0):
     """FLOPs and bytes the path must do at minimum (see the design notes).
     sel: [total_q, n_sel, 16] (n_sel = 1: one selection shared by the KV heads;
     n_sel = Hkv: one per KV head); key_bytes: index-K bytes per token (128 E4M3,
     68 MXFP4); per_head: each index head scored alone (the keys are read once per
-    head and each head writes its own scores)."""
+    head and each head writes its own scores); kv_page_bytes: K|V bytes of one
+    page of one KV head (32768 E4M3, 128 * (128 + 8) = 17408 MXFP4)."""
     import numpy as np
     cu_q = np.asarray(inp.cu_seqlens_q, np.int64)
     cu_k = np.asarray(inp.cu_seqlens_k, np.int64)
@@ -281,7 +285,7 @@ def algorithmic_work(inp, sel, key_bytes=128.0, per_head=False):
             s = sel[cu_q[b]:cu_q[b + 1], g]
             distinct += len(np.unique(s[s >= 0]))
     kv_per_page = Hkv if n_sel == 1 else 1
-    attn_bytes = total_q * Hq * 128.0 + distinct * kv_per_page * 32768.0 + total_q * Hq * 128 * 2.0
+    attn_bytes = total_q * Hq * 128.0 + distinct * kv_per_page * kv_page_bytes + total_q * Hq * 128 * 2.0
     topk_bytes = passes * 4.0 * vis_sum + 64.0 * n_sel * total_q
     return dict(score_flops=score_flops, score_bytes=score_bytes, attn_flops=attn_flops,
                 attn_bytes=attn_bytes, topk_bytes=topk_bytes, attended_tokens=int(ntok),
@@ -523,6 +527,9 @@ def main():
         del kf
         db.k_fp4 = (data, scales)
         db.ik_scale = torch.ones(1, dtype=torch.float32, device=dev)
+    if args.kv_cache == "mxfp4":
+        kv_data, kv_scales = workloads.kv_mxfp4(inp, seed=wl.seed + 1000)
+        db.use_mxfp4_kv(kv_data, kv_scales)
     attention_only = wl.random_selection
     if attention_only:
         # the benchmark script's unit: CSR build + attention (+ combine) on a
@@ -581,7 +588,8 @@ def main():
 
     sel = path.topk.cpu().numpy()
     key_bytes = 68.0 if args.index_cache == "mxfp4" else 128.0
-    work = algorithmic_work(inp, sel, key_bytes, per_head=args.per_head)
+    work = algorithmic_work(inp, sel, key_bytes, per_head=args.per_head,
+                            kv_page_bytes=17408.0 if args.kv_cache == "mxfp4" else 32768.0)
     attn_us = float(mean_us[names.index("sparse_attn")])
     attn_tflops = work["attn_flops"] / (attn_us * 1e-6) / 1e12
     attn_gbs = work["attn_bytes"] / (attn_us * 1e-6) / 1e9
@@ -593,6 +601,7 @@ def main():
               "seqlen_k": list(wl.seqlen_k), "index_heads": wl.index_heads,
               "q_heads": wl.q_heads, "kv_heads": wl.kv_heads, "page": 128, "head_dim": 128,
               "topk": 16, "cache": "cold: a 1 GiB buffer read before every timed call",
+              "kv_cache": args.kv_cache,
               "selection": ("random per KV head (benchmark-script rule)" if attention_only else
                             "per index head" if args.per_head else "index scores, one per query")}
     if not attention_only:
@@ -672,6 +681,9 @@ def main():
     result["work"] = work
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        if args.kv_cache == "mxfp4":             # the oracle reads the pages as E4M3
+            import oracle
+            inp.kv_cache = oracle.mxfp4_kv_as_e4m3(kv_data, kv_scales)
         if attention_only:
             result["cpu_baseline"] = cpu_baseline_attention(inp, sel, args.cpu_seconds)
         else:

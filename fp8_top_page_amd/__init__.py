@@ -18,7 +18,7 @@ __all__ = [
     "msa_sparse_attn_workspace_size", "msa_status_string", "msa_last_error", "msa_abi_version",
     "msa_quantize_e4m3", "msa_insert_index_k", "msa_insert_kv", "msa_index_score_mxfp4",
     "msa_insert_index_k_mxfp4", "msa_index_score_noalloc", "msa_index_score_per_head",
-    "LIB_PATH", "PAGE", "HEAD_DIM", "TOPK",
+    "msa_sparse_attn_prefill_mxfp4", "LIB_PATH", "PAGE", "HEAD_DIM", "TOPK",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
@@ -74,6 +74,11 @@ def lib():
                                               _c_p, _c_p, _c_i32, _c_p, _c_size, _c_i32, _c_f,
                                               _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p, _c_size, _c_p]
         L.msa_sparse_attn_prefill.restype = ctypes.c_int
+        L.msa_sparse_attn_prefill_mxfp4.argtypes = [vp, _c_p, _c_i64, _c_i32, _c_p, _c_p, _c_i32,
+                                                    _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_size,
+                                                    _c_i32, _c_f, _c_p, _c_p, _c_p, _c_p, _c_i64,
+                                                    _c_p, _c_size, _c_p]
+        L.msa_sparse_attn_prefill_mxfp4.restype = ctypes.c_int
         L.msa_quantize_e4m3.argtypes = [_c_p, _c_i32, _c_i64, _c_i32, _c_i64, _c_p, _c_p, _c_i64,
                                         _c_p]
         L.msa_quantize_e4m3.restype = ctypes.c_int
@@ -215,6 +220,20 @@ def msa_sparse_attn_prefill(vl: Varlen, q, num_q_heads, kv_cache, num_pages, num
         out.stride(0), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check(st, "msa_sparse_attn_prefill")
+
+
+def msa_sparse_attn_prefill_mxfp4(vl: Varlen, q, num_q_heads, kv_data, kv_scales, num_pages,
+                                  num_kv_heads, row_ptr, q_indices, n_sel_heads, schedule, topk,
+                                  softmax_scale, q_scale, k_scale, v_scale, out, workspace,
+                                  stream=None):
+    """kv_data: uint8 [pages, Hkv, 128, 128] MXFP4 codes; kv_scales: uint8 [pages, Hkv, 128, 8]."""
+    st = lib().msa_sparse_attn_prefill_mxfp4(
+        vl.ref, _ptr(q), q.stride(0), num_q_heads, _ptr(kv_data), _ptr(kv_scales), num_pages,
+        num_kv_heads, _ptr(row_ptr), _ptr(q_indices), n_sel_heads, _ptr(schedule),
+        schedule.numel(), topk, float(softmax_scale), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+        _ptr(out), out.stride(0), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "msa_sparse_attn_prefill_mxfp4")
 
 
 _DTYPES = {torch.bfloat16: 0, torch.float32: 1}     # MSA_DTYPE_BF16, MSA_DTYPE_F32

@@ -329,15 +329,18 @@ size_t msa_sparse_attn_workspace_size(const msa_varlen_t* vl, int32_t num_q_head
   return attn_workspace_bytes(vl, num_q_heads, num_kv_heads, n_sel_heads, topk);
 }
 
-msa_status_t msa_sparse_attn_prefill(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
-                                     int32_t num_q_heads, const uint8_t* kv_cache,
-                                     int32_t num_pages, int32_t num_kv_heads,
-                                     const int32_t* row_ptr, const int32_t* q_indices,
-                                     int32_t n_sel_heads, const void* schedule,
-                                     size_t schedule_bytes, int32_t topk, float softmax_scale,
-                                     const float* q_scale, const float* k_scale,
-                                     const float* v_scale, uint16_t* out, int64_t out_stride,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+// Both cache formats: kv_scales == nullptr reads E4M3 K|V rows, else MXFP4 codes
+// with their block scales (the same checks, one more pointer).
+msa_status_t sparse_attn_impl(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
+                              int32_t num_q_heads, const uint8_t* kv_cache,
+                              const uint8_t* kv_scales, int32_t num_pages, int32_t num_kv_heads,
+                              const int32_t* row_ptr, const int32_t* q_indices,
+                              int32_t n_sel_heads, const void* schedule, size_t schedule_bytes,
+                              int32_t topk, float softmax_scale, const float* q_scale,
+                              const float* k_scale, const float* v_scale, uint16_t* out,
+                              int64_t out_stride, void* workspace, size_t workspace_bytes,
+                              void* stream, const char* name) {
   msa_status_t st = check_varlen(vl);
   if (st != MSA_OK) return st;
   const int Hq = num_q_heads, Hkv = num_kv_heads;
@@ -369,14 +372,48 @@ msa_status_t msa_sparse_attn_prefill(const msa_varlen_t* vl, const uint8_t* q, i
             "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   MSA_CHECK(Hkv <= 65535 && L.max_items < (int64_t)INT32_MAX, MSA_ERR_UNSUPPORTED,
             "batch or head count too large");
+  MSA_CHECK((int64_t)vl->total_q * topk * Hq < (int64_t)INT32_MAX, MSA_ERR_UNSUPPORTED,
+            "total_q * topk * num_q_heads must be < 2^31 (split rows are indexed in 32 bits)");
   st = check_device();
   if (st != MSA_OK) return st;
   AttnArgs a{*vl, q, q_stride, Hq, Hkv, n_sel_heads, kv_cache, num_pages, row_ptr, q_indices,
              reinterpret_cast<const uint8_t*>(schedule), L, softmax_scale, q_scale, k_scale,
-             v_scale, out, out_stride, workspace};
+             v_scale, out, out_stride, workspace, kv_scales};
   hipError_t e = launch_sparse_attn(a, reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "msa_sparse_attn_prefill");
+  if (e != hipSuccess) return hip_fail(e, name);
   return MSA_OK;
+}
+}  // namespace
+
+msa_status_t msa_sparse_attn_prefill(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
+                                     int32_t num_q_heads, const uint8_t* kv_cache,
+                                     int32_t num_pages, int32_t num_kv_heads,
+                                     const int32_t* row_ptr, const int32_t* q_indices,
+                                     int32_t n_sel_heads, const void* schedule,
+                                     size_t schedule_bytes, int32_t topk, float softmax_scale,
+                                     const float* q_scale, const float* k_scale,
+                                     const float* v_scale, uint16_t* out, int64_t out_stride,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return sparse_attn_impl(vl, q, q_stride, num_q_heads, kv_cache, nullptr, num_pages, num_kv_heads,
+                          row_ptr, q_indices, n_sel_heads, schedule, schedule_bytes, topk,
+                          softmax_scale, q_scale, k_scale, v_scale, out, out_stride, workspace,
+                          workspace_bytes, stream, "msa_sparse_attn_prefill");
+}
+
+msa_status_t msa_sparse_attn_prefill_mxfp4(
+    const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride, int32_t num_q_heads,
+    const uint8_t* kv_data, const uint8_t* kv_scales, int32_t num_pages, int32_t num_kv_heads,
+    const int32_t* row_ptr, const int32_t* q_indices, int32_t n_sel_heads, const void* schedule,
+    size_t schedule_bytes, int32_t topk, float softmax_scale, const float* q_scale,
+    const float* k_scale, const float* v_scale, uint16_t* out, int64_t out_stride,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  if (vl && vl->total_q > 0)
+    MSA_CHECK(kv_scales && aligned(kv_scales, 8), MSA_ERR_INVALID_ARGUMENT,
+              "kv_scales must be non-NULL and 8-byte aligned");
+  return sparse_attn_impl(vl, q, q_stride, num_q_heads, kv_data, kv_scales, num_pages,
+                          num_kv_heads, row_ptr, q_indices, n_sel_heads, schedule, schedule_bytes,
+                          topk, softmax_scale, q_scale, k_scale, v_scale, out, out_stride,
+                          workspace, workspace_bytes, stream, "msa_sparse_attn_prefill_mxfp4");
 }
 
 

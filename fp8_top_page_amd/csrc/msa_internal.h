@@ -108,7 +108,8 @@ struct AttnArgs {
   const uint8_t* q;
   int64_t q_stride;
   int Hq, Hkv, n_sel;
-  const uint8_t* kv;
+  const uint8_t* kv;           // E4M3 K|V rows [num_pages, Hkv, 128, 256], or MXFP4 codes
+                               // [num_pages, Hkv, 128, 128] when kv_scales is set
   int32_t num_pages;
   const int32_t* row_ptr;
   const int32_t* q_indices;
@@ -121,6 +122,7 @@ struct AttnArgs {
   uint16_t* out;
   int64_t out_stride;
   void* workspace;
+  const uint8_t* kv_scales;    // MXFP4 E8M0 block scales [num_pages, Hkv, 128, 8], or nullptr
 };
 size_t attn_workspace_bytes(const msa_varlen_t* vl, int Hq, int Hkv, int n_sel, int topk);
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream);

@@ -26,8 +26,13 @@
 //
 // Each (query, q-head, page) split writes its unnormalised output row as
 // 12-bit floats (d permuted so that every lane stores 48 contiguous bytes) and the pair
-// (running max m in the log2 domain, probability sum l); the combine merges a
-// query's (at most 16) splits in slot order.
+// (running max m in the log2 domain, probability sum l).  Split rows are laid
+// out query-major, (query, selection head, slot of the page in the query's
+// selection, head), so the combine reads a query's (at most 16) splits as one
+// contiguous run; a small pass before the partials maps every CSR position to
+// its (query, selection head, slot) entry.
+#include <type_traits>
+
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -49,18 +54,21 @@ struct AttnK {
   const uint8_t* q;
   int64_t q_stride;
   int32_t G, n_sel, HP, GY;        // GY: KV heads per schedule item (Hkv if shared selection)
-  const uint8_t* kv;
+  uint32_t g_magic;                // ceil(2^20 / G): row / G == (row * g_magic) >> 20 for rows < 64 G
+  const uint8_t* kv;               // E4M3 K|V rows, or MXFP4 K|V codes (kv_scales != nullptr)
+  const uint8_t* kv_scales;        // MXFP4 E8M0 block scales [num_pages, Hkv, 128, 8], or nullptr
   int32_t num_pages, Hkv;
   const int32_t* q_indices;
+  const int32_t* q_slot;           // [nnz]: (query, selection head, slot) entry of each CSR position
   const int4* items;
   const int32_t* perm;             // order in which the items are taken, or nullptr: list order
   const int32_t* n_items;
   float logit_scale_log2;          // softmax_scale * log2(e)
   const float* q_scale;
   const float* k_scale;
-  uint8_t* part_o;                 // [nnz * HP + 1, 192 B]: 12-bit floats, unnormalised, d permuted
-  float2* part_ml;                 // [nnz, HP] (max in log2 units, probability sum)
-  int64_t trash;                   // partial row written by rows past an item's end
+  uint8_t* part_o;                 // [entries * HP + 1, 192 B]: 12-bit floats, unnormalised, d permuted
+  float2* part_ml;                 // [entries * HP + 1] (max in log2 units, probability sum)
+  int32_t trash;                   // partial row written by rows past an item's end
 };
 
 __device__ __forceinline__ uint32_t byte_of(uint32_t w, int k) { return (w >> (8 * k)) & 0xFFu; }
@@ -72,46 +80,64 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
-// Compact partials ("f12"): a float rounded to fp16 (round to nearest even), then
-// to 12 bits by rounding off the 4 low mantissa bits (nearest, ties to even):
-// sign, 5 exponent and 6 mantissa bits, relative error <= 2^-7.  Unnormalised
-// split outputs stay below 128 * 448 = 57344, inside fp16's range.  Eight
-// values pack into three dwords.
+// Compact partials ("f12"): a float rounded to fp16, then to the fp16's top 12
+// bits (sign, 5 exponent and 6 mantissa bits) by adding half of the dropped
+// range before dropping it: round to nearest, ties away from zero, relative
+// error <= 2^-7.  Unnormalised split outputs stay below 128 * 448 = 57344,
+// inside fp16's range, so the rounding never carries out of a half.  Eight
+// values v0..v7 pack into three dwords: the high bytes of v0..v3, the high bytes
+// of v4..v7, and the eight low nibbles (fp16 bits 7:4), placed so that packing
+// and unpacking are byte permutes and masks.
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack2_f12(float a, float b) {   // two 12-bit fields, one per half
-  uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
-  h += 0x00070007u + ((h >> 4) & 0x00010001u);   // finite halves: no carry between them
-  return (h >> 4) & 0x0FFF0FFFu;
+__device__ __forceinline__ uint32_t round_f16x2(float a, float b) {
+  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+  return h + 0x00080008u;
 }
 __device__ __forceinline__ uint3 pack8_f12(float v0, float v1, float v2, float v3, float v4,
                                            float v5, float v6, float v7) {
-  const uint32_t h0 = pack2_f12(v0, v1), h1 = pack2_f12(v2, v3);
-  const uint32_t h2 = pack2_f12(v4, v5), h3 = pack2_f12(v6, v7);
-  const uint32_t p0 = (h0 & 0xFFFu) | ((h0 >> 16) << 12);   // 24 bits each
-  const uint32_t p1 = (h1 & 0xFFFu) | ((h1 >> 16) << 12);
-  const uint32_t p2 = (h2 & 0xFFFu) | ((h2 >> 16) << 12);
-  const uint32_t p3 = (h3 & 0xFFFu) | ((h3 >> 16) << 12);
-  return make_uint3(p0 | (p1 << 24), (p1 >> 8) | (p2 << 16), (p2 >> 16) | (p3 << 8));
+  const uint32_t h01 = round_f16x2(v0, v1), h23 = round_f16x2(v2, v3);
+  const uint32_t h45 = round_f16x2(v4, v5), h67 = round_f16x2(v6, v7);
+  // v_perm_b32 selector bytes: 0-3 pick bytes of the second operand, 4-7 of the first
+  const uint32_t hi0 = __builtin_amdgcn_perm(h23, h01, 0x07050301u);   // high bytes v0 v1 v2 v3
+  const uint32_t hi1 = __builtin_amdgcn_perm(h67, h45, 0x07050301u);   // high bytes v4 v5 v6 v7
+  // byte 0: v0 nibble | v2 nibble, byte 2: v1 | v3 (and v4..v7 likewise)
+  const uint32_t n0 = (h01 & 0x00F000F0u) | ((h23 >> 4) & 0x000F000Fu);
+  const uint32_t n1 = (h45 & 0x00F000F0u) | ((h67 >> 4) & 0x000F000Fu);
+  return make_uint3(hi0, hi1, __builtin_amdgcn_perm(n1, n0, 0x06040200u));
 }
-__device__ __forceinline__ float f12_to_f32(uint32_t x) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(x << 4));
+__device__ __forceinline__ float2 f16x2_to_f32(uint32_t p) {
+  const f32x2 f = __builtin_convertvector(__builtin_bit_cast(f16x2, p), f32x2);
+  return make_float2(f[0], f[1]);
 }
 __device__ __forceinline__ void unpack8_f12(uint3 w, float (&v)[8]) {
-  const uint32_t p0 = w.x & 0xFFFFFFu;
-  const uint32_t p1 = (w.x >> 24) | ((w.y & 0xFFFFu) << 8);
-  const uint32_t p2 = (w.y >> 16) | ((w.z & 0xFFu) << 16);
-  const uint32_t p3 = w.z >> 8;
-  v[0] = f12_to_f32(p0 & 0xFFFu); v[1] = f12_to_f32(p0 >> 12);
-  v[2] = f12_to_f32(p1 & 0xFFFu); v[3] = f12_to_f32(p1 >> 12);
-  v[4] = f12_to_f32(p2 & 0xFFFu); v[5] = f12_to_f32(p2 >> 12);
-  v[6] = f12_to_f32(p3 & 0xFFFu); v[7] = f12_to_f32(p3 >> 12);
+  const uint32_t n = w.z, n4 = w.z << 4;      // n4: the low nibbles moved up
+  const float2 a = f16x2_to_f32(__builtin_amdgcn_perm(w.x, n, 0x05010400u) & 0xFFF0FFF0u);
+  const float2 b = f16x2_to_f32(__builtin_amdgcn_perm(w.x, n4, 0x07010600u) & 0xFFF0FFF0u);
+  const float2 c = f16x2_to_f32(__builtin_amdgcn_perm(w.y, n, 0x05030402u) & 0xFFF0FFF0u);
+  const float2 d = f16x2_to_f32(__builtin_amdgcn_perm(w.y, n4, 0x07030602u) & 0xFFF0FFF0u);
+  v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
+  v[4] = c.x; v[5] = c.y; v[6] = d.x; v[7] = d.y;
 }
 constexpr int kRowBytes = kDim * 3 / 2;   // 192 bytes per partial row
+
+// IEEE 754-2019 maximum (v_maximum_f32 / v_maximum3_f32): NaN-propagating, so
+// unlike fmaxf it needs no quieting moves on operands the compiler cannot prove
+// canonical (MFMA results, lane swaps).  A NaN score (a NaN code in q or K)
+// spoils its row with either max.
+__device__ __forceinline__ float fmax3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+__device__ __forceinline__ float max4_groups(float x) {   // max over lanes l, l^16, l^32, l^48
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 // One work item as the kernel uses it (wave-uniform values).
 struct Work {
   int start, count, g, lim_base, n_valid;
-  const uint8_t* page;             // K|V rows of (physical page, KV head g)
+  int64_t kvp;                     // physical page * Hkv + KV head g: the page's K|V rows
 };
 
 __device__ __forceinline__ Work decode_work(const AttnK& a, int64_t w, int4 x, int4 y) {
@@ -122,7 +148,7 @@ __device__ __forceinline__ Work decode_work(const AttnK& a, int64_t w, int4 x, i
   int phys = __builtin_amdgcn_readfirstlane(x.z);
   r.g = a.n_sel == 1 ? (int)(w - item * a.GY) : __builtin_amdgcn_readfirstlane(x.w);
   phys = (phys < 0 || phys >= a.num_pages) ? 0 : phys;
-  r.page = a.kv + ((int64_t)phys * a.Hkv + r.g) * (kPage * 2 * kDim);
+  r.kvp = (int64_t)phys * a.Hkv + r.g;
   r.lim_base = __builtin_amdgcn_readfirstlane(y.x);
   r.n_valid = min(__builtin_amdgcn_readfirstlane(y.y), kPage);
   return r;
@@ -134,18 +160,112 @@ struct PageRegs {
   v4u k[4];
   v4u v[4];
   int qi;                          // q_indices[start + t] for t < count
+  int sl;                          // q_slot[start + t]
 };
 
 __device__ __forceinline__ void fetch_page(PageRegs& r, const AttnK& a, const Work& w, int tid) {
+  const uint8_t* page = a.kv + w.kvp * (kPage * 2 * kDim);
   const int t = tid >> 1, h = tid & 1;
-  const v4u* ks = reinterpret_cast<const v4u*>(w.page + t * (2 * kDim) + h * 64);
+  const v4u* ks = reinterpret_cast<const v4u*>(page + t * (2 * kDim) + h * 64);
 #pragma unroll
   for (int i = 0; i < 4; ++i) r.k[i] = ks[i];
   const int m = tid >> 3, dc = tid & 7;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    r.v[i] = *reinterpret_cast<const v4u*>(w.page + (4 * m + i) * (2 * kDim) + kDim + 16 * dc);
+    r.v[i] = *reinterpret_cast<const v4u*>(page + (4 * m + i) * (2 * kDim) + kDim + 16 * dc);
   r.qi = a.q_indices[w.start + min(tid, w.count - 1)];
+  r.sl = a.q_slot[w.start + min(tid, w.count - 1)];
+}
+
+// An MXFP4 page in flight (the E4M3-staged reading of a 4-bit K|V page: every
+// code times its block scale becomes an E4M3 value before the FP8 products).
+// Rows are 128 code bytes (K elements in bytes 0..63, V in 64..127, element 2i
+// in the low nibble of byte i) with 8 E8M0 scales (K blocks 0..3, V 4..7).
+// Thread t holds the same K and V elements as PageRegs: K elements
+// 64 (t%2) .. +63 of token t/2 (blocks 2 (t%2) and 2 (t%2) + 1), and V elements
+// 16 (t%8) .. +15 (block (t%8)/2) of tokens 4 (t/8) .. +3.
+struct PageRegs4 {
+  v4u k[2];
+  uint32_t ks;                     // the two K block scales, bytes 0 and 1
+  uint2 v[4];
+  uint32_t vs;                     // each token's V block scale, one byte per token
+  int qi, sl;
+};
+
+__device__ __forceinline__ void fetch_page(PageRegs4& r, const AttnK& a, const Work& w, int tid) {
+  const uint8_t* page = a.kv + w.kvp * (kPage * kDim);
+  const uint8_t* sc = a.kv_scales + w.kvp * (kPage * 8);
+  const int t = tid >> 1, h = tid & 1;
+  const v4u* ks = reinterpret_cast<const v4u*>(page + t * kDim + h * 32);
+  r.k[0] = ks[0];
+  r.k[1] = ks[1];
+  r.ks = *reinterpret_cast<const uint16_t*>(sc + t * 8 + 2 * h);
+  const int m = tid >> 3, dc = tid & 7;
+  uint32_t vs = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r.v[i] = *reinterpret_cast<const uint2*>(page + (4 * m + i) * kDim + 64 + 8 * dc);
+    vs |= (uint32_t)sc[(4 * m + i) * 8 + 4 + (dc >> 1)] << (8 * i);
+  }
+  r.vs = vs;
+  r.qi = a.q_indices[w.start + min(tid, w.count - 1)];
+  r.sl = a.q_slot[w.start + min(tid, w.count - 1)];
+}
+
+// E4M3 code of (1 + m3/8) * 2^(E - 7), m3 in {0, 4}: nearest, ties to even,
+// saturating at 448.  Below the normal range the value is (8 + m3) * 2^(E - 1)
+// units of the subnormal step 2^-9.
+__device__ uint32_t e4m3_code(int E, int m3) {
+  if (E >= 16) return 0x7Eu;
+  if (E >= 1) return (uint32_t)((E << 3) | m3);        // E = 15 with m3 <= 4 stays <= 384
+  const int sh = 1 - E;
+  if (sh > 4) return 0u;                               // below half a step
+  const int num = 8 + m3, q = num >> sh, rem = num & ((1 << sh) - 1), half = 1 << (sh - 1);
+  return (uint32_t)(q + ((rem > half || (rem == half && (q & 1))) ? 1 : 0));
+}
+
+// The E4M3 codes of the E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 times
+// 2^(s - 127), one byte each (magnitude k in byte k); the NaN scale 0xFF gives
+// NaN codes.
+__device__ uint2 staged_magnitudes(int s) {
+  if (s == 0xFF) return make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+  const int e = s - 127;
+  const uint32_t b1 = e4m3_code(e + 6, 0);                       // 0.5 = 2^-1
+  const uint32_t b2 = e4m3_code(e + 7, 0), b3 = e4m3_code(e + 7, 4);   // 1, 1.5
+  const uint32_t b4 = e4m3_code(e + 8, 0), b5 = e4m3_code(e + 8, 4);   // 2, 3
+  const uint32_t b6 = e4m3_code(e + 9, 0), b7 = e4m3_code(e + 9, 4);   // 4, 6
+  return make_uint2((b1 << 8) | (b2 << 16) | (b3 << 24), b4 | (b5 << 8) | (b6 << 16) | (b7 << 24));
+}
+
+// Eight codes (one dword, element 2k in the low nibble of byte k) to eight E4M3
+// bytes through the block's magnitude table: byte permutes look the magnitudes
+// up, the sign bits are ORed in, and the even and odd elements are interleaved.
+__device__ __forceinline__ uint2 fp4x8_to_e4m3(uint32_t w, uint2 tab) {
+  const uint32_t ev = __builtin_amdgcn_perm(tab.y, tab.x, w & 0x07070707u) | ((w & 0x08080808u) << 4);
+  const uint32_t od = __builtin_amdgcn_perm(tab.y, tab.x, (w >> 4) & 0x07070707u) | (w & 0x80808080u);
+  return make_uint2(__builtin_amdgcn_perm(od, ev, 0x05010400u), __builtin_amdgcn_perm(od, ev, 0x07030602u));
+}
+
+__device__ __forceinline__ PageRegs to_e4m3(const PageRegs4& r, const uint2* s_tab) {
+  PageRegs o;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {                        // K blocks: 16 code bytes -> 32 E4M3 bytes
+    const uint2 tab = s_tab[(r.ks >> (8 * b)) & 0xFFu];
+    const v4u c = r.k[b];
+    const uint2 x0 = fp4x8_to_e4m3(c[0], tab), x1 = fp4x8_to_e4m3(c[1], tab);
+    const uint2 x2 = fp4x8_to_e4m3(c[2], tab), x3 = fp4x8_to_e4m3(c[3], tab);
+    o.k[2 * b] = v4u{x0.x, x0.y, x1.x, x1.y};
+    o.k[2 * b + 1] = v4u{x2.x, x2.y, x3.x, x3.y};
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {                        // V: 8 code bytes of token i -> 16 E4M3 bytes
+    const uint2 tab = s_tab[(r.vs >> (8 * i)) & 0xFFu];
+    const uint2 x0 = fp4x8_to_e4m3(r.v[i].x, tab), x1 = fp4x8_to_e4m3(r.v[i].y, tab);
+    o.v[i] = v4u{x0.x, x0.y, x1.x, x1.y};
+  }
+  o.qi = r.qi;
+  o.sl = r.sl;
+  return o;
 }
 
 __device__ __forceinline__ void stage_page(const PageRegs& r, const Work& w, uint8_t* k_lds,
@@ -180,7 +300,10 @@ __device__ __forceinline__ void stage_page(const PageRegs& r, const Work& w, uin
       }
     }
   }
-  if (tid < kAttnQCMax) s_qi[tid] = r.qi;
+  if (tid < kAttnQCMax) {
+    s_qi[tid] = r.qi;
+    s_qi[kAttnQCMax + tid] = r.sl;   // the entries' split slots follow their queries
+  }
 }
 
 // The rows of NT consecutive 16-row tiles on one wave: lane (col, grp) of tile
@@ -192,7 +315,7 @@ template <int NT>
 struct RowSet {
   v8i qb[NT];
   int lim[NT];
-  int64_t pidx[NT];
+  int32_t pidx[NT];
 };
 
 template <int NT>
@@ -204,14 +327,15 @@ __device__ __forceinline__ RowSet<NT> load_rows(const AttnK& a, const Work& w, i
   for (int u = 0; u < NT; ++u) {
     const int rid = (tile0 + u) * 16 + col;
     const bool valid = rid < n_rows;
-    const int q0 = rid / a.G;                 // branch-free: rows past the end are
-    const int ql = valid ? q0 : 0;            // clamped after the division
+    // branch-free: rows past the end are clamped after the division (exact for
+    // rid < n_rows <= 64 G; past the end the product may wrap, unused)
+    const int q0 = (int)(__umul24((uint32_t)rid, a.g_magic) >> 20);
+    const int ql = valid ? q0 : 0;
     const int h = valid ? rid - q0 * a.G : 0;
     const int hq = w.g * a.G + h;
     const int qi = s_qi[ql];
     r.lim[u] = valid ? qi + w.lim_base : kPage;
-    const int64_t p = (int64_t)(w.start + ql) * a.HP + (a.n_sel == 1 ? hq : h);
-    r.pidx[u] = valid ? p : a.trash;
+    r.pidx[u] = valid ? s_qi[kAttnQCMax + ql] * a.HP + (a.n_sel == 1 ? hq : h) : a.trash;
     r.qb[u] = load_frag_global(a.q + (int64_t)qi * a.q_stride + hq * kDim + grp * 32);
   }
   return r;
@@ -260,11 +384,15 @@ __device__ __forceinline__ void compute_set(const AttnK& a, const RowSet<NT>& r,
           s[u][T][i] = (t > r.lim[u]) ? -INFINITY : s[u][T][i];
         }
     }
+    // IEEE maximum (v_maximum3_f32): unlike fmaxf it needs no quieting of the
+    // MFMA results first; masked lanes are -inf, never NaN
     float mx = -INFINITY;
 #pragma unroll
-    for (int T = 0; T < 8; ++T)
-      mx = fmaxf(fmaxf(mx, fmaxf(s[u][T][0], s[u][T][1])), fmaxf(s[u][T][2], s[u][T][3]));
-    mx = max_across_groups(mx);
+    for (int T = 0; T < 8; ++T) {
+      mx = fmax3(mx, s[u][T][0], s[u][T][1]);
+      mx = fmax3(mx, s[u][T][2], s[u][T][3]);
+    }
+    mx = max4_groups(mx);
     // scales are positive, so the max of the raw products gives the max logit
     mz[u] = (mx == -INFINITY) ? 0.f : mx * zscale;
 #pragma unroll
@@ -298,7 +426,8 @@ __device__ __forceinline__ void compute_set(const AttnK& a, const RowSet<NT>& r,
     }
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-      uint3* dst = reinterpret_cast<uint3*>(a.part_o + r.pidx[u] * kRowBytes + grp * 48 + half * 24);
+      uint3* dst = reinterpret_cast<uint3*>(a.part_o + (int64_t)r.pidx[u] * kRowBytes + grp * 48 +
+                                            half * 24);
       dst[0] = pack8_f12(o[u][0][0], o[u][0][1], o[u][0][2], o[u][0][3], o[u][1][0], o[u][1][1],
                          o[u][1][2], o[u][1][3]);
       dst[1] = pack8_f12(o[u][2][0], o[u][2][1], o[u][2][2], o[u][2][3], o[u][3][0], o[u][3][1],
@@ -363,18 +492,24 @@ __device__ __forceinline__ void run_item_narrow(const AttnK& a, const Work& w,
   }
 }
 
-template <bool kWide>
+// kFp4: MXFP4 K|V pages, turned into E4M3 while they are staged in LDS.
+template <bool kWide, bool kFp4>
 __global__ __launch_bounds__(kThreads, kWide ? kBlocksWide : kBlocksNarrow) void attn_partial_kernel(
     AttnK a) {
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[kPage * kRowB];
   __shared__ __attribute__((aligned(16))) uint8_t vt_lds[kDim * kRowB];
-  __shared__ int s_qi[kAttnQCMax];
+  __shared__ int s_qi[2 * kAttnQCMax];     // the item's queries, then their split slots
+  __shared__ uint2 s_tab[kFp4 ? 256 : 1];  // E4M3 codes of the E2M1 magnitudes, per E8M0 scale
 
   const int n_items = *a.n_items;
   const int64_t n_work = (int64_t)n_items * a.GY;
   int64_t w = blockIdx.x;
   if (w >= n_work) return;
   const int tid = threadIdx.x, lane = tid & 63;
+  if constexpr (kFp4) {
+    static_assert(kThreads == 256, "one magnitude table entry per thread");
+    s_tab[tid] = staged_magnitudes(tid);   // read after the first barrier of the item loop
+  }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: loops below do not diverge
   const float zscale = a.logit_scale_log2 * (a.q_scale ? *a.q_scale : 1.f) *
                        (a.k_scale ? *a.k_scale : 1.f);
@@ -396,7 +531,7 @@ __global__ __launch_bounds__(kThreads, kWide ? kBlocksWide : kBlocksNarrow) void
   // a page fetch.  (The narrow kernel keeps the plain sequence: the ordered one
   // compiled to a slower schedule there.)
   Work cur;
-  PageRegs pr;
+  typename std::conditional<kFp4, PageRegs4, PageRegs>::type pr;
   int4 mx, my;
   int64_t i_nn = 0;
   if constexpr (kWide) {
@@ -415,7 +550,10 @@ __global__ __launch_bounds__(kThreads, kWide ? kBlocksWide : kBlocksNarrow) void
 
   for (;;) {
     __syncthreads();                         // the previous item is done with LDS
-    stage_page(pr, cur, k_lds, vt_lds, s_qi, tid);
+    if constexpr (kFp4)
+      stage_page(to_e4m3(pr, s_tab), cur, k_lds, vt_lds, s_qi, tid);
+    else
+      stage_page(pr, cur, k_lds, vt_lds, s_qi, tid);
     __syncthreads();
     const int64_t wn = w + gridDim.x;
     const bool has_next = wn < n_work;
@@ -446,15 +584,56 @@ __global__ __launch_bounds__(kThreads, kWide ? kBlocksWide : kBlocksNarrow) void
   }
 }
 
-struct CombineK {
-  int64_t total_q;
-  int32_t Hq, G, n_sel, HP;
+// Split slots of every CSR position, one thread per (query, selection head,
+// slot): the position of (query i, slot s) is the first position of i's bitmap
+// word in the slot's row plus the row's set bits below i in that word.  Writes
+// q_slot[position] = (i * n_sel + head) * 16 + s for the first listing of each
+// selected page, and per (query, selection head) the 16-bit mask of those slots,
+// which the combine merges (the 16 slots of one (query, head) are 16
+// consecutive lanes, so the mask is a slice of one ballot).
+struct SlotK {
+  int64_t n;                      // total_q * n_sel * 16
+  int32_t n_sel;
   const int32_t* cu_q;
   int32_t batch;
   const int32_t* rowsel;          // [total_q, n_sel, 16] CSR row of each selected page, or -1
   const int32_t* wbase;           // [rows, words] CSR position of each bitmap word's first entry
   const uint32_t* bitmap;         // [rows, words] the rows' query-slot bitmaps
   int64_t words;
+  int64_t max_pos;                // q_slot entries (positions at or past it are skipped)
+  int32_t* q_slot;
+  uint32_t* mask;                 // [total_q, n_sel]
+};
+
+__global__ __launch_bounds__(256) void attn_slot_kernel(SlotK a) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const bool in = e < a.n;
+  const int s = (int)(e & (kTopK - 1));
+  bool ok = false;
+  if (in) {
+    const int32_t* rs = a.rowsel + (e - s);
+    const int r = rs[s];
+    ok = r >= 0;
+    for (int u = 0; u < s; ++u) ok = ok && rs[u] != r;   // a page listed twice: its first slot
+    if (ok) {
+      const int64_t i = e / ((int64_t)a.n_sel * kTopK);
+      const int b = find_request(a.cu_q, a.batch, i);
+      const int local = (int)(i - a.cu_q[b]);
+      const int64_t wi = (int64_t)r * a.words + (local >> 5);
+      const int64_t p = (int64_t)a.wbase[wi] + __popc(a.bitmap[wi] & ((1u << (local & 31)) - 1u));
+      ok = p >= 0 && p < a.max_pos;
+      if (ok) a.q_slot[p] = (int32_t)e;
+    }
+  }
+  const uint64_t bal = __builtin_amdgcn_ballot_w64(ok);
+  if (in && s == 0) a.mask[e / kTopK] = (uint32_t)(bal >> (lane & ~(kTopK - 1))) & 0xFFFFu;
+}
+
+struct CombineK {
+  int64_t total_q;
+  int32_t Hq, G, n_sel, HP;
+  const uint32_t* mask;           // [total_q, n_sel] slots holding a split
   const uint8_t* part_o;
   const float2* part_ml;
   const float* v_scale;
@@ -462,55 +641,39 @@ struct CombineK {
   int64_t out_stride;
 };
 
-// One block per query, Hq * 16 threads: thread t owns q-head t / 16 and the 16
-// bytes at 8 * (t % 16) of each split row (all heads of one (query, page) pair
-// are contiguous), which hold d = 32 (c % 4) + 4 (c / 4) + {0..3} and those + 16
-// for c = t % 16.
+// One block per query, Hq * 16 threads: thread t owns q-head t / 16 and the 12
+// bytes at 12 * (t % 16) of each split row, i.e. eight of the row's values (the
+// split rows of one (query, selection head) are contiguous, slot-major, with the
+// heads of each slot together).
 __global__ __launch_bounds__(1024) void attn_combine_kernel(CombineK a) {
-  __shared__ int32_t s_pos[kMaxKvHeads * kTopK];
   const int64_t i = blockIdx.x;
   const int t = threadIdx.x;
   const int hq = t >> 4, c = t & 15;
   const int sel = a.n_sel == 1 ? 0 : hq / a.G;
   const int hp = a.n_sel == 1 ? hq : hq % a.G;
-  // CSR position of each (selection head, slot): the first position of the
-  // query's bitmap word in the row plus the row's set bits below the query
-  if (t < a.n_sel * kTopK) {
-    const int b = find_request(a.cu_q, a.batch, i);
-    const int local = (int)(i - a.cu_q[b]);
-    const int32_t* rs = a.rowsel + i * a.n_sel * kTopK;
-    int r = rs[t];
-    // a page listed twice in one selection is one CSR entry: merged once
-    for (int u = t - t % kTopK; u < t; ++u) r = rs[u] == r ? -1 : r;
-    int p = -1;
-    if (r >= 0) {
-      const int64_t wi = (int64_t)r * a.words + (local >> 5);
-      p = a.wbase[wi] + __popc(a.bitmap[wi] & ((1u << (local & 31)) - 1u));
-    }
-    s_pos[t] = p;
-  }
-  __syncthreads();
-  int32_t pi[kTopK];
-#pragma unroll
-  for (int s = 0; s < kTopK; ++s) pi[s] = s_pos[sel * kTopK + s];
-  // all split rows are loaded together (a missing split reads row 0 with weight 0)
-  float2 ml[kTopK];
-  uint3 v[kTopK];
-#pragma unroll
-  for (int s = 0; s < kTopK; ++s) {
-    const int64_t r = (int64_t)max(pi[s], 0) * a.HP + hp;
-    ml[s] = a.part_ml[r];
-    v[s] = *reinterpret_cast<const uint3*>(a.part_o + r * kRowBytes + 12 * c);
-  }
-  float M = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < kTopK; ++s) M = pi[s] >= 0 ? fmaxf(M, ml[s].x) : M;
+  const int64_t e0 = (i * a.n_sel + sel) * kTopK;
+  const uint32_t m = a.mask[i * a.n_sel + sel];
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (M != -INFINITY) {
+  if (m != 0u) {
+    // all split rows are loaded together; a slot without a split reads the
+    // first slot's (finite) row and gets weight 0
+    const int first = __builtin_ctz(m);
+    float2 ml[kTopK];
+    uint3 v[kTopK];
+#pragma unroll
+    for (int s = 0; s < kTopK; ++s) {
+      const int64_t r = (e0 + (((m >> s) & 1u) ? s : first)) * a.HP + hp;
+      ml[s] = a.part_ml[r];
+      v[s] = *reinterpret_cast<const uint3*>(a.part_o + r * kRowBytes + 12 * c);
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kTopK; ++s)
+      M = ((m >> s) & 1u) ? __builtin_elementwise_maximum(M, ml[s].x) : M;
     float L = 0.f;
 #pragma unroll
     for (int s = 0; s < kTopK; ++s) {
-      const float wgt = pi[s] >= 0 ? __builtin_amdgcn_exp2f(ml[s].x - M) : 0.f;
+      const float wgt = ((m >> s) & 1u) ? __builtin_amdgcn_exp2f(ml[s].x - M) : 0.f;
       float x[8];
       unpack8_f12(v[s], x);
 #pragma unroll
@@ -540,23 +703,56 @@ int device_cu_count() {
   return n;
 }
 
-// Partial rows: one per (CSR entry, head of its selection), plus one trash row.
+// Split rows: one per ((query, selection head, slot), head of that selection),
+// plus one trash row.
 static int64_t partial_rows(const msa_varlen_t* vl, int Hq, int n_sel, int topk) {
   return (int64_t)n_sel * vl->total_q * topk * (Hq / n_sel) + 1;
 }
 
+struct AttnWs {
+  size_t o, ml, slot, mask, total;
+};
+static AttnWs attn_ws(const msa_varlen_t* vl, int Hq, int n_sel, int topk) {
+  const int64_t rows = partial_rows(vl, Hq, n_sel, topk);
+  const int64_t entries = (int64_t)n_sel * vl->total_q * topk;
+  AttnWs w;
+  size_t off = 0;
+  w.o = off;    off += align_up((size_t)(rows * kRowBytes), 256);
+  w.ml = off;   off += align_up((size_t)(rows * sizeof(float2)), 256);
+  w.slot = off; off += align_up((size_t)(std::max<int64_t>(entries, 1) * sizeof(int32_t)), 256);
+  w.mask = off; off += align_up((size_t)(std::max<int64_t>(entries / topk, 1) * sizeof(uint32_t)), 256);
+  w.total = off;
+  return w;
+}
+
 size_t attn_workspace_bytes(const msa_varlen_t* vl, int Hq, int Hkv, int n_sel, int topk) {
   (void)Hkv;
-  const int64_t rows = partial_rows(vl, Hq, n_sel, topk);
-  return align_up((size_t)(rows * kRowBytes), 256) +
-         align_up((size_t)(rows * sizeof(float2)), 256);
+  return attn_ws(vl, Hq, n_sel, topk).total;
 }
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.vl.total_q == 0) return hipSuccess;
   const SchedLayout& L = a.L;
   const int64_t rows = partial_rows(&a.vl, a.Hq, a.n_sel, kTopK);
+  if (rows > (int64_t)INT32_MAX) return hipErrorInvalidValue;   // split rows are indexed in 32 bits
+  const AttnWs ws = attn_ws(&a.vl, a.Hq, a.n_sel, kTopK);
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(a.workspace);
   const int HP = a.Hq / a.n_sel;
+
+  SlotK sk;
+  sk.n = (int64_t)a.vl.total_q * a.n_sel * kTopK;
+  sk.n_sel = a.n_sel;
+  sk.cu_q = a.vl.cu_seqlens_q;
+  sk.batch = a.vl.batch;
+  sk.rowsel = reinterpret_cast<const int32_t*>(a.sched + L.rowsel);
+  sk.wbase = reinterpret_cast<const int32_t*>(a.sched + L.wbase);
+  sk.bitmap = reinterpret_cast<const uint32_t*>(a.sched + L.bitmap);
+  sk.words = L.words_per_row;
+  sk.max_pos = L.inv_len;
+  sk.q_slot = reinterpret_cast<int32_t*>(wsb + ws.slot);
+  sk.mask = reinterpret_cast<uint32_t*>(wsb + ws.mask);
+  hipLaunchKernelGGL(attn_slot_kernel, dim3((unsigned)ceil_div(sk.n, 256)), dim3(256), 0, stream, sk);
+
   AttnK k;
   k.q = a.q;
   k.q_stride = a.q_stride;
@@ -564,20 +760,22 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   k.n_sel = a.n_sel;
   k.HP = HP;
   k.GY = a.n_sel == 1 ? a.Hkv : 1;
+  k.g_magic = (uint32_t)(((1u << 20) + k.G - 1) / k.G);
   k.kv = a.kv;
+  k.kv_scales = a.kv_scales;
   k.num_pages = a.num_pages;
   k.Hkv = a.Hkv;
   k.q_indices = a.q_indices;
+  k.q_slot = sk.q_slot;
   k.items = reinterpret_cast<const int4*>(a.sched + L.items);
   k.perm = L.order_shift > 0 ? reinterpret_cast<const int32_t*>(a.sched + L.perm) : nullptr;
   k.n_items = reinterpret_cast<const int32_t*>(a.sched + L.hdr);
   k.logit_scale_log2 = a.softmax_scale * kLog2e;
   k.q_scale = a.q_scale;
   k.k_scale = a.k_scale;
-  k.part_o = reinterpret_cast<uint8_t*>(a.workspace);
-  k.part_ml = reinterpret_cast<float2*>(reinterpret_cast<uint8_t*>(a.workspace) +
-                                        align_up((size_t)(rows * kRowBytes), 256));
-  k.trash = rows - 1;
+  k.part_o = wsb + ws.o;
+  k.part_ml = reinterpret_cast<float2*>(wsb + ws.ml);
+  k.trash = (int32_t)(rows - 1);
   const int64_t max_work = L.max_items * k.GY;
   if (max_work > 0) {
     // Rows per item from the host bound on entries per CSR row (total_q * topk
@@ -586,10 +784,19 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
     const bool wide = std::min<int64_t>(per_row, L.item_q) * k.G >= 2 * kWaves * 16;
     const int per_cu = wide ? kBlocksWide : kBlocksNarrow;
     const int64_t grid = std::min<int64_t>(max_work, (int64_t)device_cu_count() * per_cu);
-    if (wide)
-      hipLaunchKernelGGL(attn_partial_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, k);
+    const bool fp4 = a.kv_scales != nullptr;
+    if (wide && fp4)
+      hipLaunchKernelGGL((attn_partial_kernel<true, true>), dim3((unsigned)grid), dim3(kThreads), 0,
+                         stream, k);
+    else if (wide)
+      hipLaunchKernelGGL((attn_partial_kernel<true, false>), dim3((unsigned)grid), dim3(kThreads), 0,
+                         stream, k);
+    else if (fp4)
+      hipLaunchKernelGGL((attn_partial_kernel<false, true>), dim3((unsigned)grid), dim3(kThreads), 0,
+                         stream, k);
     else
-      hipLaunchKernelGGL(attn_partial_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, k);
+      hipLaunchKernelGGL((attn_partial_kernel<false, false>), dim3((unsigned)grid), dim3(kThreads), 0,
+                         stream, k);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -599,12 +806,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   c.G = a.Hq / a.Hkv;
   c.n_sel = a.n_sel;
   c.HP = HP;
-  c.cu_q = a.vl.cu_seqlens_q;
-  c.batch = a.vl.batch;
-  c.rowsel = reinterpret_cast<const int32_t*>(a.sched + L.rowsel);
-  c.wbase = reinterpret_cast<const int32_t*>(a.sched + L.wbase);
-  c.bitmap = reinterpret_cast<const uint32_t*>(a.sched + L.bitmap);
-  c.words = L.words_per_row;
+  c.mask = sk.mask;
   c.part_o = k.part_o;
   c.part_ml = k.part_ml;
   c.v_scale = a.v_scale;

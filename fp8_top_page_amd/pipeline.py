@@ -9,7 +9,8 @@ import torch
 
 from . import (PAGE, TOPK, Varlen, msa_build_k2q_csr, msa_index_score, msa_index_score_mxfp4,
                msa_index_score_per_head, msa_index_score_workspace_size, msa_k2q_schedule_size,
-               msa_sparse_attn_prefill, msa_sparse_attn_workspace_size, msa_topk_select)
+               msa_sparse_attn_prefill, msa_sparse_attn_prefill_mxfp4,
+               msa_sparse_attn_workspace_size, msa_topk_select)
 
 
 def _dev(x, device, dtype=None):
@@ -42,6 +43,7 @@ class DeviceBatch:
                          max_seqlen_q=self.max_seqlen_q, max_seqlen_k=self.max_seqlen_k,
                          total_rows=self.total_rows, max_pages=self.max_pages)
         self.k_fp4 = None            # (data, scales) of MXFP4 index keys, if scored from those
+        self.kv_fp4 = None           # (data, scales) of an MXFP4 K|V cache, if attended over that
         self.H = int(index_q.shape[1])
         self.index_q = _dev(np.asarray(index_q).reshape(index_q.shape[0], self.H * 128), device)
         self.k_cache = _dev(index_k_cache, device)
@@ -74,6 +76,15 @@ class DeviceBatch:
                 return x.to(self.device).contiguous()
             return _dev(x, self.device)
         self.k_fp4 = (on_dev(data), on_dev(scales))
+
+    def use_mxfp4_kv(self, data, scales):
+        """Attend over an MXFP4 K|V cache (uint8 [pages, Hkv, 128, 128] codes and
+        [pages, Hkv, 128, 8] scales), host arrays or device tensors."""
+        def on_dev(x):
+            if isinstance(x, torch.Tensor):
+                return x.to(self.device).contiguous()
+            return _dev(x, self.device)
+        self.kv_fp4 = (on_dev(data), on_dev(scales))
 
 
 class MsaPath:
@@ -141,6 +152,13 @@ class MsaPath:
 
     def attend(self, stream=None):
         db = self.db
+        if db.kv_fp4 is not None:
+            msa_sparse_attn_prefill_mxfp4(db.vl, db.attn_q, db.Hq, db.kv_fp4[0], db.kv_fp4[1],
+                                          db.num_pages, db.Hkv, self.row_ptr, self.q_indices,
+                                          self.n_sel, self.schedule, TOPK, db.softmax_scale,
+                                          db.aq_scale, db.ak_scale, db.av_scale, self.out,
+                                          self.ws_attn, stream)
+            return
         msa_sparse_attn_prefill(db.vl, db.attn_q, db.Hq, db.kv, db.num_pages, db.Hkv, self.row_ptr,
                                 self.q_indices, self.n_sel, self.schedule, TOPK, db.softmax_scale,
                                 db.aq_scale, db.ak_scale, db.av_scale, self.out, self.ws_attn,

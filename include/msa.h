@@ -199,7 +199,8 @@ msa_status_t msa_build_k2q_csr(const msa_varlen_t* vl, const int32_t* topk_idx,
  * Queries with no attended token get 0.
  *   q          [total_q, Hq, 128] E4M3, token stride q_stride bytes (>= Hq*128, multiple of 16)
  *   kv_cache   [num_pages, Hkv, 128, 256] E4M3 (K|V packed per token)
- *   Hq % Hkv == 0, Hkv >= 1, Hq <= 64; n_sel_heads in {1, Hkv}; topk == 16
+ *   Hq % Hkv == 0, Hkv >= 1, Hq <= 64; n_sel_heads in {1, Hkv}; topk == 16;
+ *              total_q * topk * Hq < 2^31 (else MSA_ERR_UNSUPPORTED)
  *   row_ptr, q_indices, schedule: exactly as written by msa_build_k2q_csr for
  *              the same vl, n_sel_heads and topk
  *   q_scale, k_scale, v_scale  device fp32 scalars, or NULL for 1.0
@@ -218,6 +219,33 @@ msa_status_t msa_sparse_attn_prefill(const msa_varlen_t* vl, const uint8_t* q, i
                                      const float* q_scale, const float* k_scale,
                                      const float* v_scale, uint16_t* out, int64_t out_stride,
                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * 4b. Block-sparse prefill attention over 4-bit K|V pages  ([P2] Details: with
+ *    an E4M3 query the 4-bit K|V kernel turns each code times its block scale
+ *    into E4M3 before the FP8 products, with the K global scale on the scores
+ *    and the V global scale on the output; Claims: 8-13% faster prefill with a
+ *    4-bit K|V cache.  The pages' format is NVFP4; on gfx950 it is OCP MXFP4.)
+ *
+ * Exactly msa_sparse_attn_prefill, with the K|V cache in MXFP4:
+ *   kv_data    [num_pages, Hkv, 128, 128] uint8: per token, bytes 0..63 hold the
+ *              128 K elements and bytes 64..127 the 128 V elements as E2M1 codes,
+ *              element 2i in the low nibble of byte i; 16-byte aligned
+ *   kv_scales  [num_pages, Hkv, 128, 8] E8M0: bytes 0..3 scale K elements
+ *              32b .. 32b+31 (b = byte), bytes 4..7 the V blocks; 8-byte aligned
+ * Each element is read as E4M3: code value x 2^(scale - 127) rounded to the
+ * nearest E4M3 value (ties to even), saturating at 448; the scale 0xFF reads
+ * as NaN.  k_scale / v_scale are the per-tensor global scales.  Same workspace
+ * (msa_sparse_attn_workspace_size), schedule and errors; NULL kv_scales with
+ * total_q > 0 is MSA_ERR_INVALID_ARGUMENT.
+ * ------------------------------------------------------------------------- */
+msa_status_t msa_sparse_attn_prefill_mxfp4(
+    const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride, int32_t num_q_heads,
+    const uint8_t* kv_data, const uint8_t* kv_scales, int32_t num_pages, int32_t num_kv_heads,
+    const int32_t* row_ptr, const int32_t* q_indices, int32_t n_sel_heads, const void* schedule,
+    size_t schedule_bytes, int32_t topk, float softmax_scale, const float* q_scale,
+    const float* k_scale, const float* v_scale, uint16_t* out, int64_t out_stride,
+    void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * 5. E4M3 quantisation and the paged cache write: the step just before the

@@ -161,10 +161,12 @@ def check_csr(inp, gpu_sel, row_ptr, q_indices, n_sel=1):
     assert np.array_equal(q_indices[:nnz], ref_idx), "q_indices differ"
 
 
-def check_attention(inp, gpu_sel, gpu_out, queries, n_sel=1):
+def check_attention(inp, gpu_sel, gpu_out, queries, n_sel=1, kv_cache=None):
+    """kv_cache: the E4M3 K|V cache the reference reads (default inp.kv_cache)."""
     sel = gpu_sel.reshape(gpu_sel.shape[0], n_sel, -1)
+    kv = inp.kv_cache if kv_cache is None else kv_cache
     ref = oracle.sparse_attention(inp.cu_seqlens_q, inp.cu_seqlens_k, inp.block_table, inp.attn_q,
-                                  inp.kv_cache, sel, inp.softmax_scale, inp.attn_q_scale,
+                                  kv, sel, inp.softmax_scale, inp.attn_q_scale,
                                   inp.attn_k_scale, inp.attn_v_scale, queries=queries)
     got = gpu_out[queries].reshape(ref.shape).astype(np.float64)
     err = np.abs(got - ref)

@@ -35,7 +35,8 @@ def test_library_exports_every_declared_symbol():
         "msa_k2q_schedule_size", "msa_build_k2q_csr", "msa_sparse_attn_workspace_size",
         "msa_sparse_attn_prefill", "msa_status_string", "msa_last_error", "msa_abi_version",
         "msa_quantize_e4m3", "msa_insert_index_k", "msa_insert_kv", "msa_index_score_mxfp4",
-        "msa_insert_index_k_mxfp4", "msa_index_score_noalloc", "msa_index_score_per_head"]), names
+        "msa_insert_index_k_mxfp4", "msa_index_score_noalloc", "msa_index_score_per_head",
+        "msa_sparse_attn_prefill_mxfp4"]), names
     for n in names:
         assert hasattr(L, n), n
     assert msa.msa_abi_version() == 3
@@ -146,6 +147,26 @@ def test_attention_validation():
     assert attn(v, ws=100) == WS_SMALL
     assert attn(v, sched=100) == WS_SMALL
     assert attn(vl(total_q=0)) == OK
+
+
+def attn_mx(v, scales=FAKE, Hq=8, Hkv=1, topk=16, sm=0.088):
+    L = msa.lib()
+    sched = L.msa_k2q_schedule_size(ctypes.byref(v), 1, 16) or 1 << 20
+    ws = L.msa_sparse_attn_workspace_size(ctypes.byref(v), Hq, Hkv, 1, 16) or 1 << 20
+    return L.msa_sparse_attn_prefill_mxfp4(ctypes.byref(v), FAKE, 1024, Hq, FAKE, scales, 8, Hkv,
+                                           FAKE, FAKE, 1, 0x100000, sched, topk, sm, None, None,
+                                           None, FAKE, 1024, 0x200000, ws, None)
+
+
+def test_mxfp4_attention_validation():
+    """The MXFP4 K|V entry takes the same checks plus its scales pointer."""
+    v = vl()
+    assert attn_mx(v, scales=None) == INVALID
+    assert attn_mx(v, scales=FAKE + 4) == INVALID          # not 8-byte aligned
+    assert attn_mx(v, Hq=8, Hkv=3) == UNSUPPORTED
+    assert attn_mx(v, topk=8) == UNSUPPORTED
+    assert attn_mx(v, sm=0.0) == INVALID
+    assert attn_mx(vl(total_q=0), scales=None) == OK
 
 
 def test_workspace_sizes_grow_with_the_batch():
