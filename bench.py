@@ -48,6 +48,9 @@ def parse():
                     help="per-index-head selection (each index head scores alone and selects the "
                          "pages of its KV head)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused-select", action="store_true",
+                    help="decode-like workloads: index scores and top-16 in one fused call "
+                         "(msa_index_score_topk) instead of two")
     ap.add_argument("--kv-cache", choices=["e4m3", "mxfp4"], default="e4m3",
                     help="K|V page format the attention reads (mxfp4: seeded random MXFP4 codes "
                          "and block scales, read as E4M3)")
@@ -541,8 +544,12 @@ def main():
         calls = [path.csr, path.attend]
     else:
         path = MsaPath(db, per_head=args.per_head)
-        names = ["index_score", "topk_select", "k2q_csr", "sparse_attn"]
-        calls = [path.score, path.select, path.csr, path.attend]
+        if args.fused_select:
+            names = ["index_score_topk", "k2q_csr", "sparse_attn"]
+            calls = [path.score_select, path.csr, path.attend]
+        else:
+            names = ["index_score", "topk_select", "k2q_csr", "sparse_attn"]
+            calls = [path.score, path.select, path.csr, path.attend]
     stream = torch.cuda.current_stream()
     # cold caches: a 1 GiB buffer, written once here, is READ before a call so that
     # L2 (32 MiB) and the memory-side cache (256 MiB) hold clean lines of it; an
@@ -603,7 +610,9 @@ def main():
               "topk": 16, "cache": "cold: a 1 GiB buffer read before every timed call",
               "kv_cache": args.kv_cache,
               "selection": ("random per KV head (benchmark-script rule)" if attention_only else
-                            "per index head" if args.per_head else "index scores, one per query")}
+                            "per index head" if args.per_head else
+                            "index scores, one per query, fused with the scorer" if args.fused_select
+                            else "index scores, one per query")}
     if not attention_only:
         config["index_cache"] = args.index_cache
     result = {
@@ -655,16 +664,20 @@ def main():
                           "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                           "frac": round(score_tflops / PEAK_FP8_TFLOPS, 4)}
         result["value"] = round(score_us, 2)
-        result["value_is"] = "index_score (plan + scorer), cold, us per call"
+        result["value_is"] = ("index_score_topk (plan + fused scorer + merge), cold, us per call"
+                              if args.fused_select else
+                              "index_score (plan + scorer), cold, us per call")
         result["roofline"] = {**score_roof,
                               "traffic": (scorer_hbm_traffic(wl.name) if args.index_cache == "e4m3"
-                                          and not args.per_head else None),
+                                          and not args.per_head and not args.fused_select
+                                          else None),
                               "kernel": "index_score (plan + scorer)",
                               "flops_per_launch": work["score_flops"],
                               "algorithmic_bytes_per_launch": work["score_bytes"],
                               "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + "
                                               "WRITE_SIZE, copy-calibrated)"}
-        result["topk_gbs"] = round(work["topk_bytes"] / (float(mean_us[1]) * 1e-6) / 1e9, 1)
+        if not args.fused_select:
+            result["topk_gbs"] = round(work["topk_bytes"] / (float(mean_us[1]) * 1e-6) / 1e9, 1)
         result["context"] = {"note": "other hardware, per rank, cold L2; not a target",
                              "gb300_cute_scorer_us": 305, "rubin_cute_scorer_us": 174}
     result["breakdown_us"] = {n: round(float(m), 2) for n, m in zip(names, cold_us)}

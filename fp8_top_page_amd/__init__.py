@@ -18,7 +18,8 @@ __all__ = [
     "msa_sparse_attn_workspace_size", "msa_status_string", "msa_last_error", "msa_abi_version",
     "msa_quantize_e4m3", "msa_insert_index_k", "msa_insert_kv", "msa_index_score_mxfp4",
     "msa_insert_index_k_mxfp4", "msa_index_score_noalloc", "msa_index_score_per_head",
-    "msa_sparse_attn_prefill_mxfp4", "LIB_PATH", "PAGE", "HEAD_DIM", "TOPK",
+    "msa_sparse_attn_prefill_mxfp4", "msa_index_score_topk", "msa_index_score_topk_workspace_size",
+    "LIB_PATH", "PAGE", "HEAD_DIM", "TOPK",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
@@ -79,6 +80,11 @@ def lib():
                                                     _c_i32, _c_f, _c_p, _c_p, _c_p, _c_p, _c_i64,
                                                     _c_p, _c_size, _c_p]
         L.msa_sparse_attn_prefill_mxfp4.restype = ctypes.c_int
+        L.msa_index_score_topk_workspace_size.argtypes = [vp, _c_i32]
+        L.msa_index_score_topk_workspace_size.restype = _c_size
+        L.msa_index_score_topk.argtypes = [vp, _c_p, _c_i64, _c_i32, _c_p, _c_i32, _c_p, _c_p,
+                                           _c_i32, _c_i32, _c_p, _c_i64, _c_p, _c_size, _c_p]
+        L.msa_index_score_topk.restype = ctypes.c_int
         L.msa_quantize_e4m3.argtypes = [_c_p, _c_i32, _c_i64, _c_i32, _c_i64, _c_p, _c_p, _c_i64,
                                         _c_p]
         L.msa_quantize_e4m3.restype = ctypes.c_int
@@ -220,6 +226,21 @@ def msa_sparse_attn_prefill(vl: Varlen, q, num_q_heads, kv_cache, num_pages, num
         out.stride(0), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check(st, "msa_sparse_attn_prefill")
+
+
+def msa_index_score_topk_workspace_size(vl: Varlen, num_index_heads):
+    return lib().msa_index_score_topk_workspace_size(vl.ref, num_index_heads)
+
+
+def msa_index_score_topk(vl: Varlen, q, num_index_heads, k_cache, num_pages, q_scale, k_scale,
+                         topk, n_local, topk_out, workspace, stream=None):
+    """Decode-like batches: index scores and top-k selection in one pass.
+    q: uint8 [total_q, H*128]; topk_out: int32 [total_q, >= 16] (row stride topk_out.stride(0))."""
+    st = lib().msa_index_score_topk(
+        vl.ref, _ptr(q), q.stride(0), num_index_heads, _ptr(k_cache), num_pages, _ptr(q_scale),
+        _ptr(k_scale), topk, n_local, _ptr(topk_out), topk_out.stride(0), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "msa_index_score_topk")
 
 
 def msa_sparse_attn_prefill_mxfp4(vl: Varlen, q, num_q_heads, kv_data, kv_scales, num_pages,

@@ -77,6 +77,9 @@ struct ScoreK {
   const ItemHdr* hdr;
   const int4* items;
   const uint8_t* k_scales;   // MXFP4 keys: [num_pages, 128, 4] E8M0 block scales
+  uint64_t* cand;            // fused selection (decode kernel): [items, queries, 16] candidate keys
+  int2* first_item;          // fused selection: [total_q] (first work item, position) of each query
+  int32_t n_local;           // fused selection: forced recent pages
 };
 
 // ---------------------------------------------------------------------------
@@ -843,14 +846,86 @@ __global__ __launch_bounds__(kThreads) void index_score_kernel(ScoreK a) {
 template <int KF>
 constexpr int pp_ring() { return KF ? 8 : 4; }
 
-template <int H, int KF>
+// kSel: the fused selection keeps the item's scores in LDS ([queries, pages])
+template <int H, int KF, bool kSel = false>
 constexpr size_t score_pp_lds_bytes() {
   return pp_ring<KF>() * (KF ? kF4Slot : kLdsPage) + (size_t)score_qtiles(H) * 16 * kSRow * sizeof(float) +
-         kMaxItemPages * sizeof(int) + 2 * kScoreWaves * score_qtiles(H) * 16 * sizeof(float);
+         kMaxItemPages * sizeof(int) + 2 * kScoreWaves * score_qtiles(H) * 16 * sizeof(float) +
+         (kSel ? (size_t)score_qtiles(H) * 16 * kMaxItemPages * sizeof(float) : 0);
 }
 
-// One work item of the decode scorer (same contract as score_item).
-template <int H, int KF>
+// Candidate key of (score, page): higher score first, then lower page; 0 is
+// "no candidate" (a real key has ~page != 0 in its low half).
+__device__ __forceinline__ uint64_t cand_key(float score, int page) {
+  return ((uint64_t)float_key(score) << 32) | (uint32_t)(~(uint32_t)page);
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+template <int kCtrl>
+__device__ __forceinline__ uint64_t dpp64(uint64_t x) {   // both halves through one DPP pattern
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, kCtrl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), kCtrl, 0xF, 0xF, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+// Maximum over the wave: within each 16-lane row by DPP (quad_perm xor 1 and
+// xor 2, half-row mirror, row mirror), then across the rows with the gfx950
+// lane-swap instructions (as in max_across_groups).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+  x = umax64(x, dpp64<0xB1>(x));
+  x = umax64(x, dpp64<0x4E>(x));
+  x = umax64(x, dpp64<0x141>(x));
+  x = umax64(x, dpp64<0x140>(x));
+  auto l = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  auto h = __builtin_amdgcn_permlane32_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
+  x = umax64(((uint64_t)h[0] << 32) | l[0], ((uint64_t)h[1] << 32) | l[1]);
+  l = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  h = __builtin_amdgcn_permlane16_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
+  return umax64(((uint64_t)h[0] << 32) | l[0], ((uint64_t)h[1] << 32) | l[1]);
+}
+
+// Fused selection, end of a decode item: for each of the item's queries, the
+// item's 16 best candidate pages (pages below the query's forced recent ones),
+// by key, into cand[item, query, 0..15] (0 past the last).  Wave w takes queries
+// w, w + 16, ...; lane l holds pages p0 + l + 64 r.  The 16 picks are 16 rounds
+// of a wave-wide maximum whose holder drops it.
+template <int H>
+__device__ __forceinline__ void select_item_candidates(const ScoreK& a, int item, int q_first,
+                                                       int q_count, int p0, int p_end, int ctx,
+                                                       int cq0, const float* s_isc) {
+  constexpr int kQ = score_qtiles(H) * 16;
+  constexpr int kPer = kMaxItemPages / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int ql = wave; ql < q_count; ql += kScoreWaves) {
+    const int pos = ctx + (q_first + ql - cq0);
+    const int v = min(pos / kPage + 1, a.max_pages);
+    const int f = min(a.n_local, min(kTopK, v));
+    const int c_end = min(p_end, v - f);            // candidate pages of this item: [p0, c_end)
+    uint64_t key[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int j = lane + 64 * r;
+      key[r] = p0 + j < c_end ? cand_key(s_isc[ql * kMaxItemPages + j], p0 + j) : 0ull;
+    }
+    uint64_t mine = 0;                              // lane k keeps the k-th pick
+#pragma unroll 1
+    for (int k = 0; k < kTopK; ++k) {
+      uint64_t m = key[0];
+#pragma unroll
+      for (int r = 1; r < kPer; ++r) m = key[r] > m ? key[r] : m;
+      const uint64_t w = wave_max_u64(m);
+      if (w == 0) break;                            // wave-uniform: no candidate left
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) key[r] = key[r] == w ? 0ull : key[r];
+      mine = lane == k ? w : mine;
+    }
+    if (lane < kTopK) a.cand[((int64_t)item * kQ + ql) * kTopK + lane] = mine;
+  }
+}
+
+// One work item of the decode scorer (same contract as score_item).  kSel: the
+// fused selection, which keeps the item's scores in LDS instead of writing them
+// and leaves per-item candidate lists.
+template <int H, int KF, bool kSel = false>
 __device__ __forceinline__ void score_pp_item(const ScoreK& a, int item, uint8_t* lds) {
   constexpr int NQT = score_qtiles(H);
   constexpr int kQ = NQT * 16;                    // query slots
@@ -867,6 +942,7 @@ __device__ __forceinline__ void score_pp_item(const ScoreK& a, int item, uint8_t
   float* sbuf = reinterpret_cast<float*>(lds + kRingN * kSlot);
   int* s_phys = reinterpret_cast<int*>(lds + kRingN * kSlot + kQ * kSRow * 4);
   float* s_part = reinterpret_cast<float*>(s_phys + kMaxItemPages);
+  float* s_isc = s_part + 2 * kScoreWaves * kQ;   // kSel: [kQ, kMaxItemPages] item scores
 
   const int cq0 = a.cu_q[b];
   const int sq = a.cu_q[b + 1] - cq0;
@@ -876,7 +952,14 @@ __device__ __forceinline__ void score_pp_item(const ScoreK& a, int item, uint8_t
   const int pos_last = pos_first + q_count - 1;
   const int v_block = pos_last / kPage + 1;
   const int p_end = min(min(p0 + a.hdr->pages_per_item, v_block), a.max_pages);
-  if (p0 >= p_end) return;
+  if (p0 >= p_end) {
+    if constexpr (kSel) {                         // an empty item still leaves (empty) lists
+      for (int e = tid; e < q_count * kTopK; e += kThreads)
+        a.cand[(int64_t)item * kQ * kTopK + e] = 0ull;
+      if (p0 == 0 && tid < q_count) a.first_item[q_first + tid] = make_int2(item, ctx + (q_first + tid - cq0));
+    }
+    return;
+  }
   const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
   for (int k = tid; k < p_end - p0; k += kThreads) {
     const int phys = bt[p0 + k];
@@ -975,6 +1058,11 @@ __device__ __forceinline__ void score_pp_item(const ScoreK& a, int item, uint8_t
       const int pp = pg0 + c;
       const float* src = sbuf + ql * kSRow + c;
       const float v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
+      if constexpr (kSel) {                      // the item's score row in LDS (pages past
+        if (qi < q_end)                          // the visible ones are never read)
+          *reinterpret_cast<v4f*>(s_isc + ql * kMaxItemPages + (pp - p0)) = v4f{v0, v1, v2, v3};
+        continue;
+      }
       if (qi < q_end) {
         float* dst = a.scores + (int64_t)qi * a.ld + pp;
         const int vis_end = min(pg_hi, pos / kPage + 1);
@@ -1030,12 +1118,107 @@ __device__ __forceinline__ void score_pp_item(const ScoreK& a, int item, uint8_t
   // item reuses the ring, and the reducer's LDS reads finish before its writes
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if constexpr (kSel) {
+    select_item_candidates<H>(a, item, q_first, q_count, p0, p_end, ctx, cq0, s_isc);
+    if (p0 == 0 && tid < q_count)                 // the query's items start here
+      a.first_item[q_first + tid] = make_int2(item, ctx + (q_first + tid - cq0));
+    __syncthreads();                              // s_isc is rewritten by the next item
+  }
 }
 
 template <int H, int KF>
 __global__ __launch_bounds__(kThreads) void index_score_pp_kernel(ScoreK a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   take_items<H, KF, true>(a, lds);
+}
+
+// The decode scorer with the fused selection (E4M3 keys).
+template <int H>
+__global__ __launch_bounds__(kThreads) void index_score_sel_kernel(ScoreK a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int n_items = a.hdr->n_items;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) score_pp_item<H, 0, true>(a, item, lds);
+}
+
+// Merge of the per-item candidate lists, one wave per query: the forced recent
+// pages first (local page first), then the 16 - forced best candidates over the
+// items of the query's request (consecutive in the plan from the one the scorer
+// recorded with the query's position, each holding all of the request's
+// queries), -1 padding.
+constexpr int kMergePer = 16;                // merge candidates per lane per group
+
+struct MergeK {
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t batch;
+  int32_t total_q;
+  int32_t max_pages;
+  int32_t n_local;
+  int32_t kq;                       // queries per item list
+  const ItemHdr* hdr;
+  const int4* items;
+  const uint64_t* cand;
+  const int2* first_item;
+  int32_t* out;
+  int64_t out_stride;
+};
+
+__global__ __launch_bounds__(256) void topk_merge_kernel(MergeK a) {
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= a.total_q) return;                    // wave-uniform
+  const int2 fp = a.first_item[i];               // written by the scorer for every query
+  const int lo = fp.x, pos = fp.y;
+  const int n_items = a.hdr->n_items;
+  const int v = min(pos / kPage + 1, a.max_pages);
+  const int k_all = min(kTopK, v);
+  const int f = min(a.n_local, k_all);
+  const int ksel = k_all - f;
+  const int b = a.items[lo].x;
+  // the request's item count: consecutive items of request b from lo
+  int n_ch = 0;
+  for (;;) {
+    const int it = lo + n_ch + lane;
+    const uint64_t same = __builtin_amdgcn_ballot_w64(it < n_items && a.items[it].x == b);
+    const int run = same == ~0ull ? 64 : __builtin_ctzll(~same);
+    n_ch += run;
+    if (run < 64) break;                          // wave-uniform
+  }
+  // candidates in groups of kMergePer per lane (kMergePer * 4 items), each
+  // group merged with the 16 kept so far by 16 rounds of a wave-wide maximum
+  uint64_t keep = 0;                              // lane k < 16: the k-th best so far
+  for (int g0 = 0; ksel > 0 && g0 < n_ch * kTopK; g0 += kMergePer * 64) {
+    uint64_t c[kMergePer];
+#pragma unroll
+    for (int r = 0; r < kMergePer; ++r) {
+      const int j = g0 + r * 64 + lane;           // candidate j: item lo + j / 16, slot j % 16
+      const int it = lo + j / kTopK;
+      c[r] = j < n_ch * kTopK
+                 ? a.cand[((int64_t)it * a.kq + (i - a.items[it].y)) * kTopK + (j & (kTopK - 1))]
+                 : 0ull;
+    }
+    uint64_t nk = 0;
+#pragma unroll 1
+    for (int k = 0; k < kTopK; ++k) {
+      uint64_t m = keep;
+#pragma unroll
+      for (int r = 0; r < kMergePer; ++r) m = umax64(m, c[r]);
+      const uint64_t w = wave_max_u64(m);
+      if (w == 0) break;                          // wave-uniform
+#pragma unroll
+      for (int r = 0; r < kMergePer; ++r) c[r] = c[r] == w ? 0ull : c[r];
+      keep = keep == w ? 0ull : keep;
+      nk = lane == k ? w : nk;
+    }
+    keep = nk;
+  }
+  const uint64_t pick = (uint64_t)(uint32_t)__shfl((int)(uint32_t)keep, max(lane - f, 0));
+  if (lane < kTopK) {
+    int page = -1;
+    if (lane < f) page = v - 1 - lane;
+    else if (lane < k_all) page = (int)~(uint32_t)pick;
+    a.out[i * a.out_stride + lane] = page;
+  }
 }
 
 template <int H, int KF, bool kDecode>
@@ -1123,6 +1306,72 @@ hipError_t launch_index_score_heads(const ScoreArgs& a, int64_t head_stride, hip
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+template <int H>
+static hipError_t launch_sel(dim3 grid, hipStream_t stream, const ScoreK& k) {
+  constexpr size_t bytes = score_pp_lds_bytes<H, 0, true>();
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&index_score_sel_kernel<H>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((index_score_sel_kernel<H>), grid, dim3(kThreads), bytes, stream, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_score_topk(const ScoreArgs& a, int n_local, int32_t* out,
+                                   int64_t out_stride, hipStream_t stream) {
+  if (a.vl.total_q == 0) return hipSuccess;
+  hipError_t e = launch_plan(a, stream);
+  if (e != hipSuccess) return e;
+  ItemHdr* hdr = reinterpret_cast<ItemHdr*>(a.workspace);
+  int4* items = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(a.workspace) + sizeof(ItemHdr));
+  uint64_t* cand = reinterpret_cast<uint64_t*>(reinterpret_cast<uint8_t*>(a.workspace) +
+                                               a.plan.workspace_bytes);
+  int2* first_item = reinterpret_cast<int2*>(
+      reinterpret_cast<uint8_t*>(cand) + index_score_topk_extra_bytes(a.plan, a.H, a.vl.total_q) -
+      align_up((size_t)std::max<int64_t>(a.vl.total_q, 1) * sizeof(int2), 256));
+  ScoreK k{};
+  k.cu_q = a.vl.cu_seqlens_q;
+  k.cu_k = a.vl.cu_seqlens_k;
+  k.block_table = a.vl.block_table;
+  k.bt_stride = a.vl.block_table_stride;
+  k.batch = a.vl.batch;
+  k.num_pages = a.num_pages;
+  k.max_pages = a.vl.max_pages;
+  k.q = a.q;
+  k.q_stride = a.q_stride;
+  k.k_cache = a.k_cache;
+  k.q_scale = a.q_scale;
+  k.k_scale = a.k_scale;
+  k.scores = nullptr;
+  k.ld = 0;
+  k.hdr = hdr;
+  k.items = items;
+  k.k_scales = nullptr;
+  k.cand = cand;
+  k.first_item = first_item;
+  k.n_local = n_local;
+  dim3 grid((unsigned)std::min<int64_t>(a.plan.max_items, device_cu_count()));
+  switch (a.H) {
+    case 1: e = launch_sel<1>(grid, stream, k); break;
+    case 2: e = launch_sel<2>(grid, stream, k); break;
+    case 4: e = launch_sel<4>(grid, stream, k); break;
+    default: e = hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  MergeK m{a.vl.cu_seqlens_q, a.vl.cu_seqlens_k, a.vl.batch, (int32_t)a.vl.total_q,
+           a.vl.max_pages, n_local, score_qtiles(a.H) * 16, hdr, items, cand, first_item, out,
+           out_stride};
+  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)ceil_div(a.vl.total_q, 4)), dim3(256), 0,
+                     stream, m);
+  return hipGetLastError();
+}
+
+// Candidate lists [max_items, queries, 16], then (first item, position) per query.
+size_t index_score_topk_extra_bytes(const ScorePlan& p, int H, int64_t total_q) {
+  return align_up((size_t)p.max_items * score_qtiles(H) * 16 * kTopK * sizeof(uint64_t), 256) +
+         align_up((size_t)std::max<int64_t>(total_q, 1) * sizeof(int2), 256);
 }
 
 static hipError_t launch_plan(const ScoreArgs& a, hipStream_t stream) {

@@ -97,6 +97,13 @@ size_t msa_index_score_workspace_size(const msa_varlen_t* vl, int32_t num_index_
   return score_plan(vl, num_index_heads).workspace_bytes;
 }
 
+size_t msa_index_score_topk_workspace_size(const msa_varlen_t* vl, int32_t num_index_heads) {
+  if (!vl || vl->batch < 1 || vl->total_q < 0 || vl->max_pages < 0) return 0;
+  if (num_index_heads != 1 && num_index_heads != 2 && num_index_heads != 4) return 0;
+  const ScorePlan p = score_plan(vl, num_index_heads);
+  return p.workspace_bytes + index_score_topk_extra_bytes(p, num_index_heads, vl->total_q);
+}
+
 }  // extern "C"
 
 namespace {
@@ -254,6 +261,47 @@ msa_status_t msa_index_score_mxfp4(const msa_varlen_t* vl, const uint8_t* q, int
   return index_score_impl(vl, q, q_stride, num_index_heads, k_data, k_scales, num_pages, q_scale,
                           k_scale, scores, ld_scores, workspace, workspace_bytes, stream,
                           "msa_index_score_mxfp4");
+}
+
+msa_status_t msa_index_score_topk(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
+                                  int32_t num_index_heads, const uint8_t* k_cache,
+                                  int32_t num_pages, const float* q_scale, const float* k_scale,
+                                  int32_t topk, int32_t n_local, int32_t* topk_idx,
+                                  int64_t topk_stride, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  msa_status_t st = check_varlen(vl);
+  if (st != MSA_OK) return st;
+  const int H = num_index_heads;
+  MSA_CHECK(H == 1 || H == 2 || H == 4, MSA_ERR_UNSUPPORTED,
+            "num_index_heads must be 1, 2 or 4 (got %d)", H);
+  MSA_CHECK(topk == kTopK, MSA_ERR_UNSUPPORTED, "topk must be 16 (got %d)", topk);
+  MSA_CHECK(n_local >= 1 && n_local <= kTopK, MSA_ERR_UNSUPPORTED,
+            "n_local must be in [1, 16] (got %d)", n_local);
+  MSA_CHECK(vl->max_seqlen_q <= kScoreQueriesPerWave / H, MSA_ERR_UNSUPPORTED,
+            "the fused selection takes decode-like batches: max_seqlen_q (%d) > %d / H",
+            vl->max_seqlen_q, kScoreQueriesPerWave);
+  if (vl->total_q == 0) return MSA_OK;
+  MSA_CHECK(q && k_cache && q_scale && k_scale && topk_idx && workspace,
+            MSA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  MSA_CHECK(q_stride >= (int64_t)H * kDim && q_stride % 16 == 0, MSA_ERR_INVALID_ARGUMENT,
+            "q_stride must be >= H*128 and a multiple of 16 (got %lld)", (long long)q_stride);
+  MSA_CHECK(aligned(q, 16) && aligned(k_cache, 16) && aligned(workspace, 16),
+            MSA_ERR_INVALID_ARGUMENT, "q, k_cache and workspace must be 16-byte aligned");
+  MSA_CHECK(num_pages >= 1, MSA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
+  MSA_CHECK(topk_stride >= kTopK, MSA_ERR_INVALID_ARGUMENT, "topk_stride must be >= 16");
+  const ScorePlan plan = score_plan(vl, H);
+  const size_t need = plan.workspace_bytes + index_score_topk_extra_bytes(plan, H, vl->total_q);
+  MSA_CHECK(workspace_bytes >= need, MSA_ERR_WORKSPACE_TOO_SMALL,
+            "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  MSA_CHECK(plan.max_items < (int64_t)INT32_MAX, MSA_ERR_UNSUPPORTED, "batch too large");
+  st = check_device();
+  if (st != MSA_OK) return st;
+  ScoreArgs a{*vl, q, q_stride, H, k_cache, num_pages, q_scale, k_scale,
+              nullptr, 0, workspace, plan, nullptr};
+  hipError_t e = launch_index_score_topk(a, n_local, topk_idx, topk_stride,
+                                         reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "msa_index_score_topk");
+  return MSA_OK;
 }
 
 // ---------------------------------------------------------------------------

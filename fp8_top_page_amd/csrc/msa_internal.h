@@ -57,6 +57,13 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream);
 // Per-index-head scores: a.H single-head passes over one single-head plan,
 // head h's scores at a.scores + h * head_stride (a.plan must be score_plan(vl, 1)).
 hipError_t launch_index_score_heads(const ScoreArgs& a, int64_t head_stride, hipStream_t stream);
+// Decode-like batches (every request at most 64 / H queries): scores and the
+// top-16 selection in one scorer pass plus a merge, without writing scores.
+// The workspace holds the plan (a.plan.workspace_bytes) and then
+// index_score_topk_extra_bytes of candidate lists.
+hipError_t launch_index_score_topk(const ScoreArgs& a, int n_local, int32_t* out,
+                                   int64_t out_stride, hipStream_t stream);
+size_t index_score_topk_extra_bytes(const ScorePlan& p, int H, int64_t total_q);
 
 // ---- top-k ---------------------------------------------------------------
 struct TopkArgs {

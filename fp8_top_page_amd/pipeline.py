@@ -8,6 +8,7 @@ import numpy as np
 import torch
 
 from . import (PAGE, TOPK, Varlen, msa_build_k2q_csr, msa_index_score, msa_index_score_mxfp4,
+               msa_index_score_topk, msa_index_score_topk_workspace_size,
                msa_index_score_per_head, msa_index_score_workspace_size, msa_k2q_schedule_size,
                msa_sparse_attn_prefill, msa_sparse_attn_prefill_mxfp4,
                msa_sparse_attn_workspace_size, msa_topk_select)
@@ -134,6 +135,17 @@ class MsaPath:
         else:
             msa_index_score(db.vl, db.index_q, db.H, db.k_cache, db.num_pages, db.iq_scale,
                             db.ik_scale, self.scores, self.ws_score, stream)
+
+    def score_select(self, stream=None):
+        """Decode-like batches: scores and selection in one fused pass (the scores
+        buffer is left untouched)."""
+        db = self.db
+        if not hasattr(self, "ws_fused"):
+            self.ws_fused = torch.empty(max(msa_index_score_topk_workspace_size(db.vl, db.H), 256),
+                                        dtype=torch.uint8, device=db.device)
+        msa_index_score_topk(db.vl, db.index_q, db.H, db.k_cache, db.num_pages, db.iq_scale,
+                             db.ik_scale, TOPK, self.n_local, self.topk[:, 0, :], self.ws_fused,
+                             stream)
 
     def select(self, stream=None):
         if self.per_head:                         # one selection per (query, index head)

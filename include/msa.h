@@ -156,6 +156,30 @@ msa_status_t msa_topk_select(const msa_varlen_t* vl, const float* scores, int64_
                              int64_t topk_stride, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * 2b. Fused index scores and top-16 selection for decode-like batches
+ *    ([P1] Claims: the top-16 stays a kernel of its own, "Native Top16";
+ *    Findings: on short-Q shapes the persistent scorer loses to its schedule's
+ *    tail.  Here the selection runs inside the decode scorer's work items.)
+ *
+ * topk_idx exactly as msa_index_score followed by msa_topk_select on its
+ * scores (same tie rule: equal scores go to the lower page), without writing
+ * the scores: each scorer work item keeps its pages' scores in LDS and leaves
+ * every query's 16 best candidate pages, which a merge reduces to the top 16.
+ *   Only batches whose every request has at most 64 / H queries (the decode
+ *   scorer's shapes); others get MSA_ERR_UNSUPPORTED.
+ *   Arguments as msa_index_score (E4M3 keys) and msa_topk_select (topk == 16,
+ *   n_local in [1, 16], topk_idx [total_q, topk_stride] int32).
+ *   workspace  >= msa_index_score_topk_workspace_size(vl, H) bytes, 16-byte aligned
+ * ------------------------------------------------------------------------- */
+size_t msa_index_score_topk_workspace_size(const msa_varlen_t* vl, int32_t num_index_heads);
+msa_status_t msa_index_score_topk(const msa_varlen_t* vl, const uint8_t* q, int64_t q_stride,
+                                  int32_t num_index_heads, const uint8_t* k_cache,
+                                  int32_t num_pages, const float* q_scale, const float* k_scale,
+                                  int32_t topk, int32_t n_local, int32_t* topk_idx,
+                                  int64_t topk_stride, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* ---------------------------------------------------------------------------
  * 3. KV-page -> query CSR  ([P4] forward: build_k2q_csr(topk, cu_seqlens_q,
  *    cu_seqlens_k, 128, ..., total_rows=total_kv_blocks, qhead_per_kv, ...,
  *    return_schedule=True) -> (row_ptr, q_indices, schedule).)

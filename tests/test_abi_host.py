@@ -36,7 +36,8 @@ def test_library_exports_every_declared_symbol():
         "msa_sparse_attn_prefill", "msa_status_string", "msa_last_error", "msa_abi_version",
         "msa_quantize_e4m3", "msa_insert_index_k", "msa_insert_kv", "msa_index_score_mxfp4",
         "msa_insert_index_k_mxfp4", "msa_index_score_noalloc", "msa_index_score_per_head",
-        "msa_sparse_attn_prefill_mxfp4"]), names
+        "msa_sparse_attn_prefill_mxfp4", "msa_index_score_topk",
+        "msa_index_score_topk_workspace_size"]), names
     for n in names:
         assert hasattr(L, n), n
     assert msa.msa_abi_version() == 3
@@ -167,6 +168,28 @@ def test_mxfp4_attention_validation():
     assert attn_mx(v, topk=8) == UNSUPPORTED
     assert attn_mx(v, sm=0.0) == INVALID
     assert attn_mx(vl(total_q=0), scales=None) == OK
+
+
+def test_fused_score_topk_validation():
+    """The fused decode scores + top-k call: decode-like batches only."""
+    L = msa.lib()
+
+    def fz(v, H=1, topk=16, n_local=1, ws=None, stride=16):
+        if ws is None:
+            ws = L.msa_index_score_topk_workspace_size(ctypes.byref(v), H) or 1 << 20
+        return L.msa_index_score_topk(ctypes.byref(v), FAKE, 128 * H, H, FAKE, 8, FAKE, FAKE, topk,
+                                      n_local, FAKE, stride, 0x200000, ws, None)
+    dec = vl(batch=2, total_q=16, max_q=8)
+    assert fz(vl(total_q=100, max_q=100)) == UNSUPPORTED          # 100 > 64 queries
+    assert fz(vl(total_q=40, max_q=40), H=2) == UNSUPPORTED       # 40 > 64 / 2
+    assert fz(dec, H=3) == UNSUPPORTED
+    assert fz(dec, topk=8) == UNSUPPORTED
+    assert fz(dec, n_local=0) == UNSUPPORTED
+    assert fz(dec, stride=8) == INVALID
+    assert fz(dec, ws=64) == WS_SMALL
+    a = L.msa_index_score_topk_workspace_size(ctypes.byref(dec), 1)
+    assert a > L.msa_index_score_workspace_size(ctypes.byref(dec), 1)
+    assert L.msa_index_score_topk_workspace_size(ctypes.byref(dec), 3) == 0
 
 
 def test_workspace_sizes_grow_with_the_batch():
