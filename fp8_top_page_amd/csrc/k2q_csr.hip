@@ -420,7 +420,8 @@ constexpr int kOrderKeys = 1024;
 __global__ __launch_bounds__(kOrderThreads) void item_order_kernel(const Hdr* __restrict__ hdr,
                                                                    const int32_t* __restrict__ okey,
                                                                    int n_keys, int64_t max_items,
-                                                                   int32_t* __restrict__ perm) {
+                                                                   int32_t* __restrict__ perm,
+                                                                   int32_t* __restrict__ kstart) {
   __shared__ int s_cnt[kOrderKeys];
   __shared__ int s_wave[kOrderThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -439,6 +440,8 @@ __global__ __launch_bounds__(kOrderThreads) void item_order_kernel(const Hdr* __
   for (int k = 0; k < wave; ++k) off += s_wave[k];
   __syncthreads();
   s_cnt[tid] = off + incl - c;
+  if (tid < n_keys) kstart[tid] = off + incl - c;   // first perm position of each key
+  if (tid == kOrderThreads - 1) kstart[n_keys] = off + incl;
   __syncthreads();
   for (int i = tid; i < n; i += kOrderThreads) perm[atomicAdd(&s_cnt[key_of(i)], 1)] = i;
 }
@@ -463,21 +466,36 @@ SchedLayout sched_layout(const msa_varlen_t* vl, int n_sel, int topk) {
   // ceil(c / item_q) items; only pieces with entries yield any
   L.item_q = attn_item_queries(vl);
   const int64_t entries = (int64_t)n_sel * vl->total_q * topk;
-  const int64_t pieces = L.n_rows * std::max<int64_t>(1, L.words_per_row / kUnitWords);
+  const int64_t per_row =
+      ceil_div((int64_t)vl->total_q * topk, std::max<int64_t>(1, vl->total_rows));
+  // one long request (a fresh prefill or a long chunk): the chunked persistent
+  // attention, whose items must not cross a chunk of 2^kChunkShift queries, so
+  // pieces are cut to that many query slots
+  // Switched off: its first GPU runs (1536 queries, three chunks) did not
+  // finish, for a reason not yet found; every batch takes the split path.
+  L.fused = (kChunkedAttention && vl->batch == 1 && L.item_q == kAttnQCMax && per_row >= 512 &&
+             L.words_per_row % kUnitWords == 0 && vl->total_q < ((int64_t)1 << 19))
+                ? 1 : 0;
+  L.piece_words = (int32_t)std::min<int64_t>(L.words_per_row,
+                                             L.fused ? (1 << kChunkShift) / 32 : kUnitWords);
+  const int64_t pieces = L.n_rows * std::max<int64_t>(1, L.words_per_row / L.piece_words);
   L.max_items = ceil_div(entries, L.item_q) + std::min(entries, pieces);
   // rows of at least 512 queries on average (a long fresh prefill): items in
   // query-range order, ranges of 2048 queries (wider if there would be more
   // than kOrderKeys); shorter rows lose more page reuse than they gain
   L.order_shift = 0;
   L.order_keys = 1;
-  const int64_t per_row =
-      ceil_div((int64_t)vl->total_q * topk, std::max<int64_t>(1, vl->total_rows));
-  if (L.item_q == kAttnQCMax && per_row >= 512 && L.max_items <= (int64_t)INT32_MAX) {
+  if (L.fused && L.max_items <= (int64_t)INT32_MAX) {   // items in chunk order
+    L.order_shift = kChunkShift;
+    L.order_keys = (int32_t)((std::max<int64_t>(vl->total_q, 1) >> kChunkShift) + 1);
+  } else if (L.item_q == kAttnQCMax && per_row >= 512 && L.max_items <= (int64_t)INT32_MAX) {
+    L.fused = 0;
     int shift = 11;
     while ((std::max<int64_t>(vl->total_q, 1) >> shift) + 1 > kOrderKeys) ++shift;
     L.order_shift = shift;
     L.order_keys = (int32_t)((std::max<int64_t>(vl->total_q, 1) >> shift) + 1);
   }
+  if (L.order_shift != kChunkShift) L.fused = 0;
   size_t off = 0;
   L.hdr = off;        off += sizeof(Hdr);
   L.row_base = off;   off += align_up(sizeof(int32_t) * (vl->batch + 1), 256);
@@ -485,6 +503,7 @@ SchedLayout sched_layout(const msa_varlen_t* vl, int n_sel, int topk) {
   L.items = off;      off += align_up(2 * sizeof(int4) * std::max<int64_t>(1, L.max_items), 256);
   L.okey = off;       off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.max_items), 256);
   L.perm = off;       off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.max_items), 256);
+  L.kstart = off;     off += align_up(sizeof(int32_t) * (L.order_keys + 1), 256);
   L.rowsel = off;     off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.inv_len), 256);
   L.wbase = off;      off += align_up(sizeof(int32_t) * L.n_rows * L.words_per_row, 256);
   L.bitmap = off;     off += align_up(sizeof(uint32_t) * L.n_rows * L.words_per_row, 256);
@@ -511,7 +530,7 @@ hipError_t launch_k2q_csr(const CsrArgs& a, hipStream_t stream) {
                        wk);
   }
 
-  const int32_t G = (int32_t)std::min<int64_t>(L.words_per_row, kUnitWords);
+  const int32_t G = L.piece_words;
   const int64_t n_words = L.n_rows * L.words_per_row;
   CountK cnt{bitmap, n_words, G, blk_tot, blk_items, L.item_q};
   hipLaunchKernelGGL(csr_count_kernel, dim3((unsigned)L.n_blocks), dim3(kThreads), 0, stream, cnt);
@@ -529,7 +548,8 @@ hipError_t launch_k2q_csr(const CsrArgs& a, hipStream_t stream) {
   if (L.order_shift > 0)
     hipLaunchKernelGGL(item_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, hdr,
                        reinterpret_cast<const int32_t*>(a.sched + L.okey), L.order_keys,
-                       L.max_items, reinterpret_cast<int32_t*>(a.sched + L.perm));
+                       L.max_items, reinterpret_cast<int32_t*>(a.sched + L.perm),
+                       reinterpret_cast<int32_t*>(a.sched + L.kstart));
   return hipGetLastError();
 }
 

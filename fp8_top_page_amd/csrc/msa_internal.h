@@ -80,9 +80,18 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 // Queries (CSR entries) per attention work item, at most.
 constexpr int kAttnQCMax = 64;
 
+// Long single-request prefills run the attention as one persistent kernel over
+// query chunks of 2^kChunkShift queries (work items never cross a chunk): the
+// partials of a chunk live in one slot of a ring of kRingSlots chunks, and the
+// chunk's combine tasks run in the same kernel once its items are done.
+constexpr int kChunkShift = 9;
+constexpr bool kChunkedAttention = false;   // off: see sched_layout
+
 struct SchedLayout {
   // byte offsets inside the schedule buffer
-  size_t hdr, row_base, blk_tot, items, okey, perm, rowsel, wbase, bitmap, total;
+  size_t hdr, row_base, blk_tot, items, okey, perm, kstart, rowsel, wbase, bitmap, total;
+  int32_t fused;          // chunked persistent attention (items in query chunks, see above)
+  int32_t piece_words;    // bitmap words per item piece (items never cross one)
   int64_t n_rows;         // n_sel * total_rows
   int64_t words_per_row;  // bitmap words per row (one bit per query slot, padded)
   int64_t n_units;        // bitmap units (64 consecutive words of the row-major bitmap)

@@ -69,6 +69,7 @@ struct AttnK {
   uint8_t* part_o;                 // [entries * HP + 1, 192 B]: 12-bit floats, unnormalised, d permuted
   float2* part_ml;                 // [entries * HP + 1] (max in log2 units, probability sum)
   int32_t trash;                   // partial row written by rows past an item's end
+  uint32_t part_o_bytes, part_ml_bytes;   // chunked kernel: ring sizes (buffer-op bounds)
 };
 
 __device__ __forceinline__ uint32_t byte_of(uint32_t w, int k) { return (w >> (8 * k)) & 0xFFu; }
@@ -342,7 +343,16 @@ __device__ __forceinline__ RowSet<NT> load_rows(const AttnK& a, const Work& w, i
 }
 
 // S^T, softmax and O^T of one row set, written to its partial rows.
-template <int NT>
+// kWt: the split rows go out as write-through (device-coherent, sc1) buffer
+// stores, readable by blocks on other dies once the writer has waited for them.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+typedef unsigned v3u __attribute__((ext_vector_type(3)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+constexpr int kSc1 = 16;                  // buffer-op cache policy: device-scope coherence
+
+template <int NT, bool kWt = false>
 __device__ __forceinline__ void compute_set(const AttnK& a, const RowSet<NT>& r,
                                             const uint8_t* k_lds, const uint8_t* vt_lds,
                                             float zscale, int lane) {
@@ -426,24 +436,41 @@ __device__ __forceinline__ void compute_set(const AttnK& a, const RowSet<NT>& r,
     }
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-      uint3* dst = reinterpret_cast<uint3*>(a.part_o + (int64_t)r.pidx[u] * kRowBytes + grp * 48 +
-                                            half * 24);
-      dst[0] = pack8_f12(o[u][0][0], o[u][0][1], o[u][0][2], o[u][0][3], o[u][1][0], o[u][1][1],
-                         o[u][1][2], o[u][1][3]);
-      dst[1] = pack8_f12(o[u][2][0], o[u][2][1], o[u][2][2], o[u][2][3], o[u][3][0], o[u][3][1],
-                         o[u][3][2], o[u][3][3]);
+      const uint3 p0 = pack8_f12(o[u][0][0], o[u][0][1], o[u][0][2], o[u][0][3], o[u][1][0],
+                                 o[u][1][1], o[u][1][2], o[u][1][3]);
+      const uint3 p1 = pack8_f12(o[u][2][0], o[u][2][1], o[u][2][2], o[u][2][3], o[u][3][0],
+                                 o[u][3][1], o[u][3][2], o[u][3][3]);
+      if constexpr (kWt) {
+        const auto rs = buffer_rsrc(a.part_o, a.part_o_bytes);
+        const int off = r.pidx[u] * kRowBytes + grp * 48 + half * 24;
+        __builtin_amdgcn_raw_buffer_store_b96(v3u{p0.x, p0.y, p0.z}, rs, off, 0, kSc1);
+        __builtin_amdgcn_raw_buffer_store_b96(v3u{p1.x, p1.y, p1.z}, rs, off + 12, 0, kSc1);
+      } else {
+        uint3* dst = reinterpret_cast<uint3*>(a.part_o + (int64_t)r.pidx[u] * kRowBytes + grp * 48 +
+                                              half * 24);
+        dst[0] = p0;
+        dst[1] = p1;
+      }
     }
   }
   // every lane of a row holds the same (m, l)
 #pragma unroll
-  for (int u = 0; u < NT; ++u) a.part_ml[r.pidx[u]] = make_float2(mz[u], l[u]);
+  for (int u = 0; u < NT; ++u) {
+    if constexpr (kWt) {
+      const auto rs = buffer_rsrc(a.part_ml, a.part_ml_bytes);
+      __builtin_amdgcn_raw_buffer_store_b64(v2u{__float_as_uint(mz[u]), __float_as_uint(l[u])}, rs,
+                                            r.pidx[u] * 8, 0, kSc1);
+    } else {
+      a.part_ml[r.pidx[u]] = make_float2(mz[u], l[u]);
+    }
+  }
 }
 
 // All sets of one item on this wave.  Query rows are requested two sets ahead,
 // and the first two sets' rows before `prefetch` issues the next item's loads:
 // memory operations complete in issue order, so a wait for a row requested
 // after the prefetch would also wait for the next page.
-template <int NT, class Prefetch>
+template <int NT, bool kWt = false, class Prefetch>
 __device__ __forceinline__ void run_item(const AttnK& a, const Work& w, const uint8_t* k_lds,
                                          const uint8_t* vt_lds, const int* s_qi, float zscale,
                                          int wave, int lane, Prefetch&& prefetch) {
@@ -460,11 +487,11 @@ __device__ __forceinline__ void run_item(const AttnK& a, const Work& w, const ui
   __builtin_amdgcn_sched_barrier(0);
   for (;;) {
     if (t >= n_tiles) break;
-    compute_set<NT>(a, ra, k_lds, vt_lds, zscale, lane);
+    compute_set<NT, kWt>(a, ra, k_lds, vt_lds, zscale, lane);
     ra = load_rows<NT>(a, w, t + 2 * kStep, n_rows, s_qi, lane);
     t += kStep;
     if (t >= n_tiles) break;
-    compute_set<NT>(a, rb, k_lds, vt_lds, zscale, lane);
+    compute_set<NT, kWt>(a, rb, k_lds, vt_lds, zscale, lane);
     rb = load_rows<NT>(a, w, t + 2 * kStep, n_rows, s_qi, lane);
     t += kStep;
   }
@@ -603,7 +630,19 @@ struct SlotK {
   int64_t max_pos;                // q_slot entries (positions at or past it are skipped)
   int32_t* q_slot;
   uint32_t* mask;                 // [total_q, n_sel]
+  int32_t ring;                   // chunked kernel: entries go to ring slot (query chunk % ring)
 };
+
+constexpr int kRingSlots = 3;     // chunks whose split rows are live at once
+constexpr int kChunkQ = 1 << kChunkShift;
+
+// Split-row entry of (query i, selection head sel, slot s): query-major over the
+// whole batch, or, in the chunked kernel, inside the ring slot of i's chunk.
+__device__ __forceinline__ int64_t split_entry(int64_t i, int sel, int s, int n_sel, bool ring) {
+  if (!ring) return (i * n_sel + sel) * kTopK + s;
+  const int64_t slot = (i >> kChunkShift) % kRingSlots;
+  return ((slot * kChunkQ + (i & (kChunkQ - 1))) * n_sel + sel) * kTopK + s;
+}
 
 __global__ __launch_bounds__(256) void attn_slot_kernel(SlotK a) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -623,7 +662,10 @@ __global__ __launch_bounds__(256) void attn_slot_kernel(SlotK a) {
       const int64_t wi = (int64_t)r * a.words + (local >> 5);
       const int64_t p = (int64_t)a.wbase[wi] + __popc(a.bitmap[wi] & ((1u << (local & 31)) - 1u));
       ok = p >= 0 && p < a.max_pos;
-      if (ok) a.q_slot[p] = (int32_t)e;
+      if (ok) {
+        const int per = a.n_sel * kTopK;
+        a.q_slot[p] = (int32_t)split_entry(i, (int)((e % per) / kTopK), s, a.n_sel, a.ring != 0);
+      }
     }
   }
   const uint64_t bal = __builtin_amdgcn_ballot_w64(ok);
@@ -689,6 +731,253 @@ __global__ __launch_bounds__(1024) void attn_combine_kernel(CombineK a) {
   *reinterpret_cast<uint2*>(dst + 16) = make_uint2(pack2_bf16(o[4], o[5]), pack2_bf16(o[6], o[7]));
 }
 
+// ---------------------------------------------------------------------------
+// Chunked persistent attention (one long request).  Work items never cross a
+// chunk of kChunkQ queries and are ordered by chunk.  The split rows of chunk c
+// go to ring slot c % kRingSlots through write-through stores, so that the
+// memory-side cache (256 MiB), not HBM, holds them until they are merged; the
+// chunk's combine tasks run in the same kernel.  Tasks are dealt to kQueues
+// queues (block b takes from queue b % kQueues, one atomic per task), each in
+// the order
+//   items(0), items(1), combine(0), items(2), combine(1), ..., combine(C - 1)
+// (chunk c's items and combine tasks spread round robin over the queues).  A
+// combine task of chunk c waits until all of c's items are done; an item of
+// chunk c >= kRingSlots waits until chunk c - kRingSlots is merged (its ring
+// slot is free).  Every wait is on tasks that precede the waiting one in every
+// queue, so the kernel completes whatever subset of its blocks is resident.
+// ---------------------------------------------------------------------------
+constexpr int kQueues = 8;
+constexpr int kCombQ = 16;                       // queries per combine task
+constexpr int kCombPerChunk = kChunkQ / kCombQ;
+
+struct QueueK {
+  const int32_t* kstart;          // [chunks + 1] first perm position of each chunk's items
+  int32_t n_chunks;
+  int64_t total_q;
+  int2* queues;                   // [kQueues, qcap] (perm position or -1 - combine task, chunk)
+  int64_t qcap;
+  int32_t* qlen;                  // [kQueues]
+  int32_t* qhead;                 // [kQueues]
+  int32_t* chunk_done;            // [chunks] items finished
+  int32_t* comb_done;             // [chunks] combine tasks finished
+  int32_t* give_up;               // set once a wait ran out (later waits then return at once)
+};
+
+__device__ __forceinline__ int comb_tasks(int64_t total_q, int c) {
+  const int64_t q = min<int64_t>(kChunkQ, total_q - (int64_t)c * kChunkQ);
+  return q > 0 ? (int)((q + kCombQ - 1) / kCombQ) : 0;
+}
+__device__ __forceinline__ int share(int n, int x) {   // members m < n with m % kQueues == x
+  return n > x ? (n - x + kQueues - 1) / kQueues : 0;
+}
+
+__global__ __launch_bounds__(1024) void attn_queue_kernel(QueueK a) {
+  __shared__ int s_wave[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int C = a.n_chunks;
+  const int c = tid;                              // one chunk per thread (C <= 1024)
+  const int n_c = c < C ? a.kstart[c + 1] - a.kstart[c] : 0;
+  const int ct_prev = (c >= 1 && c < C) ? comb_tasks(a.total_q, c - 1) : 0;
+  const int ct_last = (c == C - 1) ? comb_tasks(a.total_q, c) : 0;
+  // the counters are cleared by write-through stores: they are then changed and
+  // read only by device-scope atomics, from every die
+  if (c < C) {
+    __hip_atomic_store(a.chunk_done + c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.comb_done + c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (tid < kQueues) __hip_atomic_store(a.qhead + tid, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(a.give_up, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int x = 0; x < kQueues; ++x) {
+    const int len = share(n_c, x) + share(ct_prev, x) + share(ct_last, x);
+    const int incl = wave_inclusive_scan(len);
+    __syncthreads();
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    int off = incl - len;
+    for (int w = 0; w < wave; ++w) off += s_wave[w];
+    if (tid == 1023) a.qlen[x] = off + len;
+    int2* q = a.queues + (int64_t)x * a.qcap + off;
+    if (c < C) {
+      int k = 0;
+      for (int m = x; m < n_c; m += kQueues) q[k++] = make_int2(a.kstart[c] + m, c);
+      for (int t = x; t < ct_prev; t += kQueues) q[k++] = make_int2(-1 - t, c - 1);
+      for (int t = x; t < ct_last; t += kQueues) q[k++] = make_int2(-1 - t, c);
+    }
+  }
+}
+
+struct FusedK {
+  AttnK a;
+  const int32_t* kstart;
+  const int2* queues;
+  int64_t qcap;
+  const int32_t* qlen;
+  int32_t* qhead;
+  int32_t* chunk_done;
+  int32_t* comb_done;
+  int32_t* give_up;
+  int64_t total_q;
+  int32_t Hq;
+  const uint32_t* mask;
+  const float* v_scale;
+  uint16_t* out;
+  int64_t out_stride;
+};
+
+// Wait until a device-scope counter reaches target, reading it by atomic
+// read-modify-writes (adding 0), the same coherence path as its increments.
+// The wait is bounded in time (s_memrealtime, 100 MHz) and in polls: past
+// kWaitTicks or 2^18 polls the block goes on and sets give_up, after which every wait returns at once, so
+// a broken schedule gives wrong results in a fraction of a second, never a hang.
+constexpr uint64_t kWaitTicks = 20000000;        // 0.2 s
+// Atomic add of 0 that stays an add: a literal 0 lets the compiler turn the
+// read-modify-write into a plain load (an idempotent operation).
+__device__ __forceinline__ int32_t rmw_read(int32_t* p) {
+  int zero = 0;
+  asm volatile("" : "+v"(zero));
+  return __hip_atomic_fetch_add(p, zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_count(int32_t* c, int target, int32_t* give_up) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (int spin = 0;; ++spin) {
+    if (rmw_read(c) >= target) return;
+    if ((spin & 15) == 15) {
+      if (rmw_read(give_up) != 0) return;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks || spin >= (1 << 18)) {
+        __hip_atomic_fetch_or(give_up, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+      }
+    }
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
+// Merge of queries [i0, i0 + n) of a chunk: as attn_combine_kernel, with the
+// split rows read from the chunk's ring slot by device-coherent loads.
+__device__ __forceinline__ void combine_task(const FusedK& f, int64_t i0, int n, int tid) {
+  const AttnK& a = f.a;
+  const auto ro = buffer_rsrc(a.part_o, a.part_o_bytes);
+  const auto rm = buffer_rsrc(a.part_ml, a.part_ml_bytes);
+  const int per_q = f.Hq * 16;
+  for (int u = tid; u < n * per_q; u += kThreads) {
+    const int ql = u / per_q, t = u - ql * per_q;
+    const int64_t i = i0 + ql;
+    const int hq = t >> 4, c = t & 15;
+    const int sel = a.n_sel == 1 ? 0 : hq / a.G;
+    const int hp = a.n_sel == 1 ? hq : hq % a.G;
+    const uint32_t m = f.mask[i * a.n_sel + sel];
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (m != 0u) {
+      const int first = __builtin_ctz(m);
+      const int64_t e0 = split_entry(i, sel, 0, a.n_sel, true);
+      float2 ml[kTopK];
+      uint3 v[kTopK];
+#pragma unroll
+      for (int s = 0; s < kTopK; ++s) {
+        const int r = (int)((e0 + (((m >> s) & 1u) ? s : first)) * a.HP + hp);
+        const v2u x = __builtin_amdgcn_raw_buffer_load_b64(rm, r * 8, 0, kSc1);
+        ml[s] = make_float2(__uint_as_float(x.x), __uint_as_float(x.y));
+        const v3u y = __builtin_amdgcn_raw_buffer_load_b96(ro, r * kRowBytes + 12 * c, 0, kSc1);
+        v[s] = make_uint3(y.x, y.y, y.z);
+      }
+      float M = -INFINITY;
+#pragma unroll
+      for (int s = 0; s < kTopK; ++s)
+        M = ((m >> s) & 1u) ? __builtin_elementwise_maximum(M, ml[s].x) : M;
+      float L = 0.f;
+#pragma unroll
+      for (int s = 0; s < kTopK; ++s) {
+        const float wgt = ((m >> s) & 1u) ? __builtin_amdgcn_exp2f(ml[s].x - M) : 0.f;
+        float x[8];
+        unpack8_f12(v[s], x);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] += wgt * x[k];
+        L += wgt * ml[s].y;
+      }
+      const float fs = L > 0.f ? (f.v_scale ? *f.v_scale : 1.f) / L : 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] *= fs;
+    }
+    uint16_t* dst = f.out + i * f.out_stride + hq * kDim + 32 * (c & 3) + 4 * (c >> 2);
+    *reinterpret_cast<uint2*>(dst) = make_uint2(pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3]));
+    *reinterpret_cast<uint2*>(dst + 16) = make_uint2(pack2_bf16(o[4], o[5]), pack2_bf16(o[6], o[7]));
+  }
+}
+
+template <bool kFp4>
+__global__ __launch_bounds__(kThreads, kBlocksWide) void attn_fused_kernel(FusedK f) {
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kPage * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t vt_lds[kDim * kRowB];
+  __shared__ int s_qi[2 * kAttnQCMax];
+  __shared__ uint2 s_tab[kFp4 ? 256 : 1];
+  __shared__ int2 s_task;
+  const AttnK& a = f.a;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int queue = blockIdx.x % kQueues;
+  const float zscale = a.logit_scale_log2 * (a.q_scale ? *a.q_scale : 1.f) *
+                       (a.k_scale ? *a.k_scale : 1.f);
+  if constexpr (kFp4) s_tab[tid] = staged_magnitudes(tid);
+  typename std::conditional<kFp4, PageRegs4, PageRegs>::type pr;
+  const int qlen = f.qlen[queue];
+  for (;;) {
+    if (tid == 0) {
+      const int t = atomicAdd(&f.qhead[queue], 1);
+      s_task = t < qlen ? f.queues[(int64_t)queue * f.qcap + t] : make_int2(0, -1);
+    }
+    __syncthreads();
+    const int2 task = s_task;
+    __syncthreads();                              // s_task is rewritten next round
+    if (task.y < 0) break;
+    const int chunk = task.y;
+    if (task.x < 0) {                             // combine task
+      if (tid == 0) wait_count(f.chunk_done + chunk, f.kstart[chunk + 1] - f.kstart[chunk], f.give_up);
+      __syncthreads();
+      const int64_t i0 = (int64_t)chunk * kChunkQ + (int64_t)(-1 - task.x) * kCombQ;
+      combine_task(f, i0, (int)min<int64_t>(kCombQ, f.total_q - i0), tid);
+      __syncthreads();                            // every load of the task has returned
+      if (tid == 0) __hip_atomic_fetch_add(f.comb_done + chunk, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      continue;
+    }
+    // work item: the (page, queries) item at perm position task.x, every KV head
+    const int item = a.perm[task.x];
+    const int4 mx = a.items[2 * item], my = a.items[2 * item + 1];
+    if (chunk >= kRingSlots) {                    // the chunk's ring slot must be merged
+      if (tid == 0)
+        wait_count(f.comb_done + (chunk - kRingSlots), comb_tasks(f.total_q, chunk - kRingSlots),
+                   f.give_up);
+      __syncthreads();
+    }
+    Work cur = decode_work(a, (int64_t)item * a.GY, mx, my);
+    fetch_page(pr, a, cur, tid);
+    for (int g = 0; g < a.GY; ++g) {
+      __syncthreads();                            // the previous head is done with LDS
+      if constexpr (kFp4)
+        stage_page(to_e4m3(pr, s_tab), cur, k_lds, vt_lds, s_qi, tid);
+      else
+        stage_page(pr, cur, k_lds, vt_lds, s_qi, tid);
+      __syncthreads();
+      const bool more = g + 1 < a.GY;
+      const Work nxt = more ? decode_work(a, (int64_t)item * a.GY + g + 1, mx, my) : cur;
+      auto prefetch = [&]() {
+        if (more) fetch_page(pr, a, nxt, tid);
+      };
+      const int n_tiles = (cur.count * a.G + 15) >> 4;
+      if (n_tiles >= 2 * kWaves)
+        run_item<2, true>(a, cur, k_lds, vt_lds, s_qi, zscale, wave, lane, prefetch);
+      else
+        run_item<1, true>(a, cur, k_lds, vt_lds, s_qi, zscale, wave, lane, prefetch);
+      cur = nxt;
+    }
+    // the item's split rows are written through before it counts as done
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) __hip_atomic_fetch_add(f.chunk_done + chunk, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 }  // namespace
 
 int device_cu_count() {
@@ -710,17 +999,33 @@ static int64_t partial_rows(const msa_varlen_t* vl, int Hq, int n_sel, int topk)
 }
 
 struct AttnWs {
-  size_t o, ml, slot, mask, total;
+  int64_t rows;                   // split rows (the last one is the trash row)
+  int32_t fused, n_chunks;
+  int64_t qcap;                   // chunked kernel: tasks per queue, at most
+  size_t o, ml, slot, mask, queues, qlen, qhead, chunk_done, comb_done, give_up, total;
 };
 static AttnWs attn_ws(const msa_varlen_t* vl, int Hq, int n_sel, int topk) {
-  const int64_t rows = partial_rows(vl, Hq, n_sel, topk);
+  const SchedLayout L = sched_layout(vl, n_sel, topk);
   const int64_t entries = (int64_t)n_sel * vl->total_q * topk;
   AttnWs w;
+  w.fused = L.fused;
+  w.n_chunks = L.fused ? L.order_keys : 0;
+  // chunked: a ring of kRingSlots chunks of split rows; else every query's
+  w.rows = L.fused ? (int64_t)std::min<int64_t>(kRingSlots, w.n_chunks) * kChunkQ * n_sel * topk *
+                             (Hq / n_sel) + 1
+                   : partial_rows(vl, Hq, n_sel, topk);
+  w.qcap = L.fused ? ceil_div(L.max_items, kQueues) + 6 * (int64_t)w.n_chunks + 8 : 0;
   size_t off = 0;
-  w.o = off;    off += align_up((size_t)(rows * kRowBytes), 256);
-  w.ml = off;   off += align_up((size_t)(rows * sizeof(float2)), 256);
+  w.o = off;    off += align_up((size_t)(w.rows * kRowBytes), 256);
+  w.ml = off;   off += align_up((size_t)(w.rows * sizeof(float2)), 256);
   w.slot = off; off += align_up((size_t)(std::max<int64_t>(entries, 1) * sizeof(int32_t)), 256);
   w.mask = off; off += align_up((size_t)(std::max<int64_t>(entries / topk, 1) * sizeof(uint32_t)), 256);
+  w.queues = off;     off += align_up((size_t)(kQueues * w.qcap * sizeof(int2)), 256);
+  w.qlen = off;       off += 256;
+  w.qhead = off;      off += 256;
+  w.chunk_done = off; off += align_up((size_t)std::max(w.n_chunks, 1) * sizeof(int32_t), 256);
+  w.comb_done = off;  off += align_up((size_t)std::max(w.n_chunks, 1) * sizeof(int32_t), 256);
+  w.give_up = off;    off += 256;
   w.total = off;
   return w;
 }
@@ -733,9 +1038,10 @@ size_t attn_workspace_bytes(const msa_varlen_t* vl, int Hq, int Hkv, int n_sel, 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.vl.total_q == 0) return hipSuccess;
   const SchedLayout& L = a.L;
-  const int64_t rows = partial_rows(&a.vl, a.Hq, a.n_sel, kTopK);
-  if (rows > (int64_t)INT32_MAX) return hipErrorInvalidValue;   // split rows are indexed in 32 bits
   const AttnWs ws = attn_ws(&a.vl, a.Hq, a.n_sel, kTopK);
+  const int64_t rows = ws.rows;
+  if (rows > (int64_t)INT32_MAX) return hipErrorInvalidValue;   // split rows are indexed in 32 bits
+  if (ws.fused && rows * kRowBytes > (int64_t)INT32_MAX) return hipErrorInvalidValue;   // buffer offsets
   uint8_t* wsb = reinterpret_cast<uint8_t*>(a.workspace);
   const int HP = a.Hq / a.n_sel;
 
@@ -751,6 +1057,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   sk.max_pos = L.inv_len;
   sk.q_slot = reinterpret_cast<int32_t*>(wsb + ws.slot);
   sk.mask = reinterpret_cast<uint32_t*>(wsb + ws.mask);
+  sk.ring = ws.fused;
   hipLaunchKernelGGL(attn_slot_kernel, dim3((unsigned)ceil_div(sk.n, 256)), dim3(256), 0, stream, sk);
 
   AttnK k;
@@ -776,6 +1083,44 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   k.part_o = wsb + ws.o;
   k.part_ml = reinterpret_cast<float2*>(wsb + ws.ml);
   k.trash = (int32_t)(rows - 1);
+  k.part_o_bytes = (uint32_t)std::min<int64_t>(rows * kRowBytes, INT32_MAX);
+  k.part_ml_bytes = (uint32_t)std::min<int64_t>(rows * (int64_t)sizeof(float2), INT32_MAX);
+  if (ws.fused) {
+    QueueK qk;
+    qk.kstart = reinterpret_cast<const int32_t*>(a.sched + L.kstart);
+    qk.n_chunks = ws.n_chunks;
+    qk.total_q = a.vl.total_q;
+    qk.queues = reinterpret_cast<int2*>(wsb + ws.queues);
+    qk.qcap = ws.qcap;
+    qk.qlen = reinterpret_cast<int32_t*>(wsb + ws.qlen);
+    qk.qhead = reinterpret_cast<int32_t*>(wsb + ws.qhead);
+    qk.chunk_done = reinterpret_cast<int32_t*>(wsb + ws.chunk_done);
+    qk.comb_done = reinterpret_cast<int32_t*>(wsb + ws.comb_done);
+    qk.give_up = reinterpret_cast<int32_t*>(wsb + ws.give_up);
+    hipLaunchKernelGGL(attn_queue_kernel, dim3(1), dim3(1024), 0, stream, qk);
+    FusedK f;
+    f.a = k;
+    f.kstart = qk.kstart;
+    f.queues = qk.queues;
+    f.qcap = qk.qcap;
+    f.qlen = qk.qlen;
+    f.qhead = qk.qhead;
+    f.chunk_done = qk.chunk_done;
+    f.comb_done = qk.comb_done;
+    f.give_up = qk.give_up;
+    f.total_q = a.vl.total_q;
+    f.Hq = a.Hq;
+    f.mask = sk.mask;
+    f.v_scale = a.v_scale;
+    f.out = a.out;
+    f.out_stride = a.out_stride;
+    const dim3 grid((unsigned)(device_cu_count() * kBlocksWide));
+    if (a.kv_scales)
+      hipLaunchKernelGGL((attn_fused_kernel<true>), grid, dim3(kThreads), 0, stream, f);
+    else
+      hipLaunchKernelGGL((attn_fused_kernel<false>), grid, dim3(kThreads), 0, stream, f);
+    return hipGetLastError();
+  }
   const int64_t max_work = L.max_items * k.GY;
   if (max_work > 0) {
     // Rows per item from the host bound on entries per CSR row (total_q * topk
