@@ -919,14 +919,17 @@ __global__ __launch_bounds__(kThreads, kBlocksWide) void attn_fused_kernel(Fused
                        (a.k_scale ? *a.k_scale : 1.f);
   if constexpr (kFp4) s_tab[tid] = staged_magnitudes(tid);
   typename std::conditional<kFp4, PageRegs4, PageRegs>::type pr;
-  const int qlen = f.qlen[queue];
+  const int qlen = __builtin_amdgcn_readfirstlane(f.qlen[queue]);
   for (;;) {
     if (tid == 0) {
       const int t = atomicAdd(&f.qhead[queue], 1);
       s_task = t < qlen ? f.queues[(int64_t)queue * f.qcap + t] : make_int2(0, -1);
     }
     __syncthreads();
-    const int2 task = s_task;
+    // wave-uniform by construction; readfirstlane makes it so for the compiler
+    // too, so every branch below (each holding barriers) is a scalar branch
+    const int2 task = make_int2(__builtin_amdgcn_readfirstlane(s_task.x),
+                                __builtin_amdgcn_readfirstlane(s_task.y));
     __syncthreads();                              // s_task is rewritten next round
     if (task.y < 0) break;
     const int chunk = task.y;
@@ -941,7 +944,7 @@ __global__ __launch_bounds__(kThreads, kBlocksWide) void attn_fused_kernel(Fused
       continue;
     }
     // work item: the (page, queries) item at perm position task.x, every KV head
-    const int item = a.perm[task.x];
+    const int item = __builtin_amdgcn_readfirstlane(a.perm[task.x]);
     const int4 mx = a.items[2 * item], my = a.items[2 * item + 1];
     if (chunk >= kRingSlots) {                    // the chunk's ring slot must be merged
       if (tid == 0)
