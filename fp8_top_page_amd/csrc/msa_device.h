@@ -67,6 +67,12 @@ __device__ __forceinline__ float sum_across_groups(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Raw buffer resource over `bytes` bytes at p: buffer loads past the end return
+// zero instead of reading memory, and stores past it are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
 // Monotone map float -> uint32 (larger float, larger key).  NaN maps to 0, below
 // every number (-inf maps to 0x007FFFFF).
 __device__ __forceinline__ uint32_t float_key(float f) {

@@ -345,9 +345,6 @@ __device__ __forceinline__ RowSet<NT> load_rows(const AttnK& a, const Work& w, i
 // S^T, softmax and O^T of one row set, written to its partial rows.
 // kWt: the split rows go out as write-through (device-coherent, sc1) buffer
 // stores, readable by blocks on other dies once the writer has waited for them.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
-}
 typedef unsigned v3u __attribute__((ext_vector_type(3)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 constexpr int kSc1 = 16;                  // buffer-op cache policy: device-scope coherence

@@ -7,10 +7,10 @@
 // pages (vLLM PR 64631, Details); here equal scores go to the lower page index,
 // which makes the result deterministic.
 //
-// Rows of up to 512 visible pages: one wave per query (keys in registers, every
-// key >= the wave bound fits the wave's LDS list, so no fallback is needed).
-// Longer rows: one 256-thread block per query:
-//  1. each lane takes the max orderable key over its strided share of the row;
+// Rows of up to 512 visible pages: one wave per query, four queries per wave
+// (keys in registers, every key >= the wave bound fits the wave's LDS list, so
+// no fallback is needed).  Longer rows: one 256-thread block per query:
+//  1. each lane takes the max over its strided share of the row;
 //  2. within each wave, the ksel-th largest lane maximum is a lower bound tau_w
 //     on the ksel-th largest key of the row (ksel distinct elements reach it);
 //     tau = max over waves is still such a bound;
@@ -19,6 +19,9 @@
 //  If too many keys tie at the top for the LDS list, a bisection over the
 //  32-bit key space finds the exact ksel-th key instead and equal keys are
 //  admitted in page order by a block scan.
+// Rows of 2049..8192 candidates take a leaner form of this (topk_row_kernel:
+// raw scores in registers, bound from the top 16 bits of the lane maxima and
+// verified by counting) so that a 2048-query batch is resident at once.
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -92,6 +95,88 @@ __device__ __forceinline__ void load_keys(const float* row, int c0, int ncand, i
       key[k] = j < ncand ? float_key(row[j]) : 0u;
     }
   }
+}
+
+// float_key of the float with bits u, computed without branches; 0 when !valid.
+__device__ __forceinline__ uint32_t key_bits(uint32_t u, bool valid) {
+  const uint32_t k = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+  return (valid && (u & 0x7FFFFFFFu) <= 0x7F800000u) ? k : 0u;
+}
+
+// Exact rank of up to 64 unique packed keys held one per lane of a wave (lanes
+// >= c hold none): each lane counts the larger keys, read lane by lane.
+__device__ __forceinline__ void rank_in_wave(uint64_t me, int c, int ksel, int f, int32_t* out) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t me_lo = (uint32_t)me, me_hi = (uint32_t)(me >> 32);
+  int r = 0;
+  for (int o = 0; o < c; ++o) {
+    const uint64_t other = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)me_hi, o) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)me_lo, o);
+    r += other > me ? 1 : 0;
+  }
+  if (lane < c && r < ksel) out[f + r] = (int)~me_lo;
+}
+
+// Exact rank of c unique packed candidates: the ksel best go to out[f ..].
+__device__ __forceinline__ void rank_candidates(const uint64_t* c_pk, int c, int ksel, int f,
+                                                int32_t* out) {
+  for (int e = threadIdx.x; e < c; e += kBlock) {
+    const uint64_t me = c_pk[e];
+    int r = 0;
+    int o = 0;
+    for (; o + 8 <= c; o += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r += c_pk[o + u] > me ? 1 : 0;
+    }
+    for (; o < c; ++o) r += c_pk[o] > me ? 1 : 0;
+    if (r < ksel) out[f + r] = (int)~(uint32_t)me;
+  }
+}
+
+// Many keys tie near the top (more candidates than the LDS list holds): find
+// the exact ksel-th largest key T by bisection over the 32-bit key space, list
+// the keys > T (fewer than ksel) and then the lowest pages with key == T, and
+// rank them.  Every thread of the block calls it.
+__device__ __noinline__ void exact_select(const TopkK& a, const float* row, int ncand, int ksel,
+                                          int f, int32_t* out, uint64_t* c_pk, int* red,
+                                          int* n_cand, int* n_eq_taken) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t t = T | (1u << bit);
+    int cnt = 0;
+    for (int j = tid; j < ncand; j += kBlock) cnt += float_key(row[j]) >= t ? 1 : 0;
+    cnt = block_sum(cnt, red);
+    if (cnt >= ksel) T = t;
+  }
+  __syncthreads();
+  if (tid == 0) { *n_cand = 0; *n_eq_taken = 0; }
+  __syncthreads();
+  for (int j = tid; j < ncand; j += kBlock) {
+    const uint32_t kj = float_key(row[j]);
+    if (kj > T) c_pk[atomicAdd(n_cand, 1)] = pack_key(kj, j);
+  }
+  __syncthreads();
+  const int need = ksel - *n_cand;
+  for (int base = 0; base < ncand; base += kBlock) {
+    const int j = base + tid;
+    const int is_eq = (j < ncand && float_key(row[j]) == T) ? 1 : 0;
+    // exclusive prefix of is_eq over the block in page order
+    int incl = wave_inclusive_scan(is_eq);
+    __syncthreads();
+    if (lane == 63) red[wave] = incl;
+    __syncthreads();
+    int off = *n_eq_taken;
+    for (int w = 0; w < wave; ++w) off += red[w];
+    const int r = off + incl - is_eq;
+    if (is_eq && r < need) c_pk[atomicAdd(n_cand, 1)] = pack_key(T, j);
+    __syncthreads();
+    if (tid == kBlock - 1) *n_eq_taken = off + incl;
+    __syncthreads();
+    if (*n_eq_taken >= need) break;
+  }
+  __syncthreads();
+  rank_candidates(c_pk, *n_cand, ksel, f, out);
 }
 
 // KPT keys per thread are held in registers: rows of up to kBlock * KPT
@@ -195,143 +280,306 @@ __global__ __launch_bounds__(kBlock) void topk_kernel(TopkK a) {
   int c = n_cand;
 
   if (c > kCap) {
-    // Many keys tie near the top: find the exact ksel-th largest key T.
-    uint32_t T = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t t = T | (1u << bit);
-      int cnt = 0;
-      for (int j = tid; j < ncand; j += kBlock) cnt += float_key(row[j]) >= t ? 1 : 0;
-      cnt = block_sum(cnt, red);
-      if (cnt >= ksel) T = t;
-    }
-    // keys > T (fewer than ksel), then the lowest pages with key == T
-    if (tid == 0) { n_cand = 0; n_eq_taken = 0; }
-    __syncthreads();
-    for (int j = tid; j < ncand; j += kBlock) {
-      const uint32_t kj = float_key(row[j]);
-      if (kj > T) c_pk[atomicAdd(&n_cand, 1)] = pack_key(kj, j);
-    }
-    __syncthreads();
-    const int need = ksel - n_cand;
-    for (int base = 0; base < ncand; base += kBlock) {
-      const int j = base + tid;
-      const int is_eq = (j < ncand && float_key(row[j]) == T) ? 1 : 0;
-      // exclusive prefix of is_eq over the block in page order
-      int incl = wave_inclusive_scan(is_eq);
-      __syncthreads();
-      if (lane == 63) red[wave] = incl;
-      __syncthreads();
-      int off = n_eq_taken;
-      for (int w = 0; w < wave; ++w) off += red[w];
-      const int r = off + incl - is_eq;
-      if (is_eq && r < need) c_pk[atomicAdd(&n_cand, 1)] = pack_key(T, j);
-      __syncthreads();
-      if (tid == kBlock - 1) n_eq_taken = off + incl;
-      __syncthreads();
-      if (n_eq_taken >= need) break;
-    }
-    __syncthreads();
-    c = n_cand;
+    exact_select(a, row, ncand, ksel, f, out, c_pk, red, &n_cand, &n_eq_taken);
+    return;
   }
-
   // 4. exact rank among candidates (packed keys are unique)
-  for (int e = tid; e < c; e += kBlock) {
-    const uint64_t me = c_pk[e];
-    int r = 0;
-    int o = 0;
-    for (; o + 8 <= c; o += 8) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) r += c_pk[o + u] > me ? 1 : 0;
-    }
-    for (; o < c; ++o) r += c_pk[o] > me ? 1 : 0;
-    if (r < ksel) out[f + r] = (int)~(uint32_t)me;
-  }
+  rank_candidates(c_pk, c, ksel, f, out);
 }
 
-// One wave per query for rows of at most 64 * KPT candidates.  Lane l owns pages
-// 256k + 4l + {0..3} (16-byte loads); the wave bound is taken as in the block
-// kernel and every key >= it (at most 64 * KPT) is ranked from the wave's LDS list.
-template <int KPT>
-__global__ __launch_bounds__(kBlock) void topk_wave_kernel(TopkK a) {
-  static_assert(KPT % 4 == 0, "four keys per 16-byte load");
-  constexpr int kWaves = kBlock / 64;
-  constexpr int kList = 64 * KPT;
-  __shared__ uint64_t c_pk[kWaves][kList];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t i = (int64_t)blockIdx.x * kWaves + wave;
-  if (i >= a.total_q) return;
+// Rows of 2,049 .. kBlock * KPT candidates, every score read once and kept as
+// loaded (thread t owns pages 256k + t), as dword buffer
+// loads over the row's ncand candidates: past them a load returns 0.0, which
+// may enter the lane maxima but never the list (the collection below checks
+// the page where it could).  So the bound tau taken from the lane maxima is
+// checked instead of trusted: every candidate score >= tau is listed, and only
+// if at least ksel were found (so the ksel-th best is >= tau, and with it all
+// of the top ksel) is the list ranked; otherwise the exact search runs.
+// Scores compare as floats up to the list (NaN never reaches it; +0.0 and -0.0
+// both do when tau is a zero), and the list is ranked by orderable key and
+// page as everywhere.
+constexpr int kWaveCap = 64;      // listed candidates per wave
+
+struct RowSmem {
+  uint64_t c_pk[kBlock / 64 * kWaveCap];
+  uint32_t c_xb[kBlock / 64 * kWaveCap];   // listed (score bits, page) before packing
+  int c_j[kBlock / 64 * kWaveCap];
+  uint64_t c_all[64];
+  uint32_t wave_tau[kBlock / 64];
+  int s_cnt[kBlock / 64];
+  int red[kBlock / 64];
+  int n_cand;
+  int n_eq_taken;
+};
+
+struct RowQuery {
+  const float* row;
+  int32_t* out;
+  int v, k_all, f, ksel, ncand;
+};
+
+__device__ __forceinline__ RowQuery row_query(const TopkK& a, int64_t i) {
+  RowQuery q;
   const int b = find_request(a.cu_q, a.batch, i);
   const int cq0 = a.cu_q[b];
   const int sq = a.cu_q[b + 1] - cq0;
   const int sk = a.cu_k[b + 1] - a.cu_k[b];
   const int pos = sk - sq + (int)(i - cq0);
-  const int v = min(pos / kPage + 1, a.max_pages);
-  const int k_all = min(kTopK, v);
-  const int f = min(a.n_local, k_all);
-  const int ksel = k_all - f;
-  const int ncand = v - f;
-  int32_t* out = a.out + i * a.out_stride;
-  const float* row = a.scores + i * a.ld;
-  const bool vec_ok = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+  q.v = min(pos / kPage + 1, a.max_pages);
+  q.k_all = min(kTopK, q.v);
+  q.f = min(a.n_local, q.k_all);
+  q.ksel = q.k_all - q.f;
+  q.ncand = q.v - q.f;
+  q.row = a.scores + i * a.ld;
+  q.out = a.out + i * a.out_stride;
+  return q;
+}
 
-  if (lane < kTopK) {
-    if (lane < f) out[lane] = v - 1 - lane;
-    else if (lane >= k_all) out[lane] = -1;
+// Selection for one query whose candidate scores x the block holds (thread t
+// pages 256k + t); every thread of the block calls it.
+template <int KPT>
+__device__ __forceinline__ void select_row(const TopkK& a, const RowQuery& q, const float (&x)[KPT],
+                                           RowSmem& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ksel = q.ksel, ncand = q.ncand, f = q.f;
+  int32_t* out = q.out;
+
+  // 1. lane maximum (NaN-propagating: a lane holding a NaN drops out of the bound)
+  float mf = x[0];
+#pragma unroll
+  for (int k = 1; k + 1 < KPT; k += 2)
+    mf = __builtin_elementwise_maximum(mf, __builtin_elementwise_maximum(x[k], x[k + 1]));
+  if constexpr (KPT % 2 == 0) mf = __builtin_elementwise_maximum(mf, x[KPT - 1]);
+  const uint32_t m = float_key(mf) >> 16;
+
+  // 2. wave bound: the ksel-th largest top half of the lane maxima; the block
+  //    takes the largest, as a float (the least float with that top half)
+  uint32_t tw = 0;
+  for (int bit = 15; bit >= 0; --bit) {
+    const uint32_t t = tw | (1u << bit);
+    if ((int)__popcll(__ballot(m >= t)) >= ksel) tw = t;
   }
-  if (ksel == 0) return;
+  if (lane == 0) sm.wave_tau[wave] = tw;
+  __syncthreads();
+  uint32_t tk = 0;
+#pragma unroll
+  for (int w = 0; w < kBlock / 64; ++w) tk = max(tk, sm.wave_tau[w]);
+  tk <<= 16;
+  const float tau = __uint_as_float((tk & 0x80000000u) ? (tk & 0x7FFFFFFFu) : ~tk);
 
-  uint32_t key[KPT];
+  // 3. list every candidate score >= tau in the wave's part of the list: one
+  //    compare per key, and only key slots where some lane has one do more.
+  //    Entries go in as score bits and page; each lane then packs the entry
+  //    of its own index into its key.  With tau > 0 no load past the
+  //    candidates (0.0) can reach it, so the page check is needed only else.
+  const bool check_page = !(tau > 0.f);
+  int n_w = 0;                              // wave-uniform
 #pragma unroll
-  for (int k4 = 0; k4 < KPT / 4; ++k4) {
-    const int j = k4 * 256 + lane * 4;
-    if (vec_ok && j + 3 < ncand) {
-      const float4 x = *reinterpret_cast<const float4*>(row + j);
-      key[4 * k4 + 0] = float_key(x.x);
-      key[4 * k4 + 1] = float_key(x.y);
-      key[4 * k4 + 2] = float_key(x.z);
-      key[4 * k4 + 3] = float_key(x.w);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) key[4 * k4 + e] = (j + e < ncand) ? float_key(row[j + e]) : 0u;
+  for (int k = 0; k < KPT; ++k) {
+    const bool hit = x[k] >= tau;
+    uint64_t bal = __ballot(hit);
+    if (bal != 0u) {
+      const int j = k * kBlock + tid;
+      const bool cand = hit && (!check_page || j < ncand);
+      if (check_page) bal = __ballot(cand);
+      const int off = n_w + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      if (cand && off < kWaveCap) {
+        sm.c_xb[wave * kWaveCap + off] = __float_as_uint(x[k]);
+        sm.c_j[wave * kWaveCap + off] = j;
+      }
+      n_w += (int)__popcll(bal);
     }
   }
-  uint32_t m = 0;
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) m = max(m, key[k]);
-
-  // the ksel-th largest lane maximum: ksel keys of the row reach it
-  uint32_t tau = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t t = tau | (1u << bit);
-    if ((int)__popcll(__ballot(m >= t)) >= ksel) tau = t;
+  if (lane < min(n_w, kWaveCap)) {
+    const int e = wave * kWaveCap + lane;
+    sm.c_pk[e] = pack_key(float_key(__uint_as_float(sm.c_xb[e])), sm.c_j[e]);
   }
-
-  // every candidate key >= tau goes to the list (at most 64 * KPT of them);
-  // slots past ncand are skipped by their page index
-  int mine = 0;
+  if (lane == 0) sm.s_cnt[wave] = n_w;
+  __syncthreads();
+  int c = 0;
+  bool over = false;
 #pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    const int j = (k >> 2) * 256 + lane * 4 + (k & 3);
-    mine += (j < ncand && key[k] >= tau) ? 1 : 0;
+  for (int w = 0; w < kBlock / 64; ++w) {
+    c += sm.s_cnt[w];
+    over = over || sm.s_cnt[w] > kWaveCap;
   }
-  const int incl = wave_inclusive_scan(mine);
-  const int c = __shfl(incl, 63);
-  int slot = incl - mine;
+  if (over || c < ksel) {
+    exact_select(a, q.row, ncand, ksel, f, out, sm.c_pk, sm.red, &sm.n_cand, &sm.n_eq_taken);
+  } else if (c <= 64) {
+    // 4. exact rank (listed keys are unique).  Up to 64: the four wave lists
+    //    are packed into c_all, candidate e = 16w + (lane % 16) of wave w is
+    //    compared by the lane's quarter (lane / 16) against entries 16q ..
+    //    16q + 15, and the four counts are summed across the quarters.
+    int pre = 0;
 #pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    const int j = (k >> 2) * 256 + lane * 4 + (k & 3);
-    if (j < ncand && key[k] >= tau) c_pk[wave][slot++] = pack_key(key[k], j);
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-
-  // exact rank among the candidates (packed keys are unique)
-  for (int e = lane; e < c; e += 64) {
-    const uint64_t me = c_pk[wave][e];
+    for (int w = 0; w < kBlock / 64; ++w) pre += w < wave ? sm.s_cnt[w] : 0;
+    if (lane < n_w) sm.c_all[pre + lane] = sm.c_pk[wave * kWaveCap + lane];
+    __syncthreads();
+    const int e = 16 * wave + (lane & 15), qt = lane >> 4;
+    const uint64_t me = sm.c_all[min(e, c - 1)];
     int r = 0;
-    for (int o = 0; o < c; ++o) r += c_pk[wave][o] > me ? 1 : 0;
-    if (r < ksel) out[f + r] = (int)~(uint32_t)me;
+#pragma unroll
+    for (int o = 0; o < 16; ++o) {          // all 16 reads in flight together
+      const int idx = 16 * qt + o;
+      r += (idx < c && sm.c_all[min(idx, 63)] > me) ? 1 : 0;
+    }
+    r = (int)sum_across_groups((float)r);
+    if (e < c && qt == 0 && r < ksel) out[f + r] = (int)~(uint32_t)me;
+  } else {
+    // more: thread t takes entry t of the four wave lists and counts the
+    // larger entries of all four
+    const int w = tid / kWaveCap, o = tid % kWaveCap;
+    if (o < sm.s_cnt[w]) {
+      const uint64_t me = sm.c_pk[tid];
+      int r = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < kBlock / 64; ++w2) {
+        const int n2 = sm.s_cnt[w2];
+        const uint64_t* l2 = sm.c_pk + w2 * kWaveCap;
+        for (int o2 = 0; o2 < n2; ++o2) r += l2[o2] > me ? 1 : 0;
+      }
+      if (r < ksel) out[f + r] = (int)~(uint32_t)me;
+    }
+  }
+}
+
+// NQ consecutive queries per block: the loads of all NQ rows go out first
+// (dword buffer loads over each row's ncand candidates), then the block
+// selects for one query after another.  One query per block measured fastest
+// on 2048-query batches (all of them resident at once, eight blocks per CU);
+// two per block, four blocks per CU, measured 20 % slower.
+template <int KPT, int NQ>
+__global__ __launch_bounds__(kBlock, 8 / NQ) void topk_row_kernel(TopkK a) {
+  __shared__ RowSmem sm;
+  const int tid = threadIdx.x;
+  const int64_t i0 = (int64_t)blockIdx.x * NQ;
+  RowQuery q[NQ];
+  float x[NQ][KPT];
+#pragma unroll
+  for (int qq = 0; qq < NQ; ++qq) {
+    // a query past the batch repeats the last one; nothing of it is written
+    q[qq] = row_query(a, i0 + qq < a.total_q ? i0 + qq : a.total_q - 1);
+    const auto rs = buffer_rsrc(q[qq].row, (uint32_t)max(q[qq].ncand, 0) * 4u);
+#pragma unroll
+    for (int k = 0; k < KPT; ++k)
+      x[qq][k] = __builtin_bit_cast(float,
+                                    __builtin_amdgcn_raw_buffer_load_b32(rs, (k * kBlock + tid) * 4, 0, 0));
+  }
+#pragma unroll
+  for (int qq = 0; qq < NQ; ++qq) {
+    if (i0 + qq >= a.total_q) break;
+    const RowQuery& r = q[qq];
+    if (tid < kTopK) {
+      if (tid < r.f) r.out[tid] = r.v - 1 - tid;
+      else if (tid >= r.k_all) r.out[tid] = -1;
+    }
+    if (r.ksel == 0) continue;
+    select_row<KPT>(a, r, x[qq], sm);
+    __syncthreads();                        // the lists are reused by the next query
+  }
+}
+
+// One wave per query for rows of at most 64 * KPT candidates, NQ consecutive
+// queries per wave: the loads of all NQ rows go out first (lane l owns pages
+// 64k + l, one dword buffer load each over the row's first min(ld, max_pages)
+// entries; keys past the candidates are masked), so the wave waits for memory
+// once and then selects for its queries one after another.  Per query the
+// bound is the ksel-th largest lane maximum of the keys' top 16 bits (ksel
+// keys reach it, so every key of the top ksel does too); every key whose top
+// half reaches it (at most 64 * KPT) is ranked exactly from the wave's LDS list.
+template <int KPT, int NQ>
+__global__ __launch_bounds__(kBlock) void topk_wave_kernel(TopkK a) {
+  constexpr int kWaves = kBlock / 64;
+  constexpr int kList = 64 * KPT;
+  __shared__ uint64_t c_pk[kWaves][kList];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t i0 = ((int64_t)blockIdx.x * kWaves + wave) * NQ;
+  if (i0 >= a.total_q) return;
+  const int row_len = a.ld < (int64_t)a.max_pages ? (int)a.ld : a.max_pages;
+
+  uint32_t x[NQ][KPT];
+#pragma unroll
+  for (int qq = 0; qq < NQ; ++qq) {
+    // queries past the batch re-read the last row; their results are not written
+    const int64_t i = i0 + qq < a.total_q ? i0 + qq : a.total_q - 1;
+    const auto rs = buffer_rsrc(a.scores + i * a.ld, (uint32_t)row_len * 4u);
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) x[qq][k] = __builtin_amdgcn_raw_buffer_load_b32(rs, (k * 64 + lane) * 4, 0, 0);
+  }
+  // the empty asm keeps every load unconditional
+#pragma unroll
+  for (int qq = 0; qq < NQ; ++qq)
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) asm volatile("" : "+v"(x[qq][k]));
+
+#pragma unroll
+  for (int qq = 0; qq < NQ; ++qq) {
+    const int64_t i = i0 + qq;
+    if (i >= a.total_q) break;
+    const int b = find_request(a.cu_q, a.batch, i);
+    const int cq0 = a.cu_q[b];
+    const int sq = a.cu_q[b + 1] - cq0;
+    const int sk = a.cu_k[b + 1] - a.cu_k[b];
+    const int pos = sk - sq + (int)(i - cq0);
+    const int v = min(pos / kPage + 1, a.max_pages);
+    const int k_all = min(kTopK, v);
+    const int f = min(a.n_local, k_all);
+    const int ksel = k_all - f;
+    const int ncand = v - f;
+    int32_t* out = a.out + i * a.out_stride;
+    if (lane < kTopK) {
+      if (lane < f) out[lane] = v - 1 - lane;
+      else if (lane >= k_all) out[lane] = -1;
+    }
+    if (ksel == 0) continue;
+
+    const int lim = ncand - lane;           // page 64k + lane is a candidate iff 64k < lim
+    uint32_t key[KPT];
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      key[k] = key_bits(x[qq][k], k * 64 < lim);
+      m = max(m, key[k]);
+    }
+    // the ksel-th largest lane maximum of the top halves
+    uint32_t t16 = 0;
+    m >>= 16;
+    for (int bit = 15; bit >= 0; --bit) {
+      const uint32_t t = t16 | (1u << bit);
+      if ((int)__popcll(__ballot(m >= t)) >= ksel) t16 = t;
+    }
+    const uint32_t tau = t16 << 16;
+
+    // every candidate key >= tau goes to the list
+    int mine = 0;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) mine += (k * 64 < lim && key[k] >= tau) ? 1 : 0;
+    const int incl = wave_inclusive_scan(mine);
+    const int c = __shfl(incl, 63);
+    int slot = incl - mine;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k)
+      if (k * 64 < lim && key[k] >= tau) c_pk[wave][slot++] = pack_key(key[k], k * 64 + lane);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+
+    // exact rank among the candidates (packed keys are unique): in registers
+    // for up to 64 of them, else from the list
+    if (c <= 64) {
+      rank_in_wave(lane < c ? c_pk[wave][lane] : 0u, c, ksel, f, out);
+    } else {
+      for (int e = lane; e < c; e += 64) {
+        const uint64_t me = c_pk[wave][e];
+        int r = 0;
+        for (int o = 0; o < c; ++o) r += c_pk[wave][o] > me ? 1 : 0;
+        if (r < ksel) out[f + r] = (int)~(uint32_t)me;
+      }
+    }
+    // the list is rewritten for the next query
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   }
 }
 
@@ -352,9 +600,10 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   k.out_stride = a.out_stride;
   const int need = std::max(1, a.vl.max_pages);   // candidates per query, at most
   if (need <= 512) {
-    const dim3 wgrid((unsigned)ceil_div(a.vl.total_q, kBlock / 64));
-    if (need <= 256) hipLaunchKernelGGL(topk_wave_kernel<4>, wgrid, dim3(kBlock), 0, stream, k);
-    else hipLaunchKernelGGL(topk_wave_kernel<8>, wgrid, dim3(kBlock), 0, stream, k);
+    constexpr int kNQ = 4;                        // queries per wave
+    const dim3 wgrid((unsigned)ceil_div(a.vl.total_q, (int64_t)(kBlock / 64) * kNQ));
+    if (need <= 256) hipLaunchKernelGGL((topk_wave_kernel<4, kNQ>), wgrid, dim3(kBlock), 0, stream, k);
+    else hipLaunchKernelGGL((topk_wave_kernel<8, kNQ>), wgrid, dim3(kBlock), 0, stream, k);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)a.vl.total_q);
@@ -362,7 +611,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   else if (need <= kBlock * 2) hipLaunchKernelGGL(topk_kernel<2>, grid, dim3(kBlock), 0, stream, k);
   else if (need <= kBlock * 4) hipLaunchKernelGGL(topk_kernel<4>, grid, dim3(kBlock), 0, stream, k);
   else if (need <= kBlock * 8) hipLaunchKernelGGL(topk_kernel<8>, grid, dim3(kBlock), 0, stream, k);
-  else if (need <= kBlock * 16) hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(kBlock), 0, stream, k);
+  else if (need <= kBlock * 16) hipLaunchKernelGGL((topk_row_kernel<16, 1>), grid, dim3(kBlock), 0, stream, k);
+  else if (need <= kBlock * 32) hipLaunchKernelGGL((topk_row_kernel<32, 1>), grid, dim3(kBlock), 0, stream, k);
   else hipLaunchKernelGGL(topk_kernel<32>, grid, dim3(kBlock), 0, stream, k);
   return hipGetLastError();
 }

@@ -272,6 +272,47 @@ def test_topk_rows_longer_than_one_chunk(kind):
     check_topk_exact_on_gpu_scores(meta, s, to_np(out))
 
 
+@pytest.mark.parametrize("pages", [3000, 8000])
+@pytest.mark.parametrize("kind", ["near_top", "near_many", "negative"])
+def test_topk_keys_equal_in_their_top_bits(pages, kind):
+    """Rows of 2,049..8,192 pages, whose selection keeps only the top 16 bits of
+    each key until the exact rank: scores that agree in those bits and differ
+    below them (40 such pages at the top; 3,000 of them, more than the
+    candidate list holds; all-negative rows with near ties).  The result must
+    equal the oracle's selection on the same scores."""
+    from types import SimpleNamespace
+    from fp8_top_page_amd import msa_topk_select
+    from fp8_top_page_amd.pipeline import DeviceBatch
+    print(f"\n[parity] top-k near ties: {kind}, {pages} pages", flush=True)
+    sq, sk = np.array([16, 8]), np.array([pages * 128, pages * 64 + 77])
+    cu_q = np.concatenate([[0], np.cumsum(sq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(sk)]).astype(np.int32)
+    pg = (sk + 127) // 128
+    bt = np.zeros((2, pg.max()), np.int32)                  # never read by the selection
+    db = DeviceBatch(cu_q, cu_k, bt, np.zeros((24, 1, 128), np.uint8),
+                     np.zeros((1, 128, 128), np.uint8), 1.0, 1.0)
+    meta = SimpleNamespace(cu_seqlens_q=cu_q, cu_seqlens_k=cu_k, total_q=24)
+    rng = np.random.default_rng(pages + len(kind))
+    ld = (db.max_pages + 3) // 4 * 4 + 4
+    s = rng.standard_normal((24, ld)).astype(np.float32)
+    n_tied = 40 if kind == "near_top" else 3000
+    for r in range(24):
+        b = 0 if r < 16 else 1
+        vis = (int(sk[b]) - int(sq[b]) + (r - int(cu_q[b]))) // 128 + 1
+        cols = rng.choice(vis, size=min(n_tied, vis - 1), replace=False)
+        # 5.0 plus multiples of 2^-20 of it: equal top 16 bits, distinct low bits
+        s[r, cols] = np.float32(5.0) * (1 + rng.integers(0, 60, size=len(cols)) * 2.0 ** -20)
+    if kind == "negative":
+        s = -np.abs(s) - np.float32(1.0)
+        s[:, ::3] = np.float32(-1.25) * (1 + rng.integers(0, 60, size=s[:, ::3].shape) * 2.0 ** -20)
+    s = s.astype(np.float32)
+    st = torch.from_numpy(s).cuda()
+    out = torch.full((24, 16), -7, dtype=torch.int32, device="cuda")
+    msa_topk_select(db.vl, st, 16, 1, out)
+    torch.cuda.synchronize()
+    check_topk_exact_on_gpu_scores(meta, s, to_np(out))
+
+
 def test_per_kv_head_selection_and_random_topk():
     """One selection per KV head, drawn like the benchmark script's case():
     CSR and attention against the oracle on that selection."""
