@@ -112,15 +112,6 @@ __global__ __launch_bounds__(kThreads) void csr_words_kernel(WordsK a) {
       a.row_base[b] = base;
       if (b == a.batch - 1) a.row_base[a.batch] = base + pages;
     }
-    // the CSR row of every selection slot of this block's queries
-    for (int e = tid; e < n_e; e += kThreads) {
-      const int local = 32 * w + e / per_q;
-      if (local >= sq) continue;
-      const int g = (e % per_q) / kTopK, sl = e % kTopK;
-      const int j = a.topk[(int64_t)(q0 + local) * a.tq + (int64_t)g * a.th + sl];
-      a.rowsel[(int64_t)(q0 + local) * per_q + e % per_q] =
-          (j < 0 || j >= pages || base + j >= a.total_rows) ? -1 : g * a.total_rows + base + j;
-    }
     // the last request's blocks also clear any rows past the requests' pages
     if (b == a.batch - 1) {
       const int end = base + pages;
@@ -129,18 +120,21 @@ __global__ __launch_bounds__(kThreads) void csr_words_kernel(WordsK a) {
           a.bitmap[((int64_t)g * a.total_rows + rr) * a.words + w] = 0u;
     }
   }
-  const int n_r = min(kWordRows, rows - r0);
-  if (n_r <= 0) return;
+  const int n_r = max(min(kWordRows, rows - r0), 0);
   for (int k = tid; k < n_r; k += kThreads) s_bits[k] = 0u;
   __syncthreads();
+  // each selection entry of the block's queries once: its CSR row (the first
+  // row-chunk block writes the (query, slot) -> row table) and its bit
   for (int e = tid; e < n_e; e += kThreads) {
-    const int ql = e / per_q, g = (e % per_q) / kTopK, sl = e % kTopK;
+    const int ql = e / per_q;
     const int local = 32 * w + ql;
     if (local >= sq) continue;
+    const int g = (e % per_q) / kTopK, sl = e % kTopK;
     const int j = a.topk[(int64_t)(q0 + local) * a.tq + (int64_t)g * a.th + sl];
-    if (j < 0 || j >= pages || base + j >= a.total_rows) continue;
+    const bool ok = !(j < 0 || j >= pages || base + j >= a.total_rows);
+    if (c == 0) a.rowsel[(int64_t)(q0 + local) * per_q + e % per_q] = ok ? g * a.total_rows + base + j : -1;
     const int r = g * pages + j - r0;
-    if (r >= 0 && r < n_r) atomicOr(&s_bits[r], 1u << ql);
+    if (ok && r >= 0 && r < n_r) atomicOr(&s_bits[r], 1u << ql);
   }
   __syncthreads();
   for (int k = tid; k < n_r; k += kThreads) {
@@ -156,8 +150,7 @@ __global__ __launch_bounds__(kThreads) void csr_words_kernel(WordsK a) {
 // one row; a "piece" is the part of one row inside one unit, G = min(words, 64)
 // lanes.  Work items never cross pieces.
 __device__ __forceinline__ int piece_sum(int x, int G) {   // sum over aligned groups of G lanes
-  for (int m = 1; m < G; m <<= 1) x += __shfl_xor(x, m);
-  return x;
+  return group_sum(x, G);
 }
 
 struct CountK {
@@ -306,9 +299,19 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
     base_e = a.blk_tot[blk];
     base_i = a.blk_items[blk];
   } else {
-    for (int j = tid; j < blk; j += kThreads) {
-      base_e += a.blk_tot[j];
-      base_i += a.blk_items[j];
+    // eight loads per thread in flight together; buffer loads past blk return 0
+    const auto rt = buffer_rsrc(a.blk_tot, (uint32_t)blk * 4u);
+    const auto ri = buffer_rsrc(a.blk_items, (uint32_t)blk * 4u);
+    for (int j0 = 0; j0 < blk; j0 += kThreads * 8) {
+      int te[8], ti[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int off = (j0 + u * kThreads + tid) * 4;
+        te[u] = (int)__builtin_amdgcn_raw_buffer_load_b32(rt, off, 0, 0);
+        ti[u] = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, off, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) { base_e += te[u]; base_i += ti[u]; }
     }
     base_e = wave_sum(base_e);
     base_i = wave_sum(base_i);
@@ -330,6 +333,21 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
     for (int w = 0; w < kThreads / 64; ++w) { base_e += s_red[0][w]; base_i += s_red[1][w]; }
   }
 
+  // request, page and physical page of each lane's word, the block-table load
+  // in flight during the block scan below
+  const int32_t* rbase = lds_req ? s_rb : a.row_base;
+  int req_k[kUnitsPerWave], page_k[kUnitsPerWave], phys_k[kUnitsPerWave];
+#pragma unroll
+  for (int k = 0; k < kUnitsPerWave; ++k) {
+    const int64_t fw = ((int64_t)blk * kUnitsPerBlock + wave * kUnitsPerWave + k) * kUnitWords + lane;
+    const bool valid = fw < a.n_words;
+    const int64_t row = fw / a.words;
+    const int64_t rr = row - (int64_t)(row / a.total_rows) * a.total_rows;
+    req_k[k] = valid ? find_request(rbase, a.batch, rr) : 0;
+    page_k[k] = min(max((int)(rr - rbase[req_k[k]]), 0), a.max_pages - 1);
+    phys_k[k] = valid ? a.block_table[(int64_t)req_k[k] * a.bt_stride + page_k[k]] : 0;
+  }
+
   // scan of this block's units (one lane per unit)
   static_assert(kUnitsPerBlock <= 64, "one lane per unit in the block scan");
   if (wave == 0) {
@@ -349,7 +367,6 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
   }
   __syncthreads();
 
-  const int32_t* rbase = lds_req ? s_rb : a.row_base;
   const int32_t* cq = lds_req ? s_cq : a.cu_q;
   const int32_t* ck = lds_req ? s_ck : a.cu_k;
   const int lead = lane & ~(G - 1);
@@ -363,8 +380,8 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
     const int64_t word = fw - row * a.words;
     const int g = (int)(row / a.total_rows);
     const int64_t rr = row - (int64_t)g * a.total_rows;
-    const int b = valid ? find_request(rbase, a.batch, rr) : 0;
-    const int j = min(max((int)(rr - rbase[b]), 0), a.max_pages - 1);
+    const int b = req_k[k];
+    const int j = page_k[k];
     // One lane per bitmap word: the word's first CSR position is the unit's
     // plus the bits of earlier words; the lane then writes the word's entries
     // in bit order (a wave-uniform loop as long as any lane has bits left).
@@ -399,8 +416,7 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
       if (idx < a.max_items) {
         const int sk = ck[b + 1] - ck[b];
         const int ctx = sk - (cq[b + 1] - cq[b]);
-        const int phys = a.block_table[(int64_t)b * a.bt_stride + j];
-        a.items[2 * idx] = make_int4(p_pos + t * a.qc, min(a.qc, n - t * a.qc), phys, g);
+        a.items[2 * idx] = make_int4(p_pos + t * a.qc, min(a.qc, n - t * a.qc), phys_k[k], g);
         a.items[2 * idx + 1] = make_int4(ctx - cq[b] - j * kPage, sk - j * kPage, (int)row, b);
         if (a.order_shift > 0) a.okey[idx] = (int32_t)(q_piece >> a.order_shift);
       }

@@ -100,20 +100,42 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
 
-// Inclusive scan over a 64-lane wave.
+// Inclusive scan over a 64-lane wave on the VALU, through DPP lane moves
+// instead of LDS permutes: a Hillis-Steele scan inside each 16-lane row
+// (row_shr by 1, 2, 4 and 8, zero where the source lies before the row), then
+// rows 1 and 3 add lane 15 of the row before them (row_bcast:15) and rows 2 and
+// 3 add lane 31 (row_bcast:31).
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
   return x;
 }
 
+// Sum over the wave, the same in every lane.
 __device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return __builtin_amdgcn_readlane(wave_inclusive_scan(x), 63);
+}
+
+// Sum over aligned groups of G lanes (G a power of two up to 64), in every lane
+// of the group: a butterfly of symmetric lane exchanges (quad permutes, the
+// 8- and 16-lane mirrors, then the 16- and 32-lane row swaps).
+__device__ __forceinline__ int group_sum(int x, int G) {
+  if (G >= 2) x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);
+  if (G >= 4) x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);
+  if (G >= 8) x += __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);
+  if (G >= 16) x += __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);
+  if (G >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+    x = (int)(r[0] + r[1]);
+  }
+  if (G >= 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+    x = (int)(r[0] + r[1]);
+  }
   return x;
 }
 
