@@ -52,6 +52,7 @@ constexpr int kMinItemPages = 4;             // ... and at least
 constexpr int kPlanCUs = 256;                // compute units the item sizing aims to fill
 constexpr int kPlanRounds = 6;               // item sizes for about k rounds of kPlanCUs items, k = 1..6,
 constexpr int kPlanCands = kPlanRounds + 3;   // and three sizes at and just above one round's
+constexpr int kPlanLoopItems = 16;           // items per q-block up to which its thread writes them
 
 struct ItemHdr {
   int32_t n_items;
@@ -87,8 +88,9 @@ struct ScoreK {
 // chooses the pages per item; pass 2 emits the items request by request, q-block
 // by q-block, page chunk by page chunk: item = {b, first global query, query
 // count, first page}.  For each batch of up to 256 q-blocks one thread per
-// q-block counts its page chunks, a block scan places them, then all threads
-// emit the batch's items.
+// q-block counts its page chunks and a block scan places them; the thread then
+// writes its q-block's items if every q-block has few, else all threads share
+// the batch's items, each finding its q-block by binary search.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int qblock_visible(int ctx, int qf, int qn) {
   return (ctx + qf + qn - 1) / kPage + 1;
@@ -97,9 +99,9 @@ __device__ __forceinline__ int qblock_visible(int ctx, int qf, int qn) {
 // Pages per item for about k rounds of kPlanCUs items: the w visible pages of
 // all q-blocks cut into k * kPlanCUs chunks, rounded up to a multiple of round,
 // within [kMinItemPages, kMaxItemPages].
-__device__ __forceinline__ int cand_pages(int64_t w, int k, int round) {
+__device__ __forceinline__ int cand_pages(int64_t w, int k, int round) {   // round: a power of two
   const int64_t per = (int64_t)kPlanCUs * k;
-  const int64_t pc = ((w + per - 1) / per + round - 1) / round * round;
+  const int64_t pc = ((w + per - 1) / per + round - 1) & ~(int64_t)(round - 1);
   return (int)min<int64_t>(kMaxItemPages, max<int64_t>(kMinItemPages, pc));
 }
 // The candidates: the k = 1..kPlanRounds sizes as multiples of 4, then three
@@ -129,9 +131,7 @@ template <int W, int N>
 __device__ __forceinline__ void block_sum(int (&x)[N], int (*s_red)[N]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1)
-#pragma unroll
-    for (int i = 0; i < N; ++i) x[i] += __shfl_xor(x[i], o);
+  for (int i = 0; i < N; ++i) x[i] = wave_sum(x[i]);
   if (lane == 0)
 #pragma unroll
     for (int i = 0; i < N; ++i) s_red[wave][i] = x[i];
@@ -164,9 +164,8 @@ __global__ __launch_bounds__(256) void score_plan_kernel(const int32_t* __restri
                                                          int qblock, int align, int64_t max_items,
                                                          ItemHdr* __restrict__ hdr,
                                                          int4* __restrict__ items) {
-  __shared__ int wave_tot[4];
-  __shared__ int s_off[257];
-  __shared__ int s_qf[256], s_qn[256];
+  __shared__ int wave_tot[4], wave_mx[4];
+  __shared__ int s_off[256], s_qf[256], s_qn[256];
   __shared__ int64_t running;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -189,11 +188,9 @@ __global__ __launch_bounds__(256) void score_plan_kernel(const int32_t* __restri
       vmax = max(vmax, v);
     }
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    w += __shfl_xor(w, o);
-    vmin = min(vmin, __shfl_xor(vmin, o));
-    vmax = max(vmax, __shfl_xor(vmax, o));
-  }
+  w = wave_sum64(w);
+  vmin = wave_min(vmin);
+  vmax = wave_max(vmax);
   if (lane == 0) { s_w[wave] = w; s_vmin[wave] = vmin; s_vmax[wave] = vmax; }
   __syncthreads();
   int64_t tw = 0;
@@ -236,27 +233,36 @@ __global__ __launch_bounds__(256) void score_plan_kernel(const int32_t* __restri
         nch = (qblock_visible(ctx, qf, qn) + pc - 1) / pc;
       }
       const int incl = wave_inclusive_scan(nch);
-      if (lane == 63) wave_tot[wave] = incl;
+      const int mx = wave_max(nch);
+      if (lane == 63) { wave_tot[wave] = incl; wave_mx[wave] = mx; }
       __syncthreads();
-      int wave_off = 0, total = 0;
+      int wave_off = 0, total = 0, maxc = 0;
       for (int k = 0; k < 4; ++k) {
         if (k < wave) wave_off += wave_tot[k];
         total += wave_tot[k];
+        maxc = max(maxc, wave_mx[k]);
       }
-      s_off[tid] = wave_off + incl - nch;
-      s_qf[tid] = qf;
-      s_qn[tid] = qn;
-      if (tid == 0) s_off[256] = total;
-      __syncthreads();
       const int64_t run = running;
-      for (int k = tid; k < total; k += 256) {
-        int lo = 0, hi = 255;             // last q-block of the batch with s_off <= k
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (s_off[mid] <= k) lo = mid; else hi = mid - 1;
+      if (maxc <= kPlanLoopItems) {
+        // few chunks per q-block: each q-block's thread writes its own
+        const int64_t first = run + wave_off + incl - nch;
+        for (int c = 0; c < nch; ++c)
+          if (first + c < max_items) items[first + c] = make_int4(b, q0 + qf, qn, c * pc);
+      } else {
+        // many: every thread takes items, each finding its q-block by search
+        s_off[tid] = wave_off + incl - nch;
+        s_qf[tid] = qf;
+        s_qn[tid] = qn;
+        __syncthreads();
+        for (int k = tid; k < total; k += 256) {
+          int lo = 0, hi = 255;             // last q-block of the batch with s_off <= k
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= k) lo = mid; else hi = mid - 1;
+          }
+          const int64_t dst = run + k;
+          if (dst < max_items) items[dst] = make_int4(b, q0 + s_qf[lo], s_qn[lo], (k - s_off[lo]) * pc);
         }
-        const int64_t dst = run + k;
-        if (dst < max_items) items[dst] = make_int4(b, q0 + s_qf[lo], s_qn[lo], (k - s_off[lo]) * pc);
       }
       __syncthreads();
       if (tid == 0) running = run + total;
@@ -272,7 +278,7 @@ __global__ __launch_bounds__(256) void score_plan_kernel(const int32_t* __restri
 // Same plan for batches of at most kPlanMaxB requests and kPlanMaxG q-blocks,
 // with the request table and the q-block offsets in LDS: every pass is spread
 // over all q-blocks (or all items) instead of walking the requests in turn.
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 256;
 constexpr int kPlanMaxB = 1024;
 constexpr int kPlanMaxG = 4096;
 
@@ -282,7 +288,7 @@ __global__ __launch_bounds__(kPlanThreads) void score_plan_table_kernel(
   constexpr int kW = kPlanThreads / 64;
   __shared__ int s_q0[kPlanMaxB], s_sq[kPlanMaxB], s_ctx[kPlanMaxB], s_qbase[kPlanMaxB + 1];
   __shared__ int s_first[kPlanMaxG + 1];
-  __shared__ int s_cnt[kW];
+  __shared__ int s_cnt[kW], s_mx[kW];
   __shared__ int64_t s_w[kW];
   __shared__ int s_lo[kW], s_hi[kW];
   __shared__ int s_red[kW][kPlanCands];
@@ -311,17 +317,20 @@ __global__ __launch_bounds__(kPlanThreads) void score_plan_table_kernel(
   };
 
   // pass 0: request table, q-blocks per request and their offsets
-  int nqb = 0;
-  if (tid < B) {
-    const int q0 = cu_q[tid], sq = cu_q[tid + 1] - q0;
-    s_q0[tid] = q0;
-    s_sq[tid] = sq;
-    s_ctx[tid] = (cu_k[tid + 1] - cu_k[tid]) - sq;
-    nqb = (sq + qblock - 1) / qblock;
-  }
   int G = 0;
-  const int qoff = block_scan(nqb, &G);
-  if (tid < B) s_qbase[tid] = qoff;
+  for (int r0 = 0; r0 < B; r0 += kPlanThreads) {
+    const int r = r0 + tid;
+    int nqb = 0;
+    if (r < B) {
+      const int q0 = cu_q[r], sq = cu_q[r + 1] - q0;
+      s_q0[r] = q0;
+      s_sq[r] = sq;
+      s_ctx[r] = (cu_k[r + 1] - cu_k[r]) - sq;
+      nqb = (sq + qblock - 1) / qblock;
+    }
+    const int qoff = G + block_scan(nqb, &G);
+    if (r < B) s_qbase[r] = qoff;
+  }
   __syncthreads();
   G = min(G, kPlanMaxG);
   auto visible = [&](int g, int* b_out, int* qf_out, int* qn_out) {
@@ -344,11 +353,9 @@ __global__ __launch_bounds__(kPlanThreads) void score_plan_table_kernel(
     vmin = min(vmin, v);
     vmax = max(vmax, v);
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    w += __shfl_xor(w, o);
-    vmin = min(vmin, __shfl_xor(vmin, o));
-    vmax = max(vmax, __shfl_xor(vmax, o));
-  }
+  w = wave_sum64(w);
+  vmin = wave_min(vmin);
+  vmax = wave_max(vmax);
   if (lane == 0) { s_w[wave] = w; s_lo[wave] = vmin; s_hi[wave] = vmax; }
   __syncthreads();
   int64_t tw = 0;
@@ -369,7 +376,7 @@ __global__ __launch_bounds__(kPlanThreads) void score_plan_table_kernel(
   }
 
   // pass 2: page chunks per q-block, offsets
-  int n_items = 0;
+  int n_items = 0, maxc = 0;
   for (int base = 0; base < G; base += kPlanThreads) {
     const int g = base + tid;
     int c = 0;
@@ -377,18 +384,34 @@ __global__ __launch_bounds__(kPlanThreads) void score_plan_table_kernel(
       int b, qf, qn;
       c = (visible(g, &b, &qf, &qn) + pc - 1) / pc;
     }
-    const int first = n_items + block_scan(c, &n_items);
+    const int mx = wave_max(c);
+    if (lane == 0) s_mx[wave] = mx;
+    const int first = n_items + block_scan(c, &n_items);   // its barriers publish s_mx
+#pragma unroll
+    for (int k = 0; k < kW; ++k) maxc = max(maxc, s_mx[k]);
     if (g < G) s_first[g] = first;
+    __syncthreads();                          // s_mx is rewritten by the next round
   }
   __syncthreads();
 
-  // emit: item k belongs to the last q-block whose first item is <= k
+  // emit: few chunks per q-block, each q-block's thread writes its own; many,
+  // item k goes to the last q-block whose first item is <= k
   const int64_t n_out = min<int64_t>(n_items, max_items);
-  for (int k = tid; k < n_out; k += kPlanThreads) {
-    const int g = last_le(s_first, G, k);
-    int b, qf, qn;
-    visible(g, &b, &qf, &qn);
-    items[k] = make_int4(b, s_q0[b] + qf, qn, (k - s_first[g]) * pc);
+  if (maxc <= kPlanLoopItems) {
+    for (int g = tid; g < G; g += kPlanThreads) {
+      int b, qf, qn;
+      const int c = (visible(g, &b, &qf, &qn) + pc - 1) / pc;
+      const int first = s_first[g];
+      for (int k = 0; k < c; ++k)
+        if (first + k < n_out) items[first + k] = make_int4(b, s_q0[b] + qf, qn, k * pc);
+    }
+  } else {
+    for (int k = tid; k < n_out; k += kPlanThreads) {
+      const int g = last_le(s_first, G, k);
+      int b, qf, qn;
+      visible(g, &b, &qf, &qn);
+      items[k] = make_int4(b, s_q0[b] + qf, qn, (k - s_first[g]) * pc);
+    }
   }
   if (tid == 0) {
     hdr->n_items = (int32_t)n_out;

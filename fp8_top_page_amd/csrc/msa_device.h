@@ -120,6 +120,50 @@ __device__ __forceinline__ int wave_sum(int x) {
   return __builtin_amdgcn_readlane(wave_inclusive_scan(x), 63);
 }
 
+// Reductions over the whole wave, the result in every lane: the same butterfly
+// as group_sum below, each step combining a lane with its partner.
+template <class Op>
+__device__ __forceinline__ int wave_reduce(int x, Op op) {
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false));
+  x = op(x, __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false));
+  auto r = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+  x = op((int)r[0], (int)r[1]);
+  r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return op((int)r[0], (int)r[1]);
+}
+__device__ __forceinline__ int wave_min(int x) {
+  return wave_reduce(x, [](int a, int b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ int wave_max(int x) {
+  return wave_reduce(x, [](int a, int b) { return a > b ? a : b; });
+}
+// 64-bit sum: both halves of the partner's value move through the same lane
+// pattern, then a 64-bit add.
+__device__ __forceinline__ int64_t wave_sum64(int64_t x) {
+  auto mv = [](int64_t v, auto move) -> int64_t {
+    const uint32_t lo = move((uint32_t)v), hi = move((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+  };
+  x += mv(x, [](uint32_t u) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0xB1, 0xF, 0xF, false); });
+  x += mv(x, [](uint32_t u) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xF, 0xF, false); });
+  x += mv(x, [](uint32_t u) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x141, 0xF, 0xF, false); });
+  x += mv(x, [](uint32_t u) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x140, 0xF, 0xF, false); });
+  // row swaps: the pair holds this lane's value and its partner's, in some
+  // order, so their sum is the same whichever it is
+  auto sw = [](int64_t v, bool wide) -> int64_t {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)((uint64_t)v >> 32);
+    const auto a = wide ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                        : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto b = wide ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                        : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    return (int64_t)(((uint64_t)b[0] << 32) | a[0]) + (int64_t)(((uint64_t)b[1] << 32) | a[1]);
+  };
+  x = sw(x, false);
+  return sw(x, true);
+}
+
 // Sum over aligned groups of G lanes (G a power of two up to 64), in every lane
 // of the group: a butterfly of symmetric lane exchanges (quad permutes, the
 // 8- and 16-lane mirrors, then the 16- and 32-lane row swaps).
