@@ -103,20 +103,6 @@ __device__ __forceinline__ uint32_t key_bits(uint32_t u, bool valid) {
   return (valid && (u & 0x7FFFFFFFu) <= 0x7F800000u) ? k : 0u;
 }
 
-// Exact rank of up to 64 unique packed keys held one per lane of a wave (lanes
-// >= c hold none): each lane counts the larger keys, read lane by lane.
-__device__ __forceinline__ void rank_in_wave(uint64_t me, int c, int ksel, int f, int32_t* out) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t me_lo = (uint32_t)me, me_hi = (uint32_t)(me >> 32);
-  int r = 0;
-  for (int o = 0; o < c; ++o) {
-    const uint64_t other = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)me_hi, o) << 32) |
-                           (uint32_t)__builtin_amdgcn_readlane((int)me_lo, o);
-    r += other > me ? 1 : 0;
-  }
-  if (lane < c && r < ksel) out[f + r] = (int)~me_lo;
-}
-
 // Exact rank of c unique packed candidates: the ksel best go to out[f ..].
 __device__ __forceinline__ void rank_candidates(const uint64_t* c_pk, int c, int ksel, int f,
                                                 int32_t* out) {
@@ -492,12 +478,18 @@ template <int KPT, int NQ>
 __global__ __launch_bounds__(kBlock) void topk_wave_kernel(TopkK a) {
   constexpr int kWaves = kBlock / 64;
   constexpr int kList = 64 * KPT;
-  __shared__ uint64_t c_pk[kWaves][kList];
+  __shared__ uint64_t c_pk[kWaves][kList + 64];   // the list, then one discard entry per lane
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t i0 = ((int64_t)blockIdx.x * kWaves + wave) * NQ;
   if (i0 >= a.total_q) return;
   const int row_len = a.ld < (int64_t)a.max_pages ? (int)a.ld : a.max_pages;
+  // the first query's request, looked up before the rows are requested (vector
+  // loads complete in order, so a lookup issued after them would wait for them)
+  int b = find_request(a.cu_q, a.batch, i0);
+  int cq0 = a.cu_q[b], cq1 = a.cu_q[b + 1];
+  int sk = a.cu_k[b + 1] - a.cu_k[b];
+  __builtin_amdgcn_sched_barrier(0);        // keep those loads ahead of the rows'
 
   uint32_t x[NQ][KPT];
 #pragma unroll
@@ -518,20 +510,27 @@ __global__ __launch_bounds__(kBlock) void topk_wave_kernel(TopkK a) {
   for (int qq = 0; qq < NQ; ++qq) {
     const int64_t i = i0 + qq;
     if (i >= a.total_q) break;
-    const int b = find_request(a.cu_q, a.batch, i);
-    const int cq0 = a.cu_q[b];
-    const int sq = a.cu_q[b + 1] - cq0;
-    const int sk = a.cu_k[b + 1] - a.cu_k[b];
-    const int pos = sk - sq + (int)(i - cq0);
+    if (i >= cq1) {                         // the wave's queries cross into a later request
+      b = find_request(a.cu_q, a.batch, i);
+      cq0 = a.cu_q[b];
+      cq1 = a.cu_q[b + 1];
+      sk = a.cu_k[b + 1] - a.cu_k[b];
+    }
+    const int pos = sk - (cq1 - cq0) + (int)(i - cq0);
     const int v = min(pos / kPage + 1, a.max_pages);
     const int k_all = min(kTopK, v);
     const int f = min(a.n_local, k_all);
     const int ksel = k_all - f;
     const int ncand = v - f;
-    int32_t* out = a.out + i * a.out_stride;
-    if (lane < kTopK) {
-      if (lane < f) out[lane] = v - 1 - lane;
-      else if (lane >= k_all) out[lane] = -1;
+    // stores go through a buffer over the query's 16 output slots, so a lane
+    // with nothing to write gives an offset past them and its store is
+    // dropped: no branches (each one costs scalar instructions, which limit
+    // this kernel with eight waves per SIMD)
+    const auto rs_out = buffer_rsrc(a.out + i * a.out_stride, kTopK * 4u);
+    constexpr int kDrop = 1 << 20;
+    {
+      const bool w = lane < kTopK && (lane < f || lane >= k_all);
+      __builtin_amdgcn_raw_buffer_store_b32(lane < f ? v - 1 - lane : -1, rs_out, w ? lane * 4 : kDrop, 0, 0);
     }
     if (ksel == 0) continue;
 
@@ -546,40 +545,66 @@ __global__ __launch_bounds__(kBlock) void topk_wave_kernel(TopkK a) {
     // the ksel-th largest lane maximum of the top halves
     uint32_t t16 = 0;
     m >>= 16;
+#pragma unroll
     for (int bit = 15; bit >= 0; --bit) {
       const uint32_t t = t16 | (1u << bit);
       if ((int)__popcll(__ballot(m >= t)) >= ksel) t16 = t;
     }
     const uint32_t tau = t16 << 16;
 
-    // every candidate key >= tau goes to the list
+    // every candidate key >= tau goes to the list; the others to the lane's
+    // discard entry.  The first 64 entries start at 0, below every listed key,
+    // so the rank below needs no count check.  Keys past the candidates are 0,
+    // so with tau > 0 the key alone decides (only tau == 0 checks the page).
+    c_pk[wave][lane] = 0u;
+    bool cand[KPT];
     int mine = 0;
+    const bool any_key = tau == 0u;
 #pragma unroll
-    for (int k = 0; k < KPT; ++k) mine += (k * 64 < lim && key[k] >= tau) ? 1 : 0;
+    for (int k = 0; k < KPT; ++k) {
+      cand[k] = any_key ? k * 64 < lim : key[k] >= tau;
+      mine += (int)cand[k];
+    }
     const int incl = wave_inclusive_scan(mine);
-    const int c = __shfl(incl, 63);
+    const int c = __builtin_amdgcn_readlane(incl, 63);
     int slot = incl - mine;
 #pragma unroll
-    for (int k = 0; k < KPT; ++k)
-      if (k * 64 < lim && key[k] >= tau) c_pk[wave][slot++] = pack_key(key[k], k * 64 + lane);
+    for (int k = 0; k < KPT; ++k) {
+      c_pk[wave][cand[k] ? slot : kList + lane] = pack_key(key[k], k * 64 + lane);
+      slot += (int)cand[k];
+    }
+    // a wave's LDS operations complete in order: only the compiler is held here
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    asm volatile("" ::: "memory");
 
     // exact rank among the candidates (packed keys are unique): in registers
     // for up to 64 of them, else from the list
     if (c <= 64) {
-      rank_in_wave(lane < c ? c_pk[wave][lane] : 0u, c, ksel, f, out);
+      // candidates 16 at a time, lane l taking candidate e0 + l % 16 and
+      // comparing it with every fourth entry from l / 16 on (all 16 reads in
+      // flight together); the four quarter counts are summed across lanes
+      const int qt = lane >> 4;
+      for (int e0 = 0; e0 < c; e0 += 16) {
+        const int e = e0 + (lane & 15);
+        const uint64_t me = c_pk[wave][min(e, c - 1)];
+        int r = 0;
+#pragma unroll
+        for (int o = 0; o < 16; ++o) r += c_pk[wave][4 * o + qt] > me ? 1 : 0;
+        r = (int)sum_across_groups((float)r);
+        const bool w = e < c && qt == 0 && r < ksel;
+        __builtin_amdgcn_raw_buffer_store_b32((int)~(uint32_t)me, rs_out, w ? (f + r) * 4 : kDrop, 0, 0);
+      }
     } else {
       for (int e = lane; e < c; e += 64) {
         const uint64_t me = c_pk[wave][e];
         int r = 0;
         for (int o = 0; o < c; ++o) r += c_pk[wave][o] > me ? 1 : 0;
-        if (r < ksel) out[f + r] = (int)~(uint32_t)me;
+        if (r < ksel) a.out[i * a.out_stride + f + r] = (int)~(uint32_t)me;
       }
     }
     // the list is rewritten for the next query
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    asm volatile("" ::: "memory");
   }
 }
 
