@@ -542,9 +542,7 @@ __global__ __launch_bounds__(kThreads, kWide ? kBlocksWide : kBlocksNarrow) void
   auto item_of = [&](int64_t x) -> int64_t {
     const int64_t it = x / a.GY;
     const int64_t c = it < n_items - 1 ? it : (int64_t)(n_items - 1);
-    if constexpr (kWide) {                   // only long rows are ordered
-      if (a.perm) return (int64_t)a.perm[c];
-    }
+    if (a.perm) return (int64_t)a.perm[c];   // only long rows are ordered
     return c;
   };
 
@@ -1123,10 +1121,11 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   }
   const int64_t max_work = L.max_items * k.GY;
   if (max_work > 0) {
-    // Rows per item from the host bound on entries per CSR row (total_q * topk
-    // entries over total_rows rows, at most L.item_q queries per item).
-    const int64_t per_row = ceil_div((int64_t)a.vl.total_q * kTopK, std::max(a.vl.total_rows, 1));
-    const bool wide = std::min<int64_t>(per_row, L.item_q) * k.G >= 2 * kWaves * 16;
+    // Every batch takes the one-tile kernel at three blocks per CU: the
+    // two-tile kernel (two blocks per CU, each K/V fragment read serving two
+    // 16-row tiles) measured 1 to 5 % slower on items of many rows too, whose
+    // time goes to the split rows' memory traffic rather than to LDS reads.
+    const bool wide = false;
     const int per_cu = wide ? kBlocksWide : kBlocksNarrow;
     const int64_t grid = std::min<int64_t>(max_work, (int64_t)device_cu_count() * per_cu);
     const bool fp4 = a.kv_scales != nullptr;
