@@ -288,8 +288,7 @@ constexpr int kWaveCap = 64;      // listed candidates per wave
 
 struct RowSmem {
   uint64_t c_pk[kBlock / 64 * kWaveCap];
-  uint32_t c_xb[kBlock / 64 * kWaveCap];   // listed (score bits, page) before packing
-  int c_j[kBlock / 64 * kWaveCap];
+  int c_j[kBlock / 64 * kWaveCap];          // listed pages before packing
   uint64_t c_all[64];
   uint32_t wave_tau[kBlock / 64];
   int s_cnt[kBlock / 64];
@@ -353,33 +352,31 @@ __device__ __forceinline__ void select_row(const TopkK& a, const RowQuery& q, co
   tk <<= 16;
   const float tau = __uint_as_float((tk & 0x80000000u) ? (tk & 0x7FFFFFFFu) : ~tk);
 
-  // 3. list every candidate score >= tau in the wave's part of the list: one
-  //    compare per key, and only key slots where some lane has one do more.
-  //    Entries go in as score bits and page; each lane then packs the entry
-  //    of its own index into its key.  With tau > 0 no load past the
-  //    candidates (0.0) can reach it, so the page check is needed only else.
-  const bool check_page = !(tau > 0.f);
-  int n_w = 0;                              // wave-uniform
+  // 3. list every candidate score >= tau in the wave's part of the list: each
+  //    lane first marks its candidate key slots in a bit mask (compares only,
+  //    no branches: the scalar unit the CU's waves share is the scarce
+  //    resource here), then writes the pages of its set bits.  The listed
+  //    scores are read again in full (from cache) by the lane that packs them.
+  const int lim = ncand - tid;              // key slot k is a candidate page iff k * kBlock < lim
+  const int nvalid = lim <= 0 ? 0 : min(KPT, (lim + kBlock - 1) / kBlock);
+  uint32_t cm = 0;
 #pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    const bool hit = x[k] >= tau;
-    uint64_t bal = __ballot(hit);
-    if (bal != 0u) {
-      const int j = k * kBlock + tid;
-      const bool cand = hit && (!check_page || j < ncand);
-      if (check_page) bal = __ballot(cand);
-      const int off = n_w + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-      if (cand && off < kWaveCap) {
-        sm.c_xb[wave * kWaveCap + off] = __float_as_uint(x[k]);
-        sm.c_j[wave * kWaveCap + off] = j;
-      }
-      n_w += (int)__popcll(bal);
-    }
+  for (int k = 0; k < KPT; ++k) cm |= (x[k] >= tau ? 1u : 0u) << k;
+  cm &= nvalid >= 32 ? 0xFFFFFFFFu : (1u << nvalid) - 1u;
+  const int mine = __popc(cm);
+  const int incl = wave_inclusive_scan(mine);
+  const int n_w = __builtin_amdgcn_readlane(incl, 63);
+  int slot = incl - mine;
+  while (cm != 0u) {
+    const int k = __builtin_ctz(cm);
+    cm &= cm - 1u;
+    if (slot < kWaveCap) sm.c_j[wave * kWaveCap + slot] = k * kBlock + tid;
+    ++slot;
   }
   if (lane < min(n_w, kWaveCap)) {
     const int e = wave * kWaveCap + lane;
-    sm.c_pk[e] = pack_key(float_key(__uint_as_float(sm.c_xb[e])), sm.c_j[e]);
+    const int j = sm.c_j[e];
+    sm.c_pk[e] = pack_key(float_key(q.row[j]), j);
   }
   if (lane == 0) sm.s_cnt[wave] = n_w;
   __syncthreads();
@@ -397,21 +394,24 @@ __device__ __forceinline__ void select_row(const TopkK& a, const RowQuery& q, co
     //    are packed into c_all, candidate e = 16w + (lane % 16) of wave w is
     //    compared by the lane's quarter (lane / 16) against entries 16q ..
     //    16q + 15, and the four counts are summed across the quarters.
+    //    Entries past c hold 0, below every listed key, so the counts need no
+    //    bound check; the store goes through a buffer over the query's 16
+    //    outputs and lanes with nothing to write give an offset past it.
     int pre = 0;
 #pragma unroll
     for (int w = 0; w < kBlock / 64; ++w) pre += w < wave ? sm.s_cnt[w] : 0;
     if (lane < n_w) sm.c_all[pre + lane] = sm.c_pk[wave * kWaveCap + lane];
+    if (wave == 0 && lane >= c) sm.c_all[lane] = 0u;
     __syncthreads();
     const int e = 16 * wave + (lane & 15), qt = lane >> 4;
     const uint64_t me = sm.c_all[min(e, c - 1)];
     int r = 0;
 #pragma unroll
-    for (int o = 0; o < 16; ++o) {          // all 16 reads in flight together
-      const int idx = 16 * qt + o;
-      r += (idx < c && sm.c_all[min(idx, 63)] > me) ? 1 : 0;
-    }
+    for (int o = 0; o < 16; ++o) r += sm.c_all[16 * qt + o] > me ? 1 : 0;   // all reads in flight together
     r = (int)sum_across_groups((float)r);
-    if (e < c && qt == 0 && r < ksel) out[f + r] = (int)~(uint32_t)me;
+    const bool wr = e < c && qt == 0 && r < ksel;
+    __builtin_amdgcn_raw_buffer_store_b32((int)~(uint32_t)me, buffer_rsrc(out, kTopK * 4u),
+                                          wr ? (f + r) * 4 : 1 << 20, 0, 0);
   } else {
     // more: thread t takes entry t of the four wave lists and counts the
     // larger entries of all four
