@@ -33,6 +33,8 @@
 // its (query, selection head, slot) entry.
 #include <type_traits>
 
+#include <utility>
+
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -639,29 +641,36 @@ __device__ __forceinline__ int64_t split_entry(int64_t i, int sel, int s, int n_
   return ((slot * kChunkQ + (i & (kChunkQ - 1))) * n_sel + sel) * kTopK + s;
 }
 
+// r differs from the values of the lanes 1 .. 15 places down this lane's
+// 16-lane row (row_shr by D + 1; a lane whose source lies before the row start
+// sees -2, no row index)
+template <int... D>
+__device__ __forceinline__ bool first_in_row(int r, std::integer_sequence<int, D...>) {
+  return ((__builtin_amdgcn_update_dpp(-2, r, 0x111 + D, 0xF, 0xF, false) != r) && ...);
+}
+
 __global__ __launch_bounds__(256) void attn_slot_kernel(SlotK a) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  // entries number fewer than 2^31 (the call checks total_q * n_sel * 16)
+  const int e = (int)blockIdx.x * 256 + (int)threadIdx.x;
   const int lane = threadIdx.x & 63;
   const bool in = e < a.n;
-  const int s = (int)(e & (kTopK - 1));
-  bool ok = false;
-  if (in) {
-    const int32_t* rs = a.rowsel + (e - s);
-    const int r = rs[s];
-    ok = r >= 0;
-    for (int u = 0; u < s; ++u) ok = ok && rs[u] != r;   // a page listed twice: its first slot
-    if (ok) {
-      const int64_t i = e / ((int64_t)a.n_sel * kTopK);
-      const int b = find_request(a.cu_q, a.batch, i);
-      const int local = (int)(i - a.cu_q[b]);
-      const int64_t wi = (int64_t)r * a.words + (local >> 5);
-      const int64_t p = (int64_t)a.wbase[wi] + __popc(a.bitmap[wi] & ((1u << (local & 31)) - 1u));
-      ok = p >= 0 && p < a.max_pos;
-      if (ok) {
-        const int per = a.n_sel * kTopK;
-        a.q_slot[p] = (int32_t)split_entry(i, (int)((e % per) / kTopK), s, a.n_sel, a.ring != 0);
-      }
-    }
+  const int s = e & (kTopK - 1);
+  const int r = a.rowsel[in ? e : (int)a.n - 1];
+  // a page listed twice counts at its first slot: the 16 slots of one (query,
+  // selection head) are one 16-lane row, so the slots below s are the lanes
+  // 1 .. s places down the row (row_shr; past the row start the old value, -2,
+  // stays)
+  bool ok = in && r >= 0 && first_in_row(r, std::make_integer_sequence<int, kTopK - 1>{});
+  if (ok) {
+    const int qs = e >> 4;                              // query * n_sel + head
+    const int64_t i = a.n_sel == 1 ? qs : qs / a.n_sel;
+    const int b = find_request(a.cu_q, a.batch, i);
+    const int local = (int)(i - a.cu_q[b]);
+    const int64_t wi = (int64_t)r * a.words + (local >> 5);
+    const int64_t p = (int64_t)a.wbase[wi] + __popc(a.bitmap[wi] & ((1u << (local & 31)) - 1u));
+    ok = p >= 0 && p < a.max_pos;
+    if (ok)
+      a.q_slot[p] = a.ring ? (int32_t)split_entry(i, qs - (int)i * a.n_sel, s, a.n_sel, true) : e;
   }
   const uint64_t bal = __builtin_amdgcn_ballot_w64(ok);
   if (in && s == 0) a.mask[e / kTopK] = (uint32_t)(bal >> (lane & ~(kTopK - 1))) & 0xFFFFu;
