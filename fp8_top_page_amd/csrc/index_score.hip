@@ -42,6 +42,12 @@
 namespace msa {
 namespace {
 
+// Maximum of two floats as v_maximum_f32 (IEEE 754-2019 maximum, a NaN
+// operand gives NaN): fmaxf's NaN-dropping form costs a quieting move per
+// operand, and a dot product that is NaN (a NaN code in the keys or queries)
+// makes the page score NaN, as a plain maximum over the products does.
+__device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 constexpr int kLdsPage = kPage * kDim;       // 16 KiB: 128 rows of 128 B, 16-byte pieces swizzled
 constexpr int kThreads = kScoreWaves * 64;
 constexpr int kFlush = 16;                   // pages per score-tile flush (decode kernel)
@@ -525,14 +531,14 @@ __device__ __forceinline__ void page_max(const uint8_t* __restrict__ pg, const v
       if (T > 0 || n > 0) {
         const int pn = n > 0 ? n - 1 : NQT - 1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rmax[pn][i] = fmaxf(rmax[pn][i], prev[i]);
+        for (int i = 0; i < 4; ++i) rmax[pn][i] = fmax_nan(rmax[pn][i], prev[i]);
       }
       prev = acc;
     }
     if (T < 7) a_cur = a_nxt;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) rmax[NQT - 1][i] = fmaxf(rmax[NQT - 1][i], prev[i]);
+  for (int i = 0; i < 4; ++i) rmax[NQT - 1][i] = fmax_nan(rmax[NQT - 1][i], prev[i]);
 }
 
 // Same with the causal cut: token (16T + 4*grp + i) of the page counts for the
@@ -562,13 +568,13 @@ __device__ __forceinline__ void page_max_causal(const uint8_t* __restrict__ pg,
       for (int h = 1; h < H; ++h) acc = mfma_e4m3(a_cur, qf[n][h], acc);
       if (16 * T + 15 <= lo) {                       // visible to every query of the tile
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rmax[n][i] = fmaxf(rmax[n][i], acc[i]);
+        for (int i = 0; i < 4; ++i) rmax[n][i] = fmax_nan(rmax[n][i], acc[i]);
       } else {
         const int lim = lim0 + 16 * n;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float v = (T * 16 + grp * 4 + i > lim) ? -INFINITY : acc[i];
-          rmax[n][i] = fmaxf(rmax[n][i], v);
+          rmax[n][i] = fmax_nan(rmax[n][i], v);
         }
       }
     }
@@ -600,7 +606,7 @@ __device__ __forceinline__ void page_max_f4(const uint8_t* __restrict__ pg, cons
       if (T > 0 || n > 0) {
         const int pn = n > 0 ? n - 1 : NQT - 1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rmax[pn][i] = fmaxf(rmax[pn][i], prev[i]);
+        for (int i = 0; i < 4; ++i) rmax[pn][i] = fmax_nan(rmax[pn][i], prev[i]);
       }
       prev = acc;
     }
@@ -610,7 +616,7 @@ __device__ __forceinline__ void page_max_f4(const uint8_t* __restrict__ pg, cons
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) rmax[NQT - 1][i] = fmaxf(rmax[NQT - 1][i], prev[i]);
+  for (int i = 0; i < 4; ++i) rmax[NQT - 1][i] = fmax_nan(rmax[NQT - 1][i], prev[i]);
 }
 
 template <int H, int NQT>
@@ -633,13 +639,13 @@ __device__ __forceinline__ void page_max_causal_f4(const uint8_t* __restrict__ p
       for (int h = 1; h < H; ++h) acc = mfma_f4_e4m3(a_cur, qf[n][h], acc, s_cur);
       if (16 * T + 15 <= lo) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rmax[n][i] = fmaxf(rmax[n][i], acc[i]);
+        for (int i = 0; i < 4; ++i) rmax[n][i] = fmax_nan(rmax[n][i], acc[i]);
       } else {
         const int lim = lim0 + 16 * n;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float v = (T * 16 + grp * 4 + i > lim) ? -INFINITY : acc[i];
-          rmax[n][i] = fmaxf(rmax[n][i], v);
+          rmax[n][i] = fmax_nan(rmax[n][i], v);
         }
       }
     }
@@ -777,8 +783,8 @@ __device__ __forceinline__ void score_item(const ScoreK& a, int item, uint8_t* l
       const int pp = pg0 + 4 * h;
       const v4f g0 = *reinterpret_cast<const v4f*>(sbuf + ql * kSRowG + 8 * h);
       const v4f g1 = *reinterpret_cast<const v4f*>(sbuf + ql * kSRowG + 8 * h + 4);
-      const v4f m = v4f{fmaxf(g0[0], g0[1]), fmaxf(g0[2], g0[3]), fmaxf(g1[0], g1[1]),
-                        fmaxf(g1[2], g1[3])} * scale;
+      const v4f m = v4f{fmax_nan(g0[0], g0[1]), fmax_nan(g0[2], g0[3]), fmax_nan(g1[0], g1[1]),
+                        fmax_nan(g1[2], g1[3])} * scale;
       if (qi < q_end) {
         const int pos = ctx + (qi - cq0);
         const int hi = min(pg_hi, pos / kPage + 1);        // pages [pg_lo, hi) are written
@@ -813,9 +819,9 @@ __device__ __forceinline__ void score_item(const ScoreK& a, int item, uint8_t* l
     const int pc = p & 7;                      // slot in the 8-page group
 #pragma unroll
     for (int n = 0; n < NQT; ++n) {
-      float m = fmaxf(fmaxf(rmax[n][0], rmax[n][1]), fmaxf(rmax[n][2], rmax[n][3]));
+      float m = fmax_nan(fmax_nan(rmax[n][0], rmax[n][1]), fmax_nan(rmax[n][2], rmax[n][3]));
       const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-      m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));   // lane groups g and g ^ 2
+      m = fmax_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));   // lane groups g and g ^ 2
       if (grp < 2) sbuf[(n * 16 + col) * kSRowG + pc * 2 + grp] = m;
     }
     if (pc == 7 || p == p_end - 1) flush(p - pc, max(p0, p - pc), p + 1);
@@ -1062,9 +1068,9 @@ __device__ __forceinline__ void score_pp_item(const ScoreK& a, int item, uint8_t
         const int lim = my_pos0 + 16 * n;
         m = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, tok0 + i > lim ? -INFINITY : acc[i]);
+        for (int i = 0; i < 4; ++i) m = fmax_nan(m, tok0 + i > lim ? -INFINITY : acc[i]);
       } else {
-        m = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+        m = fmax_nan(fmax_nan(acc[0], acc[1]), fmax_nan(acc[2], acc[3]));
       }
       m = max_across_groups(m);
       if ((n & 3) == grp) dst[n * 16 + col] = m;
@@ -1105,7 +1111,7 @@ __device__ __forceinline__ void score_pp_item(const ScoreK& a, int item, uint8_t
     if (lane < kQ) {
       float m = -INFINITY;
 #pragma unroll
-      for (int T = 0; T < 8; ++T) m = fmaxf(m, src[(j * 8 + T) * kQ + lane]);
+      for (int T = 0; T < 8; ++T) m = fmax_nan(m, src[(j * 8 + T) * kQ + lane]);
       sbuf[lane * kSRow + pc] = m * scale;
     }
     if (pc == kFlush - 1 || pr == p_end - 1) flush(pr - pc, pr + 1);
