@@ -54,11 +54,12 @@ __device__ __forceinline__ v8i load_frag_lds(const uint8_t* p) {
 // 16-lane rows, so with both operands equal to x the pair it returns holds x and
 // x's partner (in some order) and a symmetric max/sum of the two completes one
 // butterfly step.
+// (The maximum is IEEE 754-2019 maximum: a NaN in any lane gives NaN.)
 __device__ __forceinline__ float max_across_groups(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  x = __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
   r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_across_groups(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -185,6 +185,46 @@ def test_per_index_head_selection(sq, sk, H):
                     n_sel=H)
 
 
+@pytest.mark.parametrize("sq,sk,H", [((300,), (1000,), 2), ((8, 8, 5), (3000, 5000, 900), 1)])
+def test_nan_codes_give_nan_scores(sq, sk, H):
+    """A NaN E4M3 code in a visible index key makes that page's score NaN for
+    every query that sees the token, and a NaN in a query's index vector makes
+    all of its page scores NaN, as the maximum over the products does in the
+    oracle (prefill and page-parallel scorers).  The selection ranks NaN
+    scores last, ties by page, as the oracle's top-k does on the same scores."""
+    from fp8_top_page_amd.pipeline import DeviceBatch, MsaPath
+    inp = _small_inputs(sq, sk, H, 8, 1, seed=31)
+    kc = inp.index_k_cache.copy()
+    bt = np.asarray(inp.block_table)
+    kc[bt[0, 1], 17, 5] = 0x7F                  # token 128 + 17 of request 0
+    if len(sq) > 1:
+        kc[bt[2, 3], 100, 0] = 0x7F             # token 3 * 128 + 100 of request 2
+    q = inp.index_q.copy()
+    q[3, 0, 9] = 0x7F                           # every score of query 3 (request 0)
+    inp.index_k_cache, inp.index_q = kc, q
+    db = DeviceBatch.from_inputs(inp)
+    path = MsaPath(db)
+    path.score()
+    path.select()
+    torch.cuda.synchronize()
+    scores = to_np(path.scores)
+    sel = to_np(path.topk)[:, 0, :]
+    ref = oracle.index_scores(inp.cu_seqlens_q, inp.cu_seqlens_k, inp.block_table, inp.index_q,
+                              inp.index_k_cache, inp.index_q_scale, inp.index_k_scale)
+    _, pos = oracle.query_positions(inp.cu_seqlens_q, inp.cu_seqlens_k)
+    n_nan = 0
+    for i in range(inp.total_q):
+        v = int(pos[i] // 128 + 1)
+        r, g = ref[i, :v], scores[i, :v].astype(np.float64)
+        assert np.array_equal(np.isnan(r), np.isnan(g)), f"query {i}: NaN pattern differs"
+        n_nan += int(np.isnan(r).sum())
+        ok = ~np.isnan(r)
+        tol = 1e-3 * np.maximum(np.abs(r[ok]), float(np.sqrt(np.mean(r[ok] ** 2))) if ok.any() else 1.0)
+        assert np.all(np.abs(g[ok] - r[ok]) <= tol), f"query {i}: scores out of tolerance"
+    assert n_nan > 0
+    check_topk_exact_on_gpu_scores(inp, scores, sel)
+
+
 def test_empty_batch_is_a_no_op():
     inp = _small_inputs((0, 0), (300, 128))
     path = run_path(inp)
