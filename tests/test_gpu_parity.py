@@ -312,14 +312,15 @@ def test_topk_rows_longer_than_one_chunk(kind):
     check_topk_exact_on_gpu_scores(meta, s, to_np(out))
 
 
-@pytest.mark.parametrize("pages", [3000, 8000])
+@pytest.mark.parametrize("pages", [300, 1500, 3000, 8000])
 @pytest.mark.parametrize("kind", ["near_top", "near_many", "negative"])
 def test_topk_keys_equal_in_their_top_bits(pages, kind):
-    """Rows of 2,049..8,192 pages, whose selection keeps only the top 16 bits of
-    each key until the exact rank: scores that agree in those bits and differ
-    below them (40 such pages at the top; 3,000 of them, more than the
-    candidate list holds; all-negative rows with near ties).  The result must
-    equal the oracle's selection on the same scores."""
+    """Scores that agree in their top 16 bits and differ below them (40 such
+    pages at the top; 3,000 of them, more than the candidate list holds;
+    all-negative rows with near ties).  Rows of 2,049..8,192 pages (3,000 and
+    8,000) bound the selection by those 16 bits alone until the exact rank;
+    300 and 1,500 pages take the wave-per-query and block-per-query kernels.
+    The result must equal the oracle's selection on the same scores."""
     from types import SimpleNamespace
     from fp8_top_page_amd import msa_topk_select
     from fp8_top_page_amd.pipeline import DeviceBatch
