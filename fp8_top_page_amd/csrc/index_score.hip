@@ -59,6 +59,7 @@ constexpr int kPlanCUs = 256;                // compute units the item sizing ai
 constexpr int kPlanRounds = 6;               // item sizes for about k rounds of kPlanCUs items, k = 1..6,
 constexpr int kPlanCands = kPlanRounds + 3;   // and three sizes at and just above one round's
 constexpr int kPlanLoopItems = 16;           // items per q-block up to which its thread writes them
+constexpr int kDirectMaxQBlocks = 128;       // one-request batches planned on the host, at most
 
 struct ItemHdr {
   int32_t n_items;
@@ -87,6 +88,13 @@ struct ScoreK {
   uint64_t* cand;            // fused selection (decode kernel): [items, queries, 16] candidate keys
   int2* first_item;          // fused selection: [total_q] (first work item, position) of each query
   int32_t n_local;           // fused selection: forced recent pages
+  // A one-request batch planned on the host: direct_items > 0 items of
+  // direct_pc pages, q-block by q-block, decoded from these values instead of
+  // read from hdr / items (neither is written then).
+  int32_t direct_items;
+  int32_t direct_pc;
+  int32_t direct_sq;         // the request's queries
+  int32_t direct_ctx;        // its context: seqlen_k - seqlen_q
 };
 
 // ---------------------------------------------------------------------------
@@ -98,17 +106,24 @@ struct ScoreK {
 // writes its q-block's items if every q-block has few, else all threads share
 // the batch's items, each finding its q-block by binary search.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int qblock_visible(int ctx, int qf, int qn) {
+// The sizing helpers below also run on the host, which plans one-request
+// batches itself (plan_one_request).
+template <class T>
+__host__ __device__ constexpr T plan_min(T a, T b) { return a < b ? a : b; }
+template <class T>
+__host__ __device__ constexpr T plan_max(T a, T b) { return a < b ? b : a; }
+
+__host__ __device__ __forceinline__ int qblock_visible(int ctx, int qf, int qn) {
   return (ctx + qf + qn - 1) / kPage + 1;
 }
 
 // Pages per item for about k rounds of kPlanCUs items: the w visible pages of
 // all q-blocks cut into k * kPlanCUs chunks, rounded up to a multiple of round,
 // within [kMinItemPages, kMaxItemPages].
-__device__ __forceinline__ int cand_pages(int64_t w, int k, int round) {   // round: a power of two
+__host__ __device__ __forceinline__ int cand_pages(int64_t w, int k, int round) {   // round: a power of two
   const int64_t per = (int64_t)kPlanCUs * k;
   const int64_t pc = ((w + per - 1) / per + round - 1) & ~(int64_t)(round - 1);
-  return (int)min<int64_t>(kMaxItemPages, max<int64_t>(kMinItemPages, pc));
+  return (int)plan_min<int64_t>(kMaxItemPages, plan_max<int64_t>(kMinItemPages, pc));
 }
 // The candidates: the k = 1..kPlanRounds sizes as multiples of 4, then three
 // sizes at and just above one round's: ceil(w / kPlanCUs) + 0, 1, 2 pages (the
@@ -117,19 +132,19 @@ __device__ __forceinline__ int cand_pages(int64_t w, int k, int round) {   // ro
 // whose score flush is 16-byte aligned relative to an item's first page) keeps
 // every size a multiple of 4: the last three become the one-round size + 4, 8,
 // 12.  The prefill kernel's flush follows absolute 8-page groups: align = 1.
-__device__ __forceinline__ void plan_candidates(int64_t w, int align, int (&cand)[kPlanCands]) {
+__host__ __device__ __forceinline__ void plan_candidates(int64_t w, int align, int (&cand)[kPlanCands]) {
 #pragma unroll
   for (int k = 0; k < kPlanRounds; ++k) cand[k] = cand_pages(w, k + 1, 4);
   const int one = cand_pages(w, 1, align);
 #pragma unroll
   for (int j = 0; j < kPlanCands - kPlanRounds; ++j)
-    cand[kPlanRounds + j] = min(kMaxItemPages, one + (align == 1 ? j : 4 * (j + 1)));
+    cand[kPlanRounds + j] = plan_min(kMaxItemPages, one + (align == 1 ? j : 4 * (j + 1)));
 }
 // Predicted run time of n items of at most pc pages, in fifths of a page: the
 // items run in rounds of kPlanCUs (one block per compute unit), each round as
 // long as a full item, whose start-up (query fragments, first page copies)
 // costs about 1.2 pages.  The plan keeps the candidate with the least.
-__device__ __forceinline__ int64_t cand_cost(int64_t n, int pc) {
+__host__ __device__ __forceinline__ int64_t cand_cost(int64_t n, int pc) {
   return (n + kPlanCUs - 1) / kPlanCUs * (5 * (int64_t)pc + 6);
 }
 // Block-wide sums of per-thread values over W waves (result in every thread).
@@ -152,10 +167,10 @@ __device__ __forceinline__ void block_sum(int (&x)[N], int (*s_red)[N]) {
 // Query blocks that all see about the same number of pages (every decode batch,
 // a short chunk over a long context) get about one item per compute unit; only
 // uneven batches weigh the candidates.
-__device__ __forceinline__ bool plan_uniform(int vmin, int vmax) { return (vmax - vmin) * 8 <= vmax; }
+__host__ __device__ __forceinline__ bool plan_uniform(int vmin, int vmax) { return (vmax - vmin) * 8 <= vmax; }
 
 // The candidate with the least predicted time (the first one on ties).
-__device__ __forceinline__ int best_pages(const int (&cand)[kPlanCands], const int (&n)[kPlanCands]) {
+__host__ __device__ __forceinline__ int best_pages(const int (&cand)[kPlanCands], const int (&n)[kPlanCands]) {
   int best = cand[0];
   int64_t best_cost = cand_cost(n[0], best);
   for (int k = 1; k < kPlanCands; ++k) {
@@ -666,12 +681,11 @@ constexpr size_t score_lds_bytes() {
 // flight and every wave is past the item's last use of LDS.
 // KF: index-K format, 0 = E4M3 rows of 128 bytes, 1 = MXFP4.
 template <int H, int KF>
-__device__ __forceinline__ void score_item(const ScoreK& a, int item, uint8_t* lds) {
+__device__ __forceinline__ void score_item(const ScoreK& a, int4 it, int pc, uint8_t* lds) {
   constexpr int NQT = score_qtiles(H);   // 16-query tiles per wave
   static_assert(NQT >= 1, "at least one query tile per wave");
   constexpr int kSlot = KF ? kF4Slot : kLdsPage;
 
-  const int4 it = a.items[item];
   const int b = it.x, q_first = it.y, q_count = it.z, p0 = it.w;
 
   // The lane values below are recomputed per item (the empty asm hides that the
@@ -690,7 +704,7 @@ __device__ __forceinline__ void score_item(const ScoreK& a, int item, uint8_t* l
   const int pos_first = ctx + (q_first - cq0);
   const int pos_last = pos_first + q_count - 1;
   const int v_block = pos_last / kPage + 1;
-  const int p_end = min(min(p0 + a.hdr->pages_per_item, v_block), a.max_pages);
+  const int p_end = min(min(p0 + pc, v_block), a.max_pages);
   if (p0 >= p_end) return;
   const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
 
@@ -955,14 +969,13 @@ __device__ __forceinline__ void select_item_candidates(const ScoreK& a, int item
 // fused selection, which keeps the item's scores in LDS instead of writing them
 // and leaves per-item candidate lists.
 template <int H, int KF, bool kSel = false>
-__device__ __forceinline__ void score_pp_item(const ScoreK& a, int item, uint8_t* lds) {
+__device__ __forceinline__ void score_pp_item(const ScoreK& a, int item, int4 it, int pc, uint8_t* lds) {
   constexpr int NQT = score_qtiles(H);
   constexpr int kQ = NQT * 16;                    // query slots
   constexpr int kSlot = KF ? kF4Slot : kLdsPage;
   constexpr int kRingN = pp_ring<KF>();
   constexpr int kReducer = 0;        // the wave that reduces the partials and stores the scores
 
-  const int4 it = a.items[item];
   const int b = it.x, q_first = it.y, q_count = it.z, p0 = it.w;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -980,7 +993,7 @@ __device__ __forceinline__ void score_pp_item(const ScoreK& a, int item, uint8_t
   const int pos_first = ctx + (q_first - cq0);
   const int pos_last = pos_first + q_count - 1;
   const int v_block = pos_last / kPage + 1;
-  const int p_end = min(min(p0 + a.hdr->pages_per_item, v_block), a.max_pages);
+  const int p_end = min(min(p0 + pc, v_block), a.max_pages);
   if (p0 >= p_end) {
     if constexpr (kSel) {                         // an empty item still leaves (empty) lists
       for (int e = tid; e < q_count * kTopK; e += kThreads)
@@ -1166,7 +1179,8 @@ template <int H>
 __global__ __launch_bounds__(kThreads) void index_score_sel_kernel(ScoreK a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int n_items = a.hdr->n_items;
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) score_pp_item<H, 0, true>(a, item, lds);
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x)
+    score_pp_item<H, 0, true>(a, item, a.items[item], a.hdr->pages_per_item, lds);
 }
 
 // Merge of the per-item candidate lists, one wave per query: the forced recent
@@ -1252,13 +1266,40 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(MergeK a) {
 
 template <int H, int KF, bool kDecode>
 __device__ __forceinline__ void take_items(const ScoreK& a, uint8_t* lds) {
-  const int n_items = a.hdr->n_items;
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  auto run = [&](int item, int4 it, int pc) {
     if constexpr (kDecode)
-      score_pp_item<H, KF>(a, item, lds);
+      score_pp_item<H, KF>(a, item, it, pc, lds);
     else
-      score_item<H, KF>(a, item, lds);
+      score_item<H, KF>(a, it, pc, lds);
+  };
+  if (a.direct_items > 0) {
+    // Lane l holds the inclusive prefix of the chunk counts of q-blocks l and
+    // 64 + l (the host allows at most kDirectMaxQBlocks), so an item's q-block
+    // is the number of q-blocks whose items all come before it.
+    constexpr int kQB = score_qblock(H);
+    const int pc = a.direct_pc, sq = a.direct_sq, ctx = a.direct_ctx;
+    const int nqb = (sq + kQB - 1) / kQB;
+    const int lane = threadIdx.x & 63;
+    auto chunks = [&](int qb) {
+      const int qf = qb * kQB;
+      return qb < nqb ? (qblock_visible(ctx, qf, plan_min(sq - qf, kQB)) + pc - 1) / pc : 0;
+    };
+    const int pre0 = wave_inclusive_scan(chunks(lane));
+    const int pre1 = wave_inclusive_scan(chunks(64 + lane)) + __builtin_amdgcn_readlane(pre0, 63);
+    const int q0 = a.cu_q[0];
+    for (int item = blockIdx.x; item < a.direct_items; item += gridDim.x) {
+      const int g = (int)__popcll(__ballot(pre0 <= item)) + (int)__popcll(__ballot(pre1 <= item));
+      const int base = g == 0 ? 0
+                       : g <= 64 ? __builtin_amdgcn_readlane(pre0, g - 1)
+                                 : __builtin_amdgcn_readlane(pre1, g - 65);
+      const int qf = g * kQB;
+      run(item, make_int4(0, q0 + qf, plan_min(sq - qf, kQB), (item - base) * pc), pc);
+    }
+    return;
   }
+  const int n_items = a.hdr->n_items;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x)
+    run(item, a.items[item], a.hdr->pages_per_item);
 }
 
 }  // namespace
@@ -1313,25 +1354,78 @@ ScorePlan score_plan(const msa_varlen_t* vl, int H) {
 // The device plan (work list of a.H-head q-blocks) into the workspace, then the
 // scorer over (q, scores); per-head scoring runs the single-head scorer once per
 // head over the same plan.
+namespace {
+// A one-request batch planned on the host (no plan kernel, no work list).
+struct DirectPlan {
+  int32_t items = 0, pc = 0, sq = 0, ctx = 0;
+};
+}  // namespace
+
+// The device plan's choice for a single request, made on the host from the
+// descriptor's sizes: total_q is the request's query count; its token count is
+// known to within one page (total_rows pages, at most max_seqlen_k tokens), so
+// the plan takes the largest count that fits, which can only add items that
+// find no visible page and end at once.  Items are the same (q-block, chunk)
+// list the device plan writes, with q-blocks of up to kDirectMaxQBlocks.
+static bool plan_one_request(const msa_varlen_t& vl, int H, DirectPlan* d) {
+  if (vl.batch != 1 || vl.total_q <= 0) return false;
+  const int qb = score_qblock(H);
+  const int64_t sq = vl.total_q;
+  const int64_t sk = std::min<int64_t>((int64_t)vl.total_rows * kPage, vl.max_seqlen_k);
+  if (sk < sq || ceil_div(sq, qb) > kDirectMaxQBlocks) return false;
+  const int ctx = (int)(sk - sq), nqb = (int)ceil_div(sq, qb);
+  const int align = vl.max_seqlen_q <= score_qtiles(H) * 16 ? 4 : 1;
+  auto vis = [&](int g) { return qblock_visible(ctx, g * qb, (int)std::min<int64_t>(sq - g * qb, qb)); };
+  int64_t w = 0;
+  int vmin = INT32_MAX, vmax = 0;
+  for (int g = 0; g < nqb; ++g) {
+    w += vis(g);
+    vmin = std::min(vmin, vis(g));
+    vmax = std::max(vmax, vis(g));
+  }
+  int pc = cand_pages(w, 1, 4);
+  if (!plan_uniform(vmin, vmax)) {
+    int cand[kPlanCands], n[kPlanCands] = {};
+    plan_candidates(w, align, cand);
+    for (int g = 0; g < nqb; ++g)
+      for (int k = 0; k < kPlanCands; ++k) n[k] += (vis(g) + cand[k] - 1) / cand[k];
+    pc = best_pages(cand, n);
+  }
+  int64_t items = 0;
+  for (int g = 0; g < nqb; ++g) items += (vis(g) + pc - 1) / pc;
+  d->items = (int32_t)items;
+  d->pc = pc;
+  d->sq = (int32_t)sq;
+  d->ctx = ctx;
+  return true;
+}
+
 static hipError_t launch_plan(const ScoreArgs& a, hipStream_t stream);
 static hipError_t launch_scorer_pass(const ScoreArgs& a, const uint8_t* q, float* scores,
-                                     hipStream_t stream);
+                                     const DirectPlan& d, hipStream_t stream);
 
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
   if (a.vl.total_q == 0) return hipSuccess;
-  hipError_t e = launch_plan(a, stream);
-  if (e != hipSuccess) return e;
-  return launch_scorer_pass(a, a.q, a.scores, stream);
+  DirectPlan d;
+  if (!plan_one_request(a.vl, a.H, &d)) {
+    hipError_t e = launch_plan(a, stream);
+    if (e != hipSuccess) return e;
+  }
+  return launch_scorer_pass(a, a.q, a.scores, d, stream);
 }
 
 hipError_t launch_index_score_heads(const ScoreArgs& a, int64_t head_stride, hipStream_t stream) {
   if (a.vl.total_q == 0) return hipSuccess;
   ScoreArgs one = a;
   one.H = 1;                                  // every pass scores one index head
-  hipError_t e = launch_plan(one, stream);
-  if (e != hipSuccess) return e;
+  DirectPlan d;
+  if (!plan_one_request(one.vl, 1, &d)) {
+    hipError_t e = launch_plan(one, stream);
+    if (e != hipSuccess) return e;
+  }
   for (int h = 0; h < a.H; ++h) {
-    e = launch_scorer_pass(one, a.q + (int64_t)h * kDim, a.scores + (int64_t)h * head_stride, stream);
+    hipError_t e = launch_scorer_pass(one, a.q + (int64_t)h * kDim,
+                                      a.scores + (int64_t)h * head_stride, d, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -1381,6 +1475,7 @@ hipError_t launch_index_score_topk(const ScoreArgs& a, int n_local, int32_t* out
   k.cand = cand;
   k.first_item = first_item;
   k.n_local = n_local;
+  k.direct_items = 0;   // the merge reads the plan's list
   dim3 grid((unsigned)std::min<int64_t>(a.plan.max_items, device_cu_count()));
   switch (a.H) {
     case 1: e = launch_sel<1>(grid, stream, k); break;
@@ -1422,7 +1517,7 @@ static hipError_t launch_plan(const ScoreArgs& a, hipStream_t stream) {
 }
 
 static hipError_t launch_scorer_pass(const ScoreArgs& a, const uint8_t* q, float* scores,
-                                     hipStream_t stream) {
+                                     const DirectPlan& d, hipStream_t stream) {
   ItemHdr* hdr = reinterpret_cast<ItemHdr*>(a.workspace);
   int4* items = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(a.workspace) + sizeof(ItemHdr));
   ScoreK k;
@@ -1443,8 +1538,16 @@ static hipError_t launch_scorer_pass(const ScoreArgs& a, const uint8_t* q, float
   k.hdr = hdr;
   k.items = items;
   k.k_scales = a.k_scales;
+  k.cand = nullptr;
+  k.first_item = nullptr;
+  k.n_local = 0;
+  k.direct_items = d.items;
+  k.direct_pc = d.pc;
+  k.direct_sq = d.sq;
+  k.direct_ctx = d.ctx;
   // persistent blocks: one per compute unit (the kernels' LDS allows no more)
-  dim3 grid((unsigned)std::min<int64_t>(a.plan.max_items, device_cu_count()));
+  const int64_t n_blocks = d.items > 0 ? d.items : a.plan.max_items;
+  dim3 grid((unsigned)std::min<int64_t>(n_blocks, device_cu_count()));
   if (a.k_scales) return launch_scorer_h<1>(grid, stream, k, a.H, a.vl.max_seqlen_q);   // MXFP4 keys
   return launch_scorer_h<0>(grid, stream, k, a.H, a.vl.max_seqlen_q);
 }

@@ -225,6 +225,52 @@ def test_nan_codes_give_nan_scores(sq, sk, H):
     check_topk_exact_on_gpu_scores(inp, scores, sel)
 
 
+@pytest.mark.parametrize("sq,sk,H", [
+    (3000, 40077, 2),      # a chunk over a context: q-blocks of about equal reach
+    (3000, 3000, 4),       # a fresh prefill: uneven q-blocks, the plan weighs its sizes
+    (2048, 133000, 1),     # two q-blocks over 1,040 pages
+    (5, 70000, 1),         # one decode-like request: the page-parallel scorer
+])
+def test_one_request_plan_matches_device_plan(sq, sk, H):
+    """A one-request batch is planned on the host from the descriptor's sizes
+    (no plan kernel, no work list).  Its scores must equal, bit for bit, those
+    of the same request planned on the device (as the first of two requests,
+    the second empty) and those of a descriptor whose max_seqlen_k only bounds
+    the length (within the last page); and the oracle's on a sample."""
+    from fp8_top_page_amd import Varlen, msa_index_score, msa_index_score_workspace_size
+    from fp8_top_page_amd.pipeline import DeviceBatch
+    print(f"\n[parity] one-request plan sq={sq} sk={sk} H={H}", flush=True)
+    inp = _small_inputs((sq,), (sk,), H, 8, 1, seed=23)
+    db = DeviceBatch.from_inputs(inp)
+    ld = (db.max_pages + 3) // 4 * 4
+
+    def score(vl):
+        out = torch.full((db.total_q, ld), float("nan"), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(msa_index_score_workspace_size(vl, H), 256), dtype=torch.uint8,
+                         device="cuda")
+        msa_index_score(vl, db.index_q, H, db.k_cache, db.num_pages, db.iq_scale, db.ik_scale,
+                        out, ws)
+        torch.cuda.synchronize()
+        return out
+
+    direct = score(db.vl)
+    loose = score(Varlen(db.cu_q, db.cu_k, db.block_table, total_q=db.total_q,
+                         max_seqlen_q=db.max_seqlen_q,
+                         max_seqlen_k=min(db.max_pages * 128, sk + 100),
+                         total_rows=db.total_rows, max_pages=db.max_pages))
+    cu_q2 = torch.tensor([0, sq, sq], dtype=torch.int32, device="cuda")
+    cu_k2 = torch.tensor([0, sk, sk], dtype=torch.int32, device="cuda")
+    bt2 = torch.zeros((2, db.block_table.shape[1]), dtype=torch.int32, device="cuda")
+    bt2[0] = db.block_table[0]
+    listed = score(Varlen(cu_q2, cu_k2, bt2, total_q=db.total_q, max_seqlen_q=db.max_seqlen_q,
+                          max_seqlen_k=db.max_seqlen_k, total_rows=db.total_rows,
+                          max_pages=db.max_pages))
+    for name, other in (("loose max_seqlen_k", loose), ("device plan", listed)):
+        assert torch.equal(torch.isnan(direct), torch.isnan(other)), name
+        assert torch.equal(direct.nan_to_num(0.0), other.nan_to_num(0.0)), name
+    check_scores(inp, to_np(direct), spread_queries(inp, min(sq, 256), seed=3))
+
+
 def test_empty_batch_is_a_no_op():
     inp = _small_inputs((0, 0), (300, 128))
     path = run_path(inp)
