@@ -2,7 +2,7 @@
 """Benchmark of the MSA sparse-prefill hot path on one MI355X.
 
 One step = one pass of the whole path over one synthetic batch with inputs
-already resident in HBM: index scoring (device plan + fp8 scorer), top-16
+already resident in HBM: index scoring (work plan + fp8 scorer), top-16
 selection, KV-page -> query CSR build, and block-sparse attention (partials +
 combine).  The workload is 2048 new tokens at the end of a 1,048,576-token KV
 (8192 pages of 128), one index head, 8 query heads over one KV head, D = 128
@@ -11,12 +11,13 @@ combine).  The workload is 2048 new tokens at the end of a 1,048,576-token KV
 Prints ONE JSON line.  The GPU is first kept busy for --prewarm-ms so its
 clocks reach their sustained level, then W warmup steps run, then exactly K
 steps are timed (synchronised on both sides; `ms_per_step`).  `value` is the
-index-scoring time per layer in microseconds: the msa_index_score call (device
-plan + scorer) issued K times back to back on the stream the kernels run on,
-between two HIP events (so no event marker sits between the calls).  Each of
-the other calls is timed the same way for the breakdown.  Roofline,
-per-call times and the CPU oracle's time on a bounded sample are reported
-beside it.
+index-scoring time per layer in microseconds with a cold cache, as the pages
+measure it: the msa_index_score call (the scorer, after a plan kernel for
+batches of several requests; one request is planned on the host) timed by one
+HIP event pair on the kernels' stream after a 1 GiB read, mean of K calls.
+Each of the other calls is timed the same way for the breakdown, and also
+warm (K calls back to back between two events).  Roofline, per-call times and
+the CPU oracle's time on a bounded sample are reported beside it.
 """
 from __future__ import annotations
 
@@ -666,12 +667,12 @@ def main():
         result["value"] = round(score_us, 2)
         result["value_is"] = ("index_score_topk (plan + fused scorer + merge), cold, us per call"
                               if args.fused_select else
-                              "index_score (plan + scorer), cold, us per call")
+                              "index_score (plan if several requests + scorer), cold, us per call")
         result["roofline"] = {**score_roof,
                               "traffic": (scorer_hbm_traffic(wl.name) if args.index_cache == "e4m3"
                                           and not args.per_head and not args.fused_select
                                           else None),
-                              "kernel": "index_score (plan + scorer)",
+                              "kernel": "index_score (plan if several requests + scorer)",
                               "flops_per_launch": work["score_flops"],
                               "algorithmic_bytes_per_launch": work["score_bytes"],
                               "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + "

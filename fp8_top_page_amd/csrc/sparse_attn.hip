@@ -19,14 +19,15 @@
 //   l   = 1^T P^T         1 MFMA against a constant all-ones operand
 // Because S^T leaves each lane with tokens {16T + 4g + i} of one row, V^T is
 // stored with its token axis permuted to the same order, so no shuffles are
-// needed between the two products.  When an item has enough rows, a wave runs
-// two tiles per fragment read so each K/V fragment fetched from LDS feeds two
-// MFMAs.  Blocks are persistent: while one item is computed, the next item's
-// page and query list are already being fetched into registers.
+// needed between the two products.  (A form that runs two tiles per fragment
+// read is kept in the source, switched off.)  Blocks are persistent: while one
+// item is computed, the next item's page and query list are already being
+// fetched into registers.
 //
-// Each (query, q-head, page) split writes its unnormalised output row as
-// 12-bit floats (d permuted so that every lane stores 48 contiguous bytes) and the pair
-// (running max m in the log2 domain, probability sum l).  Split rows are laid
+// Each (query, q-head, page) split writes its unnormalised output row as int8
+// codes with one power-of-two scale per 16 values, staged in LDS so that whole
+// rows go out as 16-byte stores, with the pair (running max m in the log2
+// domain, probability sum l) in the same 144-byte row.  Split rows are laid
 // out query-major, (query, selection head, slot of the page in the query's
 // selection, head), so the combine reads a query's (at most 16) splits as one
 // contiguous run; a small pass before the partials maps every CSR position to
@@ -68,8 +69,8 @@ struct AttnK {
   float logit_scale_log2;          // softmax_scale * log2(e)
   const float* q_scale;
   const float* k_scale;
-  uint8_t* part_o;                 // [entries * HP + 1, 192 B]: 12-bit floats, unnormalised, d permuted
-  float2* part_ml;                 // [entries * HP + 1] (max in log2 units, probability sum)
+  uint8_t* part_o;                 // [entries * HP + 1] rows: int8 (144 B), or f12 (192 B) when chunked
+  float2* part_ml;                 // chunked kernel: [entries * HP + 1] (max in log2 units, probability sum)
   int32_t trash;                   // partial row written by rows past an item's end
   uint32_t part_o_bytes, part_ml_bytes;   // chunked kernel: ring sizes (buffer-op bounds)
 };
@@ -121,7 +122,49 @@ __device__ __forceinline__ void unpack8_f12(uint3 w, float (&v)[8]) {
   v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
   v[4] = c.x; v[5] = c.y; v[6] = d.x; v[7] = d.y;
 }
-constexpr int kRowBytes = kDim * 3 / 2;   // 192 bytes per partial row
+constexpr int kRowBytes = kDim * 3 / 2;   // 192 bytes per f12 partial row (chunked kernel)
+
+// Block-scaled int8 partials (the split rows of the default kernels): each
+// group of 16 values is stored as 8-bit integer codes with one power-of-two
+// scale, as in the OCP Microscaling MXINT8 format (blocks of 16 here).  With
+// e = floor(log2(max |x|)) - 6, the codes are the nearest integers of x 2^-e,
+// saturated to [-127, 127], and a value decodes as code * 2^e: the error is at
+// most 2^e <= max |x| / 64 for a saturated code and 2^(e-1) otherwise, i.e.
+// within 1/127 of the group's largest magnitude.  e = -128 marks a group that
+// held a NaN (it decodes as NaN); smaller scales than 2^-127 are not used.
+// A row is 144 bytes: 128 codes (value j at byte j), the split's (max, sum)
+// as two floats, and the 8 group exponents as signed bytes.
+constexpr int kRowBytesI8 = kDim + 16;
+constexpr int kI8Meta = kDim;             // byte offset of (max, sum, exponents)
+constexpr float kI8Magic = 12582912.f;    // 1.5 * 2^23: x + magic keeps rint(x) in its low mantissa bits
+__device__ __forceinline__ int quant16_i8(const float (&x)[16], uint4& q) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = __builtin_elementwise_maximum(amax, __builtin_fabsf(x[i]));
+  const int ex = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+  const int e = ex == 0xFF ? -128 : (ex - 133 < -127 ? -127 : ex - 133);
+  const float sc = __uint_as_float((uint32_t)(127 - e) << 23);    // 2^-e (inf for the NaN mark)
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // x 2^-e + magic rounds once to the nearest integer (ties to even); the
+      // clamp keeps the code within [-127, 127]; its low byte is the code
+      const float f = __builtin_amdgcn_fmed3f(__builtin_fmaf(x[4 * k + i], sc, kI8Magic),
+                                              kI8Magic - 127.f, kI8Magic + 127.f);
+      b[i] = __float_as_uint(f) & 0xFFu;
+    }
+    w[k] = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+  }
+  q = make_uint4(w[0], w[1], w[2], w[3]);
+  return e;
+}
+// 2^e for a group exponent byte (NaN for the NaN mark).
+__device__ __forceinline__ float i8_scale(int e) {
+  return e == -128 ? __builtin_nanf("") : __builtin_ldexpf(1.f, e);
+}
 
 // IEEE 754-2019 maximum (v_maximum_f32 / v_maximum3_f32): NaN-propagating, so
 // unlike fmaxf it needs no quieting moves on operands the compiler cannot prove
@@ -354,7 +397,7 @@ constexpr int kSc1 = 16;                  // buffer-op cache policy: device-scop
 template <int NT, bool kWt = false>
 __device__ __forceinline__ void compute_set(const AttnK& a, const RowSet<NT>& r,
                                             const uint8_t* k_lds, const uint8_t* vt_lds,
-                                            float zscale, int lane) {
+                                            uint8_t* stage, float zscale, int lane) {
   const int col = lane & 15, grp = lane >> 4;
   // The page fragments are re-read from LDS for every set rather than kept
   // live across sets (128 registers); the laundered zero offset stops the
@@ -421,9 +464,10 @@ __device__ __forceinline__ void compute_set(const AttnK& a, const RowSet<NT>& r,
 #pragma unroll
   for (int u = 0; u < NT; ++u) l[u] = mfma_e4m3(ones, pb[u], v4f{0.f, 0.f, 0.f, 0.f})[0];
 
-  // O^T = V^T P^T in two halves of 64 output dims, each stored as soon as it is
-  // done.  Lane (row, group g) holds d = 16 dt + 4 g + i; in the partial row
-  // those 32 values sit at 32 g + 4 dt + i, so a half is 32 contiguous bytes.
+  // O^T = V^T P^T in two halves of 64 output dims.  Lane (row, group g) holds
+  // d = 16 dt + 4 g + i; in the partial row those 32 values sit at
+  // 32 g + 4 dt + i, so a half is 32 contiguous bytes (24 packed).  The packed
+  // rows are staged in the wave's LDS area and then written out whole (below).
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     v4f o[NT][4];
@@ -435,33 +479,64 @@ __device__ __forceinline__ void compute_set(const AttnK& a, const RowSet<NT>& r,
     }
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-      const uint3 p0 = pack8_f12(o[u][0][0], o[u][0][1], o[u][0][2], o[u][0][3], o[u][1][0],
-                                 o[u][1][1], o[u][1][2], o[u][1][3]);
-      const uint3 p1 = pack8_f12(o[u][2][0], o[u][2][1], o[u][2][2], o[u][2][3], o[u][3][0],
-                                 o[u][3][1], o[u][3][2], o[u][3][3]);
       if constexpr (kWt) {
+        const uint3 p0 = pack8_f12(o[u][0][0], o[u][0][1], o[u][0][2], o[u][0][3], o[u][1][0],
+                                   o[u][1][1], o[u][1][2], o[u][1][3]);
+        const uint3 p1 = pack8_f12(o[u][2][0], o[u][2][1], o[u][2][2], o[u][2][3], o[u][3][0],
+                                   o[u][3][1], o[u][3][2], o[u][3][3]);
         const auto rs = buffer_rsrc(a.part_o, a.part_o_bytes);
         const int off = r.pidx[u] * kRowBytes + grp * 48 + half * 24;
         __builtin_amdgcn_raw_buffer_store_b96(v3u{p0.x, p0.y, p0.z}, rs, off, 0, kSc1);
         __builtin_amdgcn_raw_buffer_store_b96(v3u{p1.x, p1.y, p1.z}, rs, off + 12, 0, kSc1);
       } else {
-        uint3* dst = reinterpret_cast<uint3*>(a.part_o + (int64_t)r.pidx[u] * kRowBytes + grp * 48 +
-                                              half * 24);
-        dst[0] = p0;
-        dst[1] = p1;
+        // values 32 grp + 16 half + j (j = 4 k + i of o[u][k][i]) as one group
+        const float x[16] = {o[u][0][0], o[u][0][1], o[u][0][2], o[u][0][3],
+                             o[u][1][0], o[u][1][1], o[u][1][2], o[u][1][3],
+                             o[u][2][0], o[u][2][1], o[u][2][2], o[u][2][3],
+                             o[u][3][0], o[u][3][1], o[u][3][2], o[u][3][3]};
+        uint4 q;
+        const int e = quant16_i8(x, q);
+        uint8_t* row = stage + (u * 16 + col) * kRowBytesI8;
+        *reinterpret_cast<uint4*>(row + grp * 32 + half * 16) = q;
+        row[kI8Meta + 8 + 2 * grp + half] = (uint8_t)e;
       }
     }
   }
-  // every lane of a row holds the same (m, l)
+  if constexpr (kWt) {
 #pragma unroll
-  for (int u = 0; u < NT; ++u) {
-    if constexpr (kWt) {
+    for (int u = 0; u < NT; ++u) {
       const auto rs = buffer_rsrc(a.part_ml, a.part_ml_bytes);
       __builtin_amdgcn_raw_buffer_store_b64(v2u{__float_as_uint(mz[u]), __float_as_uint(l[u])}, rs,
                                             r.pidx[u] * 8, 0, kSc1);
-    } else {
-      a.part_ml[r.pidx[u]] = make_float2(mz[u], l[u]);
     }
+  } else {
+    // the row's (max, sum) beside its codes (every lane of a row holds them)
+#pragma unroll
+    for (int u = 0; u < NT; ++u)
+      if (grp == 0)
+        *reinterpret_cast<float2*>(stage + (u * 16 + col) * kRowBytesI8 + kI8Meta) =
+            make_float2(mz[u], l[u]);
+    // Whole rows out as 16-byte stores, lane c of the 144 pieces of a tile
+    // taking row c / 9, bytes 16 (c % 9): the rows of one query (its q-heads
+    // of this KV head) are consecutive in the split buffer, so a store
+    // instruction covers whole cache lines.  A wave's LDS operations complete
+    // in order: only the compiler is held here.
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    constexpr int kPieces = 16 * kRowBytesI8 / 16;
+#pragma unroll
+    for (int u = 0; u < NT; ++u)
+#pragma unroll
+      for (int k = 0; k < (kPieces + 63) / 64; ++k) {
+        const int c = k * 64 + lane;
+        const int row = c / 9, off = (c - row * 9) * 16;
+        const int prow = __shfl(r.pidx[u], row & 15);    // lane `row` holds that row's index
+        if (k * 64 + 64 <= kPieces || c < kPieces) {
+          const uint4 v = *reinterpret_cast<const uint4*>(stage + (u * 16 + row) * kRowBytesI8 + off);
+          *reinterpret_cast<uint4*>(a.part_o + (int64_t)prow * kRowBytesI8 + off) = v;
+        }
+      }
+    asm volatile("" ::: "memory");                      // the next set's staging stays behind
   }
 }
 
@@ -471,8 +546,8 @@ __device__ __forceinline__ void compute_set(const AttnK& a, const RowSet<NT>& r,
 // after the prefetch would also wait for the next page.
 template <int NT, bool kWt = false, class Prefetch>
 __device__ __forceinline__ void run_item(const AttnK& a, const Work& w, const uint8_t* k_lds,
-                                         const uint8_t* vt_lds, const int* s_qi, float zscale,
-                                         int wave, int lane, Prefetch&& prefetch) {
+                                         const uint8_t* vt_lds, uint8_t* stage, const int* s_qi,
+                                         float zscale, int wave, int lane, Prefetch&& prefetch) {
   constexpr int kStep = NT * kWaves;
   const int n_rows = w.count * a.G;
   const int n_tiles = (n_rows + 15) >> 4;
@@ -486,11 +561,11 @@ __device__ __forceinline__ void run_item(const AttnK& a, const Work& w, const ui
   __builtin_amdgcn_sched_barrier(0);
   for (;;) {
     if (t >= n_tiles) break;
-    compute_set<NT, kWt>(a, ra, k_lds, vt_lds, zscale, lane);
+    compute_set<NT, kWt>(a, ra, k_lds, vt_lds, stage, zscale, lane);
     ra = load_rows<NT>(a, w, t + 2 * kStep, n_rows, s_qi, lane);
     t += kStep;
     if (t >= n_tiles) break;
-    compute_set<NT, kWt>(a, rb, k_lds, vt_lds, zscale, lane);
+    compute_set<NT, kWt>(a, rb, k_lds, vt_lds, stage, zscale, lane);
     rb = load_rows<NT>(a, w, t + 2 * kStep, n_rows, s_qi, lane);
     t += kStep;
   }
@@ -501,8 +576,8 @@ __device__ __forceinline__ void run_item(const AttnK& a, const Work& w, const ui
 template <class Prefetch>
 __device__ __forceinline__ void run_item_narrow(const AttnK& a, const Work& w,
                                                 const uint8_t* k_lds, const uint8_t* vt_lds,
-                                                const int* s_qi, float zscale, int wave, int lane,
-                                                Prefetch&& prefetch) {
+                                                uint8_t* stage, const int* s_qi, float zscale,
+                                                int wave, int lane, Prefetch&& prefetch) {
   const int n_rows = w.count * a.G;
   const int n_tiles = (n_rows + 15) >> 4;
   int t = wave;
@@ -511,7 +586,7 @@ __device__ __forceinline__ void run_item_narrow(const AttnK& a, const Work& w,
   prefetch();
   __builtin_amdgcn_sched_barrier(0);
   while (t < n_tiles) {
-    compute_set<1>(a, r, k_lds, vt_lds, zscale, lane);
+    compute_set<1>(a, r, k_lds, vt_lds, stage, zscale, lane);
     t += kWaves;
     if (t >= n_tiles) break;
     r = load_rows<1>(a, w, t, n_rows, s_qi, lane);
@@ -526,6 +601,8 @@ __global__ __launch_bounds__(kThreads, kWide ? kBlocksWide : kBlocksNarrow) void
   __shared__ __attribute__((aligned(16))) uint8_t vt_lds[kDim * kRowB];
   __shared__ int s_qi[2 * kAttnQCMax];     // the item's queries, then their split slots
   __shared__ uint2 s_tab[kFp4 ? 256 : 1];  // E4M3 codes of the E2M1 magnitudes, per E8M0 scale
+  constexpr int kStageTiles = kWide ? 2 : 1;   // 16-row tiles per set
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[kWaves * kStageTiles * 16 * kRowBytesI8];
 
   const int n_items = *a.n_items;
   const int64_t n_work = (int64_t)n_items * a.GY;
@@ -537,6 +614,7 @@ __global__ __launch_bounds__(kThreads, kWide ? kBlocksWide : kBlocksNarrow) void
     s_tab[tid] = staged_magnitudes(tid);   // read after the first barrier of the item loop
   }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: loops below do not diverge
+  uint8_t* const stage = s_stage + wave * (kStageTiles * 16 * kRowBytesI8);   // the wave's staging rows
   const float zscale = a.logit_scale_log2 * (a.q_scale ? *a.q_scale : 1.f) *
                        (a.k_scale ? *a.k_scale : 1.f);
   // item of work index x (clamped to the last item, so the loads are always
@@ -597,11 +675,11 @@ __global__ __launch_bounds__(kThreads, kWide ? kBlocksWide : kBlocksNarrow) void
     };
     const int n_tiles = (cur.count * a.G + 15) >> 4;
     if (!kWide)
-      run_item_narrow(a, cur, k_lds, vt_lds, s_qi, zscale, wave, lane, prefetch);
+      run_item_narrow(a, cur, k_lds, vt_lds, stage, s_qi, zscale, wave, lane, prefetch);
     else if (n_tiles >= 2 * kWaves)
-      run_item<2>(a, cur, k_lds, vt_lds, s_qi, zscale, wave, lane, prefetch);
+      run_item<2>(a, cur, k_lds, vt_lds, stage, s_qi, zscale, wave, lane, prefetch);
     else
-      run_item<1>(a, cur, k_lds, vt_lds, s_qi, zscale, wave, lane, prefetch);
+      run_item<1>(a, cur, k_lds, vt_lds, stage, s_qi, zscale, wave, lane, prefetch);
     if (!has_next) break;
     cur = nxt;
     w = wn;
@@ -687,10 +765,11 @@ struct CombineK {
   int64_t out_stride;
 };
 
-// One block per query, Hq * 16 threads: thread t owns q-head t / 16 and the 12
-// bytes at 12 * (t % 16) of each split row, i.e. eight of the row's values (the
-// split rows of one (query, selection head) are contiguous, slot-major, with the
-// heads of each slot together).
+// One block per query, Hq * 16 threads: thread t owns q-head t / 16 and the 8
+// codes at 8 * (t % 16) of each split row, i.e. eight of the row's values, with
+// the row's (max, sum) and group exponents (the split rows of one (query,
+// selection head) are contiguous, slot-major, with the heads of each slot
+// together).
 __global__ __launch_bounds__(1024) void attn_combine_kernel(CombineK a) {
   const int64_t i = blockIdx.x;
   const int t = threadIdx.x;
@@ -704,27 +783,31 @@ __global__ __launch_bounds__(1024) void attn_combine_kernel(CombineK a) {
     // all split rows are loaded together; a slot without a split reads the
     // first slot's (finite) row and gets weight 0
     const int first = __builtin_ctz(m);
-    float2 ml[kTopK];
-    uint3 v[kTopK];
+    uint4 meta[kTopK];              // (max, sum, exponents 0..3, exponents 4..7)
+    uint2 v[kTopK];
 #pragma unroll
     for (int s = 0; s < kTopK; ++s) {
       const int64_t r = (e0 + (((m >> s) & 1u) ? s : first)) * a.HP + hp;
-      ml[s] = a.part_ml[r];
-      v[s] = *reinterpret_cast<const uint3*>(a.part_o + r * kRowBytes + 12 * c);
+      meta[s] = *reinterpret_cast<const uint4*>(a.part_o + r * kRowBytesI8 + kI8Meta);
+      v[s] = *reinterpret_cast<const uint2*>(a.part_o + r * kRowBytesI8 + 8 * c);
     }
     float M = -INFINITY;
 #pragma unroll
     for (int s = 0; s < kTopK; ++s)
-      M = ((m >> s) & 1u) ? __builtin_elementwise_maximum(M, ml[s].x) : M;
+      M = ((m >> s) & 1u) ? __builtin_elementwise_maximum(M, __uint_as_float(meta[s].x)) : M;
     float L = 0.f;
+    const int eshift = 8 * ((c >> 1) & 3);   // this thread's group exponent: byte c / 2
 #pragma unroll
     for (int s = 0; s < kTopK; ++s) {
-      const float wgt = ((m >> s) & 1u) ? __builtin_amdgcn_exp2f(ml[s].x - M) : 0.f;
-      float x[8];
-      unpack8_f12(v[s], x);
+      const float wgt = ((m >> s) & 1u) ? __builtin_amdgcn_exp2f(__uint_as_float(meta[s].x) - M) : 0.f;
+      const uint32_t ew = (c >> 3) ? meta[s].w : meta[s].z;
+      const float ws = wgt * i8_scale((int)(int8_t)(ew >> eshift));
 #pragma unroll
-      for (int k = 0; k < 8; ++k) o[k] += wgt * x[k];
-      L += wgt * ml[s].y;
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t word = k < 4 ? v[s].x : v[s].y;
+        o[k] += ws * (float)(int8_t)(word >> (8 * (k & 3)));
+      }
+      L += wgt * __uint_as_float(meta[s].y);
     }
     const float f = L > 0.f ? (a.v_scale ? *a.v_scale : 1.f) / L : 0.f;
 #pragma unroll
@@ -972,9 +1055,9 @@ __global__ __launch_bounds__(kThreads, kBlocksWide) void attn_fused_kernel(Fused
       };
       const int n_tiles = (cur.count * a.G + 15) >> 4;
       if (n_tiles >= 2 * kWaves)
-        run_item<2, true>(a, cur, k_lds, vt_lds, s_qi, zscale, wave, lane, prefetch);
+        run_item<2, true>(a, cur, k_lds, vt_lds, nullptr, s_qi, zscale, wave, lane, prefetch);
       else
-        run_item<1, true>(a, cur, k_lds, vt_lds, s_qi, zscale, wave, lane, prefetch);
+        run_item<1, true>(a, cur, k_lds, vt_lds, nullptr, s_qi, zscale, wave, lane, prefetch);
       cur = nxt;
     }
     // the item's split rows are written through before it counts as done
@@ -1023,8 +1106,10 @@ static AttnWs attn_ws(const msa_varlen_t* vl, int Hq, int n_sel, int topk) {
                    : partial_rows(vl, Hq, n_sel, topk);
   w.qcap = L.fused ? ceil_div(L.max_items, kQueues) + 6 * (int64_t)w.n_chunks + 8 : 0;
   size_t off = 0;
-  w.o = off;    off += align_up((size_t)(w.rows * kRowBytes), 256);
-  w.ml = off;   off += align_up((size_t)(w.rows * sizeof(float2)), 256);
+  // f12 rows and a (max, sum) array in the chunked kernel; 144-byte int8 rows
+  // that hold their (max, sum) otherwise
+  w.o = off;    off += align_up((size_t)(w.rows * (L.fused ? kRowBytes : kRowBytesI8)), 256);
+  w.ml = off;   off += L.fused ? align_up((size_t)(w.rows * sizeof(float2)), 256) : 256;
   w.slot = off; off += align_up((size_t)(std::max<int64_t>(entries, 1) * sizeof(int32_t)), 256);
   w.mask = off; off += align_up((size_t)(std::max<int64_t>(entries / topk, 1) * sizeof(uint32_t)), 256);
   w.queues = off;     off += align_up((size_t)(kQueues * w.qcap * sizeof(int2)), 256);
