@@ -204,8 +204,9 @@ def test_workspace_sizes_grow_with_the_batch():
     a = L.msa_sparse_attn_workspace_size(ctypes.byref(small), 8, 1, 1, 16)
     b = L.msa_sparse_attn_workspace_size(ctypes.byref(big), 8, 1, 1, 16)
     assert 0 < a < b
-    # partial rows: 16 slots x 8 heads x (128 12-bit values + max and sum) per query
-    assert b >= 2048 * 16 * 8 * (192 + 8)
+    # partial rows: 16 slots x 8 heads x 144 bytes (128 int8 codes, max and sum,
+    # 8 block exponents) per query
+    assert b >= 2048 * 16 * 8 * 144
 
 
 @pytest.mark.skipif(not NO_GPU, reason="host-pointer marshalling check, CPU container only")
