@@ -182,6 +182,14 @@ inline int32_t attn_item_queries(const msa_varlen_t* vl) {
       ceil_div((int64_t)vl->total_q * kTopK, vl->total_rows > 0 ? vl->total_rows : 1);
   return per_row >= kAttnQCMax ? kAttnQCMax : 32;
 }
+// Whether the attention stages each 16-row tile of split rows in LDS and writes
+// whole rows (rows averaging at least 16 queries: many tiles per item, so the
+// staging overlaps other tiles' work), or stores each lane's codes directly
+// (rows of a few queries, where an item is one or two tiles and the staging
+// round trip would sit on its critical path).
+inline bool attn_stage_rows(const msa_varlen_t* vl) {
+  return ceil_div((int64_t)vl->total_q * kTopK, vl->total_rows > 0 ? vl->total_rows : 1) >= 16;
+}
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace msa

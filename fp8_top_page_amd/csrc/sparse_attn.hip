@@ -394,7 +394,7 @@ typedef unsigned v3u __attribute__((ext_vector_type(3)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 constexpr int kSc1 = 16;                  // buffer-op cache policy: device-scope coherence
 
-template <int NT, bool kWt = false>
+template <int NT, bool kWt = false, bool kStage = true>
 __device__ __forceinline__ void compute_set(const AttnK& a, const RowSet<NT>& r,
                                             const uint8_t* k_lds, const uint8_t* vt_lds,
                                             uint8_t* stage, float zscale, int lane) {
@@ -464,6 +464,7 @@ __device__ __forceinline__ void compute_set(const AttnK& a, const RowSet<NT>& r,
 #pragma unroll
   for (int u = 0; u < NT; ++u) l[u] = mfma_e4m3(ones, pb[u], v4f{0.f, 0.f, 0.f, 0.f})[0];
 
+  uint32_t ex[NT] = {};              // unstaged rows: the lane's two group exponents
   // O^T = V^T P^T in two halves of 64 output dims.  Lane (row, group g) holds
   // d = 16 dt + 4 g + i; in the partial row those 32 values sit at
   // 32 g + 4 dt + i, so a half is 32 contiguous bytes (24 packed).  The packed
@@ -496,9 +497,15 @@ __device__ __forceinline__ void compute_set(const AttnK& a, const RowSet<NT>& r,
                              o[u][3][0], o[u][3][1], o[u][3][2], o[u][3][3]};
         uint4 q;
         const int e = quant16_i8(x, q);
-        uint8_t* row = stage + (u * 16 + col) * kRowBytesI8;
-        *reinterpret_cast<uint4*>(row + grp * 32 + half * 16) = q;
-        row[kI8Meta + 8 + 2 * grp + half] = (uint8_t)e;
+        if constexpr (kStage) {
+          uint8_t* row = stage + (u * 16 + col) * kRowBytesI8;
+          *reinterpret_cast<uint4*>(row + grp * 32 + half * 16) = q;
+          row[kI8Meta + 8 + 2 * grp + half] = (uint8_t)e;
+        } else {
+          *reinterpret_cast<uint4*>(a.part_o + (int64_t)r.pidx[u] * kRowBytesI8 + grp * 32 +
+                                    half * 16) = q;
+          ex[u] |= (uint32_t)(e & 0xFF) << (8 * half);
+        }
       }
     }
   }
@@ -508,6 +515,15 @@ __device__ __forceinline__ void compute_set(const AttnK& a, const RowSet<NT>& r,
       const auto rs = buffer_rsrc(a.part_ml, a.part_ml_bytes);
       __builtin_amdgcn_raw_buffer_store_b64(v2u{__float_as_uint(mz[u]), __float_as_uint(l[u])}, rs,
                                             r.pidx[u] * 8, 0, kSc1);
+    }
+  } else if constexpr (!kStage) {
+    // each lane's two group exponents (its 16-bit piece of the row's 8), and
+    // the row's (max, sum) from one lane of the row
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      uint8_t* row = a.part_o + (int64_t)r.pidx[u] * kRowBytesI8;
+      *reinterpret_cast<uint16_t*>(row + kI8Meta + 8 + 2 * grp) = (uint16_t)ex[u];
+      if (grp == 0) *reinterpret_cast<float2*>(row + kI8Meta) = make_float2(mz[u], l[u]);
     }
   } else {
     // the row's (max, sum) beside its codes (every lane of a row holds them)
@@ -573,7 +589,7 @@ __device__ __forceinline__ void run_item(const AttnK& a, const Work& w, const ui
 
 // Items of a few rows: one-tile sets, rows requested one set ahead only (a wave
 // rarely has a second set), which keeps the register count at three blocks per CU.
-template <class Prefetch>
+template <bool kStage, class Prefetch>
 __device__ __forceinline__ void run_item_narrow(const AttnK& a, const Work& w,
                                                 const uint8_t* k_lds, const uint8_t* vt_lds,
                                                 uint8_t* stage, const int* s_qi, float zscale,
@@ -586,7 +602,7 @@ __device__ __forceinline__ void run_item_narrow(const AttnK& a, const Work& w,
   prefetch();
   __builtin_amdgcn_sched_barrier(0);
   while (t < n_tiles) {
-    compute_set<1>(a, r, k_lds, vt_lds, stage, zscale, lane);
+    compute_set<1, false, kStage>(a, r, k_lds, vt_lds, stage, zscale, lane);
     t += kWaves;
     if (t >= n_tiles) break;
     r = load_rows<1>(a, w, t, n_rows, s_qi, lane);
@@ -594,7 +610,7 @@ __device__ __forceinline__ void run_item_narrow(const AttnK& a, const Work& w,
 }
 
 // kFp4: MXFP4 K|V pages, turned into E4M3 while they are staged in LDS.
-template <bool kWide, bool kFp4>
+template <bool kWide, bool kFp4, bool kStage>
 __global__ __launch_bounds__(kThreads, kWide ? kBlocksWide : kBlocksNarrow) void attn_partial_kernel(
     AttnK a) {
   __shared__ __attribute__((aligned(16))) uint8_t k_lds[kPage * kRowB];
@@ -602,7 +618,8 @@ __global__ __launch_bounds__(kThreads, kWide ? kBlocksWide : kBlocksNarrow) void
   __shared__ int s_qi[2 * kAttnQCMax];     // the item's queries, then their split slots
   __shared__ uint2 s_tab[kFp4 ? 256 : 1];  // E4M3 codes of the E2M1 magnitudes, per E8M0 scale
   constexpr int kStageTiles = kWide ? 2 : 1;   // 16-row tiles per set
-  __shared__ __attribute__((aligned(16))) uint8_t s_stage[kWaves * kStageTiles * 16 * kRowBytesI8];
+  __shared__ __attribute__((aligned(16)))
+  uint8_t s_stage[kStage || kWide ? kWaves * kStageTiles * 16 * kRowBytesI8 : 16];
 
   const int n_items = *a.n_items;
   const int64_t n_work = (int64_t)n_items * a.GY;
@@ -675,7 +692,7 @@ __global__ __launch_bounds__(kThreads, kWide ? kBlocksWide : kBlocksNarrow) void
     };
     const int n_tiles = (cur.count * a.G + 15) >> 4;
     if (!kWide)
-      run_item_narrow(a, cur, k_lds, vt_lds, stage, s_qi, zscale, wave, lane, prefetch);
+      run_item_narrow<kStage>(a, cur, k_lds, vt_lds, stage, s_qi, zscale, wave, lane, prefetch);
     else if (n_tiles >= 2 * kWaves)
       run_item<2>(a, cur, k_lds, vt_lds, stage, s_qi, zscale, wave, lane, prefetch);
     else
@@ -1223,18 +1240,20 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
     const int per_cu = wide ? kBlocksWide : kBlocksNarrow;
     const int64_t grid = std::min<int64_t>(max_work, (int64_t)device_cu_count() * per_cu);
     const bool fp4 = a.kv_scales != nullptr;
+    const bool stage = attn_stage_rows(&a.vl);
+    const dim3 g((unsigned)grid), b(kThreads);
     if (wide && fp4)
-      hipLaunchKernelGGL((attn_partial_kernel<true, true>), dim3((unsigned)grid), dim3(kThreads), 0,
-                         stream, k);
+      hipLaunchKernelGGL((attn_partial_kernel<true, true, true>), g, b, 0, stream, k);
     else if (wide)
-      hipLaunchKernelGGL((attn_partial_kernel<true, false>), dim3((unsigned)grid), dim3(kThreads), 0,
-                         stream, k);
+      hipLaunchKernelGGL((attn_partial_kernel<true, false, true>), g, b, 0, stream, k);
+    else if (fp4 && stage)
+      hipLaunchKernelGGL((attn_partial_kernel<false, true, true>), g, b, 0, stream, k);
     else if (fp4)
-      hipLaunchKernelGGL((attn_partial_kernel<false, true>), dim3((unsigned)grid), dim3(kThreads), 0,
-                         stream, k);
+      hipLaunchKernelGGL((attn_partial_kernel<false, true, false>), g, b, 0, stream, k);
+    else if (stage)
+      hipLaunchKernelGGL((attn_partial_kernel<false, false, true>), g, b, 0, stream, k);
     else
-      hipLaunchKernelGGL((attn_partial_kernel<false, false>), dim3((unsigned)grid), dim3(kThreads), 0,
-                         stream, k);
+      hipLaunchKernelGGL((attn_partial_kernel<false, false, false>), g, b, 0, stream, k);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
