@@ -161,6 +161,17 @@ __device__ __forceinline__ int quant16_i8(const float (&x)[16], uint4& q) {
   q = make_uint4(w[0], w[1], w[2], w[3]);
   return e;
 }
+// A block barrier that orders LDS only: the waves' LDS operations complete,
+// then all waves meet.  __syncthreads also waits for every global store in
+// flight, and the partial kernel's item boundaries need no such wait (its
+// split rows are read by the combine, a later launch), so the stores of one
+// item drain while the next is staged.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // 2^e for a group exponent byte (NaN for the NaN mark).
 __device__ __forceinline__ float i8_scale(int e) {
   return e == -128 ? __builtin_nanf("") : __builtin_ldexpf(1.f, e);
@@ -589,7 +600,7 @@ __device__ __forceinline__ void run_item(const AttnK& a, const Work& w, const ui
 
 // Items of a few rows: one-tile sets, rows requested one set ahead only (a wave
 // rarely has a second set), which keeps the register count at three blocks per CU.
-template <bool kStage, class Prefetch>
+template <bool kStage, bool kPeel, class Prefetch>
 __device__ __forceinline__ void run_item_narrow(const AttnK& a, const Work& w,
                                                 const uint8_t* k_lds, const uint8_t* vt_lds,
                                                 uint8_t* stage, const int* s_qi, float zscale,
@@ -601,11 +612,27 @@ __device__ __forceinline__ void run_item_narrow(const AttnK& a, const Work& w,
   __builtin_amdgcn_sched_barrier(0);        // keep the row loads ahead of the prefetch
   prefetch();
   __builtin_amdgcn_sched_barrier(0);
-  while (t < n_tiles) {
+  if constexpr (kPeel) {
+    // Items of one or two tiles: the first set is computed outside the loop.
+    // On this path the compiler knows how many loads (the prefetch) follow its
+    // rows and waits for the rows alone; at a loop header shared with the back
+    // edge it would wait for every load in flight, i.e. for the next item's
+    // page as well.  (Items of many tiles keep the loop: there the page wait
+    // is spread over many sets, and a second copy of the set's code would
+    // not fit the registers; nor does it with MXFP4 pages.)
+    if (t >= n_tiles) return;
     compute_set<1, false, kStage>(a, r, k_lds, vt_lds, stage, zscale, lane);
-    t += kWaves;
-    if (t >= n_tiles) break;
-    r = load_rows<1>(a, w, t, n_rows, s_qi, lane);
+    for (t += kWaves; t < n_tiles; t += kWaves) {
+      r = load_rows<1>(a, w, t, n_rows, s_qi, lane);
+      compute_set<1, false, kStage>(a, r, k_lds, vt_lds, stage, zscale, lane);
+    }
+  } else {
+    while (t < n_tiles) {
+      compute_set<1, false, kStage>(a, r, k_lds, vt_lds, stage, zscale, lane);
+      t += kWaves;
+      if (t >= n_tiles) break;
+      r = load_rows<1>(a, w, t, n_rows, s_qi, lane);
+    }
   }
 }
 
@@ -636,44 +663,40 @@ __global__ __launch_bounds__(kThreads, kWide ? kBlocksWide : kBlocksNarrow) void
                        (a.k_scale ? *a.k_scale : 1.f);
   // item of work index x (clamped to the last item, so the loads are always
   // valid), through the order table when there is one
-  auto item_of = [&](int64_t x) -> int64_t {
+  // (32-bit: item counts are checked against INT32_MAX, and a 64-bit index
+  // would be sign-extended right after the table load, i.e. waited for there)
+  auto item_of = [&](int64_t x) -> int {
     const int64_t it = x / a.GY;
-    const int64_t c = it < n_items - 1 ? it : (int64_t)(n_items - 1);
-    if (a.perm) return (int64_t)a.perm[c];   // only long rows are ordered
+    const int c = (int)(it < n_items - 1 ? it : (int64_t)(n_items - 1));
+    if (a.perm) return a.perm[c];   // only long rows are ordered
     return c;
   };
 
   // prologue: the first item's page in registers, the second item's metadata in
-  // flight.  With an order table (wide kernel), the item index of the one after
-  // that is known too: a table lookup is made one work step before the item's
-  // metadata is requested, so requesting it never waits on a load issued after
-  // a page fetch.  (The narrow kernel keeps the plain sequence: the ordered one
-  // compiled to a slower schedule there.)
+  // flight, and the index of the item after that (an order-table lookup, when
+  // there is one) known: a table lookup is made one work step before the
+  // item's metadata is requested, so neither waits on a load issued after a
+  // page fetch (memory operations complete in issue order).
   Work cur;
   typename std::conditional<kFp4, PageRegs4, PageRegs>::type pr;
   int4 mx, my;
-  int64_t i_nn = 0;
-  if constexpr (kWide) {
-    const int64_t i0 = item_of(w), i1 = item_of(w + gridDim.x);
+  int i_nn;
+  {
+    const int i0 = item_of(w), i1 = item_of(w + gridDim.x);
     i_nn = item_of(w + 2 * (int64_t)gridDim.x);
     cur = decode_work(a, w, a.items[2 * i0], a.items[2 * i0 + 1]);
     mx = a.items[2 * i1];
     my = a.items[2 * i1 + 1];
     fetch_page(pr, a, cur, tid);
-  } else {
-    cur = decode_work(a, w, a.items[2 * item_of(w)], a.items[2 * item_of(w) + 1]);
-    fetch_page(pr, a, cur, tid);
-    mx = a.items[2 * item_of(w + gridDim.x)];
-    my = a.items[2 * item_of(w + gridDim.x) + 1];
   }
 
   for (;;) {
-    __syncthreads();                         // the previous item is done with LDS
+    lds_barrier();                           // the previous item is done with LDS
     if constexpr (kFp4)
       stage_page(to_e4m3(pr, s_tab), cur, k_lds, vt_lds, s_qi, tid);
     else
       stage_page(pr, cur, k_lds, vt_lds, s_qi, tid);
-    __syncthreads();
+    lds_barrier();
     const int64_t wn = w + gridDim.x;
     const bool has_next = wn < n_work;
     // past the last item the "next" item is the current one again: its loads
@@ -681,18 +704,14 @@ __global__ __launch_bounds__(kThreads, kWide ? kBlocksWide : kBlocksNarrow) void
     const Work nxt = has_next ? decode_work(a, wn, mx, my) : cur;
     auto prefetch = [&]() {
       fetch_page(pr, a, nxt, tid);
-      if constexpr (kWide) {
-        mx = a.items[2 * i_nn];
-        my = a.items[2 * i_nn + 1];
-        i_nn = item_of(wn + 2 * (int64_t)gridDim.x);
-      } else {
-        mx = a.items[2 * item_of(wn + gridDim.x)];
-        my = a.items[2 * item_of(wn + gridDim.x) + 1];
-      }
+      mx = a.items[2 * i_nn];
+      my = a.items[2 * i_nn + 1];
+      i_nn = item_of(wn + 2 * (int64_t)gridDim.x);
     };
     const int n_tiles = (cur.count * a.G + 15) >> 4;
     if (!kWide)
-      run_item_narrow<kStage>(a, cur, k_lds, vt_lds, stage, s_qi, zscale, wave, lane, prefetch);
+      run_item_narrow<kStage, !kStage && !kFp4>(a, cur, k_lds, vt_lds, stage, s_qi, zscale, wave,
+                                                lane, prefetch);
     else if (n_tiles >= 2 * kWaves)
       run_item<2>(a, cur, k_lds, vt_lds, stage, s_qi, zscale, wave, lane, prefetch);
     else
