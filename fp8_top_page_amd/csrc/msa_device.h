@@ -68,6 +68,16 @@ __device__ __forceinline__ float sum_across_groups(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// A block barrier that orders LDS only: the waves' LDS operations complete,
+// then all waves meet.  __syncthreads also waits for every global memory
+// operation in flight (stores included: on gfx950 loads and stores share one
+// counter), which a barrier that only hands LDS between waves does not need.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Raw buffer resource over `bytes` bytes at p: buffer loads past the end return
 // zero instead of reading memory, and stores past it are dropped.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {

@@ -161,17 +161,6 @@ __device__ __forceinline__ int quant16_i8(const float (&x)[16], uint4& q) {
   q = make_uint4(w[0], w[1], w[2], w[3]);
   return e;
 }
-// A block barrier that orders LDS only: the waves' LDS operations complete,
-// then all waves meet.  __syncthreads also waits for every global store in
-// flight, and the partial kernel's item boundaries need no such wait (its
-// split rows are read by the combine, a later launch), so the stores of one
-// item drain while the next is staged.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // 2^e for a group exponent byte (NaN for the NaN mark).
 __device__ __forceinline__ float i8_scale(int e) {
   return e == -128 ? __builtin_nanf("") : __builtin_ldexpf(1.f, e);
