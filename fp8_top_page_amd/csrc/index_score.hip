@@ -59,7 +59,8 @@ constexpr int kPlanCUs = 256;                // compute units the item sizing ai
 constexpr int kPlanRounds = 6;               // item sizes for about k rounds of kPlanCUs items, k = 1..6,
 constexpr int kPlanCands = kPlanRounds + 3;   // and three sizes at and just above one round's
 constexpr int kPlanLoopItems = 16;           // items per q-block up to which its thread writes them
-constexpr int kDirectMaxQBlocks = 128;       // one-request batches planned on the host, at most
+constexpr int kDirectMaxQBlocks = 128;       // q-blocks of a batch planned without the plan kernel, at most
+constexpr int kWavePlanMaxB = 64;            // requests of a batch planned by the scorer's waves, at most
 
 struct ItemHdr {
   int32_t n_items;
@@ -95,6 +96,11 @@ struct ScoreK {
   int32_t direct_pc;
   int32_t direct_sq;         // the request's queries
   int32_t direct_ctx;        // its context: seqlen_k - seqlen_q
+  // A batch of at most kWavePlanMaxB requests and kDirectMaxQBlocks q-blocks:
+  // every wave plans it from cu_seqlens (wave_plan != 0), with this alignment
+  // of the chunk sizes (plan_align), instead of reading hdr / items.
+  int32_t wave_plan;
+  int32_t plan_align;
 };
 
 // ---------------------------------------------------------------------------
@@ -1297,6 +1303,65 @@ __device__ __forceinline__ void take_items(const ScoreK& a, uint8_t* lds) {
     }
     return;
   }
+  if (a.wave_plan) {
+    // Several requests, planned by every wave from cu_seqlens: the plan
+    // kernel's sizing and item order, in registers.  Lane b holds request b,
+    // lane l q-blocks l and 64 + l.
+    constexpr int kQB = score_qblock(H);
+    const int lane = threadIdx.x & 63;
+    const int B = a.batch;
+    const int rb = lane < B ? lane : B - 1;
+    const int q0r = a.cu_q[rb];
+    const int sqr = lane < B ? a.cu_q[rb + 1] - q0r : 0;
+    const int ctxr = (a.cu_k[rb + 1] - a.cu_k[rb]) - sqr;
+    const int nqbr = (sqr + kQB - 1) / kQB;                  // q-blocks of request `lane`
+    const int preq = wave_inclusive_scan(nqbr);
+    const int nqb = __builtin_amdgcn_readlane(preq, 63);
+    struct QB { int b, qf, qn, v; };
+    auto qblock = [&](int g) {
+      int cnt = 0;                                           // requests ending at or before g
+      for (int k = 0; k < B; ++k) cnt += __builtin_amdgcn_readlane(preq, k) <= g ? 1 : 0;
+      QB r;
+      r.b = cnt < B ? cnt : B - 1;
+      r.qf = (g - (__shfl(preq, r.b) - __shfl(nqbr, r.b))) * kQB;
+      r.qn = plan_min(__shfl(sqr, r.b) - r.qf, kQB);
+      // every lane takes part in the shuffle (a lane reading from an inactive
+      // one would get 0), so it is not inside the condition
+      const int ctx = __shfl(ctxr, r.b);
+      r.v = g < nqb ? qblock_visible(ctx, r.qf, r.qn) : 0;
+      return r;
+    };
+    const QB g0 = qblock(lane), g1 = qblock(64 + lane);
+    const int64_t w = wave_sum64((int64_t)g0.v + g1.v);
+    const int vmin = wave_min(plan_min(lane < nqb ? g0.v : INT32_MAX, 64 + lane < nqb ? g1.v : INT32_MAX));
+    const int vmax = wave_max(plan_max(g0.v, g1.v));
+    int pc = cand_pages(w, 1, 4);
+    if (!plan_uniform(vmin, vmax)) {
+      int cand[kPlanCands], n[kPlanCands];
+      plan_candidates(w, a.plan_align, cand);
+#pragma unroll
+      for (int k = 0; k < kPlanCands; ++k)
+        n[k] = wave_sum((g0.v + cand[k] - 1) / cand[k] + (g1.v + cand[k] - 1) / cand[k]);
+      pc = best_pages(cand, n);
+    }
+    pc = __builtin_amdgcn_readfirstlane(pc);     // equal in every lane; made known as such
+    const int pre0 = wave_inclusive_scan((g0.v + pc - 1) / pc);
+    const int pre1 = wave_inclusive_scan((g1.v + pc - 1) / pc) + __builtin_amdgcn_readlane(pre0, 63);
+    const int n_items = __builtin_amdgcn_readlane(pre1, 63);
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+      const int g = (int)__popcll(__ballot(pre0 <= item)) + (int)__popcll(__ballot(pre1 <= item));
+      const int base = g == 0 ? 0
+                       : g <= 64 ? __builtin_amdgcn_readlane(pre0, g - 1)
+                                 : __builtin_amdgcn_readlane(pre1, g - 65);
+      const int gl = g & 63;
+      const bool lo = g < 64;
+      const int b = __builtin_amdgcn_readlane(lo ? g0.b : g1.b, gl);
+      const int qf = __builtin_amdgcn_readlane(lo ? g0.qf : g1.qf, gl);
+      const int qn = __builtin_amdgcn_readlane(lo ? g0.qn : g1.qn, gl);
+      run(item, make_int4(b, __builtin_amdgcn_readlane(q0r, b) + qf, qn, (item - base) * pc), pc);
+    }
+    return;
+  }
   const int n_items = a.hdr->n_items;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x)
     run(item, a.items[item], a.hdr->pages_per_item);
@@ -1358,6 +1423,7 @@ namespace {
 // A one-request batch planned on the host (no plan kernel, no work list).
 struct DirectPlan {
   int32_t items = 0, pc = 0, sq = 0, ctx = 0;
+  int32_t wave = 0, align = 1;     // planned by the scorer's waves, with this chunk alignment
 };
 }  // namespace
 
@@ -1400,6 +1466,18 @@ static bool plan_one_request(const msa_varlen_t& vl, int H, DirectPlan* d) {
   return true;
 }
 
+// Batches of 2..kWavePlanMaxB requests and at most kDirectMaxQBlocks q-blocks
+// are planned by the scorer's waves themselves (the q-block count is bounded
+// by ceil(total_q / q-block) + batch).
+static bool plan_in_waves(const msa_varlen_t& vl, int H, DirectPlan* d) {
+  if (vl.batch < 2 || vl.batch > kWavePlanMaxB ||
+      ceil_div(vl.total_q, score_qblock(H)) + vl.batch > kDirectMaxQBlocks)
+    return false;
+  d->wave = 1;
+  d->align = vl.max_seqlen_q <= score_qtiles(H) * 16 ? 4 : 1;   // as the plan kernel's
+  return true;
+}
+
 static hipError_t launch_plan(const ScoreArgs& a, hipStream_t stream);
 static hipError_t launch_scorer_pass(const ScoreArgs& a, const uint8_t* q, float* scores,
                                      const DirectPlan& d, hipStream_t stream);
@@ -1407,7 +1485,7 @@ static hipError_t launch_scorer_pass(const ScoreArgs& a, const uint8_t* q, float
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t stream) {
   if (a.vl.total_q == 0) return hipSuccess;
   DirectPlan d;
-  if (!plan_one_request(a.vl, a.H, &d)) {
+  if (!plan_one_request(a.vl, a.H, &d) && !plan_in_waves(a.vl, a.H, &d)) {
     hipError_t e = launch_plan(a, stream);
     if (e != hipSuccess) return e;
   }
@@ -1419,7 +1497,7 @@ hipError_t launch_index_score_heads(const ScoreArgs& a, int64_t head_stride, hip
   ScoreArgs one = a;
   one.H = 1;                                  // every pass scores one index head
   DirectPlan d;
-  if (!plan_one_request(one.vl, 1, &d)) {
+  if (!plan_one_request(one.vl, 1, &d) && !plan_in_waves(one.vl, 1, &d)) {
     hipError_t e = launch_plan(one, stream);
     if (e != hipSuccess) return e;
   }
@@ -1476,6 +1554,7 @@ hipError_t launch_index_score_topk(const ScoreArgs& a, int n_local, int32_t* out
   k.first_item = first_item;
   k.n_local = n_local;
   k.direct_items = 0;   // the merge reads the plan's list
+  k.wave_plan = 0;
   dim3 grid((unsigned)std::min<int64_t>(a.plan.max_items, device_cu_count()));
   switch (a.H) {
     case 1: e = launch_sel<1>(grid, stream, k); break;
@@ -1545,6 +1624,8 @@ static hipError_t launch_scorer_pass(const ScoreArgs& a, const uint8_t* q, float
   k.direct_pc = d.pc;
   k.direct_sq = d.sq;
   k.direct_ctx = d.ctx;
+  k.wave_plan = d.wave;
+  k.plan_align = d.align;
   // persistent blocks: one per compute unit (the kernels' LDS allows no more)
   const int64_t n_blocks = d.items > 0 ? d.items : a.plan.max_items;
   dim3 grid((unsigned)std::min<int64_t>(n_blocks, device_cu_count()));

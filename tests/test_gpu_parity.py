@@ -230,16 +230,18 @@ def test_nan_codes_give_nan_scores(sq, sk, H):
     (3000, 3000, 4),       # a fresh prefill: uneven q-blocks, the plan weighs its sizes
     (2048, 133000, 1),     # two q-blocks over 1,040 pages
     (5, 70000, 1),         # one decode-like request: the page-parallel scorer
+    (33000, 33000, 4),     # 129 q-blocks: too many to plan without a plan kernel
 ])
-def test_one_request_plan_matches_device_plan(sq, sk, H):
-    """A one-request batch is planned on the host from the descriptor's sizes
-    (no plan kernel, no work list).  Its scores must equal, bit for bit, those
-    of the same request planned on the device (as the first of two requests,
-    the second empty) and those of a descriptor whose max_seqlen_k only bounds
-    the length (within the last page); and the oracle's on a sample."""
+def test_plans_agree(sq, sk, H):
+    """The scorer's work is planned on the host (one request), by the scorer's
+    own waves (2..64 requests, at most 128 q-blocks) or by a plan kernel (more).
+    One request scored alone, with one empty request after it, and with 65
+    empty requests after it -- and with a max_seqlen_k that only bounds its
+    length -- must give the same scores bit for bit, and the oracle's on a
+    sample."""
     from fp8_top_page_amd import Varlen, msa_index_score, msa_index_score_workspace_size
     from fp8_top_page_amd.pipeline import DeviceBatch
-    print(f"\n[parity] one-request plan sq={sq} sk={sk} H={H}", flush=True)
+    print(f"\n[parity] plans sq={sq} sk={sk} H={H}", flush=True)
     inp = _small_inputs((sq,), (sk,), H, 8, 1, seed=23)
     db = DeviceBatch.from_inputs(inp)
     ld = (db.max_pages + 3) // 4 * 4
@@ -253,22 +255,25 @@ def test_one_request_plan_matches_device_plan(sq, sk, H):
         torch.cuda.synchronize()
         return out
 
-    direct = score(db.vl)
+    def with_empty(n_empty):
+        cu_q = torch.tensor([0] + [sq] * (n_empty + 1), dtype=torch.int32, device="cuda")
+        cu_k = torch.tensor([0] + [sk] * (n_empty + 1), dtype=torch.int32, device="cuda")
+        bt = torch.zeros((n_empty + 1, db.block_table.shape[1]), dtype=torch.int32, device="cuda")
+        bt[0] = db.block_table[0]
+        return Varlen(cu_q, cu_k, bt, total_q=db.total_q, max_seqlen_q=db.max_seqlen_q,
+                      max_seqlen_k=db.max_seqlen_k, total_rows=db.total_rows,
+                      max_pages=db.max_pages)
+
+    alone = score(db.vl)
     loose = score(Varlen(db.cu_q, db.cu_k, db.block_table, total_q=db.total_q,
                          max_seqlen_q=db.max_seqlen_q,
                          max_seqlen_k=min(db.max_pages * 128, sk + 100),
                          total_rows=db.total_rows, max_pages=db.max_pages))
-    cu_q2 = torch.tensor([0, sq, sq], dtype=torch.int32, device="cuda")
-    cu_k2 = torch.tensor([0, sk, sk], dtype=torch.int32, device="cuda")
-    bt2 = torch.zeros((2, db.block_table.shape[1]), dtype=torch.int32, device="cuda")
-    bt2[0] = db.block_table[0]
-    listed = score(Varlen(cu_q2, cu_k2, bt2, total_q=db.total_q, max_seqlen_q=db.max_seqlen_q,
-                          max_seqlen_k=db.max_seqlen_k, total_rows=db.total_rows,
-                          max_pages=db.max_pages))
-    for name, other in (("loose max_seqlen_k", loose), ("device plan", listed)):
-        assert torch.equal(torch.isnan(direct), torch.isnan(other)), name
-        assert torch.equal(direct.nan_to_num(0.0), other.nan_to_num(0.0)), name
-    check_scores(inp, to_np(direct), spread_queries(inp, min(sq, 256), seed=3))
+    for name, other in (("loose max_seqlen_k", loose), ("one empty request after", score(with_empty(1))),
+                        ("65 empty requests after", score(with_empty(65)))):
+        assert torch.equal(torch.isnan(alone), torch.isnan(other)), name
+        assert torch.equal(alone.nan_to_num(0.0), other.nan_to_num(0.0)), name
+    check_scores(inp, to_np(alone), spread_queries(inp, min(sq, 256), seed=3))
 
 
 def test_empty_batch_is_a_no_op():

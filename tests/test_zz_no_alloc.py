@@ -1,8 +1,11 @@
 """msa_index_score_noalloc (work list in the library's built-in buffer) against
 msa_index_score (work list in a caller workspace), through the C ABI: calls in
-a row on one stream -- a prefill chunk, then a smaller decode batch, then a
-smaller ragged batch -- each bit-identical to the workspace call's scores,
-entries past the visible pages left unwritten by both."""
+a row on one stream -- a prefill chunk (one request, planned on the host), then
+a decode batch of 80 requests and a smaller ragged batch of 70 (more requests
+than the scorer's waves plan themselves, so both go through the plan kernel
+and the built-in buffer, the second call smaller than the first), then a
+3-request batch that the waves plan -- each bit-identical to the workspace
+call's scores, entries past the visible pages left unwritten by both."""
 import numpy as np
 import pytest
 import torch
@@ -16,8 +19,9 @@ pytestmark = pytest.mark.gpu
 
 CASES = [
     ("prefill chunk", (3000,), (40000,), 4),          # 3000 queries, prefill scorer
-    ("decode batch", (8,) * 24, (9000,) * 24, 1),     # 192 queries, page-parallel scorer
-    ("ragged batch", (200, 0, 50), (5000, 100, 900), 2),   # 250 queries
+    ("decode batch", (8,) * 80, (9000,) * 80, 1),     # 640 queries, page-parallel scorer
+    ("ragged batch", (200, 0, 50) + (3,) * 67, (5000, 100, 900) + (700,) * 67, 2),   # 451 queries
+    ("small batch", (200, 0, 50), (5000, 100, 900), 2),   # 250 queries
 ]
 
 
