@@ -357,7 +357,9 @@ msa_status_t msa_insert_index_k_mxfp4(const void* k, int32_t src_dtype, int64_t 
  *    allocations, serving loops and harnesses that forbid allocation): exactly
  *    msa_index_score (section 1), same arguments, layouts, results and errors,
  *    except that the scorer's work list lives in a buffer built into the
- *    library instead of a caller workspace.
+ *    library instead of a caller workspace.  (Batches of one request, and of
+ *    at most 64 requests and 128 query blocks, need no work list: their
+ *    scorer plans its work itself and the buffer is not touched.)
  *
  * The built-in buffer holds 1 MiB per GPU (kept until the process ends); a
  * batch whose work list needs more (msa_index_score_workspace_size(vl, H) >
