@@ -128,7 +128,7 @@ constexpr int kRowBytes = kDim * 3 / 2;   // 192 bytes per f12 partial row (chun
 // group of 16 values is stored as 8-bit integer codes with one power-of-two
 // scale, as in the OCP Microscaling MXINT8 format (blocks of 16 here).  With
 // e = floor(log2(max |x|)) - 6, the codes are the nearest integers of x 2^-e,
-// saturated to [-127, 127], and a value decodes as code * 2^e: the error is at
+// saturated to [-128, 127], and a value decodes as code * 2^e: the error is at
 // most 2^e <= max |x| / 64 for a saturated code and 2^(e-1) otherwise, i.e.
 // within 1/127 of the group's largest magnitude.  e = -128 marks a group that
 // held a NaN (it decodes as NaN); smaller scales than 2^-127 are not used.
@@ -136,7 +136,6 @@ constexpr int kRowBytes = kDim * 3 / 2;   // 192 bytes per f12 partial row (chun
 // as two floats, and the 8 group exponents as signed bytes.
 constexpr int kRowBytesI8 = kDim + 16;
 constexpr int kI8Meta = kDim;             // byte offset of (max, sum, exponents)
-constexpr float kI8Magic = 12582912.f;    // 1.5 * 2^23: x + magic keeps rint(x) in its low mantissa bits
 __device__ __forceinline__ int quant16_i8(const float (&x)[16], uint4& q) {
   float amax = 0.f;
 #pragma unroll
@@ -147,16 +146,14 @@ __device__ __forceinline__ int quant16_i8(const float (&x)[16], uint4& q) {
   uint32_t w[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    uint32_t b[4];
+    // x 2^-e + 128 lies in (0, 256); v_cvt_pk_u8_f32 rounds it to the nearest
+    // integer (ties to even), saturates to [0, 255] and writes it as byte i of
+    // the word; flipping bit 7 of each byte turns code + 128 into the
+    // two's-complement code.  (The fma's own rounding is 2^-16 of a step.)
+    uint32_t b = 0u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // x 2^-e + magic rounds once to the nearest integer (ties to even); the
-      // clamp keeps the code within [-127, 127]; its low byte is the code
-      const float f = __builtin_amdgcn_fmed3f(__builtin_fmaf(x[4 * k + i], sc, kI8Magic),
-                                              kI8Magic - 127.f, kI8Magic + 127.f);
-      b[i] = __float_as_uint(f) & 0xFFu;
-    }
-    w[k] = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    for (int i = 0; i < 4; ++i) b = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(x[4 * k + i], sc, 128.f), i, b);
+    w[k] = b ^ 0x80808080u;
   }
   q = make_uint4(w[0], w[1], w[2], w[3]);
   return e;
