@@ -19,15 +19,19 @@
 //   words  -- one block per (request, 32 query slots): sets the bits of those
 //             slots for every row of the request in LDS and writes the word
 //             column out (so the bitmap needs no clearing and no global
-//             atomics); also row_base[b] (page rows of earlier requests) and
-//             the (query, slot) -> CSR row table (-1 for empty slots)
+//             atomics); also row_base[b] (page rows of earlier requests), per
+//             (query, selection head) the mask of slots holding a page's first
+//             listing, and per bitmap word with bits set the first-listing slot
+//             of each of its queries (4 bits each)
 //   count  -- one wave per unit: entries and attention items of the unit, and
 //             per-block totals
 //   (scan) -- large grids only: exclusive prefix sums of the block totals
 //   fill   -- per block: base offsets from the totals of earlier blocks, scan of
 //             its units, then one wave per unit (one lane per bitmap word)
-//             writes q_indices (ascending), each word's first CSR position,
-//             row_ptr and the work items of at most 32 or 64 entries each
+//             writes q_indices (ascending) and beside each entry its split
+//             slot ((query, selection head, slot): where the attention puts the
+//             entry's partial), row_ptr and the work items of at most 32 or 64
+//             entries each
 //             (64 when the rows average at least 64 queries):
 //               {first entry, count, physical page, selection head}
 //               {context - cu_seqlens_q[b] - 128 j, valid tokens of the page, row, request}
@@ -36,9 +40,9 @@
 //   (order) -- rows of >= 512 queries on average only: the items' order for
 //             the attention, sorted by the query range of their piece (a key
 //             the fill writes per item)
-// The CSR position of (query i, slot s) is then the first position of i's word
-// in its row plus the set bits below i in that word; the attention's combine
-// computes it from the row table, the word positions and the bitmap.
+// For the chunked attention (switched off) the words kernel writes the
+// (query, slot) -> CSR row table instead and the fill each word's first CSR
+// position, from which that attention's slot kernel finds the split slots.
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -69,7 +73,11 @@ struct WordsK {
   int32_t* row_base;
   uint32_t* bitmap;
   int64_t words;          // per row
-  int32_t* rowsel;        // [total_q, n_sel, 16]: CSR row of each selected page, or -1
+  int32_t* rowsel;        // chunked attention: [total_q, n_sel, 16] CSR row of each selected
+                          // page, or -1; else null
+  uint32_t* mask;         // else: [total_q, n_sel] slots holding a page's first listing
+  uint4* nib;             // else: [rows, words] first-listing slot of each query bit, 4 bits
+                          // per query slot (words with no bits set are not written)
   int32_t n_chunks;       // blocks per (request, word): ceil(n_sel * max_pages / kWordRows)
   int32_t max_pages;
 };
@@ -85,6 +93,7 @@ __device__ __forceinline__ int request_pages(const int32_t* cu_k, int b, int max
 // rows c * kWordRows .. of the request (g-major: r = g * pages + j).
 __global__ __launch_bounds__(kThreads) void csr_words_kernel(WordsK a) {
   __shared__ uint32_t s_bits[kWordRows];
+  __shared__ __align__(16) uint32_t s_nib[kWordRows][4];
   __shared__ int s_red[kThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t bw = blockIdx.x / a.n_chunks;
@@ -121,10 +130,19 @@ __global__ __launch_bounds__(kThreads) void csr_words_kernel(WordsK a) {
     }
   }
   const int n_r = max(min(kWordRows, rows - r0), 0);
-  for (int k = tid; k < n_r; k += kThreads) s_bits[k] = 0u;
+  for (int k = tid; k < n_r; k += kThreads) {
+    s_bits[k] = 0u;
+    if (!a.rowsel) *reinterpret_cast<uint4*>(s_nib[k]) = make_uint4(0u, 0u, 0u, 0u);
+  }
   __syncthreads();
-  // each selection entry of the block's queries once: its CSR row (the first
-  // row-chunk block writes the (query, slot) -> row table) and its bit
+  // each selection entry of the block's queries once, its bit set in its row.
+  // The 16 slots of one (query, selection head) are one 16-lane row (kThreads
+  // and n_sel * 16 are multiples of 16, and a row's lanes skip or run
+  // together), so a page listed twice is found by comparing with the lanes
+  // below: its first slot is the one the attention writes a split row for.
+  // The first row-chunk block writes the (query, selection head) masks of those
+  // slots (or, for the chunked attention, the (query, slot) -> row table); each
+  // block records the first slot of each of its rows' bits.
   for (int e = tid; e < n_e; e += kThreads) {
     const int ql = e / per_q;
     const int local = 32 * w + ql;
@@ -132,15 +150,27 @@ __global__ __launch_bounds__(kThreads) void csr_words_kernel(WordsK a) {
     const int g = (e % per_q) / kTopK, sl = e % kTopK;
     const int j = a.topk[(int64_t)(q0 + local) * a.tq + (int64_t)g * a.th + sl];
     const bool ok = !(j < 0 || j >= pages || base + j >= a.total_rows);
-    if (c == 0) a.rowsel[(int64_t)(q0 + local) * per_q + e % per_q] = ok ? g * a.total_rows + base + j : -1;
     const int r = g * pages + j - r0;
+    if (a.rowsel) {
+      if (c == 0) a.rowsel[(int64_t)(q0 + local) * per_q + e % per_q] = ok ? g * a.total_rows + base + j : -1;
+    } else {
+      const bool first = ok && first_in_row16(ok ? j : -1);
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(first);
+      if (c == 0 && sl == 0)
+        a.mask[(int64_t)(q0 + local) * a.n_sel + g] = (uint32_t)(bal >> (lane & ~(kTopK - 1))) & 0xFFFFu;
+      if (first && r >= 0 && r < n_r) atomicOr(&s_nib[r][ql >> 3], (uint32_t)sl << (4 * (ql & 7)));
+    }
     if (ok && r >= 0 && r < n_r) atomicOr(&s_bits[r], 1u << ql);
   }
   __syncthreads();
   for (int k = tid; k < n_r; k += kThreads) {
     const int r = r0 + k, g = r / pages, j = r - g * pages;
-    if (base + j < a.total_rows)
-      a.bitmap[((int64_t)g * a.total_rows + base + j) * a.words + w] = s_bits[k];
+    if (base + j < a.total_rows) {
+      const int64_t wi = ((int64_t)g * a.total_rows + base + j) * a.words + w;
+      const uint32_t bits = s_bits[k];
+      a.bitmap[wi] = bits;
+      if (!a.rowsel && bits != 0u) a.nib[wi] = *reinterpret_cast<const uint4*>(s_nib[k]);
+    }
   }
 }
 
@@ -259,7 +289,12 @@ struct FillK {
   int32_t prefixed;
   int32_t* row_ptr;
   int32_t* q_indices;
-  int32_t* wbase;          // [n_rows, words]: CSR position of each word's first entry
+  int32_t* wbase;          // chunked attention: [n_rows, words] CSR position of each word's
+                           // first entry; else null
+  const uint4* nib;        // else: [n_rows, words] first-listing slot of each query bit
+  int32_t* q_slot;         // else: [nnz] split-row entry (query, selection head, slot) of each
+                           // CSR position
+  int32_t n_sel;
   int4* items;
   int64_t max_items;
   Hdr* hdr;
@@ -337,6 +372,7 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
   // in flight during the block scan below
   const int32_t* rbase = lds_req ? s_rb : a.row_base;
   int req_k[kUnitsPerWave], page_k[kUnitsPerWave], phys_k[kUnitsPerWave];
+  uint4 nib_k[kUnitsPerWave];
 #pragma unroll
   for (int k = 0; k < kUnitsPerWave; ++k) {
     const int64_t fw = ((int64_t)blk * kUnitsPerBlock + wave * kUnitsPerWave + k) * kUnitWords + lane;
@@ -346,6 +382,9 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
     req_k[k] = valid ? find_request(rbase, a.batch, rr) : 0;
     page_k[k] = min(max((int)(rr - rbase[req_k[k]]), 0), a.max_pages - 1);
     phys_k[k] = valid ? a.block_table[(int64_t)req_k[k] * a.bt_stride + page_k[k]] : 0;
+    // the words kernel writes slot nibbles only for words with bits set
+    nib_k[k] = make_uint4(0u, 0u, 0u, 0u);
+    if (a.nib && bits[k] != 0u) nib_k[k] = a.nib[fw];
   }
 
   // scan of this block's units (one lane per unit)
@@ -390,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
     const int incl = wave_inclusive_scan(c);
     int pos = s_pos[ku] + incl - c;
     if (valid) {
-      a.wbase[fw] = pos;
+      if (a.wbase) a.wbase[fw] = pos;
       if (word == 0) a.row_ptr[row] = pos;
     }
     // work items of the lane's piece: (row, first entry, count), lane t of the
@@ -403,9 +442,15 @@ __global__ __launch_bounds__(kThreads) void csr_fill_kernel(FillK a) {
     const int p_item = s_item[ku] + __shfl(iincl - it, lead);
     uint32_t x = bits_k;
     const int64_t q_word = cq[b] + word * 32;
+    const uint4 nb = nib_k[k];
     while (__builtin_amdgcn_ballot_w64(x != 0u) != 0) {
       if (x != 0u) {
-        a.q_indices[pos++] = (int32_t)(q_word + __builtin_ctz(x));
+        const int bit = __builtin_ctz(x);
+        const int64_t i = q_word + bit;
+        const uint32_t nw = bit < 16 ? (bit < 8 ? nb.x : nb.y) : (bit < 24 ? nb.z : nb.w);
+        if (a.q_slot)
+          a.q_slot[pos] = (int32_t)((i * a.n_sel + g) * kTopK + ((nw >> (4 * (bit & 7))) & 15u));
+        a.q_indices[pos++] = (int32_t)i;
         x &= x - 1u;
       }
     }
@@ -520,9 +565,19 @@ SchedLayout sched_layout(const msa_varlen_t* vl, int n_sel, int topk) {
   L.okey = off;       off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.max_items), 256);
   L.perm = off;       off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.max_items), 256);
   L.kstart = off;     off += align_up(sizeof(int32_t) * (L.order_keys + 1), 256);
-  L.rowsel = off;     off += align_up(sizeof(int32_t) * std::max<int64_t>(1, L.inv_len), 256);
-  L.wbase = off;      off += align_up(sizeof(int32_t) * L.n_rows * L.words_per_row, 256);
-  L.bitmap = off;     off += align_up(sizeof(uint32_t) * L.n_rows * L.words_per_row, 256);
+  // the chunked attention finds each CSR position's split slot itself, from
+  // the (query, slot) -> row table and the words' first positions; otherwise the
+  // fill writes it (from the words kernel's slot nibbles) with the combine's
+  // first-listing masks
+  const int64_t n_words = L.n_rows * L.words_per_row;
+  const int64_t chunked = L.fused ? 1 : 0;
+  L.rowsel = off;     off += align_up(sizeof(int32_t) * (chunked ? std::max<int64_t>(1, L.inv_len) : 1), 256);
+  L.wbase = off;      off += align_up(sizeof(int32_t) * (chunked ? n_words : 1), 256);
+  L.bitmap = off;     off += align_up(sizeof(uint32_t) * n_words, 256);
+  L.qslot = off;      off += align_up(sizeof(int32_t) * (chunked ? 1 : std::max<int64_t>(1, L.inv_len)), 256);
+  L.smask = off;
+  off += align_up(sizeof(uint32_t) * (chunked ? 1 : std::max<int64_t>(1, (int64_t)vl->total_q * n_sel)), 256);
+  L.nib = off;        off += align_up(16 * (chunked ? 1 : std::max<int64_t>(1, n_words)), 256);
   L.total = off;
   return L;
 }
@@ -534,13 +589,17 @@ hipError_t launch_k2q_csr(const CsrArgs& a, hipStream_t stream) {
   int32_t* blk_tot = reinterpret_cast<int32_t*>(a.sched + L.blk_tot);
   int32_t* blk_items = blk_tot + L.n_blocks;
   int4* items = reinterpret_cast<int4*>(a.sched + L.items);
-  int32_t* rowsel = reinterpret_cast<int32_t*>(a.sched + L.rowsel);
-  int32_t* wbase = reinterpret_cast<int32_t*>(a.sched + L.wbase);
+  const bool chunked = L.fused != 0;
+  int32_t* rowsel = chunked ? reinterpret_cast<int32_t*>(a.sched + L.rowsel) : nullptr;
+  int32_t* wbase = chunked ? reinterpret_cast<int32_t*>(a.sched + L.wbase) : nullptr;
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(a.sched + L.bitmap);
+  int32_t* q_slot = chunked ? nullptr : reinterpret_cast<int32_t*>(a.sched + L.qslot);
+  uint32_t* smask = chunked ? nullptr : reinterpret_cast<uint32_t*>(a.sched + L.smask);
+  uint4* nib = chunked ? nullptr : reinterpret_cast<uint4*>(a.sched + L.nib);
 
   if (a.vl.batch > 0 && L.words_per_row > 0) {
     WordsK wk{a.vl.cu_seqlens_q, a.vl.cu_seqlens_k, a.vl.batch, a.topk, a.tq_stride, a.th_stride,
-              a.n_sel, a.vl.total_rows, row_base, bitmap, L.words_per_row, rowsel,
+              a.n_sel, a.vl.total_rows, row_base, bitmap, L.words_per_row, rowsel, smask, nib,
               (int32_t)L.word_chunks, std::max(a.vl.max_pages, 1)};
     hipLaunchKernelGGL(csr_words_kernel, dim3((unsigned)L.word_blocks), dim3(kThreads), 0, stream,
                        wk);
@@ -558,7 +617,7 @@ hipError_t launch_k2q_csr(const CsrArgs& a, hipStream_t stream) {
   FillK fk{a.vl.cu_seqlens_q, a.vl.cu_seqlens_k, a.vl.batch, a.vl.block_table,
            a.vl.block_table_stride, a.vl.total_rows, row_base, bitmap, L.words_per_row, G,
            n_words, L.n_rows, (int32_t)L.n_blocks, blk_tot, blk_items, prefixed, a.row_ptr,
-           a.q_indices, wbase, items, L.max_items, hdr, L.item_q, L.order_shift,
+           a.q_indices, wbase, nib, q_slot, a.n_sel, items, L.max_items, hdr, L.item_q, L.order_shift,
            reinterpret_cast<int32_t*>(a.sched + L.okey), std::max(a.vl.max_pages, 1)};
   hipLaunchKernelGGL(csr_fill_kernel, dim3((unsigned)L.n_blocks), dim3(kThreads), 0, stream, fk);
   if (L.order_shift > 0)

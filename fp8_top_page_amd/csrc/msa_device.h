@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace msa {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -66,6 +68,18 @@ __device__ __forceinline__ float sum_across_groups(float x) {
   x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// r differs from the values of the lanes 1 .. 15 places down this lane's
+// 16-lane row (row_shr by D + 1; a lane whose source lies before the row start
+// sees -2, which no caller uses as a value).  Every lane of the row must be
+// active.
+template <int... D>
+__device__ __forceinline__ bool first_in_row(int r, std::integer_sequence<int, D...>) {
+  return ((__builtin_amdgcn_update_dpp(-2, r, 0x111 + D, 0xF, 0xF, false) != r) && ...);
+}
+__device__ __forceinline__ bool first_in_row16(int r) {
+  return first_in_row(r, std::make_integer_sequence<int, 15>{});
 }
 
 // A block barrier that orders LDS only: the waves' LDS operations complete,

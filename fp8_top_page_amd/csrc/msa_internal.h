@@ -89,7 +89,8 @@ constexpr bool kChunkedAttention = false;   // off: see sched_layout
 
 struct SchedLayout {
   // byte offsets inside the schedule buffer
-  size_t hdr, row_base, blk_tot, items, okey, perm, kstart, rowsel, wbase, bitmap, total;
+  size_t hdr, row_base, blk_tot, items, okey, perm, kstart, rowsel, wbase, bitmap, qslot, smask,
+      nib, total;
   int32_t fused;          // chunked persistent attention (items in query chunks, see above)
   int32_t piece_words;    // bitmap words per item piece (items never cross one)
   int64_t n_rows;         // n_sel * total_rows

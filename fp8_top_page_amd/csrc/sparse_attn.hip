@@ -708,8 +708,9 @@ __global__ __launch_bounds__(kThreads, kWide ? kBlocksWide : kBlocksNarrow) void
   }
 }
 
-// Split slots of every CSR position, one thread per (query, selection head,
-// slot): the position of (query i, slot s) is the first position of i's bitmap
+// Chunked attention only (the CSR build writes these otherwise).  Split slots
+// of every CSR position, one thread per (query, selection head, slot): the
+// position of (query i, slot s) is the first position of i's bitmap
 // word in the slot's row plus the row's set bits below i in that word.  Writes
 // q_slot[position] = (i * n_sel + head) * 16 + s for the first listing of each
 // selected page, and per (query, selection head) the 16-bit mask of those slots,
@@ -741,14 +742,6 @@ __device__ __forceinline__ int64_t split_entry(int64_t i, int sel, int s, int n_
   return ((slot * kChunkQ + (i & (kChunkQ - 1))) * n_sel + sel) * kTopK + s;
 }
 
-// r differs from the values of the lanes 1 .. 15 places down this lane's
-// 16-lane row (row_shr by D + 1; a lane whose source lies before the row start
-// sees -2, no row index)
-template <int... D>
-__device__ __forceinline__ bool first_in_row(int r, std::integer_sequence<int, D...>) {
-  return ((__builtin_amdgcn_update_dpp(-2, r, 0x111 + D, 0xF, 0xF, false) != r) && ...);
-}
-
 __global__ __launch_bounds__(256) void attn_slot_kernel(SlotK a) {
   // entries number fewer than 2^31 (the call checks total_q * n_sel * 16)
   const int e = (int)blockIdx.x * 256 + (int)threadIdx.x;
@@ -760,7 +753,7 @@ __global__ __launch_bounds__(256) void attn_slot_kernel(SlotK a) {
   // selection head) are one 16-lane row, so the slots below s are the lanes
   // 1 .. s places down the row (row_shr; past the row start the old value, -2,
   // stays)
-  bool ok = in && r >= 0 && first_in_row(r, std::make_integer_sequence<int, kTopK - 1>{});
+  bool ok = in && r >= 0 && first_in_row16(r);
   if (ok) {
     const int qs = e >> 4;                              // query * n_sel + head
     const int64_t i = a.n_sel == 1 ? qs : qs / a.n_sel;
@@ -1132,8 +1125,11 @@ static AttnWs attn_ws(const msa_varlen_t* vl, int Hq, int n_sel, int topk) {
   // that hold their (max, sum) otherwise
   w.o = off;    off += align_up((size_t)(w.rows * (L.fused ? kRowBytes : kRowBytesI8)), 256);
   w.ml = off;   off += L.fused ? align_up((size_t)(w.rows * sizeof(float2)), 256) : 256;
-  w.slot = off; off += align_up((size_t)(std::max<int64_t>(entries, 1) * sizeof(int32_t)), 256);
-  w.mask = off; off += align_up((size_t)(std::max<int64_t>(entries / topk, 1) * sizeof(uint32_t)), 256);
+  // chunked: split slots and masks found by the slot kernel (the CSR build
+  // writes them into the schedule otherwise)
+  const int64_t slots = L.fused ? std::max<int64_t>(entries, 1) : 1;
+  w.slot = off; off += align_up((size_t)(slots * sizeof(int32_t)), 256);
+  w.mask = off; off += align_up((size_t)(std::max<int64_t>(slots / topk, 1) * sizeof(uint32_t)), 256);
   w.queues = off;     off += align_up((size_t)(kQueues * w.qcap * sizeof(int2)), 256);
   w.qlen = off;       off += 256;
   w.qhead = off;      off += 256;
@@ -1159,6 +1155,10 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   uint8_t* wsb = reinterpret_cast<uint8_t*>(a.workspace);
   const int HP = a.Hq / a.n_sel;
 
+  // split slot of each CSR position and the combine's masks: written by the
+  // CSR build, or (chunked) by the slot kernel from its row table
+  const int32_t* q_slot = reinterpret_cast<const int32_t*>(a.sched + L.qslot);
+  const uint32_t* smask = reinterpret_cast<const uint32_t*>(a.sched + L.smask);
   SlotK sk;
   sk.n = (int64_t)a.vl.total_q * a.n_sel * kTopK;
   sk.n_sel = a.n_sel;
@@ -1172,7 +1172,11 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   sk.q_slot = reinterpret_cast<int32_t*>(wsb + ws.slot);
   sk.mask = reinterpret_cast<uint32_t*>(wsb + ws.mask);
   sk.ring = ws.fused;
-  hipLaunchKernelGGL(attn_slot_kernel, dim3((unsigned)ceil_div(sk.n, 256)), dim3(256), 0, stream, sk);
+  if (ws.fused) {
+    hipLaunchKernelGGL(attn_slot_kernel, dim3((unsigned)ceil_div(sk.n, 256)), dim3(256), 0, stream, sk);
+    q_slot = sk.q_slot;
+    smask = sk.mask;
+  }
 
   AttnK k;
   k.q = a.q;
@@ -1187,7 +1191,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   k.num_pages = a.num_pages;
   k.Hkv = a.Hkv;
   k.q_indices = a.q_indices;
-  k.q_slot = sk.q_slot;
+  k.q_slot = q_slot;
   k.items = reinterpret_cast<const int4*>(a.sched + L.items);
   k.perm = L.order_shift > 0 ? reinterpret_cast<const int32_t*>(a.sched + L.perm) : nullptr;
   k.n_items = reinterpret_cast<const int32_t*>(a.sched + L.hdr);
@@ -1268,7 +1272,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t stream) {
   c.G = a.Hq / a.Hkv;
   c.n_sel = a.n_sel;
   c.HP = HP;
-  c.mask = sk.mask;
+  c.mask = smask;
   c.part_o = k.part_o;
   c.part_ml = k.part_ml;
   c.v_scale = a.v_scale;
