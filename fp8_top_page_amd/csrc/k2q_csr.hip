@@ -136,13 +136,17 @@ __global__ __launch_bounds__(kThreads) void csr_words_kernel(WordsK a) {
   }
   __syncthreads();
   // each selection entry of the block's queries once, its bit set in its row.
-  // The 16 slots of one (query, selection head) are one 16-lane row (kThreads
-  // and n_sel * 16 are multiples of 16, and a row's lanes skip or run
-  // together), so a page listed twice is found by comparing with the lanes
-  // below: its first slot is the one the attention writes a split row for.
+  // A page listed twice counts at its first slot (the one the attention writes
+  // a split row for).  Both listings then set the same bit of the same row, so
+  // the bit's old value shows a repeat among the block's rows; the 16 slots of
+  // one (query, selection head) are one 16-lane row (kThreads and n_sel * 16
+  // are multiples of 16, and a row's lanes skip or run together), and a wave
+  // with a repeat, or a block that writes masks without holding all of its
+  // queries' rows, finds the first listings by comparing with the lanes below.
   // The first row-chunk block writes the (query, selection head) masks of those
   // slots (or, for the chunked attention, the (query, slot) -> row table); each
   // block records the first slot of each of its rows' bits.
+  const bool all_rows = c > 0 || a.n_chunks == 1;
   for (int e = tid; e < n_e; e += kThreads) {
     const int ql = e / per_q;
     const int local = 32 * w + ql;
@@ -151,16 +155,20 @@ __global__ __launch_bounds__(kThreads) void csr_words_kernel(WordsK a) {
     const int j = a.topk[(int64_t)(q0 + local) * a.tq + (int64_t)g * a.th + sl];
     const bool ok = !(j < 0 || j >= pages || base + j >= a.total_rows);
     const int r = g * pages + j - r0;
+    const bool here = ok && r >= 0 && r < n_r;
+    uint32_t old = 0u;
+    if (here) old = atomicOr(&s_bits[r], 1u << ql);
     if (a.rowsel) {
       if (c == 0) a.rowsel[(int64_t)(q0 + local) * per_q + e % per_q] = ok ? g * a.total_rows + base + j : -1;
     } else {
-      const bool first = ok && first_in_row16(ok ? j : -1);
+      bool first = ok;
+      if (!all_rows || __builtin_amdgcn_ballot_w64(here && ((old >> ql) & 1u)) != 0)
+        first = ok && first_in_row16(ok ? j : -1);
       const uint64_t bal = __builtin_amdgcn_ballot_w64(first);
       if (c == 0 && sl == 0)
         a.mask[(int64_t)(q0 + local) * a.n_sel + g] = (uint32_t)(bal >> (lane & ~(kTopK - 1))) & 0xFFFFu;
-      if (first && r >= 0 && r < n_r) atomicOr(&s_nib[r][ql >> 3], (uint32_t)sl << (4 * (ql & 7)));
+      if (first && here) atomicOr(&s_nib[r][ql >> 3], (uint32_t)sl << (4 * (ql & 7)));
     }
-    if (ok && r >= 0 && r < n_r) atomicOr(&s_bits[r], 1u << ql);
   }
   __syncthreads();
   for (int k = tid; k < n_r; k += kThreads) {

@@ -443,6 +443,29 @@ def test_page_listed_twice_is_merged_once():
     check_attention(inp, sel[:, 0, :], out, np.arange(inp.total_q))
 
 
+def test_page_listed_twice_over_many_row_chunks():
+    """Repeated pages where one CSR build block cannot hold all of a query's
+    rows: 1,563 pages per selection head (rows in two chunks of 1,024), the
+    local page (in the second chunk) and an older page each listed twice, plus
+    a second request over 700 pages.  CSR bit-exact, attention on every query
+    against the oracle."""
+    from fp8_top_page_amd.pipeline import DeviceBatch, MsaPath
+    inp = _small_inputs((48, 20), (200000, 89600), 1, 16, 2, seed=23)
+    sel = workloads.random_topk(inp, n_sel=2, seed=6)
+    sel[:, 0, 12] = np.where(sel[:, 0, 12] >= 0, sel[:, 0, 0], -1)   # the local page again
+    sel[:, 1, 15] = sel[:, 1, 3]                                      # an older page again
+    sel[:, 1, 7] = np.where(sel[:, 1, 7] >= 0, sel[:, 1, 0], -1)
+    db = DeviceBatch.from_inputs(inp)
+    path = MsaPath(db, n_sel=2)
+    path.topk.copy_(torch.from_numpy(sel))
+    path.csr()
+    path.attend()
+    torch.cuda.synchronize()
+    assert inp.total_rows > 1024                   # the CSR build's rows come in two chunks
+    check_csr(inp, sel, to_np(path.row_ptr), to_np(path.q_indices), n_sel=2)
+    out = to_np(path.out.float()).reshape(inp.total_q, 16, 128)
+    check_attention(inp, sel, out, np.arange(inp.total_q), n_sel=2)
+
 def test_large_csr_grid_random_topk():
     """A CSR large enough that its per-block totals go through the separate
     prefix-scan launch (16384 queries of one request over 4160 pages, plus a
