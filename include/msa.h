@@ -195,9 +195,11 @@ msa_status_t msa_index_score_topk(const msa_varlen_t* vl, const uint8_t* q, int6
  *              (logical pages; negative = empty slot; pages >= the request's page
  *              count are ignored)
  *   schedule   >= msa_k2q_schedule_size(vl, n_sel_heads, topk) bytes, 16-byte
- *              aligned: the attention's work list, written here and read by
- *              msa_sparse_attn_prefill.  Opaque.  It records each row's physical
- *              page as vl->block_table maps it at the time of this call.
+ *              aligned: the attention's work list, each CSR entry's split slot
+ *              and each (query, selection head)'s set of distinct selected pages,
+ *              written here and read by msa_sparse_attn_prefill.  Opaque.  It
+ *              records each row's physical page as vl->block_table maps it at the
+ *              time of this call.
  * ------------------------------------------------------------------------- */
 size_t msa_k2q_schedule_size(const msa_varlen_t* vl, int32_t n_sel_heads, int32_t topk);
 msa_status_t msa_build_k2q_csr(const msa_varlen_t* vl, const int32_t* topk_idx,
