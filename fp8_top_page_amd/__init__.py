@@ -19,6 +19,7 @@ __all__ = [
     "msa_quantize_e4m3", "msa_insert_index_k", "msa_insert_kv", "msa_index_score_mxfp4",
     "msa_insert_index_k_mxfp4", "msa_index_score_noalloc", "msa_index_score_per_head",
     "msa_sparse_attn_prefill_mxfp4", "msa_index_score_topk", "msa_index_score_topk_workspace_size",
+    "msa_check_varlen", "BAD_FLAGS",
     "LIB_PATH", "PAGE", "HEAD_DIM", "TOPK",
 ]
 
@@ -69,6 +70,8 @@ def lib():
         L.msa_build_k2q_csr.argtypes = [vp, _c_p, _c_i64, _c_i64, _c_i32, _c_i32, _c_p, _c_p,
                                         _c_p, _c_size, _c_p]
         L.msa_build_k2q_csr.restype = ctypes.c_int
+        L.msa_check_varlen.argtypes = [vp, _c_i32, _c_p, _c_p]
+        L.msa_check_varlen.restype = ctypes.c_int
         L.msa_sparse_attn_workspace_size.argtypes = [vp, _c_i32, _c_i32, _c_i32, _c_i32]
         L.msa_sparse_attn_workspace_size.restype = _c_size
         L.msa_sparse_attn_prefill.argtypes = [vp, _c_p, _c_i64, _c_i32, _c_p, _c_i32, _c_i32,
@@ -196,6 +199,18 @@ def msa_topk_select(vl: Varlen, scores, topk, n_local, topk_idx, stream=None):
 
 def msa_k2q_schedule_size(vl: Varlen, n_sel_heads: int, topk: int) -> int:
     return int(lib().msa_k2q_schedule_size(vl.ref, n_sel_heads, topk))
+
+
+# flag bits of msa_check_varlen (include/msa.h, MSA_BAD_*)
+BAD_FLAGS = {"cu_q": 1, "cu_k": 2, "max_q": 4, "max_k": 8, "pages": 16, "rows": 32, "block": 64}
+
+
+def msa_check_varlen(vl: Varlen, num_pages, flags, stream=None):
+    """flags: int32 device tensor of at least one element; flags[0] gets the OR of
+    the MSA_BAD_* bits the batch's device metadata violates (0: consistent)."""
+    assert flags.dtype == torch.int32 and flags.is_cuda and flags.numel() >= 1
+    _check(lib().msa_check_varlen(vl.ref, int(num_pages), _ptr(flags), _stream(stream)),
+           "msa_check_varlen")
 
 
 def msa_build_k2q_csr(vl: Varlen, topk_idx, n_sel_heads, topk, row_ptr, q_indices, schedule,

@@ -615,3 +615,80 @@ msa_status_t msa_insert_index_k_mxfp4(const void* k, int32_t src_dtype, int64_t 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Device-side check of a batch's metadata against its host-side sizes: one
+// block; thread b takes request b's bounds, then all threads take each
+// request's block-table entries in turn.  Every read stays inside the arrays
+// the host-side sizes describe (block-table columns below min(pages,
+// max_pages)), whatever the device data holds.
+namespace {
+
+constexpr int kCheckThreads = 1024;
+
+__global__ __launch_bounds__(kCheckThreads) void varlen_check_kernel(msa_varlen_t vl, int32_t num_pages,
+                                                                      int32_t* flags) {
+  __shared__ int s_or[kCheckThreads / 64];
+  __shared__ long long s_rows[kCheckThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int f = 0;
+  long long rows = 0;
+  for (int b = tid; b < vl.batch; b += kCheckThreads) {
+    const int q0 = vl.cu_seqlens_q[b], q1 = vl.cu_seqlens_q[b + 1];
+    const int k0 = vl.cu_seqlens_k[b], k1 = vl.cu_seqlens_k[b + 1];
+    if ((b == 0 && q0 != 0) || q1 < q0 || q1 > vl.total_q) f |= MSA_BAD_CU_Q;
+    if ((b == 0 && k0 != 0) || k1 < k0) f |= MSA_BAD_CU_K;
+    const int sq = q1 - q0, sk = k1 - k0;
+    if (sq > sk) f |= MSA_BAD_CU_K;
+    if (sq > vl.max_seqlen_q) f |= MSA_BAD_MAX_Q;
+    if (sk > vl.max_seqlen_k) f |= MSA_BAD_MAX_K;
+    const long long pages = sk > 0 ? ((long long)sk + kPage - 1) / kPage : 0;
+    if (pages > vl.max_pages) f |= MSA_BAD_PAGES;
+    rows += pages;
+  }
+  if (tid == 0 && vl.cu_seqlens_q[vl.batch] != vl.total_q) f |= MSA_BAD_CU_Q;
+  for (int b = 0; b < vl.batch; ++b) {
+    const int sk = vl.cu_seqlens_k[b + 1] - vl.cu_seqlens_k[b];
+    const int np = sk > 0 ? min((int)(((long long)sk + kPage - 1) / kPage), vl.max_pages) : 0;
+    const int32_t* row = vl.block_table + (int64_t)b * vl.block_table_stride;
+    for (int j = tid; j < np; j += kCheckThreads) {
+      const int p = row[j];
+      if (p < 0 || p >= num_pages) f |= MSA_BAD_BLOCK;
+    }
+  }
+  // block-wide OR of the flags and sum of the page counts
+  for (int o = 32; o > 0; o >>= 1) {
+    f |= __shfl_xor(f, o);
+    rows += __shfl_xor(rows, o);
+  }
+  if (lane == 0) { s_or[wave] = f; s_rows[wave] = rows; }
+  __syncthreads();
+  if (tid == 0) {
+    int all = 0;
+    long long total = 0;
+    for (int k = 0; k < kCheckThreads / 64; ++k) { all |= s_or[k]; total += s_rows[k]; }
+    if (total != vl.total_rows) all |= MSA_BAD_ROWS;
+    flags[0] = all;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status_t msa_check_varlen(const msa_varlen_t* vl, int32_t num_pages, int32_t* flags,
+                              void* stream) {
+  msa_status_t st = check_varlen(vl);
+  if (st != MSA_OK) return st;
+  MSA_CHECK(num_pages >= 1, MSA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1 (got %d)", num_pages);
+  MSA_CHECK(flags != nullptr, MSA_ERR_INVALID_ARGUMENT, "flags is NULL");
+  st = check_device();
+  if (st != MSA_OK) return st;
+  hipLaunchKernelGGL(varlen_check_kernel, dim3(1), dim3(kCheckThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), *vl, num_pages, flags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "msa_check_varlen");
+  return MSA_OK;
+}
+
+}  // extern "C"

@@ -386,6 +386,39 @@ const char* msa_last_error(void);   /* thread-local detail of this thread's last
 int32_t msa_abi_version(void);      /* MSA_ABI_VERSION */
 #define MSA_ABI_VERSION 3
 
+/* ---------------------------------------------------------------------------
+ * 8. Metadata check, for callers whose device metadata may be wrong.  The
+ *    other calls clamp device indices that contradict the host-side sizes so
+ *    that they do not fault, and then give unspecified results; this call
+ *    reports such contradictions instead.  (The batch layout it checks is the
+ *    one the other calls take: [P2] script and [P4] forward, cu_seqlens_q/k,
+ *    block_table, total_kv_blocks.)
+ *
+ * Queues one small kernel on `stream` that writes flags[0] (device int32,
+ * overwritten, not accumulated) with the OR of:
+ *   MSA_BAD_CU_Q   cu_seqlens_q[0] != 0, a decrease, an entry > total_q, or
+ *                  cu_seqlens_q[batch] != total_q
+ *   MSA_BAD_CU_K   cu_seqlens_k[0] != 0, a decrease, or a request with more
+ *                  new tokens than tokens (seqlen_q_b > seqlen_k_b)
+ *   MSA_BAD_MAX_Q  a request with seqlen_q_b > max_seqlen_q
+ *   MSA_BAD_MAX_K  a request with seqlen_k_b > max_seqlen_k
+ *   MSA_BAD_PAGES  a request with more than max_pages pages
+ *   MSA_BAD_ROWS   sum_b ceil(seqlen_k_b / 128) != total_rows
+ *   MSA_BAD_BLOCK  a block_table entry of a used page (j < min(pages_b,
+ *                  max_pages)) outside [0, num_pages)
+ * 0 means the metadata agrees with the host-side sizes.  Reads only inside the
+ * arrays the host-side sizes describe; host-side errors as for the other calls.
+ * ------------------------------------------------------------------------- */
+#define MSA_BAD_CU_Q 1
+#define MSA_BAD_CU_K 2
+#define MSA_BAD_MAX_Q 4
+#define MSA_BAD_MAX_K 8
+#define MSA_BAD_PAGES 16
+#define MSA_BAD_ROWS 32
+#define MSA_BAD_BLOCK 64
+msa_status_t msa_check_varlen(const msa_varlen_t* vl, int32_t num_pages, int32_t* flags,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
         "msa_quantize_e4m3", "msa_insert_index_k", "msa_insert_kv", "msa_index_score_mxfp4",
         "msa_insert_index_k_mxfp4", "msa_index_score_noalloc", "msa_index_score_per_head",
         "msa_sparse_attn_prefill_mxfp4", "msa_index_score_topk",
-        "msa_index_score_topk_workspace_size"]), names
+        "msa_index_score_topk_workspace_size", "msa_check_varlen"]), names
     for n in names:
         assert hasattr(L, n), n
     assert msa.msa_abi_version() == 3
@@ -322,3 +322,16 @@ def test_per_head_scoring_validation():
     assert ph(vl(total_q=0)) == OK
     if NO_GPU:
         assert ph(vl()) == NO_DEV
+
+
+def test_metadata_check_validation():
+    """msa_check_varlen rejects bad host arguments before launching anything;
+    a valid call without a GPU reports the missing device."""
+    L = msa.lib()
+    v = vl()
+    assert L.msa_check_varlen(None, 8, FAKE, None) == INVALID
+    assert L.msa_check_varlen(ctypes.byref(v), 0, FAKE, None) == INVALID
+    assert L.msa_check_varlen(ctypes.byref(v), 8, None, None) == INVALID
+    assert L.msa_check_varlen(ctypes.byref(vl(stride=4)), 8, FAKE, None) == INVALID
+    if NO_GPU:
+        assert L.msa_check_varlen(ctypes.byref(v), 8, FAKE, None) == NO_DEV
